@@ -1,0 +1,64 @@
+"""Pure-Python brute force for tiny paged-decode inputs -- TEST INFRASTRUCTURE.
+
+No numpy arithmetic: values are read element by element, widened to Python
+floats (float64) and combined with ``math.exp`` in plain loops, following the
+walk through the block table described on the devpress.csdn.net/amd vLLM
+walkthrough ("核心代码拆解" section): for each sequence and head, visit the
+logical blocks in order, translate each to its physical block, take the
+scaled dot of q with every K row up to the context length, then softmax and
+the weighted sum of V.  Used only to pin the numpy oracle on small cases.
+"""
+from __future__ import annotations
+
+import math
+import struct
+from typing import List
+
+
+def _value(x, dtype: str) -> float:
+    if dtype == "f32":
+        return float(x)
+    # bfloat16 bits: the high 16 bits of an IEEE binary32
+    return struct.unpack("<f", struct.pack("<I", (int(x) & 0xFFFF) << 16))[0]
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, block_size: int,
+           dtype: str) -> List[List[List[float]]]:
+    S = len(q)
+    Hq = len(q[0])
+    D = len(q[0][0])
+    Hkv = len(k_cache[0][0])
+    G = Hq // Hkv
+    sc = float(scale)
+    out = []
+    for s in range(S):
+        L = int(context_lens[s])
+        rows = []
+        for h in range(Hq):
+            g = h // G
+            scores = []
+            kv_pos = []
+            nblocks = (L + block_size - 1) // block_size
+            for j in range(nblocks):
+                phys = int(block_tables[s][j])
+                for o in range(block_size):
+                    if j * block_size + o >= L:
+                        break
+                    dot = 0.0
+                    for d in range(D):
+                        dot += _value(q[s][h][d], dtype) * _value(k_cache[phys][o][g][d], dtype)
+                    scores.append(sc * dot)
+                    kv_pos.append((phys, o))
+            if not scores:
+                rows.append([0.0] * D)
+                continue
+            m = max(scores)
+            w = [math.exp(x - m) for x in scores]
+            tot = sum(w)
+            acc = [0.0] * D
+            for wi, (phys, o) in zip(w, kv_pos):
+                for d in range(D):
+                    acc[d] += wi * _value(v_cache[phys][o][g][d], dtype)
+            rows.append([a / tot for a in acc])
+        out.append(rows)
+    return out

@@ -1,0 +1,15 @@
+"""Seeded synthetic inputs for paged decode (shared by the oracle tests, the GPU
+tests and the benchmark).
+
+This package draws values and builds index arrays (block tables, context
+lengths, slot mapping, copy pairs); it holds none of the attention arithmetic.
+"""
+from .generate import (  # noqa: F401
+    Case,
+    CONFIG_NAMES,
+    bf16_bits_from_f32,
+    make_case,
+    make_fork_case,
+    make_prefix_case,
+    make_private_case,
+)
