@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark: one paged-decode serving step on one MI355X.
+
+A step is the whole hot path over one batch: the copy-on-write block copies,
+the write of every sequence's new token into the pool, and paged decode
+attention (with its split-K merge).  The default workload is the GQA
+prefix-sharing batch: 256 sequences, lognormal context lengths (median 1024,
+cap 8192), 32 query / 8 KV heads, head_dim 128, 16-token blocks, bf16, each
+group of 16 sequences sharing the physical blocks of a 1024-token prefix.
+Inputs are seeded synthetic data resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is the step's algorithmic HBM bytes (each
+distinct KV slot read once, plus q, out, tables, partials and the edits) per
+second of step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode achieved HBM GB/s (% of peak) and attended KV tokens/s, 1 GPU"
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_386_amd", "csrc", "decode.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_counters.json")
+
+
+# ---------------------------------------------------------------- byte model
+
+def kv_row_bytes(case) -> int:
+    """Bytes of one token's K (or V) row over all KV heads."""
+    return case.num_kv_heads * case.head_dim * (4 if case.dtype == "f32" else 2)
+
+
+def unique_slots(case) -> int:
+    """Distinct (physical block, offset) pairs decode reads: a slot shared by
+    several sequences (a prefix block) counts once."""
+    import numpy as np
+    B = case.block_size
+    ids = []
+    for s, L in enumerate(case.context_lens.tolist()):
+        pos = np.arange(L, dtype=np.int64)
+        ids.append(case.block_tables[s, pos // B].astype(np.int64) * B + pos % B)
+    return int(np.unique(np.concatenate(ids)).size) if ids else 0
+
+
+def decode_bytes(case, num_partitions: int, partition_size: int, unique: bool) -> int:
+    """Algorithmic bytes of one decode call: K and V rows (each distinct slot
+    once when ``unique``, else once per attending sequence), q, out, the used
+    block-table entries, context lengths and, for split sequences, the
+    partition partials written by decode and read by the merge."""
+    import numpy as np
+    L = case.context_lens.astype(np.int64)
+    S, Hq, D, B = case.num_seqs, case.num_q_heads, case.head_dim, case.block_size
+    el = 4 if case.dtype == "f32" else 2
+    slots = unique_slots(case) if unique else int(L.sum())
+    kv = 2 * slots * kv_row_bytes(case)
+    qo = S * Hq * D * (el + 4)
+    tables = int(((L + B - 1) // B).sum()) * 4 + S * 4
+    partials = 0
+    if num_partitions > 1:
+        n = np.minimum((L + partition_size - 1) // partition_size, num_partitions)
+        split = n[n > 1].sum()
+        partials = 2 * int(split) * Hq * (D + 2) * 4
+    return kv + qo + tables + partials
+
+
+def edit_bytes(case) -> int:
+    """Algorithmic bytes of the step's cache edits: each copied block read and
+    written in K and V; each new token's K and V rows read and written."""
+    if not case.has_step:
+        return 0
+    blk = case.block_size * kv_row_bytes(case)
+    copies = 2 * 2 * blk * len(case.copy_pairs)
+    T = len(case.slot_mapping)
+    writes = 2 * 2 * kv_row_bytes(case) * T + 4 * T + 8 * len(case.copy_pairs)
+    return copies + writes
+
+
+# ---------------------------------------------------------------- helpers
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Measured HBM bytes per decode launch from the committed counter runs,
+    or None when absent or taken on a different decode kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("decode_src_sha256_16") != source_hash(DECODE_SRC):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def to_dev(a, dev):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the oracle (single thread) on the same workload: the step's edits
+    and decode for as many sequences as fit the time budget (all of them for
+    the default workload)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import oracle as O
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kc, vc = case.k_cache, case.v_cache
+        if case.has_step:
+            kc, vc = O.copy_blocks(case.copy_pairs, kc, vc)
+            kc, vc = O.kv_cache_write(case.k_new, case.v_new, case.slot_mapping, kc, vc,
+                                      case.block_size)
+        t_edit = time.perf_counter() - t0
+        done = 0
+        t_dec = 0.0
+        for s in range(case.num_seqs):
+            t1 = time.perf_counter()
+            O.paged_attention_decode(case.q[s:s + 1], kc, vc, case.block_tables[s:s + 1],
+                                     case.context_lens[s:s + 1], case.scale, case.block_size,
+                                     case.dtype)
+            t_dec += time.perf_counter() - t1
+            done += 1
+            if t_edit + t_dec > budget_s:
+                break
+    frac = done / case.num_seqs
+    tokens = int(case.context_lens[:done].sum())
+    # scale the oracle's time to the whole step (edits once, decode pro rata)
+    est_step = t_edit + t_dec / max(frac, 1e-9)
+    return {
+        "seconds": t_edit + t_dec,
+        "est_step_seconds": est_step,
+        "seqs": done,
+        "tokens": tokens,
+        "tokens_per_s": tokens / t_dec if t_dec > 0 else None,
+    }
+
+
+# ---------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4],
+                    help="workload (default 2: the GQA prefix-sharing batch)")
+    ap.add_argument("--block-size", type=int, default=None, help="config 3 only: 512 or 16")
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="split-K partition in tokens (0 = library policy, -1 = never)")
+    ap.add_argument("--cpu-budget", type=float, default=25.0,
+                    help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the paged-decode "
+              "path has no cross-GPU exchange in this build", file=sys.stderr)
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_386_amd as pa
+    from workloads import make_case
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pa.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    case = make_case(args.config, poison=False, block_size=args.block_size)
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] workload {case.name}: {case.description}; generated in {t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+
+    q = to_dev(case.q, dev)
+    kc = to_dev(case.k_cache, dev)
+    vc = to_dev(case.v_cache, dev)
+    tables = torch.from_numpy(case.block_tables).to(dev)
+    lens = torch.from_numpy(case.context_lens).to(dev)
+    out = torch.empty(case.q.shape, dtype=torch.float32, device=dev)
+    has_step = case.has_step
+    if has_step:
+        pairs = torch.from_numpy(case.copy_pairs).to(dev)
+        slots = torch.from_numpy(case.slot_mapping).to(dev)
+        k_new = to_dev(case.k_new, dev)
+        v_new = to_dev(case.v_new, dev)
+    max_ctx = case.max_context_len
+    S, Hq, Hkv, D = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
+    P = pa.num_partitions(S, Hkv, max_ctx, args.partition_size)
+    ws_bytes = pa.workspace_size(S, Hq, Hkv, D, max_ctx, args.partition_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ps = args.partition_size if args.partition_size > 0 else (512 if P > 1 else 0)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if has_step:
+            pa.copy_blocks(pairs, kc, vc, stream=stream)
+            pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
+        pa.paged_attention_decode(q, kc, vc, tables, lens, float(case.scale), out,
+                                  max_context_len=max_ctx, partition_size=args.partition_size,
+                                  workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        if has_step:
+            pa.copy_blocks(pairs, kc, vc, stream=stream)
+            pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
+        ev[i][0].record(stream)
+        pa.paged_attention_decode(q, kc, vc, tables, lens, float(case.scale), out,
+                                  max_context_len=max_ctx, partition_size=args.partition_size,
+                                  workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    dec_us = float(dec_ms.mean() * 1e3)
+
+    dec_unique = decode_bytes(case, P, ps, unique=True)
+    dec_attended = decode_bytes(case, P, ps, unique=False)
+    step_bytes = dec_unique + edit_bytes(case)
+    tokens = int(case.context_lens.astype(np.int64).sum())
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_unique / (dec_us * 1e-6) / 1e9
+    workload = f"cfg{args.config}" + (f"-B{case.block_size}" if args.config == 3 else "")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V; lengths, prefix groups and forks as described)",
+        "config": {
+            "workload": f"{workload}: {case.description}",
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "block_size": case.block_size, "max_context_len": max_ctx,
+            "total_context_tokens": tokens, "unique_kv_slots": unique_slots(case),
+            "copy_pairs": int(len(case.copy_pairs)), "new_tokens": int(len(case.slot_mapping)),
+            "partition_size": ps if P > 1 else None, "num_partitions": P,
+            "step": ("copy_blocks + kv_cache_write + " if has_step else "") +
+                    "paged_attention_decode (+ split-K merge)",
+        },
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 2),
+        "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "decode_us": round(dec_us, 2),
+        "decode_attended_gbps": round(dec_attended / (dec_us * 1e-6) / 1e9, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode (decode + merge launches)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes_per_launch": dec_unique,
+            "traffic": load_traffic(workload),
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline and rank == 0:
+        from threadpoolctl import threadpool_info  # noqa: F401
+        cb = cpu_baseline(case, args.cpu_budget)
+        cpu_value = step_bytes / cb["est_step_seconds"] / 1e9
+        rec["cpu_baseline"] = {
+            "value": round(cpu_value, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, one thread: the step's edits plus decode of "
+                       f"{cb['seqs']}/{S} sequences ({cb['tokens']} context tokens) in "
+                       f"{cb['seconds']:.1f}s; value scales the decode time to all {S} "
+                       f"sequences and uses the same byte count as `value`"),
+            "tokens_per_s": round(cb["tokens_per_s"], 1) if cb["tokens_per_s"] else None,
+        }
+    if rank == 0:
+        print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,182 @@
+/*
+ * libpagedattn -- PagedAttention decode and its KV-cache edits for AMD Instinct
+ * MI355X (gfx950), behind a plain C ABI.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [P1] "vLLM 深度拆解：当大模型推理学会「分页注意力」——PagedAttention、连续批处理与
+ *       V1 引擎如何重写 GPU 推理服务的心智模型" (chenxutan.com/d/4834.html)
+ *  [P2] "vLLM为何成为大模型推理的事实标准？技术拆解来了"
+ *       (devpress.csdn.net/awstech/6a9264832b83d06f0ec8e065.html)
+ *  [P3] the vLLM PagedAttention walkthrough at
+ *       devpress.csdn.net/amd/6a31086710ee7a33f27dd05a.html
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" point to GPU memory on the current HIP device;
+ *    the caller owns every buffer.  The library never allocates, frees or keeps
+ *    a pointer after the call returns, and holds no mutable global state.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously on it; nothing is synchronised.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    negative pa_status is returned on bad arguments (nothing is enqueued) or
+ *    when the launch itself fails.  Nothing aborts, prints or throws.
+ *  - Index contents on the device (block ids, slots, context lengths) are not
+ *    validated on the host.  The kernels clamp or skip out-of-range values so
+ *    that they never read or write outside the buffers described by the sizes
+ *    passed in; the numbers produced for such inputs are unspecified.
+ *
+ * KV pool layout (one layer): k_cache and v_cache are each
+ *   [num_blocks][block_size][num_kv_heads][head_dim], head_dim contiguous,
+ * so one token's row for one KV head is head_dim contiguous elements and one
+ * token's rows for all KV heads are num_kv_heads*head_dim contiguous elements.
+ * The slot of logical position t of a sequence whose block table row is `tbl`
+ * is tbl[t / block_size] * block_size + t % block_size ([P1] section 2.1 block
+ * table; [P1] section 3.3 append into the current block until it is full).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes */
+  PA_ERR_DTYPE = -3,       /* unknown dtype code */
+  PA_ERR_UNSUPPORTED = -4, /* valid but not compiled in (head_dim, group size) */
+  PA_ERR_WORKSPACE = -5,   /* split-K workspace missing or too small */
+  PA_ERR_ALIAS = -6,       /* copy pairs overlap (checked only when requested) */
+  PA_ERR_LAUNCH = -7       /* the HIP runtime refused the launch */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,  /* IEEE binary32 */
+  PA_BF16 = 1  /* bfloat16 (the high half of a binary32), stored as 16-bit words */
+} pa_dtype;
+
+/*
+ * paged_attention_decode -- one decode step of attention over a paged KV pool.
+ *
+ * For every sequence s and query head h, with G = num_q_heads / num_kv_heads,
+ * g = h / G and L = context_lens[s]:
+ *   K_t, V_t = rows of KV head g at the slots of positions t = 0 .. L-1
+ *   x_t      = scale * dot(q[s][h], K_t)
+ *   out[s][h] = sum_t exp(x_t - max x) V_t / sum_t exp(x_t - max x)
+ * ([P3] section "核心代码拆解": translate each logical block through the block
+ * table, read K, take the scaled dot with q, then softmax and the weighted sum
+ * of V; [P1] section 2.1 block table; [P1] section 2.3 decode reads the whole
+ * KV cache per generated token).  L = 0 gives zeros.  Arithmetic is fp32 with
+ * an online (running-maximum) softmax; bf16 inputs are read exactly.
+ *
+ *   q              device, [num_seqs][num_q_heads][head_dim], dtype
+ *   k_cache,
+ *   v_cache        device, the pool described above, dtype
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                  ceil(L/block_size) are never read
+ *   context_lens   device int32 [num_seqs]; must not exceed max_context_len
+ *   scale          softmax scale applied to the dot product (e.g. 1/sqrt(d))
+ *   out            device float32 [num_seqs][num_q_heads][head_dim]; written
+ *                  for every (s, h); must not alias an input
+ *   max_context_len host upper bound of context_lens (sizes the launch);
+ *                  must be <= max_blocks_per_seq * block_size
+ *   dtype          element type of q, k_cache and v_cache
+ *   partition_size split-K partition in tokens: 0 = automatic, negative = never
+ *                  split, positive = that many tokens (a multiple of 16).  With
+ *                  more than one partition, per-partition (max, sum, output)
+ *                  partials go to the workspace and a second kernel merges them
+ *                  in ascending partition order.
+ *   workspace      device scratch of workspace_bytes bytes, at least
+ *                  paged_attention_workspace_size(...) for the same arguments;
+ *                  may be NULL when that size is 0.  Its contents on entry do
+ *                  not matter; it must not be used by other work in flight.
+ *
+ * Supported: head_dim 64 or 128; G in {1, 2, 4, 8}; block_size a power of two
+ * in [1, 1024]; num_blocks * block_size < 2^31.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
+ * PA_ERR_WORKSPACE, PA_ERR_LAUNCH.
+ */
+int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               float scale, float *out,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int32_t dtype, int32_t partition_size,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace paged_attention_decode needs for these arguments (0 when
+ * the call will not split).  Returns 0 for arguments decode would reject.
+ */
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len, int32_t partition_size);
+
+/*
+ * The number of split-K partitions decode will use for these arguments
+ * (1 = no split), or a negative pa_status for a partition_size decode rejects.
+ */
+int32_t paged_attention_num_partitions(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t partition_size);
+
+/*
+ * kv_cache_write -- store each new token's K and V rows in the pool.
+ *
+ * For i in [0, num_tokens) with slot = slot_mapping[i] >= 0: copies
+ * k[i] and v[i] (num_kv_heads*head_dim elements each) to block
+ * slot / block_size, offset slot % block_size of k_cache and v_cache, bit for
+ * bit ([P1] section 3.1: the generated token's K/V is written back to the
+ * cache; section 3.3 append_slot).  Negative slots are skipped (padding);
+ * slots >= num_blocks*block_size are skipped too.  Two tokens must not share a
+ * slot (the winner would be unspecified).
+ *
+ *   k, v           device, [num_tokens][num_kv_heads][head_dim], dtype
+ *   slot_mapping   device int32 [num_tokens]
+ *   k_cache,
+ *   v_cache        device pool (layout above), modified in place
+ * head_dim must be a multiple of 8.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH.
+ */
+int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
+                       int32_t num_tokens, void *k_cache, void *v_cache,
+                       int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t dtype, void *stream);
+
+/*
+ * copy_blocks -- copy-on-write block copies.
+ *
+ * For each pair i, copies physical block src = pairs[2i] onto dst = pairs[2i+1]
+ * in both k_cache and v_cache (block_size*num_kv_heads*head_dim elements each),
+ * bit for bit ([P3] section "关键设计二：Copy-on-Write": a shared last block is
+ * copied into a new block before the forked sequence appends to it).
+ * Semantics are those of applying the pairs in list order; the pairs run
+ * concurrently, so every dst must be distinct and no dst may also be a src
+ * (checked on the host, reading the pairs from host memory, only when
+ * host_pairs is non-NULL: PA_ERR_ALIAS).  Pairs with an id outside
+ * [0, num_blocks) or src == dst are skipped.
+ *
+ *   src_dst_pairs  device int32 [num_pairs][2]
+ *   host_pairs     optional host copy of the same pairs for the alias check
+ * head_dim must be a multiple of 8.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIAS, PA_ERR_LAUNCH.
+ */
+int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cache,
+                    void *v_cache, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                    const int32_t *host_pairs, void *stream);
+
+/* A static English description of a pa_status value. */
+const char *pagedattn_status_string(int32_t status);
+
+/* Library version string, e.g. "libpagedattn 0.1 gfx950". */
+const char *pagedattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,17 @@
+"""libpagedattn: PagedAttention decode, KV-cache write and copy-on-write block
+copy as hand-written HIP kernels for gfx950 (MI355X), behind a C ABI.
+
+The Python names mirror the C entry points in ``include/pagedattn.h``; they
+only marshal arguments (torch supplies device memory and the stream).
+"""
+from ._lib import (  # noqa: F401
+    PA_BF16,
+    PA_F32,
+    PagedAttnError,
+    copy_blocks,
+    kv_cache_write,
+    lib,
+    num_partitions,
+    paged_attention_decode,
+    workspace_size,
+)

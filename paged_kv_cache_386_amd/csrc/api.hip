@@ -1,0 +1,216 @@
+// The C ABI of libpagedattn: argument validation, the split-K partition
+// policy, workspace sizing, status strings and the kernel launches.  All
+// entry points are declared (and their contracts described) in
+// include/pagedattn.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <new>
+
+#include "internal.h"
+#include "pagedattn.h"
+
+namespace {
+
+constexpr int32_t kChunkTokens = 16;
+constexpr int32_t kAutoPartition = 512;
+constexpr int64_t kMaxTokensPerSeq = int64_t(1) << 30;
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2_exact(int64_t x) {
+  int n = 0;
+  while ((int64_t(1) << n) < x) ++n;
+  return n;
+}
+
+int64_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+bool known_dtype(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+
+// Partition policy.  Returns the number of partitions (>= 1) and the partition
+// size through *ps, or a negative pa_status.
+//   partition_size < 0: never split;
+//   partition_size > 0: that many tokens, a multiple of the 16-token chunk;
+//   partition_size == 0: split contexts longer than 512 tokens into 512-token
+//     partitions, which keeps every workgroup's share of the sequence short
+//     enough that long and short sequences balance over the 256 CUs.
+int32_t resolve_partitions(int32_t max_context_len, int32_t partition_size, int32_t *ps) {
+  if (max_context_len < 0) return PA_ERR_SHAPE;
+  int32_t want = partition_size;
+  if (want == 0) want = max_context_len > kAutoPartition ? kAutoPartition : -1;
+  if (want > 0 && want % kChunkTokens != 0) return PA_ERR_SHAPE;
+  if (want < 0 || max_context_len <= want) {
+    *ps = want > 0 ? want : kChunkTokens;
+    return 1;
+  }
+  *ps = want;
+  return (int32_t)(((int64_t)max_context_len + want - 1) / want);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pagedattn_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case PA_ERR_DTYPE: return "unknown dtype";
+    case PA_ERR_UNSUPPORTED: return "head_dim or query-group size not compiled in";
+    case PA_ERR_WORKSPACE: return "split-K workspace missing or too small";
+    case PA_ERR_ALIAS: return "copy pairs overlap (a dst repeats or is also a src)";
+    case PA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    default: return "unknown status";
+  }
+}
+
+const char *pagedattn_version(void) { return "libpagedattn 0.1 gfx950"; }
+
+int32_t paged_attention_num_partitions(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t partition_size) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  int32_t ps = 0;
+  return resolve_partitions(max_context_len, partition_size, &ps);
+}
+
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  int32_t ps = 0;
+  const int32_t P = resolve_partitions(max_context_len, partition_size, &ps);
+  (void)num_kv_heads;
+  if (P <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
+}
+
+int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               float scale, float *out, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int32_t dtype, int32_t partition_size,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  if (!known_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+  if (!pa::decode_supported(dtype, head_dim, num_q_heads / num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+
+  int32_t ps = 0;
+  const int32_t P = resolve_partitions(max_context_len, partition_size, &ps);
+  if (P < 0) return P;
+  if ((int64_t)num_seqs * num_kv_heads * P >= (int64_t(1) << 32)) return PA_ERR_SHAPE;
+  if ((int64_t)num_seqs * num_q_heads >= (int64_t(1) << 32)) return PA_ERR_SHAPE;
+
+  pa::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws_o = nullptr;
+  a.ws_ml = nullptr;
+  a.scale = scale;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.log2_block_size = log2_exact(block_size);
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_partitions = P;
+  a.dtype = dtype;
+  if (P > 1) {
+    const size_t need = (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    a.ws_o = static_cast<float *>(workspace);
+    a.ws_ml = a.ws_o + (size_t)num_seqs * num_q_heads * P * head_dim;
+    a.partition_size = ps;
+  } else {
+    // one partition covers any context the kernel will accept after clamping
+    a.partition_size = (int32_t)((int64_t)max_blocks_per_seq * block_size);
+  }
+  const hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
+                       int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t dtype, void *stream) {
+  if (!known_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      head_dim % 8 != 0)
+    return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
+  if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
+  if (row_bytes / 16 > (int64_t)128 * 65535) return PA_ERR_SHAPE;
+  const hipError_t e =
+      pa::launch_kv_cache_write(k, v, slot_mapping, num_tokens, k_cache, v_cache,
+                                (int64_t)num_blocks * block_size, row_bytes,
+                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cache,
+                    void *v_cache, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                    const int32_t *host_pairs, void *stream) {
+  if (!known_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      head_dim % 8 != 0)
+    return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
+  if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst_pairs || !k_cache || !v_cache) return PA_ERR_NULL;
+  if (host_pairs) {
+    // every dst distinct and never a src: then the pairs commute and may run
+    // concurrently.  Ids outside the pool are skipped by the kernel and
+    // ignored here.
+    bool *is_dst = new (std::nothrow) bool[(size_t)num_blocks]();
+    bool *is_src = new (std::nothrow) bool[(size_t)num_blocks]();
+    int32_t status = PA_OK;
+    if (!is_dst || !is_src) {
+      status = PA_ERR_SHAPE;
+    } else {
+      for (int32_t i = 0; i < num_pairs && status == PA_OK; ++i) {
+        const int32_t s = host_pairs[2 * i], d = host_pairs[2 * i + 1];
+        if (s >= 0 && s < num_blocks && d >= 0 && d < num_blocks && s != d) {
+          if (is_dst[d]) status = PA_ERR_ALIAS;
+          is_dst[d] = true;
+          is_src[s] = true;
+        }
+      }
+      for (int32_t b = 0; b < num_blocks && status == PA_OK; ++b)
+        if (is_dst[b] && is_src[b]) status = PA_ERR_ALIAS;
+    }
+    delete[] is_dst;
+    delete[] is_src;
+    if (status != PA_OK) return status;
+  }
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes(dtype);
+  const hipError_t e = pa::launch_copy_blocks(src_dst_pairs, num_pairs, k_cache, v_cache,
+                                              num_blocks, block_bytes,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

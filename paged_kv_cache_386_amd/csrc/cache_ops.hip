@@ -1,0 +1,99 @@
+// KV-cache edits of a decode step, for gfx950:
+//
+//  * kv_cache_write: each new token's K and V rows (all KV heads, one
+//    contiguous row of num_kv_heads*head_dim elements in the pool layout) are
+//    stored at its slot ("3.1" and "3.3" sections of the chenxutan.com vLLM
+//    deep-dive: the generated token's K/V goes back into the cache, appended
+//    into the sequence's current block);
+//  * copy_blocks: whole physical blocks copied onto others, the copy-on-write
+//    step taken before a forked sequence appends to a shared block
+//    ("关键设计二：Copy-on-Write" section of the devpress.csdn.net/amd vLLM
+//    walkthrough).
+//
+// Both move raw bits with 16-byte vector loads and stores (NaN payloads and
+// signed zeros survive), and both skip indices outside the pool so a bad index
+// can never touch memory outside it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace pa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWriteThreads = 128;
+constexpr int kCopyThreads = 256;
+constexpr int kCopyVecsPerThread = 4;
+
+// grid.x = token, grid.y = stripe of the row; a row is row_vecs 16-byte vectors.
+__global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(
+    const u32x4 *__restrict__ k, const u32x4 *__restrict__ v,
+    const int32_t *__restrict__ slot_mapping, u32x4 *__restrict__ kc, u32x4 *__restrict__ vc,
+    int64_t num_slots, int64_t row_vecs) {
+  const int64_t i = blockIdx.x;
+  const int64_t j = (int64_t)blockIdx.y * kWriteThreads + threadIdx.x;
+  if (j >= row_vecs) return;
+  const int32_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const u32x4 kx = k[i * row_vecs + j];
+  const u32x4 vx = v[i * row_vecs + j];
+  kc[(int64_t)slot * row_vecs + j] = kx;
+  vc[(int64_t)slot * row_vecs + j] = vx;
+}
+
+// grid.x = pair, grid.y = stripe of kCopyThreads*kCopyVecsPerThread vectors of
+// the block, grid.z = 0 for K, 1 for V.
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    const int32_t *__restrict__ pairs, u32x4 *__restrict__ kc, u32x4 *__restrict__ vc,
+    int32_t num_blocks, int64_t block_vecs) {
+  const int32_t src = pairs[2 * blockIdx.x];
+  const int32_t dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  u32x4 *cache = blockIdx.z == 0 ? kc : vc;
+  const u32x4 *s = cache + (int64_t)src * block_vecs;
+  u32x4 *d = cache + (int64_t)dst * block_vecs;
+  const int64_t base = (int64_t)blockIdx.y * kCopyThreads * kCopyVecsPerThread + threadIdx.x;
+  u32x4 tmp[kCopyVecsPerThread];
+#pragma unroll
+  for (int u = 0; u < kCopyVecsPerThread; ++u) {
+    const int64_t j = base + (int64_t)u * kCopyThreads;
+    if (j < block_vecs) tmp[u] = s[j];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyVecsPerThread; ++u) {
+    const int64_t j = base + (int64_t)u * kCopyThreads;
+    if (j < block_vecs) d[j] = tmp[u];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
+                                 int32_t num_tokens, void *k_cache, void *v_cache,
+                                 int64_t num_slots, int64_t row_bytes, hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  const int64_t row_vecs = row_bytes / 16;
+  const int64_t stripes = (row_vecs + kWriteThreads - 1) / kWriteThreads;
+  hipLaunchKernelGGL(kv_cache_write_kernel, dim3((uint32_t)num_tokens, (uint32_t)stripes),
+                     dim3(kWriteThreads), 0, stream, static_cast<const u32x4 *>(k),
+                     static_cast<const u32x4 *>(v), slot_mapping, static_cast<u32x4 *>(k_cache),
+                     static_cast<u32x4 *>(v_cache), num_slots, row_vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const int32_t *pairs, int32_t num_pairs, void *k_cache,
+                              void *v_cache, int32_t num_blocks, int64_t block_bytes,
+                              hipStream_t stream) {
+  if (num_pairs <= 0) return hipSuccess;
+  const int64_t block_vecs = block_bytes / 16;
+  const int64_t per = (int64_t)kCopyThreads * kCopyVecsPerThread;
+  const int64_t stripes = (block_vecs + per - 1) / per;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)num_pairs, (uint32_t)stripes, 2),
+                     dim3(kCopyThreads), 0, stream, pairs, static_cast<u32x4 *>(k_cache),
+                     static_cast<u32x4 *>(v_cache), num_blocks, block_vecs);
+  return hipGetLastError();
+}
+
+}  // namespace pa

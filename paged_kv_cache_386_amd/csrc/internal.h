@@ -1,0 +1,42 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  float *out;
+  float *ws_o;   // [S][Hq][P][D] normalised partition outputs (P > 1 only)
+  float *ws_ml;  // [S][Hq][P][2] partition (max, sum) in the log2 domain (P > 1 only)
+  float scale;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int32_t log2_block_size, num_blocks, max_blocks_per_seq;
+  int32_t partition_size;  // tokens per partition (>= every context when P == 1)
+  int32_t num_partitions;  // P
+  int32_t dtype;           // 0 = f32, 1 = bf16
+};
+
+// Enqueues decode (and the partition merge when P > 1).  Returns hipSuccess or
+// the launch error; hipErrorNotSupported when no kernel is compiled for the
+// (dtype, head_dim, group) combination.
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group);
+
+hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
+                                 int32_t num_tokens, void *k_cache, void *v_cache,
+                                 int64_t num_slots, int64_t row_bytes, hipStream_t stream);
+
+hipError_t launch_copy_blocks(const int32_t *pairs, int32_t num_pairs, void *k_cache,
+                              void *v_cache, int32_t num_blocks, int64_t block_bytes,
+                              hipStream_t stream);
+
+}  // namespace pa

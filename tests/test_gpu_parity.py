@@ -1,0 +1,208 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Element-by-element at sizes the oracle finishes in seconds (several 16-token
+chunks, several workgroup partitions and a ragged tail), and on sampled
+(sequence, head) rows at the five named workloads' full sizes, run in the
+launch configuration the benchmark times.  Cache edits are compared bit for
+bit over the whole pool.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from workloads import make_case, make_fork_case, make_prefix_case, make_private_case
+from workloads.generate import permute_pool
+
+from gpu_helpers import TOL, DeviceCase, bits, host_bits, max_err, oracle_step, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_386_amd as pa
+    pa.lib()  # fail loudly if the library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def full_oracle(case):
+    kc, vc = oracle_step(case)
+    return O.paged_attention_decode(case.q, kc, vc, case.block_tables, case.context_lens,
+                                    case.scale, case.block_size, case.dtype), kc, vc
+
+
+def run_and_compare(case, name, partition_size=0, check_pool=True):
+    say(f"{name}: S={case.num_seqs} Hq={case.num_q_heads} Hkv={case.num_kv_heads} "
+        f"D={case.head_dim} B={case.block_size} {case.dtype} max_ctx={case.max_context_len} "
+        f"ps={partition_size} step={case.has_step}")
+    dc = DeviceCase(case)
+    out = dc.run_step(partition_size).cpu().numpy()
+    torch.cuda.synchronize()
+    ref, kc, vc = full_oracle(case)
+    err = max_err(out, ref)
+    assert err <= TOL[case.dtype], f"{name}: max abs err {err}"
+    if check_pool and case.has_step:
+        assert np.array_equal(bits(dc.k_cache), host_bits(kc))
+        assert np.array_equal(bits(dc.v_cache), host_bits(vc))
+    return out, ref, dc
+
+
+# ---------------------------------------------------------------- config 0
+
+@pytest.mark.parametrize("ps", [0, -1, 16, 32, 48])
+def test_config0_fp32_all_outputs(ps):
+    out, ref, _ = run_and_compare(make_case(0), "cfg0", ps)
+    # one-token sequence returns its V row exactly
+    c = make_case(0)
+    v = c.v_cache[c.block_tables[0, 0], 0]  # [Hkv, D]
+    assert np.array_equal(out[0], v.astype(np.float32))
+
+
+# ---------------------------------------------------------------- shapes
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G,Hkv", [(1, 3), (2, 2), (4, 2), (8, 1)])
+def test_shapes_all_outputs(dtype, D, G, Hkv):
+    lens = [1, 15, 16, 17, 63, 64, 65, 200, 513, 1030]
+    c = make_private_case(f"shape-{dtype}-{D}-{G}", lens, G * Hkv, Hkv, D, 16, dtype,
+                          100 + D + G)
+    for ps in (0, -1, 64):
+        run_and_compare(c, c.name, ps)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64, 512, 1024])
+def test_block_sizes(B):
+    lens = [1, 3, 17, 100, 257, 700]
+    c = make_private_case(f"B{B}", lens, 8, 2, 128, B, "bf16", 7 + B)
+    for ps in (0, -1, 32):
+        run_and_compare(c, c.name, ps)
+
+
+def test_empty_and_tiny_contexts():
+    c = make_private_case("empty", [0, 1, 0, 2, 5], 4, 2, 64, 16, "bf16", 3)
+    out, ref, _ = run_and_compare(c, "empty", 16)
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+
+
+# ---------------------------------------------------------------- step structures
+
+@pytest.mark.parametrize("B", [4, 16])
+def test_prefix_step_small(B):
+    rng = np.random.default_rng(21)
+    lens = np.clip(np.rint(rng.lognormal(np.log(256), 1.0, 48)), 1, 2048).astype(int)
+    c = make_prefix_case(f"prefix-B{B}", lens, 16, 256, 32, 8, 128, B, "bf16", 21)
+    assert len(c.copy_pairs) > 0
+    for ps in (0, 128):
+        run_and_compare(c, c.name, ps)
+
+
+def test_fork_step_small():
+    rng = np.random.default_rng(22)
+    lens = rng.integers(16, 700, size=40)
+    c = make_fork_case("fork", lens, 4, 4, 32, 8, 128, 16, "bf16", 22)
+    run_and_compare(c, c.name, 0)
+
+
+def test_longctx_small_both_block_sizes():
+    outs = []
+    for B in (512, 16):
+        c = make_private_case(f"long-B{B}", [4096, 4096], 64, 8, 128, B, "bf16", 33,
+                              max_blocks_per_seq=4096 // B)
+        outs.append(run_and_compare(c, c.name, 512)[0])
+    assert np.abs(outs[0] - outs[1]).max() <= 2 * TOL["bf16"]
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_determinism_and_permutation_invariance():
+    c = make_prefix_case("perm", [1, 40, 300, 77, 1000, 5, 64, 65], 4, 64, 8, 2, 128, 16,
+                         "bf16", 9)
+    say("perm: base run twice")
+    a = DeviceCase(c).run_step(64).cpu().numpy()
+    a2 = DeviceCase(c).run_step(64).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), a2.view(np.uint32))
+    k2, v2, t2, _, pairs2, sm2 = permute_pool(c, 5)
+    say("perm: permuted pool")
+    b = DeviceCase(c, tables=t2, k_cache=k2, v_cache=v2, pairs=pairs2, slots=sm2).run_step(64)
+    assert np.array_equal(a.view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+def test_identical_keys_give_mean_of_v():
+    c = make_private_case("idk", [1, 33, 500], 4, 2, 128, 16, "bf16", 4)
+    kc = c.k_cache.copy()
+    for s, L in enumerate(c.context_lens.tolist()):
+        row = kc[c.block_tables[s, 0], 0].copy()
+        for t in range(L):
+            kc[c.block_tables[s, t // 16], t % 16] = row
+    say("identical keys")
+    dc = DeviceCase(c, k_cache=kc)
+    out = dc.run_decode(0).cpu().numpy()
+    for s, L in enumerate(c.context_lens.tolist()):
+        V = np.stack([O.to_f64(c.v_cache[c.block_tables[s, t // 16], t % 16], "bf16")
+                      for t in range(L)]).mean(axis=0)
+        for h in range(4):
+            assert np.abs(out[s, h] - V[h // 2]).max() <= TOL["bf16"]
+
+
+def test_poison_is_never_read():
+    # every unused slot and table entry is NaN / the NaN block: outputs stay finite
+    c = make_fork_case("poison", [30, 30, 30, 30, 7, 100, 1], 1, 4, 8, 2, 128, 16, "bf16", 8)
+    say("poison")
+    out = DeviceCase(c).run_step(0).cpu().numpy()
+    assert np.isfinite(out).all()
+
+
+def test_status_codes_with_real_tensors():
+    import paged_kv_cache_386_amd as pa
+    c = make_private_case("status", [600, 700], 4, 2, 128, 16, "bf16", 2)
+    dc = DeviceCase(c)
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.paged_attention_decode(dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
+                                  dc.context_lens, 0.1, dc.out, max_context_len=700,
+                                  partition_size=64,
+                                  workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == -5
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.paged_attention_decode(dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
+                                  dc.context_lens, 0.1, dc.out, max_context_len=10 ** 6)
+    assert e.value.status == -2
+
+
+# ---------------------------------------------------------------- named workloads, full size
+
+def _sample_rows(case, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    S, H = case.num_seqs, case.num_q_heads
+    rows = {(int(rng.integers(S)), int(rng.integers(H))) for _ in range(n)}
+    L = case.context_lens
+    for s in (int(np.argmax(L)), int(np.argmin(L))):
+        rows |= {(s, 0), (s, H - 1)}
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("cfg,B", [(1, None), (2, None), (3, 512), (3, 16), (4, None)])
+def test_named_workload_full_size(cfg, B):
+    say(f"cfg{cfg} B={B}: generating")
+    c = make_case(cfg, block_size=B)
+    say(f"cfg{cfg} B={B}: S={c.num_seqs} max_ctx={c.max_context_len} NB={c.num_blocks} "
+        f"pairs={len(c.copy_pairs)}; running step (auto partitions)")
+    dc = DeviceCase(c)
+    out = dc.run_step(512 if cfg == 3 else 0).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(out).all()
+    kc, vc = oracle_step(c)
+    if c.has_step:
+        assert np.array_equal(bits(dc.k_cache), host_bits(kc))
+        assert np.array_equal(bits(dc.v_cache), host_bits(vc))
+    rows = _sample_rows(c, seed=cfg)
+    ref = O.paged_attention_decode_rows(c.q, kc, vc, c.block_tables, c.context_lens, c.scale,
+                                        c.block_size, c.dtype, rows)
+    got = np.stack([out[s, h] for s, h in rows])
+    err = max_err(got, ref)
+    say(f"cfg{cfg} B={B}: {len(rows)} sampled rows, max abs err {err:.3e}")
+    assert err <= TOL[c.dtype]
