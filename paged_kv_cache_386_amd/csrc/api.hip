@@ -101,6 +101,8 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
   if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  // offsets inside one block are 32-bit in the kernels
+  if ((int64_t)block_size * num_kv_heads * head_dim >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
   if (!pa::decode_supported(dtype, head_dim, num_q_heads / num_kv_heads))

@@ -438,12 +438,7 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
                      a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions <= 1) return e;
-  hipLaunchKernelGGL((paged_decode_merge_kernel<D>),
-                     dim3((uint32_t)((int64_t)a.num_seqs * a.num_q_heads)), dim3(D), 0, stream,
-                     a.context_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads,
-                     a.max_blocks_per_seq << a.log2_block_size,
-                     a.partition_size, a.num_partitions);
-  return hipGetLastError();
+  return launch_partition_merge(a, stream);
 }
 
 template <typename T, int D, int G>
@@ -480,7 +475,28 @@ bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group) {
   return group == 1 || group == 2 || group == 4 || group == 8;
 }
 
+hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream) {
+  const uint32_t rows = (uint32_t)((int64_t)a.num_seqs * a.num_q_heads);
+  const int cap = a.max_blocks_per_seq << a.log2_block_size;
+  switch (a.head_dim) {
+    case 64:
+      hipLaunchKernelGGL((paged_decode_merge_kernel<64>), dim3(rows), dim3(64), 0, stream,
+                         a.context_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, cap,
+                         a.partition_size, a.num_partitions);
+      break;
+    case 128:
+      hipLaunchKernelGGL((paged_decode_merge_kernel<128>), dim3(rows), dim3(128), 0, stream,
+                         a.context_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, cap,
+                         a.partition_size, a.num_partitions);
+      break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (decode_mfma_supported(a.dtype, a.head_dim, a.num_q_heads / a.num_kv_heads))
+    return launch_decode_mfma(a, stream);
   if (a.dtype == 0) return launch_d<float>(a, stream);
   if (a.dtype == 1) return launch_d<uint16_t>(a, stream);
   return hipErrorNotSupported;

@@ -1,0 +1,410 @@
+// PagedAttention decode on the matrix cores of gfx950, for bfloat16 K/V with
+// head_dim 128 and a GQA group of 4 or 8 query heads per KV head.
+//
+// The operation is the one of decode.hip (the "核心代码拆解" section of the
+// devpress.csdn.net/amd vLLM walkthrough: table lookup per logical block, scaled
+// q.k, softmax, weighted sum of V).  With G >= 4 query heads sharing a KV head,
+// every K/V row meets G queries, and on the vector ALU those G multiply-adds per
+// element are what bounds the kernel; here both products run on MFMA:
+//
+//  * q.K: v_mfma_f32_16x16x32_bf16.  A = 16 K rows of a 16-token tile (lane
+//    n = lane%16 loads token n, elements 32s + 8g .. +7 for k-step s, where
+//    g = lane/16), B = the G query rows repeated over the 16 columns
+//    (column n holds query n % G).  Products of bfloat16 values are exact and
+//    accumulate in fp32.  The result gives lane (g, n) the scores of query
+//    n % G with tokens 4g .. 4g+3 of the tile.
+//  * p.V, G = 4: v_mfma_f32_4x4x1f32 (16 independent 4x4 blocks, fp32
+//    operands).  Block b = lane/4 takes A = the probabilities of its 4 lanes
+//    (the 4 query heads, one token of the lane group) and B = one fp32 element
+//    of V per lane: lane (g, n) loads elements 8n .. 8n+7 of token 4g+j's V row
+//    and feeds them to 8 MFMAs.  Each lane group (16 lanes) keeps its own
+//    running maximum and sum, since its accumulators only ever see its own
+//    tokens, so the hot loop has no cross-lane traffic; the lane groups are
+//    merged once at the end.
+//  * p.V, G = 8: v_mfma_f32_16x16x4f32.  A = the probabilities of the 16
+//    columns (query n % G) for the 4 tokens 4g+j of step j, B = the same V
+//    elements as above; the MFMA sums over the 4 lane groups, so the running
+//    maximum is shared by the wave (two cross-lane max steps per tile) and half
+//    as many accumulators are live as a second 4x4 pass would need.
+//  * Probabilities stay fp32, so no precision is lost in p.V.  A running
+//    maximum is raised only when a tile's maximum exceeds it by more than 8
+//    (log2 units), so accumulators are rarely rescaled; probabilities stay
+//    below 2^8 and the result is the same ratio of sums.
+
+// Work split, tiles, partitions and the merge of partition partials are those
+// of decode.hip: one workgroup of 4 waves per (sequence, KV head, partition),
+// 16-token tiles round-robin over the waves, double-buffered in registers.
+// Accumulation order depends only on logical token positions, so results are
+// bitwise reproducible and invariant under a relabelling of physical blocks.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.f;  // allowed growth of scores over the running max (log2)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// Broadcast lane R of each quad of 4 lanes to the whole quad.
+template <int R>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), R * 0x55, 0xF, 0xF, false));
+}
+
+struct Tile {
+  u32x4 k[4];  // token n of the tile, elements 32s + 8g .. +7 (s = 0..3)
+  u32x4 v[4];  // token 4g + j of the tile, elements 8n .. 8n+7 (j = 0..3)
+};
+
+template <int G, bool SMALLB>
+struct MfmaDecode {
+  // WIDE: p.V on 16x16x4 with a wave-shared running maximum (G = 8);
+  // otherwise 4x4x1 blocks with one running maximum per lane group (G = 4).
+  static constexpr bool WIDE = G > 4;
+
+  // Issue the loads of the tile starting at token cs.  Rows of tokens at or
+  // past t1 are not read (their registers are zero) when MASK is set.
+  template <bool MASK>
+  static __device__ __forceinline__ void load(Tile &T, const uint16_t *__restrict__ kc,
+                                              const uint16_t *__restrict__ vc,
+                                              const int32_t *__restrict__ tbl, int cs, int t1,
+                                              int lgB, int nb, int g, int n, int row_elems,
+                                              int head_off, int64_t block_elems) {
+    const int bm1 = (1 << lgB) - 1;
+    if constexpr (!SMALLB) {
+      // a 16-aligned tile lies inside one block: one scalar table read
+      const uint32_t pid = min((uint32_t)tbl[cs >> lgB], (uint32_t)(nb - 1));
+      const int64_t base = (int64_t)pid * block_elems + head_off;
+      const int o = cs & bm1;
+      const u32x4 *kp = reinterpret_cast<const u32x4 *>(kc + base + (o + n) * row_elems + 8 * g);
+      const bool okk = !MASK || cs + n < t1;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) T.k[s] = okk ? kp[4 * s] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 *vp =
+            reinterpret_cast<const u32x4 *>(vc + base + (o + 4 * g + j) * row_elems + 8 * n);
+        const bool ok = !MASK || cs + 4 * g + j < t1;
+        T.v[j] = ok ? *vp : u32x4{0, 0, 0, 0};
+      }
+    } else {
+      // blocks shorter than a tile: each token row looks up its own block
+      const int tk = cs + n;
+      if (!MASK || tk < t1) {
+        const uint32_t pid = min((uint32_t)tbl[tk >> lgB], (uint32_t)(nb - 1));
+        const u32x4 *kp = reinterpret_cast<const u32x4 *>(
+            kc + (int64_t)pid * block_elems + head_off + (tk & bm1) * row_elems + 8 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) T.k[s] = kp[4 * s];
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) T.k[s] = u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tv = cs + 4 * g + j;
+        if (!MASK || tv < t1) {
+          const uint32_t pid = min((uint32_t)tbl[tv >> lgB], (uint32_t)(nb - 1));
+          T.v[j] = *reinterpret_cast<const u32x4 *>(
+              vc + (int64_t)pid * block_elems + head_off + (tv & bm1) * row_elems + 8 * n);
+        } else {
+          T.v[j] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+    // keep these loads ahead of the computation that follows them
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // acc[i] += p (x) V elements 8n + i of one token row, for i = 0..7.
+  static __device__ __forceinline__ void pv(const u32x4 &w, float p, f32x4 (&acc)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __uint_as_float(w[e] << 16);
+      const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
+      if constexpr (WIDE) {
+        acc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, lo, acc[2 * e], 0, 0, 0);
+        acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, hi, acc[2 * e + 1], 0, 0, 0);
+      } else {
+        acc[2 * e] = __builtin_amdgcn_mfma_f32_4x4x1f32(p, lo, acc[2 * e], 0, 0, 0);
+        acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(p, hi, acc[2 * e + 1], 0, 0, 0);
+      }
+    }
+  }
+
+  // Fold one tile into the running (max, sum, accumulators).  m is this
+  // lane's query head's running maximum: of its lane group (G = 4) or of the
+  // wave (WIDE); lsum covers the lane group's tokens in both cases.
+  template <bool MASK>
+  static __device__ __forceinline__ void compute(const Tile &T, const bf16x8 (&qb)[4],
+                                                 f32x4 (&acc)[8], float &m, float &lsum, int cs,
+                                                 int t1, int g, float sl2) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[s]), qb[s], c, 0,
+                                                   0, 0);
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (!MASK || cs + 4 * g + j < t1) ? c[j] * sl2 : neg_inf();
+    float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if constexpr (WIDE) {
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+    }
+    const bool need = cm > m + kSlack;  // false while both are -inf
+    float alpha = 1.f;
+    if (need) {
+      alpha = __builtin_amdgcn_exp2f(m - cm);  // 0 when m was -inf
+      lsum *= alpha;
+      m = cm;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      float a[4];
+      if constexpr (WIDE) {
+        // accumulator row r of lane group g is query head (4g + r) % G, whose
+        // factor lane 4g + r holds
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = __shfl(alpha, 4 * g + r);
+      } else {
+        // accumulator row r is the query head of lane r of the quad
+        a[0] = quad_bcast<0>(alpha);
+        a[1] = quad_bcast<1>(alpha);
+        a[2] = quad_bcast<2>(alpha);
+        a[3] = quad_bcast<3>(alpha);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][r] *= a[r];
+    }
+    const float mu = (m == neg_inf()) ? 0.f : m;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(x[j] - mu);
+      lsum += p[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pv(T.v[j], p[j], acc);
+  }
+};
+
+template <int G, bool SMALLB>
+__global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, float *__restrict__ out, float *__restrict__ ws_o,
+    float *__restrict__ ws_ml, float sl2, int num_seqs, int hkv, int lgB, int nb, int mb, int ps,
+    int P) {
+  using K = MfmaDecode<G, SMALLB>;
+  constexpr bool WIDE = K::WIDE;
+
+  // work item: KV head fastest, then sequence, then partition (as in decode.hip)
+  const int id = blockIdx.x;
+  const int kvh = id % hkv;
+  const int s = (id / hkv) % num_seqs;
+  const int p = id / (hkv * num_seqs);
+  const int hq = hkv * G;
+
+  int L = context_lens[s];
+  L = max(0, min(L, mb << lgB));
+  const int nparts = min((L + ps - 1) / ps, P);
+  if (p >= max(nparts, 1)) return;
+  const int t0 = p * ps;
+  const int t1 = min(L, t0 + ps);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int32_t *tbl = block_tables + (int64_t)s * mb;
+
+  // B operand of q.K: column n is query head n % G of this KV head
+  bf16x8 qb[4];
+  {
+    const uint16_t *qrow = q + ((int64_t)s * hq + kvh * G + n % G) * kD + 8 * g;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      qb[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * k));
+  }
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = neg_inf(), lsum = 0.f;
+
+  const int row_elems = hkv * kD;
+  const int head_off = kvh * kD;
+  const int64_t block_elems = ((int64_t)row_elems) << lgB;
+
+  // full tiles round-robin over the waves (this wave's j-th tile is tile
+  // wave + 4j), two-stage register pipeline, the last one or two peeled; the
+  // final partial tile goes to the wave it falls to, with masked loads
+  const int nfull = (t1 - t0) / kTile;
+  const int nw = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
+  {
+    Tile A, Bt;
+    auto cstart = [&](int j) { return t0 + (wave + kWaves * j) * kTile; };
+    if (nw > 0) {
+      K::template load<false>(A, kc, vc, tbl, cstart(0), t1, lgB, nb, g, n, row_elems, head_off,
+                              block_elems);
+      int j = 0;
+      for (; j + 2 < nw; j += 2) {
+        K::template load<false>(Bt, kc, vc, tbl, cstart(j + 1), t1, lgB, nb, g, n, row_elems,
+                                head_off, block_elems);
+        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
+        K::template load<false>(A, kc, vc, tbl, cstart(j + 2), t1, lgB, nb, g, n, row_elems,
+                                head_off, block_elems);
+        K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2);
+      }
+      if (j + 2 == nw) {
+        K::template load<false>(Bt, kc, vc, tbl, cstart(j + 1), t1, lgB, nb, g, n, row_elems,
+                                head_off, block_elems);
+        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
+        K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2);
+      } else {
+        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
+      }
+    }
+    if (t0 + nfull * kTile < t1 && nfull % kWaves == wave) {
+      const int cs = t0 + nfull * kTile;
+      K::template load<true>(A, kc, vc, tbl, cs, t1, lgB, nb, g, n, row_elems, head_off,
+                             block_elems);
+      K::template compute<true>(A, qb, acc, m, lsum, cs, t1, g, sl2);
+    }
+  }
+
+  // This wave's maximum and sum per accumulator row, with the lane groups'
+  // shares combined.  Afterwards lane (g, n) holds, for row r, query head
+  //   WIDE: (4g + r) % G, elements 8n + i (the MFMA summed the lane groups);
+  //   G=4:  r, elements 8n + i (identical in every lane group).
+  float Mr[4], Lr[4];
+  if constexpr (WIDE) {
+    float l = lsum;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Mr[r] = __shfl(m, 4 * g + r);
+      Lr[r] = __shfl(l, 4 * g + r);
+    }
+  } else {
+    const float mq[4] = {quad_bcast<0>(m), quad_bcast<1>(m), quad_bcast<2>(m), quad_bcast<3>(m)};
+    const float lq[4] = {quad_bcast<0>(lsum), quad_bcast<1>(lsum), quad_bcast<2>(lsum),
+                         quad_bcast<3>(lsum)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float M = fmaxf(mq[r], __shfl_xor(mq[r], 16));
+      M = fmaxf(M, __shfl_xor(M, 32));
+      const float f = (mq[r] == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mq[r] - M);
+      float l = lq[r] * f;
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      Mr[r] = M;
+      Lr[r] = l;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float a = acc[i][r] * f;
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        acc[i][r] = a;
+      }
+    }
+  }
+
+  // Merge the waves through LDS.
+  __shared__ float sm_acc[kWaves][G][kD];
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+  if (g < G / 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qr = 4 * g + r;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm_acc[wave][qr][8 * n + i] = acc[i][r];
+      if (n == 0) {
+        sm_m[wave][qr] = Mr[r];
+        sm_l[wave][qr] = Lr[r];
+      }
+    }
+  }
+  __syncthreads();
+  const bool final_out = nparts <= 1;
+  for (int i = threadIdx.x; i < G * kD; i += kThreads) {
+    const int h = i / kD;
+    const int d = i % kD;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    float ls = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_m[w][h];
+      const float f = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      ls = fmaf(sm_l[w][h], f, ls);
+      o = fmaf(sm_acc[w][h][d], f, o);
+    }
+    const int64_t row = (int64_t)s * hq + kvh * G + h;
+    if (final_out) {
+      out[row * kD + d] = ls > 0.f ? o / ls : 0.f;
+    } else {
+      ws_o[(row * P + p) * kD + d] = o / ls;
+      if (d == 0) {
+        ws_ml[(row * P + p) * 2 + 0] = M;
+        ws_ml[(row * P + p) * 2 + 1] = ls;
+      }
+    }
+  }
+}
+
+template <int G, bool SMALLB>
+hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
+  if (grid <= 0) return hipSuccess;
+  const float sl2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<G, SMALLB>), dim3((uint32_t)grid), dim3(kThreads),
+                     0, stream, static_cast<const uint16_t *>(a.q),
+                     static_cast<const uint16_t *>(a.k_cache),
+                     static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
+                     a.out, a.ws_o, a.ws_ml, sl2, a.num_seqs, a.num_kv_heads, a.log2_block_size,
+                     a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_partitions <= 1) return e;
+  return launch_partition_merge(a, stream);
+}
+
+template <int G>
+hipError_t launch_b(const DecodeArgs &a, hipStream_t stream) {
+  if (a.log2_block_size >= 4) return launch_typed<G, false>(a, stream);
+  return launch_typed<G, true>(a, stream);
+}
+
+}  // namespace
+
+bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
+  return dtype == 1 && head_dim == kD && (group == 4 || group == 8);
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 4: return launch_b<4>(a, stream);
+    case 8: return launch_b<8>(a, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace pa

@@ -31,6 +31,13 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group);
 
+// The matrix-core decode (decode_mfma.hip): bfloat16, head_dim 128, G in {4, 8}.
+bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
+
+// Merge of the per-partition partials into `out` (P > 1 only).
+hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream);
+
 hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                                  int32_t num_tokens, void *k_cache, void *v_cache,
                                  int64_t num_slots, int64_t row_bytes, hipStream_t stream);
