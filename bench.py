@@ -11,16 +11,34 @@ Inputs are seeded synthetic data resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is the step's algorithmic HBM bytes (each
 distinct KV slot read once, plus q, out, tables, partials and the edits) per
-second of step time.
+second of step time.  `roofline` prices the decode call (decode kernel plus
+partition merge, timed with HIP events on the stream they run on) against the
+MI355X HBM peak; `traffic` is the bytes the rocprofv3 FETCH_SIZE/WRITE_SIZE
+counters saw per decode call, scaled by what the same counters read for a
+copy of known size (`--copy-calibration`), when the committed counter summary
+was taken on the current decode sources.
+
+Other modes:
+  --copy-calibration      also run one copy_blocks call over a 1 GiB pool first
+                          (512 MiB read + 512 MiB written): the reference
+                          dispatch for the counter scale factors
+  --summarize-counters F W
+                          read the rocprofv3 counter CSVs of a FETCH_SIZE run
+                          (directory F) and a WRITE_SIZE run (directory W) of
+                          this script with --copy-calibration, and print the
+                          JSON record kept in profiles/decode_counters.json
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
 import sys
 import time
+from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -28,8 +46,18 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode achieved HBM GB/s (% of peak) and attended KV tokens/s, 1 GPU"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_386_amd", "csrc", "decode.hip")
+CSRC = os.path.join(ROOT, "paged_kv_cache_386_amd", "csrc")
+DECODE_SOURCES = ["api.hip", "decode.hip", "decode_mfma.hip", "internal.h"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_counters.json")
+DECODE_KERNELS = ("paged_decode_mfma_kernel", "paged_decode_kernel", "paged_decode_merge_kernel")
+
+# calibration copy: CAL_PAIRS blocks of CAL_BLOCK_BYTES in each of two caches
+CAL_BLOCKS = 16384
+CAL_PAIRS = 8192
+CAL_SHAPE = (CAL_BLOCKS, 16, 8, 128)  # bf16 -> 32 KiB per block
+CAL_BLOCK_BYTES = 16 * 8 * 128 * 2
+CAL_READ_BYTES = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
+CAL_WRITE_BYTES = CAL_READ_BYTES
 
 
 # ---------------------------------------------------------------- byte model
@@ -84,26 +112,81 @@ def edit_bytes(case) -> int:
     return copies + writes
 
 
-# ---------------------------------------------------------------- helpers
+# ---------------------------------------------------------------- counters
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str):
-    """Measured HBM bytes per decode launch from the committed counter runs,
-    or None when absent or taken on a different decode kernel source."""
+    """Measured HBM bytes per decode call from the committed counter summary,
+    or None when absent or taken on different decode sources."""
     try:
         with open(COUNTERS_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("decode_src_sha256_16") != source_hash(DECODE_SRC):
+    if not entry or entry.get("decode_src_sha256_16") != decode_source_hash():
         return None
-    return entry.get("bytes_per_launch")
+    return entry.get("bytes_per_call")
 
+
+def _counter_rows(directory: str, counter: str):
+    """(dispatch id, kernel name, grid size, value in KiB) of every dispatch."""
+    paths = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    rows = []
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]),
+                                 float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> dict:
+    """Scale factors from the calibration copy (the first copy_blocks dispatch,
+    whose grid covers CAL_PAIRS pairs) and measured bytes per decode call
+    (decode kernel plus merge, averaged over the calls after the first)."""
+    out = {}
+    for counter, directory, true_bytes in (("FETCH_SIZE", fetch_dir, CAL_READ_BYTES),
+                                           ("WRITE_SIZE", write_dir, CAL_WRITE_BYTES)):
+        rows = _counter_rows(directory, counter)
+        cal = [r for r in rows if "copy_blocks_kernel" in r[1]]
+        if not cal:
+            raise SystemExit("no calibration copy_blocks dispatch: run bench.py --copy-calibration")
+        factor = true_bytes / (cal[0][3] * 1024.0)
+        # one decode call = one decode-kernel dispatch plus the merge that follows it
+        calls = []
+        for did, name, grid, kib in rows:
+            if "paged_decode_mfma_kernel" in name or "paged_decode_kernel" in name:
+                calls.append(kib)
+            elif "paged_decode_merge_kernel" in name and calls:
+                calls[-1] += kib
+        if len(calls) < 2:
+            raise SystemExit(f"{counter}: fewer than two decode calls in {directory}")
+        per_call = sum(calls[1:]) / len(calls[1:]) * 1024.0 * factor
+        out[counter] = {"factor": round(factor, 4), "raw_kib_calibration": cal[0][3],
+                        "bytes_per_call": int(per_call), "calls": len(calls)}
+    return {
+        workload: {
+            "bytes_per_call": out["FETCH_SIZE"]["bytes_per_call"] + out["WRITE_SIZE"]["bytes_per_call"],
+            "fetch": out["FETCH_SIZE"],
+            "write": out["WRITE_SIZE"],
+            "decode_src_sha256_16": decode_source_hash(),
+        }
+    }
+
+
+# ---------------------------------------------------------------- helpers
 
 def to_dev(a, dev):
     import numpy as np
@@ -113,11 +196,27 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
+def copy_calibration(dev) -> None:
+    """One copy_blocks call of known size: CAL_PAIRS blocks copied in each of
+    two bf16 caches of CAL_BLOCKS 32 KiB blocks (1 GiB in all)."""
+    import torch
+
+    import paged_kv_cache_386_amd as pa
+    kc = torch.ones(CAL_SHAPE, dtype=torch.bfloat16, device=dev)
+    vc = torch.ones(CAL_SHAPE, dtype=torch.bfloat16, device=dev)
+    src = torch.arange(CAL_PAIRS, dtype=torch.int32)
+    pairs = torch.stack([src, src + CAL_PAIRS], dim=1).contiguous().to(dev)
+    torch.cuda.synchronize()
+    pa.copy_blocks(pairs, kc, vc)
+    torch.cuda.synchronize()
+    del kc, vc, pairs
+    torch.cuda.empty_cache()
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the oracle (single thread) on the same workload: the step's edits
     and decode for as many sequences as fit the time budget (all of them for
     the default workload)."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import oracle as O
@@ -169,7 +268,14 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=25.0,
                     help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+
+    workload = f"cfg{args.config}" + (f"-B{args.block_size or 512}" if args.config == 3 else "")
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(*args.summarize_counters, workload), indent=1))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the paged-decode "
@@ -189,6 +295,8 @@ def main() -> int:
     pa.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(dev)
 
     t_gen = time.perf_counter()
     case = make_case(args.config, poison=False, block_size=args.block_size)
@@ -213,19 +321,22 @@ def main() -> int:
     P = pa.num_partitions(S, Hkv, max_ctx, args.partition_size)
     ws_bytes = pa.workspace_size(S, Hq, Hkv, D, max_ctx, args.partition_size)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    ps = args.partition_size if args.partition_size > 0 else (512 if P > 1 else 0)
+    ps = pa.partition_tokens(max_ctx, args.partition_size) if P > 1 else 0
     stream = torch.cuda.current_stream()
 
-    def step():
-        if has_step:
-            pa.copy_blocks(pairs, kc, vc, stream=stream)
-            pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
+    def edits():
+        pa.copy_blocks(pairs, kc, vc, stream=stream)
+        pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
+
+    def decode():
         pa.paged_attention_decode(q, kc, vc, tables, lens, float(case.scale), out,
                                   max_context_len=max_ctx, partition_size=args.partition_size,
                                   workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
-        step()
+        if has_step:
+            edits()
+        decode()
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -237,12 +348,9 @@ def main() -> int:
     start.record(stream)
     for i in range(args.steps):
         if has_step:
-            pa.copy_blocks(pairs, kc, vc, stream=stream)
-            pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
+            edits()
         ev[i][0].record(stream)
-        pa.paged_attention_decode(q, kc, vc, tables, lens, float(case.scale), out,
-                                  max_context_len=max_ctx, partition_size=args.partition_size,
-                                  workspace=ws, stream=stream)
+        decode()
         ev[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -257,7 +365,6 @@ def main() -> int:
     tokens = int(case.context_lens.astype(np.int64).sum())
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dec_unique / (dec_us * 1e-6) / 1e9
-    workload = f"cfg{args.config}" + (f"-B{case.block_size}" if args.config == 3 else "")
 
     rec = {
         "metric": METRIC,
@@ -288,18 +395,18 @@ def main() -> int:
         "decode_attended_gbps": round(dec_attended / (dec_us * 1e-6) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode (decode + merge launches)",
+            "kernel": "paged_attention_decode (decode kernel + partition merge, one call)",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "algorithmic_bytes_per_launch": dec_unique,
             "traffic": load_traffic(workload),
+            "algorithmic_bytes_per_call": dec_unique,
+            "attended_bytes_per_call": dec_attended,
         },
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline and rank == 0:
-        from threadpoolctl import threadpool_info  # noqa: F401
         cb = cpu_baseline(case, args.cpu_budget)
         cpu_value = step_bytes / cb["est_step_seconds"] / 1e9
         rec["cpu_baseline"] = {

@@ -13,5 +13,6 @@ from ._lib import (  # noqa: F401
     lib,
     num_partitions,
     paged_attention_decode,
+    partition_tokens,
     workspace_size,
 )

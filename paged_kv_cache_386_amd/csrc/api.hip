@@ -13,7 +13,7 @@
 namespace {
 
 constexpr int32_t kChunkTokens = 16;
-constexpr int32_t kAutoPartition = 512;
+constexpr int32_t kAutoPartition = 2048;
 constexpr int64_t kMaxTokensPerSeq = int64_t(1) << 30;
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -32,9 +32,12 @@ bool known_dtype(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
 // size through *ps, or a negative pa_status.
 //   partition_size < 0: never split;
 //   partition_size > 0: that many tokens, a multiple of the 16-token chunk;
-//   partition_size == 0: split contexts longer than 512 tokens into 512-token
-//     partitions, which keeps every workgroup's share of the sequence short
-//     enough that long and short sequences balance over the 256 CUs.
+//   partition_size == 0: split contexts longer than 2048 tokens into
+//     2048-token partitions.  Shorter partitions balance long and short
+//     sequences better over the 256 CUs, but every workgroup pays a fixed
+//     start-up latency (context length, table, first tile) and every split
+//     sequence a merge; 2048 was the fastest size measured on the GQA
+//     prefix-sharing batch (lognormal lengths, median 1024, cap 8192).
 int32_t resolve_partitions(int32_t max_context_len, int32_t partition_size, int32_t *ps) {
   if (max_context_len < 0) return PA_ERR_SHAPE;
   int32_t want = partition_size;
@@ -74,6 +77,13 @@ int32_t paged_attention_num_partitions(int32_t num_seqs, int32_t num_kv_heads,
   (void)num_kv_heads;
   int32_t ps = 0;
   return resolve_partitions(max_context_len, partition_size, &ps);
+}
+
+int32_t paged_attention_partition_tokens(int32_t max_context_len, int32_t partition_size) {
+  int32_t ps = 0;
+  const int32_t P = resolve_partitions(max_context_len, partition_size, &ps);
+  if (P < 0) return P;
+  return P > 1 ? ps : max_context_len;
 }
 
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,

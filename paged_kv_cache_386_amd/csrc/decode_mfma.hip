@@ -80,13 +80,15 @@ struct MfmaDecode {
   template <bool MASK>
   static __device__ __forceinline__ void load(Tile &T, const uint16_t *__restrict__ kc,
                                               const uint16_t *__restrict__ vc,
-                                              const int32_t *__restrict__ tbl, int cs, int t1,
+                                              const int32_t *__restrict__ tbl, int ent, int cs,
+                                              int t1,
                                               int lgB, int nb, int g, int n, int row_elems,
                                               int head_off, int64_t block_elems) {
     const int bm1 = (1 << lgB) - 1;
     if constexpr (!SMALLB) {
-      // a 16-aligned tile lies inside one block: one scalar table read
-      const uint32_t pid = min((uint32_t)tbl[cs >> lgB], (uint32_t)(nb - 1));
+      // a 16-aligned tile lies inside one block, whose id the caller read
+      // ahead of time (ent)
+      const uint32_t pid = min((uint32_t)ent, (uint32_t)(nb - 1));
       const int64_t base = (int64_t)pid * block_elems + head_off;
       const int o = cs & bm1;
       const u32x4 *kp = reinterpret_cast<const u32x4 *>(kc + base + (o + n) * row_elems + 8 * g);
@@ -213,8 +215,8 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   using K = MfmaDecode<G, SMALLB>;
   constexpr bool WIDE = K::WIDE;
 
-  // work item: KV head fastest, then sequence, then partition (as in decode.hip)
   const int id = blockIdx.x;
+  // work item: KV head fastest, then sequence, then partition (as in decode.hip)
   const int kvh = id % hkv;
   const int s = (id / hkv) % num_seqs;
   const int p = id / (hkv * num_seqs);
@@ -256,24 +258,43 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   // final partial tile goes to the wave it falls to, with masked loads
   const int nfull = (t1 - t0) / kTile;
   const int nw = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
+  auto cstart = [&](int j) { return t0 + (wave + kWaves * j) * kTile; };
+
+  // Block ids of this wave's tiles, read 64 tiles at a time into a register
+  // (lane i: tile 64c + i) one chunk ahead of use, so no table read sits
+  // between a tile's loads and the previous tile's.
+  int ent_cur = 0, ent_next = 0;
+  auto chunk_entries = [&](int c) {
+    const int cs = cstart(64 * c + lane);
+    return (!SMALLB && cs < t1) ? tbl[cs >> lgB] : 0;
+  };
+  ent_cur = chunk_entries(0);
+  ent_next = chunk_entries(1);
+  auto entry = [&](int j) {
+    if constexpr (SMALLB) return 0;
+    if (j > 0 && (j & 63) == 0) {
+      ent_cur = ent_next;
+      ent_next = chunk_entries((j >> 6) + 1);
+    }
+    return __builtin_amdgcn_readlane(ent_cur, j & 63);
+  };
   {
     Tile A, Bt;
-    auto cstart = [&](int j) { return t0 + (wave + kWaves * j) * kTile; };
     if (nw > 0) {
-      K::template load<false>(A, kc, vc, tbl, cstart(0), t1, lgB, nb, g, n, row_elems, head_off,
-                              block_elems);
+      K::template load<false>(A, kc, vc, tbl, entry(0), cstart(0), t1, lgB, nb, g, n, row_elems,
+                              head_off, block_elems);
       int j = 0;
       for (; j + 2 < nw; j += 2) {
-        K::template load<false>(Bt, kc, vc, tbl, cstart(j + 1), t1, lgB, nb, g, n, row_elems,
-                                head_off, block_elems);
+        K::template load<false>(Bt, kc, vc, tbl, entry(j + 1), cstart(j + 1), t1, lgB, nb, g, n,
+                                row_elems, head_off, block_elems);
         K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
-        K::template load<false>(A, kc, vc, tbl, cstart(j + 2), t1, lgB, nb, g, n, row_elems,
-                                head_off, block_elems);
+        K::template load<false>(A, kc, vc, tbl, entry(j + 2), cstart(j + 2), t1, lgB, nb, g, n,
+                                row_elems, head_off, block_elems);
         K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2);
       }
       if (j + 2 == nw) {
-        K::template load<false>(Bt, kc, vc, tbl, cstart(j + 1), t1, lgB, nb, g, n, row_elems,
-                                head_off, block_elems);
+        K::template load<false>(Bt, kc, vc, tbl, entry(j + 1), cstart(j + 1), t1, lgB, nb, g, n,
+                                row_elems, head_off, block_elems);
         K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
         K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2);
       } else {
@@ -282,8 +303,8 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     }
     if (t0 + nfull * kTile < t1 && nfull % kWaves == wave) {
       const int cs = t0 + nfull * kTile;
-      K::template load<true>(A, kc, vc, tbl, cs, t1, lgB, nb, g, n, row_elems, head_off,
-                             block_elems);
+      K::template load<true>(A, kc, vc, tbl, entry(nw), cs, t1, lgB, nb, g, n, row_elems,
+                             head_off, block_elems);
       K::template compute<true>(A, qb, acc, m, lsum, cs, t1, g, sl2);
     }
   }

@@ -27,6 +27,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("paged_attention_decode", "kv_cache_write", "copy_blocks",
                  "paged_attention_workspace_size", "paged_attention_num_partitions",
+                 "paged_attention_partition_tokens",
                  "pagedattn_status_string", "pagedattn_version"):
         assert want in names
 
@@ -86,9 +87,14 @@ def test_partition_policy():
     lib = _lib.lib()
     assert lib.paged_attention_num_partitions(8, 8, 32768, 512) == 64
     assert lib.paged_attention_num_partitions(8, 8, 32768, -1) == 1
-    assert lib.paged_attention_num_partitions(8, 8, 512, 0) == 1
-    assert lib.paged_attention_num_partitions(8, 8, 513, 0) == 2
+    assert lib.paged_attention_num_partitions(8, 8, 2048, 0) == 1
+    assert lib.paged_attention_num_partitions(8, 8, 2049, 0) == 2
+    assert lib.paged_attention_num_partitions(256, 8, 8192, 0) == 4
     assert lib.paged_attention_num_partitions(8, 8, 100, 24) == -2
+    assert lib.paged_attention_partition_tokens(8192, 0) == 2048
+    assert lib.paged_attention_partition_tokens(1500, 0) == 1500
+    assert lib.paged_attention_partition_tokens(32768, 512) == 512
+    assert lib.paged_attention_partition_tokens(100, 24) == -2
     assert lib.paged_attention_workspace_size(8, 64, 8, 128, 32768, 512) == 8 * 64 * 64 * 130 * 4
     assert lib.paged_attention_workspace_size(8, 64, 8, 128, 500, 0) == 0
 
