@@ -321,7 +321,7 @@ def main() -> int:
     P = pa.num_partitions(S, Hkv, max_ctx, args.partition_size)
     ws_bytes = pa.workspace_size(S, Hq, Hkv, D, max_ctx, args.partition_size)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    ps = pa.partition_tokens(max_ctx, args.partition_size) if P > 1 else 0
+    ps = pa.partition_tokens(S, Hkv, max_ctx, args.partition_size) if P > 1 else 0
     stream = torch.cuda.current_stream()
 
     def edits():

@@ -85,8 +85,11 @@ typedef enum pa_dtype {
  *                  must be <= max_blocks_per_seq * block_size
  *   dtype          element type of q, k_cache and v_cache
  *   partition_size split-K partition in tokens: 0 = automatic (2048-token
- *                  partitions for contexts above 2048), negative = never
- *                  split, positive = that many tokens (a multiple of 16).  With
+ *                  partitions for contexts above 2048 when there are at least
+ *                  256 (sequence, KV head) pairs; with fewer, floor(512 /
+ *                  pairs) equal partitions per context, at least 512
+ *                  tokens), negative = never split, positive = that many
+ *                  tokens (a multiple of 16).  With
  *                  more than one partition, per-partition (max, sum, output)
  *                  partials go to the workspace and a second kernel merges them
  *                  in ascending partition order.
@@ -129,7 +132,8 @@ int32_t paged_attention_num_partitions(int32_t num_seqs, int32_t num_kv_heads,
  * arguments: the partition length when it splits, else max_context_len; or a
  * negative pa_status for a partition_size decode rejects.
  */
-int32_t paged_attention_partition_tokens(int32_t max_context_len, int32_t partition_size);
+int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                         int32_t max_context_len, int32_t partition_size);
 
 /*
  * kv_cache_write -- store each new token's K and V rows in the pool.

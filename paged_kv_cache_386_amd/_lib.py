@@ -31,7 +31,7 @@ SIGNATURES = {
                                       _VP, ctypes.c_size_t, _VP]),
     "paged_attention_workspace_size": (ctypes.c_size_t, [_I32] * 6),
     "paged_attention_num_partitions": (_I32, [_I32] * 4),
-    "paged_attention_partition_tokens": (_I32, [_I32] * 2),
+    "paged_attention_partition_tokens": (_I32, [_I32] * 4),
     "kv_cache_write": (_I32, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
     "copy_blocks": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
     "pagedattn_status_string": (ctypes.c_char_p, [_I32]),
@@ -102,8 +102,10 @@ def num_partitions(num_seqs: int, num_kv_heads: int, max_context_len: int,
                                                      partition_size))
 
 
-def partition_tokens(max_context_len: int, partition_size: int = 0) -> int:
-    return int(lib().paged_attention_partition_tokens(max_context_len, partition_size))
+def partition_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int,
+                     partition_size: int = 0) -> int:
+    return int(lib().paged_attention_partition_tokens(num_seqs, num_kv_heads, max_context_len,
+                                                      partition_size))
 
 
 def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,

@@ -14,6 +14,9 @@ namespace {
 
 constexpr int32_t kChunkTokens = 16;
 constexpr int32_t kAutoPartition = 2048;
+constexpr int64_t kCUs = 256;                // MI355X compute units
+constexpr int64_t kTargetWorkgroups = 512;  // about two per CU
+constexpr int64_t kMinAutoPartition = 512;
 constexpr int64_t kMaxTokensPerSeq = int64_t(1) << 30;
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -32,16 +35,32 @@ bool known_dtype(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
 // size through *ps, or a negative pa_status.
 //   partition_size < 0: never split;
 //   partition_size > 0: that many tokens, a multiple of the 16-token chunk;
-//   partition_size == 0: split contexts longer than 2048 tokens into
-//     2048-token partitions.  Shorter partitions balance long and short
-//     sequences better over the 256 CUs, but every workgroup pays a fixed
-//     start-up latency (context length, table, first tile) and every split
-//     sequence a merge; 2048 was the fastest size measured on the GQA
-//     prefix-sharing batch (lognormal lengths, median 1024, cap 8192).
-int32_t resolve_partitions(int32_t max_context_len, int32_t partition_size, int32_t *ps) {
+//   partition_size == 0: automatic.  With at least one (sequence, KV head)
+//     pair per CU, contexts longer than 2048 tokens are split into 2048-token
+//     partitions: shorter ones balance long and short sequences better over
+//     the 256 CUs, but every workgroup pays a fixed start-up latency (context
+//     length, table, first tile) and every split sequence a merge; 2048 was
+//     the fastest size measured on the GQA prefix-sharing batch (lognormal
+//     lengths, median 1024, cap 8192).  With fewer pairs (a few long
+//     sequences), each pair's context is cut into floor(512 / pairs) equal
+//     partitions (a multiple of 16 tokens, at least 512), about two
+//     workgroups per CU: on 8 sequences of 32768 tokens with 8 KV heads,
+//     4096-token partitions (512 workgroups) were faster than 2048, 2736
+//     (768 workgroups) or 8192 (256 workgroups).
+int32_t resolve_partitions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                           int32_t partition_size, int32_t *ps) {
   if (max_context_len < 0) return PA_ERR_SHAPE;
   int32_t want = partition_size;
-  if (want == 0) want = max_context_len > kAutoPartition ? kAutoPartition : -1;
+  if (want == 0) {
+    int64_t size = kAutoPartition;
+    const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+    if (pairs > 0 && pairs < kCUs) {
+      const int64_t parts = kTargetWorkgroups / pairs;
+      size = ((max_context_len + parts - 1) / parts + kChunkTokens - 1) / kChunkTokens * kChunkTokens;
+      if (size < kMinAutoPartition) size = kMinAutoPartition;
+    }
+    want = max_context_len > size ? (int32_t)size : -1;
+  }
   if (want > 0 && want % kChunkTokens != 0) return PA_ERR_SHAPE;
   if (want < 0 || max_context_len <= want) {
     *ps = want > 0 ? want : kChunkTokens;
@@ -73,15 +92,15 @@ const char *pagedattn_version(void) { return "libpagedattn 0.1 gfx950"; }
 
 int32_t paged_attention_num_partitions(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t max_context_len, int32_t partition_size) {
-  (void)num_seqs;
-  (void)num_kv_heads;
   int32_t ps = 0;
-  return resolve_partitions(max_context_len, partition_size, &ps);
+  return resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps);
 }
 
-int32_t paged_attention_partition_tokens(int32_t max_context_len, int32_t partition_size) {
+int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                         int32_t max_context_len, int32_t partition_size) {
   int32_t ps = 0;
-  const int32_t P = resolve_partitions(max_context_len, partition_size, &ps);
+  const int32_t P =
+      resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps);
   if (P < 0) return P;
   return P > 1 ? ps : max_context_len;
 }
@@ -91,7 +110,7 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t max_context_len, int32_t partition_size) {
   if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
   int32_t ps = 0;
-  const int32_t P = resolve_partitions(max_context_len, partition_size, &ps);
+  const int32_t P = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps);
   (void)num_kv_heads;
   if (P <= 1) return 0;
   return (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
@@ -111,8 +130,9 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
   if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
-  // offsets inside one block are 32-bit in the kernels
-  if ((int64_t)block_size * num_kv_heads * head_dim >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  // byte offsets inside one block are 32-bit in the kernels
+  if ((int64_t)block_size * num_kv_heads * head_dim * elem_bytes(dtype) >= (int64_t(1) << 31))
+    return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
   if (!pa::decode_supported(dtype, head_dim, num_q_heads / num_kv_heads))
@@ -121,7 +141,7 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
 
   int32_t ps = 0;
-  const int32_t P = resolve_partitions(max_context_len, partition_size, &ps);
+  const int32_t P = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps);
   if (P < 0) return P;
   if ((int64_t)num_seqs * num_kv_heads * P >= (int64_t(1) << 32)) return PA_ERR_SHAPE;
   if ((int64_t)num_seqs * num_q_heads >= (int64_t(1) << 32)) return PA_ERR_SHAPE;

@@ -49,6 +49,20 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
+// Buffer descriptor over `bytes` bytes from `base` (raw buffer, no stride):
+// loads at offsets past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// Cache policies of a buffer load: normal, or non-temporal (streamed once).
+constexpr int kCacheNormal = 0;
+constexpr int kCacheStream = 2;
+template <int POLICY>
+__device__ __forceinline__ u32x4 buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -111,29 +125,55 @@ struct Decode {
   // past t1 are not read (their registers are zeroed) when MASK is set.
   // lane_off: this lane's element offset inside a token-row group
   // ((r * hkv + kvh) * D + c * EPV); row_elems = hkv * D; block_elems =
-  // block_size * hkv * D.
+  // block_size * hkv * D; mb = the table row length; has_prev / has_next:
+  // whether the sequence has a neighbour row in the table.
   template <bool MASK>
   static __device__ __forceinline__ void load(Regs &R, const T *__restrict__ kc,
                                               const T *__restrict__ vc,
                                               const int32_t *__restrict__ tbl, int cs, int t1,
                                               int lgB, int nb, int r, uint32_t lane_off,
-                                              int row_elems, int64_t block_elems) {
+                                              int row_elems, int64_t block_elems, int mb,
+                                              bool has_prev, bool has_next) {
     const int bm1 = (1 << lgB) - 1;
     if constexpr (!SMALLB) {
-      // the whole 16-token chunk lies in one block: one (scalar) table read
-      const uint32_t pid = min((uint32_t)tbl[cs >> lgB], (uint32_t)(nb - 1));
-      const int64_t base = (int64_t)pid * block_elems + (int64_t)(cs & bm1) * row_elems;
+      // the whole 16-token chunk lies in one block: one (scalar) table read,
+      // then buffer loads through descriptors spanning the block.  Cache
+      // hint: a block the previous or next sequence also holds at this
+      // logical position (a shared prefix, forked siblings) is read normally;
+      // any other block is streamed with non-temporal loads.
+      const int jb = cs >> lgB;
+      const int e = tbl[jb];
+      const bool reused = (has_prev && tbl[jb - mb] == e) || (has_next && tbl[jb + mb] == e);
+      const uint32_t pid = min((uint32_t)e, (uint32_t)(nb - 1));
+      const uint32_t bbytes = (uint32_t)(block_elems * (int64_t)sizeof(T));
+      const auto rk = block_rsrc(kc + (int64_t)pid * block_elems, bbytes);
+      const auto rv = block_rsrc(vc + (int64_t)pid * block_elems, bbytes);
+      const uint32_t base = (uint32_t)((cs & bm1) * row_elems) + lane_off;
+      uint32_t off[TPL];
+      bool ok[TPL];
 #pragma unroll
       for (int k = 0; k < TPL; ++k) {
-        const int64_t kb = base + (int64_t)(ROWS * k) * row_elems;
-        const u32x4 *kp = reinterpret_cast<const u32x4 *>(kc + kb + lane_off);
-        const u32x4 *vp = reinterpret_cast<const u32x4 *>(vc + kb + lane_off);
-        const bool ok = !MASK || cs + r + ROWS * k < t1;
+        off[k] = (base + (uint32_t)(ROWS * k * row_elems)) * (uint32_t)sizeof(T);
+        ok[k] = !MASK || cs + r + ROWS * k < t1;
+      }
+      if (reused) {
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          R.k[k][v] = ok ? kp[LPR * v] : u32x4{0, 0, 0, 0};
-          R.v[k][v] = ok ? vp[LPR * v] : u32x4{0, 0, 0, 0};
-        }
+        for (int k = 0; k < TPL; ++k)
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) {
+            const uint32_t o = off[k] + 16 * LPR * v;
+            R.k[k][v] = ok[k] ? buffer_load<kCacheNormal>(rk, o) : u32x4{0, 0, 0, 0};
+            R.v[k][v] = ok[k] ? buffer_load<kCacheNormal>(rv, o) : u32x4{0, 0, 0, 0};
+          }
+      } else {
+#pragma unroll
+        for (int k = 0; k < TPL; ++k)
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) {
+            const uint32_t o = off[k] + 16 * LPR * v;
+            R.k[k][v] = ok[k] ? buffer_load<kCacheStream>(rk, o) : u32x4{0, 0, 0, 0};
+            R.v[k][v] = ok[k] ? buffer_load<kCacheStream>(rv, o) : u32x4{0, 0, 0, 0};
+          }
       }
     } else {
       // blocks shorter than a chunk: every token row looks up its own block
@@ -149,8 +189,8 @@ struct Decode {
           const u32x4 *vp = reinterpret_cast<const u32x4 *>(vc + kb + lane_off);
 #pragma unroll
           for (int v = 0; v < VPL; ++v) {
-            R.k[k][v] = kp[LPR * v];
-            R.v[k][v] = vp[LPR * v];
+            R.k[k][v] = __builtin_nontemporal_load(kp + LPR * v);
+            R.v[k][v] = __builtin_nontemporal_load(vp + LPR * v);
           }
         } else {
 #pragma unroll
@@ -246,14 +286,15 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
   constexpr int TPL = K::TPL, VPL = K::VPL, LPR = K::LPR, EPV = K::EPV, DPL = K::DPL;
   (void)TPL;
 
-  // Work item: KV head fastest, then sequence, then partition.  With the
+  // Work item: KV head fastest, then sequence, then partition from the last
+  // down (long sequences' later partitions start first, short tails last).  With the
   // hardware's round-robin placement of consecutive workgroups over the 8 XCDs,
   // items that share a KV head (and so a prefix block's head slice) land on
   // the same XCD whenever num_kv_heads is a multiple of 8.
   const int id = blockIdx.x;
   const int kvh = id % hkv;
   const int s = (id / hkv) % num_seqs;
-  const int p = id / (hkv * num_seqs);
+  const int p = (P - 1) - id / (hkv * num_seqs);
   const int hq = hkv * G;
 
   int L = context_lens[s];
@@ -268,6 +309,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
   const int r = lane / LPR;
   const int c = lane % LPR;
   const int32_t *tbl = block_tables + (int64_t)s * mb;
+  const bool has_prev = s > 0, has_next = s + 1 < num_seqs;
 
   u32x4 qv[G][VPL];
 #pragma unroll
@@ -306,19 +348,19 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
     auto cstart = [&](int j) { return t0 + (wave + kWaves * j) * kChunk; };
     if (nw > 0) {
       K::template load<false>(A, kc, vc, tbl, cstart(0), t1, lgB, nb, r, lane_off, row_elems,
-                              block_elems);
+                              block_elems, mb, has_prev, has_next);
       int j = 0;
       for (; j + 2 < nw; j += 2) {
         K::template load<false>(Bq, kc, vc, tbl, cstart(j + 1), t1, lgB, nb, r, lane_off,
-                                row_elems, block_elems);
+                                row_elems, block_elems, mb, has_prev, has_next);
         K::template compute<false>(A, qv, acc, m, l, cstart(j), t1, r, sl2);
         K::template load<false>(A, kc, vc, tbl, cstart(j + 2), t1, lgB, nb, r, lane_off,
-                                row_elems, block_elems);
+                                row_elems, block_elems, mb, has_prev, has_next);
         K::template compute<false>(Bq, qv, acc, m, l, cstart(j + 1), t1, r, sl2);
       }
       if (j + 2 == nw) {
         K::template load<false>(Bq, kc, vc, tbl, cstart(j + 1), t1, lgB, nb, r, lane_off,
-                                row_elems, block_elems);
+                                row_elems, block_elems, mb, has_prev, has_next);
         K::template compute<false>(A, qv, acc, m, l, cstart(j), t1, r, sl2);
         K::template compute<false>(Bq, qv, acc, m, l, cstart(j + 1), t1, r, sl2);
       } else {
@@ -328,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
     if (t0 + nfull * kChunk < t1 && nfull % kWaves == wave) {
       const int cs = t0 + nfull * kChunk;
       K::template load<true>(A, kc, vc, tbl, cs, t1, lgB, nb, r, lane_off, row_elems,
-                             block_elems);
+                             block_elems, mb, has_prev, has_next);
       K::template compute<true>(A, qv, acc, m, l, cs, t1, r, sl2);
     }
   }

@@ -57,6 +57,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
+// Buffer descriptor over `bytes` bytes from `base` (raw buffer, no stride):
+// loads at offsets past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// Cache policies of a buffer load: normal, or non-temporal (streamed once).
+constexpr int kCacheNormal = 0;
+constexpr int kCacheStream = 2;
+template <int POLICY>
+__device__ __forceinline__ u32x4 buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+}
+
 // Broadcast lane R of each quad of 4 lanes to the whole quad.
 template <int R>
 __device__ __forceinline__ float quad_bcast(float x) {
@@ -80,27 +94,40 @@ struct MfmaDecode {
   template <bool MASK>
   static __device__ __forceinline__ void load(Tile &T, const uint16_t *__restrict__ kc,
                                               const uint16_t *__restrict__ vc,
-                                              const int32_t *__restrict__ tbl, int ent, int cs,
-                                              int t1,
+                                              const int32_t *__restrict__ tbl, int ent,
+                                              bool stream_v, int cs, int t1,
                                               int lgB, int nb, int g, int n, int row_elems,
                                               int head_off, int64_t block_elems) {
     const int bm1 = (1 << lgB) - 1;
     if constexpr (!SMALLB) {
       // a 16-aligned tile lies inside one block, whose id the caller read
-      // ahead of time (ent)
+      // ahead of time (ent); its rows are read through buffer descriptors
+      // spanning the block (reads past it return zeros)
       const uint32_t pid = min((uint32_t)ent, (uint32_t)(nb - 1));
-      const int64_t base = (int64_t)pid * block_elems + head_off;
+      const uint32_t bbytes = (uint32_t)(block_elems * 2);
+      const auto rk = block_rsrc(kc + (int64_t)pid * block_elems, bbytes);
+      const auto rv = block_rsrc(vc + (int64_t)pid * block_elems, bbytes);
       const int o = cs & bm1;
-      const u32x4 *kp = reinterpret_cast<const u32x4 *>(kc + base + (o + n) * row_elems + 8 * g);
+      const uint32_t koff = (uint32_t)(((o + n) * row_elems + head_off + 8 * g) * 2);
       const bool okk = !MASK || cs + n < t1;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) T.k[s] = okk ? kp[4 * s] : u32x4{0, 0, 0, 0};
+      for (int s = 0; s < 4; ++s)
+        T.k[s] = okk ? buffer_load<kCacheNormal>(rk, koff + 64 * s) : u32x4{0, 0, 0, 0};
+      uint32_t voff[4];
+      bool ok[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4 *vp =
-            reinterpret_cast<const u32x4 *>(vc + base + (o + 4 * g + j) * row_elems + 8 * n);
-        const bool ok = !MASK || cs + 4 * g + j < t1;
-        T.v[j] = ok ? *vp : u32x4{0, 0, 0, 0};
+        voff[j] = (uint32_t)(((o + 4 * g + j) * row_elems + head_off + 8 * n) * 2);
+        ok[j] = !MASK || cs + 4 * g + j < t1;
+      }
+      if (stream_v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          T.v[j] = ok[j] ? buffer_load<kCacheStream>(rv, voff[j]) : u32x4{0, 0, 0, 0};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          T.v[j] = ok[j] ? buffer_load<kCacheNormal>(rv, voff[j]) : u32x4{0, 0, 0, 0};
       }
     } else {
       // blocks shorter than a tile: each token row looks up its own block
@@ -120,8 +147,8 @@ struct MfmaDecode {
         const int tv = cs + 4 * g + j;
         if (!MASK || tv < t1) {
           const uint32_t pid = min((uint32_t)tbl[tv >> lgB], (uint32_t)(nb - 1));
-          T.v[j] = *reinterpret_cast<const u32x4 *>(
-              vc + (int64_t)pid * block_elems + head_off + (tv & bm1) * row_elems + 8 * n);
+          T.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+              vc + (int64_t)pid * block_elems + head_off + (tv & bm1) * row_elems + 8 * n));
         } else {
           T.v[j] = u32x4{0, 0, 0, 0};
         }
@@ -216,10 +243,11 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   constexpr bool WIDE = K::WIDE;
 
   const int id = blockIdx.x;
-  // work item: KV head fastest, then sequence, then partition (as in decode.hip)
+  // work item: KV head fastest, then sequence, then partition from the last
+  // down (as in decode.hip)
   const int kvh = id % hkv;
   const int s = (id / hkv) % num_seqs;
-  const int p = id / (hkv * num_seqs);
+  const int p = (P - 1) - id / (hkv * num_seqs);
   const int hq = hkv * G;
 
   int L = context_lens[s];
@@ -262,38 +290,66 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
 
   // Block ids of this wave's tiles, read 64 tiles at a time into a register
   // (lane i: tile 64c + i) one chunk ahead of use, so no table read sits
-  // between a tile's loads and the previous tile's.
+  // between a tile's loads and the previous tile's.  With them, a cache hint
+  // per tile: a block that the previous or next sequence holds at the same
+  // logical position (a shared prefix, forked siblings) is likely to be read
+  // again soon, so its V rows are read normally; every other block's V rows
+  // are streamed with non-temporal loads.  (The hint only steers caching;
+  // entries past a neighbour's length may match by chance, which is harmless.)
   int ent_cur = 0, ent_next = 0;
-  auto chunk_entries = [&](int c) {
+  uint64_t nt_cur = 0, nt_next = 0;
+  auto chunk_entries = [&](int c, uint64_t &ntmask) {
     const int cs = cstart(64 * c + lane);
-    return (!SMALLB && cs < t1) ? tbl[cs >> lgB] : 0;
+    int e = 0;
+    bool stream = false;
+    if (!SMALLB && cs < t1) {
+      const int jb = cs >> lgB;
+      e = tbl[jb];
+      const bool prev_same = s > 0 && tbl[jb - mb] == e;
+      const bool next_same = s + 1 < num_seqs && tbl[jb + mb] == e;
+      stream = !prev_same && !next_same;
+    }
+    ntmask = __builtin_amdgcn_ballot_w64(stream);
+    return e;
   };
-  ent_cur = chunk_entries(0);
-  ent_next = chunk_entries(1);
-  auto entry = [&](int j) {
-    if constexpr (SMALLB) return 0;
+  ent_cur = chunk_entries(0, nt_cur);
+  ent_next = chunk_entries(1, nt_next);
+  // the j-th tile's block id; stream_v receives its hint
+  auto entry = [&](int j, bool &stream_v) {
+    if constexpr (SMALLB) {
+      stream_v = true;
+      return 0;
+    }
     if (j > 0 && (j & 63) == 0) {
       ent_cur = ent_next;
-      ent_next = chunk_entries((j >> 6) + 1);
+      nt_cur = nt_next;
+      ent_next = chunk_entries((j >> 6) + 1, nt_next);
     }
+    stream_v = (nt_cur >> (j & 63)) & 1;
     return __builtin_amdgcn_readlane(ent_cur, j & 63);
   };
   {
     Tile A, Bt;
+    bool sv = true;
+    int ent = 0;
     if (nw > 0) {
-      K::template load<false>(A, kc, vc, tbl, entry(0), cstart(0), t1, lgB, nb, g, n, row_elems,
+      ent = entry(0, sv);
+      K::template load<false>(A, kc, vc, tbl, ent, sv, cstart(0), t1, lgB, nb, g, n, row_elems,
                               head_off, block_elems);
       int j = 0;
       for (; j + 2 < nw; j += 2) {
-        K::template load<false>(Bt, kc, vc, tbl, entry(j + 1), cstart(j + 1), t1, lgB, nb, g, n,
+        ent = entry(j + 1, sv);
+        K::template load<false>(Bt, kc, vc, tbl, ent, sv, cstart(j + 1), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
         K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
-        K::template load<false>(A, kc, vc, tbl, entry(j + 2), cstart(j + 2), t1, lgB, nb, g, n,
+        ent = entry(j + 2, sv);
+        K::template load<false>(A, kc, vc, tbl, ent, sv, cstart(j + 2), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
         K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2);
       }
       if (j + 2 == nw) {
-        K::template load<false>(Bt, kc, vc, tbl, entry(j + 1), cstart(j + 1), t1, lgB, nb, g, n,
+        ent = entry(j + 1, sv);
+        K::template load<false>(Bt, kc, vc, tbl, ent, sv, cstart(j + 1), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
         K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
         K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2);
@@ -303,7 +359,8 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     }
     if (t0 + nfull * kTile < t1 && nfull % kWaves == wave) {
       const int cs = t0 + nfull * kTile;
-      K::template load<true>(A, kc, vc, tbl, entry(nw), cs, t1, lgB, nb, g, n, row_elems,
+      ent = entry(nw, sv);
+      K::template load<true>(A, kc, vc, tbl, ent, sv, cs, t1, lgB, nb, g, n, row_elems,
                              head_off, block_elems);
       K::template compute<true>(A, qb, acc, m, lsum, cs, t1, g, sl2);
     }

@@ -87,14 +87,22 @@ def test_partition_policy():
     lib = _lib.lib()
     assert lib.paged_attention_num_partitions(8, 8, 32768, 512) == 64
     assert lib.paged_attention_num_partitions(8, 8, 32768, -1) == 1
-    assert lib.paged_attention_num_partitions(8, 8, 2048, 0) == 1
-    assert lib.paged_attention_num_partitions(8, 8, 2049, 0) == 2
+    assert lib.paged_attention_num_partitions(8, 8, 2048, 0) == 4  # 64 pairs: 512-token parts
+    assert lib.paged_attention_num_partitions(256, 8, 2048, 0) == 1
+    assert lib.paged_attention_num_partitions(8, 8, 2049, 0) == 5  # 8 parts of 272 -> 512 floor
     assert lib.paged_attention_num_partitions(256, 8, 8192, 0) == 4
     assert lib.paged_attention_num_partitions(8, 8, 100, 24) == -2
-    assert lib.paged_attention_partition_tokens(8192, 0) == 2048
-    assert lib.paged_attention_partition_tokens(1500, 0) == 1500
-    assert lib.paged_attention_partition_tokens(32768, 512) == 512
-    assert lib.paged_attention_partition_tokens(100, 24) == -2
+    assert lib.paged_attention_partition_tokens(256, 8, 8192, 0) == 2048
+    assert lib.paged_attention_partition_tokens(256, 8, 1500, 0) == 1500
+    assert lib.paged_attention_partition_tokens(8, 8, 32768, 512) == 512
+    assert lib.paged_attention_partition_tokens(8, 8, 100, 24) == -2
+    # few (sequence, KV head) pairs: about two workgroups per CU
+    assert lib.paged_attention_partition_tokens(8, 8, 32768, 0) == 4096
+    assert lib.paged_attention_num_partitions(8, 8, 32768, 0) == 8
+    assert lib.paged_attention_partition_tokens(100, 1, 32768, 0) == 6560  # 5 parts
+    assert lib.paged_attention_partition_tokens(255, 1, 4096, 0) == 2048  # 2 parts
+    assert lib.paged_attention_partition_tokens(8, 8, 1000, 0) == 512  # 512 minimum
+    assert lib.paged_attention_partition_tokens(8, 8, 500, 0) == 500  # shorter: no split
     assert lib.paged_attention_workspace_size(8, 64, 8, 128, 32768, 512) == 8 * 64 * 64 * 130 * 4
     assert lib.paged_attention_workspace_size(8, 64, 8, 128, 500, 0) == 0
 

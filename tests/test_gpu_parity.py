@@ -11,7 +11,8 @@ import pytest
 import torch
 
 from oracle import oracle as O
-from workloads import make_case, make_fork_case, make_prefix_case, make_private_case
+from workloads import (make_aliased_case, make_case, make_fork_case, make_prefix_case,
+                       make_private_case)
 from workloads.generate import permute_pool
 
 from gpu_helpers import TOL, DeviceCase, bits, host_bits, max_err, oracle_step, say
@@ -115,6 +116,52 @@ def test_longctx_small_both_block_sizes():
                               max_blocks_per_seq=4096 // B)
         outs.append(run_and_compare(c, c.name, 512)[0])
     assert np.abs(outs[0] - outs[1]).max() <= 2 * TOL["bf16"]
+
+
+# ---------------------------------------------------------------- shared blocks
+
+@pytest.mark.parametrize("ps", [0, 32, 64])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G,Hkv", [(4, 2), (8, 1)])
+def test_arbitrary_block_sharing(G, Hkv, B, ps):
+    """Tables that share blocks in arbitrary runs (holes, several donors, runs
+    across the 16/G-sequence groups the kernel reads shared blocks for), with
+    empty and equal-length sequences among them."""
+    rng = np.random.default_rng(100 + G + B)
+    lens = rng.integers(1, 300, size=13).tolist() + [0, 160, 160, 161, 257]
+    c = make_aliased_case(f"alias-G{G}-B{B}", lens, G * Hkv, Hkv, 128, B, "bf16", 40 + G + B,
+                          n_alias=60)
+    run_and_compare(c, c.name, ps)
+
+
+@pytest.mark.parametrize("G,Hkv", [(4, 2), (8, 1)])
+def test_identical_sequences_share_everything(G, Hkv):
+    """Every sequence of each run of 16/G has the same table and length: all of
+    their blocks are read by shared items, none by private ones."""
+    R = 16 // G
+    base = make_private_case("same", [37, 64, 200, 5], G * Hkv, Hkv, 128, 16, "bf16", 11)
+    lens = np.repeat(base.context_lens, R)
+    tables = np.repeat(base.block_tables, R, axis=0)
+    q = make_private_case("q", [1] * len(lens), G * Hkv, Hkv, 128, 16, "bf16", 12).q
+    c = make_private_case("same", [1] * len(lens), G * Hkv, Hkv, 128, 16, "bf16", 13)
+    c.context_lens = lens.astype(np.int32)
+    c.block_tables = np.ascontiguousarray(tables)
+    c.k_cache, c.v_cache, c.q = base.k_cache, base.v_cache, q
+    for ps in (0, 32):
+        out, _, _ = run_and_compare(c, "same-seqs", ps)
+
+
+def test_sharing_determinism_and_permutation_invariance():
+    c = make_aliased_case("alias-perm", [40, 300, 77, 1000, 5, 64, 65, 512, 513, 33, 16, 999],
+                          32, 8, 128, 16, "bf16", 19, n_alias=40)
+    say("alias-perm: base run twice")
+    a = DeviceCase(c).run_decode(64).cpu().numpy()
+    a2 = DeviceCase(c).run_decode(64).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), a2.view(np.uint32))
+    k2, v2, t2, _, _, _ = permute_pool(c, 4)
+    say("alias-perm: permuted pool")
+    b = DeviceCase(c, tables=t2, k_cache=k2, v_cache=v2).run_decode(64).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 # ---------------------------------------------------------------- invariants

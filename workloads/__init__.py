@@ -8,6 +8,7 @@ from .generate import (  # noqa: F401
     Case,
     CONFIG_NAMES,
     bf16_bits_from_f32,
+    make_aliased_case,
     make_case,
     make_fork_case,
     make_prefix_case,

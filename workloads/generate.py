@@ -382,6 +382,35 @@ def make_fork_case(name: str, lens, n_groups: int, fork_n: int, num_q_heads: int
                 k_new=k_new, v_new=v_new, logical_k=lk, logical_v=lv)
 
 
+def make_aliased_case(name: str, lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      block_size: int, dtype: str, seed: int, n_alias: int, *,
+                      poison: bool = True) -> Case:
+    """A decode-only case whose block tables share blocks in arbitrary
+    patterns, not just prefixes: starting from private blocks, ``n_alias``
+    seeded times a sequence's logical block j is pointed at the physical block
+    another sequence holds at the same logical position (both blocks full in
+    both sequences, so no poisoned slot is ever attended).  Blocks of the
+    second sequence that lose their last reference stay in the pool unread.
+    The attended values follow from the tables alone."""
+    c = make_private_case(name, lens, num_q_heads, num_kv_heads, head_dim, block_size, dtype,
+                          seed, poison=poison)
+    rng = np.random.default_rng([seed, 2])
+    B = block_size
+    L = c.context_lens.astype(np.int64)
+    S = len(L)
+    tables = c.block_tables.copy()
+    for _ in range(n_alias):
+        a, b = (int(x) for x in rng.integers(0, S, size=2))
+        full = int(min(L[a], L[b]) // B)
+        if a == b or full == 0:
+            continue
+        lo = int(rng.integers(0, full))
+        hi = int(rng.integers(lo + 1, full + 1))
+        tables[b, lo:hi] = tables[a, lo:hi]
+    c.block_tables = tables
+    return c
+
+
 def config_lengths(config: int, rng: np.random.Generator) -> np.ndarray:
     """Context lengths of the five named workloads (drawn first from the
     structure stream)."""
