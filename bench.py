@@ -54,8 +54,8 @@ DECODE_KERNELS = ("paged_decode_mfma_kernel", "paged_decode_kernel", "paged_deco
 # calibration copy: CAL_PAIRS blocks of CAL_BLOCK_BYTES in each of two caches
 CAL_BLOCKS = 16384
 CAL_PAIRS = 8192
-CAL_SHAPE = (CAL_BLOCKS, 16, 8, 128)  # bf16 -> 32 KiB per block
-CAL_BLOCK_BYTES = 16 * 8 * 128 * 2
+CAL_SHAPE = (CAL_BLOCKS, 8, 16, 128)  # [blocks][kv_heads][block_size][head_dim], bf16: 32 KiB
+CAL_BLOCK_BYTES = 8 * 16 * 128 * 2
 CAL_READ_BYTES = 2 * CAL_PAIRS * CAL_BLOCK_BYTES
 CAL_WRITE_BYTES = CAL_READ_BYTES
 

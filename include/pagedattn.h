@@ -25,12 +25,16 @@
  *    passed in; the numbers produced for such inputs are unspecified.
  *
  * KV pool layout (one layer): k_cache and v_cache are each
- *   [num_blocks][block_size][num_kv_heads][head_dim], head_dim contiguous,
- * so one token's row for one KV head is head_dim contiguous elements and one
- * token's rows for all KV heads are num_kv_heads*head_dim contiguous elements.
- * The slot of logical position t of a sequence whose block table row is `tbl`
- * is tbl[t / block_size] * block_size + t % block_size ([P1] section 2.1 block
- * table; [P1] section 3.3 append into the current block until it is full).
+ *   [num_blocks][num_kv_heads][block_size][head_dim], head_dim contiguous
+ * (the order of the cache in [P3] section "核心代码拆解"): one token's row for
+ * one KV head is head_dim contiguous elements, and a KV head's rows of one
+ * block are block_size*head_dim contiguous elements.  The slot of logical
+ * position t of a sequence whose block table row is `tbl` is
+ * tbl[t / block_size] * block_size + t % block_size ([P1] section 2.1 block
+ * table; [P1] section 3.3 append into the current block until it is full);
+ * its row for KV head h is at element
+ * ((slot / block_size * num_kv_heads + h) * block_size + slot % block_size)
+ * * head_dim.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -139,9 +143,9 @@ int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  * kv_cache_write -- store each new token's K and V rows in the pool.
  *
  * For i in [0, num_tokens) with slot = slot_mapping[i] >= 0: copies
- * k[i] and v[i] (num_kv_heads*head_dim elements each) to block
- * slot / block_size, offset slot % block_size of k_cache and v_cache, bit for
- * bit ([P1] section 3.1: the generated token's K/V is written back to the
+ * k[i] and v[i] (num_kv_heads rows of head_dim elements each) to block
+ * slot / block_size, offset slot % block_size of every KV head of k_cache and
+ * v_cache, bit for bit ([P1] section 3.1: the generated token's K/V is written back to the
  * cache; section 3.3 append_slot).  Negative slots are skipped (padding);
  * slots >= num_blocks*block_size are skipped too.  Two tokens must not share a
  * slot (the winner would be unspecified).

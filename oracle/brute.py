@@ -27,7 +27,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, block_
     S = len(q)
     Hq = len(q[0])
     D = len(q[0][0])
-    Hkv = len(k_cache[0][0])
+    Hkv = len(k_cache[0])  # pool [blocks][kv_heads][block_size][head_dim]
     G = Hq // Hkv
     sc = float(scale)
     out = []
@@ -46,7 +46,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, block_
                         break
                     dot = 0.0
                     for d in range(D):
-                        dot += _value(q[s][h][d], dtype) * _value(k_cache[phys][o][g][d], dtype)
+                        dot += _value(q[s][h][d], dtype) * _value(k_cache[phys][g][o][d], dtype)
                     scores.append(sc * dot)
                     kv_pos.append((phys, o))
             if not scores:
@@ -58,7 +58,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, block_
             acc = [0.0] * D
             for wi, (phys, o) in zip(w, kv_pos):
                 for d in range(D):
-                    acc[d] += wi * _value(v_cache[phys][o][g][d], dtype)
+                    acc[d] += wi * _value(v_cache[phys][g][o][d], dtype)
             rows.append([a / tot for a in acc])
         out.append(rows)
     return out

@@ -25,7 +25,9 @@ What is computed, and where the pages say so:
 Readings taken where the pages are silent (each also listed in the design
 notes):
 
-* cache layout ``[num_blocks, block_size, num_kv_heads, head_dim]``;
+* cache layout ``[num_blocks, num_kv_heads, block_size, head_dim]``: the
+  order of the key/value caches of the kernel in the devpress.csdn.net/amd
+  walkthrough's "核心代码拆解" section (blocks, heads, block_size, head_size);
 * query head h reads KV head ``h // (num_q_heads // num_kv_heads)``;
 * a sequence attends exactly its positions ``[0, context_len)``; a context of
   length 0 produces zeros;
@@ -74,6 +76,7 @@ def gather_sequence(k_cache: np.ndarray, v_cache: np.ndarray, table_row: np.ndar
                     kv_head: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """K and V of one sequence in logical order, as float64.
 
+    The pool is ``[num_blocks, num_kv_heads, block_size, head_dim]``.
     Returns ``[L, Hkv, D]`` arrays, or ``[L, D]`` for one KV head.  Positions
     at or beyond ``context_len`` are never touched, nor are table entries past
     ``ceil(context_len / B)``."""
@@ -82,11 +85,11 @@ def gather_sequence(k_cache: np.ndarray, v_cache: np.ndarray, table_row: np.ndar
     phys = np.asarray(table_row)[pos // block_size]
     off = pos % block_size
     if kv_head is None:
-        k = k_cache[phys, off]
-        v = v_cache[phys, off]
+        k = k_cache[phys, :, off]  # advanced indices first: [L, Hkv, D]
+        v = v_cache[phys, :, off]
     else:
-        k = k_cache[phys, off, kv_head]
-        v = v_cache[phys, off, kv_head]
+        k = k_cache[phys, kv_head, off]
+        v = v_cache[phys, kv_head, off]
     return to_f64(k, dtype), to_f64(v, dtype)
 
 
@@ -118,7 +121,7 @@ def paged_attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarr
     ``context_lens[s]`` positions, gathered through ``block_tables[s]``.
     Returns float64 ``[S, Hq, D]``."""
     S, Hq, D = q.shape
-    Hkv = k_cache.shape[2]
+    Hkv = k_cache.shape[1]
     G = _group(Hq, Hkv)
     qf = to_f64(q, dtype)
     out = np.zeros((S, Hq, D), np.float64)
@@ -138,7 +141,7 @@ def paged_attention_decode_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.
     """The same as ``paged_attention_decode`` for selected (seq, q_head) pairs
     only; returns ``[len(rows), D]``."""
     S, Hq, D = q.shape
-    Hkv = k_cache.shape[2]
+    Hkv = k_cache.shape[1]
     G = _group(Hq, Hkv)
     qf = to_f64(q, dtype)
     res = []
@@ -159,7 +162,7 @@ def paged_attention_decode_partitioned(q: np.ndarray, k_cache: np.ndarray, v_cac
     ``l_p * exp(m_p - max_p m_p)``.  Equal to ``paged_attention_decode`` up to
     rounding."""
     S, Hq, D = q.shape
-    Hkv = k_cache.shape[2]
+    Hkv = k_cache.shape[1]
     G = _group(Hq, Hkv)
     qf = to_f64(q, dtype)
     sc = np.float64(np.float32(scale))
@@ -201,8 +204,8 @@ def kv_cache_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray, k_cac
     for i, slot in enumerate(np.asarray(slot_mapping).tolist()):
         if slot < 0:
             continue
-        kc[slot // block_size, slot % block_size] = k[i]
-        vc[slot // block_size, slot % block_size] = v[i]
+        kc[slot // block_size, :, slot % block_size] = k[i]
+        vc[slot // block_size, :, slot % block_size] = v[i]
     return kc, vc
 
 

@@ -113,13 +113,13 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
                            stream=None) -> None:
     """Decode attention through the block tables (see include/pagedattn.h).
 
-    q: [S, Hq, D]; k_cache/v_cache: [NB, B, Hkv, D] (float32 or bfloat16);
+    q: [S, Hq, D]; k_cache/v_cache: [NB, Hkv, B, D] (float32 or bfloat16);
     block_tables: int32 [S, MB]; context_lens: int32 [S]; out: float32 [S, Hq, D].
     ``workspace`` (a uint8 device tensor) is allocated here when needed and not
     given; callers timing the kernel pass one in."""
     import torch
     S, Hq, D = q.shape
-    NB, B, Hkv, D2 = k_cache.shape
+    NB, Hkv, B, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("q/k_cache/v_cache shapes disagree")
     MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
@@ -140,7 +140,7 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
 def kv_cache_write(k, v, slot_mapping, k_cache, v_cache, *, stream=None) -> None:
     """Store k[i], v[i] ([T, Hkv, D]) at slot slot_mapping[i] of the pool."""
     T = k.shape[0]
-    NB, B, Hkv, D = k_cache.shape
+    NB, Hkv, B, D = k_cache.shape
     for t in (k, v, slot_mapping, k_cache, v_cache):
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
@@ -154,7 +154,7 @@ def copy_blocks(src_dst_pairs, k_cache, v_cache, *, host_pairs=None, stream=None
     ``src_dst_pairs`` (int32 [P, 2] on the device).  ``host_pairs`` (a
     contiguous int32 CPU tensor or numpy array with the same pairs) turns on the
     host-side overlap check."""
-    NB, B, Hkv, D = k_cache.shape
+    NB, Hkv, B, D = k_cache.shape
     P = src_dst_pairs.shape[0] if src_dst_pairs.dim() == 2 else 0
     hp = None
     keep = None

@@ -192,12 +192,13 @@ int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping
   if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
+  const int64_t head_row_bytes = (int64_t)head_dim * elem_bytes(dtype);
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_row_bytes;
+  // the grid covers a token's rows in stripes of 128 vectors
   if (row_bytes / 16 > (int64_t)128 * 65535) return PA_ERR_SHAPE;
-  const hipError_t e =
-      pa::launch_kv_cache_write(k, v, slot_mapping, num_tokens, k_cache, v_cache,
-                                (int64_t)num_blocks * block_size, row_bytes,
-                                static_cast<hipStream_t>(stream));
+  const hipError_t e = pa::launch_kv_cache_write(
+      k, v, slot_mapping, num_tokens, k_cache, v_cache, (int64_t)num_blocks * block_size,
+      log2_exact(block_size), num_kv_heads, head_row_bytes, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

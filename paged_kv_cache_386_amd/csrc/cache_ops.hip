@@ -1,8 +1,8 @@
 // KV-cache edits of a decode step, for gfx950:
 //
-//  * kv_cache_write: each new token's K and V rows (all KV heads, one
-//    contiguous row of num_kv_heads*head_dim elements in the pool layout) are
-//    stored at its slot ("3.1" and "3.3" sections of the chenxutan.com vLLM
+//  * kv_cache_write: each new token's K and V rows (one head_dim row per KV
+//    head; in the pool [blocks][kv_heads][block_size][head_dim] each goes to
+//    its head's slab of the slot's block) are stored at its slot ("3.1" and "3.3" sections of the chenxutan.com vLLM
 //    deep-dive: the generated token's K/V goes back into the cache, appended
 //    into the sequence's current block);
 //  * copy_blocks: whole physical blocks copied onto others, the copy-on-write
@@ -27,20 +27,28 @@ constexpr int kWriteThreads = 128;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyVecsPerThread = 4;
 
-// grid.x = token, grid.y = stripe of the row; a row is row_vecs 16-byte vectors.
+// grid.x = token, grid.y = stripe of the token's rows (hkv heads of head_vecs
+// 16-byte vectors each, contiguous in the source).  Vector j belongs to head
+// j / head_vecs and lands in that head's slab of the slot's block.
 __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ v,
     const int32_t *__restrict__ slot_mapping, u32x4 *__restrict__ kc, u32x4 *__restrict__ vc,
-    int64_t num_slots, int64_t row_vecs) {
+    int64_t num_slots, int lgB, int hkv, int head_vecs) {
   const int64_t i = blockIdx.x;
-  const int64_t j = (int64_t)blockIdx.y * kWriteThreads + threadIdx.x;
+  const int row_vecs = hkv * head_vecs;
+  const int j = blockIdx.y * kWriteThreads + threadIdx.x;
   if (j >= row_vecs) return;
   const int32_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_slots) return;
+  const int h = j / head_vecs;
+  const int jj = j - h * head_vecs;
+  const int64_t blk = slot >> lgB;
+  const int off = slot & ((1 << lgB) - 1);
+  const int64_t dst = (((blk * hkv + h) << lgB) + off) * head_vecs + jj;
   const u32x4 kx = k[i * row_vecs + j];
   const u32x4 vx = v[i * row_vecs + j];
-  kc[(int64_t)slot * row_vecs + j] = kx;
-  vc[(int64_t)slot * row_vecs + j] = vx;
+  kc[dst] = kx;
+  vc[dst] = vx;
 }
 
 // grid.x = pair, grid.y = stripe of kCopyThreads*kCopyVecsPerThread vectors of
@@ -72,14 +80,17 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
 
 hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                                  int32_t num_tokens, void *k_cache, void *v_cache,
-                                 int64_t num_slots, int64_t row_bytes, hipStream_t stream) {
+                                 int64_t num_slots, int32_t log2_block_size, int32_t num_kv_heads,
+                                 int64_t head_row_bytes, hipStream_t stream) {
   if (num_tokens <= 0) return hipSuccess;
-  const int64_t row_vecs = row_bytes / 16;
+  const int64_t head_vecs = head_row_bytes / 16;
+  const int64_t row_vecs = head_vecs * num_kv_heads;
   const int64_t stripes = (row_vecs + kWriteThreads - 1) / kWriteThreads;
   hipLaunchKernelGGL(kv_cache_write_kernel, dim3((uint32_t)num_tokens, (uint32_t)stripes),
                      dim3(kWriteThreads), 0, stream, static_cast<const u32x4 *>(k),
                      static_cast<const u32x4 *>(v), slot_mapping, static_cast<u32x4 *>(k_cache),
-                     static_cast<u32x4 *>(v_cache), num_slots, row_vecs);
+                     static_cast<u32x4 *>(v_cache), num_slots, (int)log2_block_size,
+                     (int)num_kv_heads, (int)head_vecs);
   return hipGetLastError();
 }
 

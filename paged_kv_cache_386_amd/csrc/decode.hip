@@ -11,9 +11,10 @@
 //
 //  * one workgroup of 4 wave64s per (sequence, KV head, partition); the G query
 //    heads of a GQA group share every K/V read;
-//  * KV rows are head_dim contiguous elements ([blocks][block_size][kv_heads]
-//    [head_dim]), so a row of LPR lanes reads one whole row with 16-byte loads
-//    and a wave reads 64/LPR rows per load instruction;
+//  * the pool is [blocks][kv_heads][block_size][head_dim]: a KV head's rows
+//    of one block are contiguous, a row of LPR lanes reads one whole row with
+//    16-byte loads and a wave reads 64/LPR consecutive rows per load
+//    instruction;
 //  * each wave takes 16-token chunks round-robin and double-buffers them in
 //    registers (the next chunk's loads are in flight while the current one is
 //    computed); a 16-aligned chunk never straddles a block when
@@ -123,8 +124,9 @@ struct Decode {
 
   // Issue the loads of one chunk's K and V rows for this lane.  Tokens at or
   // past t1 are not read (their registers are zeroed) when MASK is set.
-  // lane_off: this lane's element offset inside a token-row group
-  // ((r * hkv + kvh) * D + c * EPV); row_elems = hkv * D; block_elems =
+  // lane_off: this lane's element offset inside a block
+  // ((kvh * block_size + r) * D + c * EPV); row_elems = D (token stride of
+  // one KV head); block_elems =
   // block_size * hkv * D; mb = the table row length; has_prev / has_next:
   // whether the sequence has a neighbour row in the table.
   template <bool MASK>
@@ -330,9 +332,9 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
     for (int j = 0; j < DPL; ++j) acc[h][j] = 0.f;
   }
 
-  const uint32_t lane_off = (uint32_t)((r * hkv + kvh) * D + c * EPV);
-  const int row_elems = hkv * D;
-  const int64_t block_elems = ((int64_t)row_elems) << lgB;
+  const uint32_t lane_off = (uint32_t)(((kvh << lgB) + r) * D + c * EPV);
+  const int row_elems = D;
+  const int64_t block_elems = ((int64_t)hkv * D) << lgB;
 
   // Full 16-token chunks go round-robin over the waves (this wave's j-th chunk
   // is chunk wave + 4j) through a two-stage register pipeline: the loads of

@@ -277,9 +277,11 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = neg_inf(), lsum = 0.f;
 
-  const int row_elems = hkv * kD;
-  const int head_off = kvh * kD;
-  const int64_t block_elems = ((int64_t)row_elems) << lgB;
+  // pool layout [blocks][kv_heads][block_size][head_dim]: consecutive tokens of
+  // one KV head are kD elements apart, a head's slab of a block is kD << lgB
+  const int row_elems = kD;
+  const int head_off = kvh * (kD << lgB);
+  const int64_t block_elems = ((int64_t)hkv * kD) << lgB;
 
   // full tiles round-robin over the waves (this wave's j-th tile is tile
   // wave + 4j), two-stage register pipeline, the last one or two peeled; the

@@ -40,7 +40,8 @@ hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream);
 
 hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                                  int32_t num_tokens, void *k_cache, void *v_cache,
-                                 int64_t num_slots, int64_t row_bytes, hipStream_t stream);
+                                 int64_t num_slots, int32_t log2_block_size, int32_t num_kv_heads,
+                                 int64_t head_row_bytes, hipStream_t stream);
 
 hipError_t launch_copy_blocks(const int32_t *pairs, int32_t num_pairs, void *k_cache,
                               void *v_cache, int32_t num_blocks, int64_t block_bytes,

@@ -63,7 +63,7 @@ def one_token_mismatches(case, decode=None) -> int:
             continue
         p = case.block_tables[s, 0]
         for h in range(case.num_q_heads):
-            v = O.to_f64(case.v_cache[p, 0, h // G], case.dtype)
+            v = O.to_f64(case.v_cache[p, h // G, 0], case.dtype)
             bad += int(not np.array_equal(got[s, h], v))
     return bad
 
@@ -79,9 +79,9 @@ def identical_keys_error(case, decode=None) -> float:
         if L == 0:
             continue
         p0 = case.block_tables[s, 0]
-        row = kc[p0, 0].copy()
+        row = kc[p0, :, 0].copy()
         for t in range(L):
-            kc[case.block_tables[s, t // B], t % B] = row
+            kc[case.block_tables[s, t // B], :, t % B] = row
     got = decode(case.q, kc, case.v_cache, case.block_tables, case.context_lens, case.scale,
                  B, case.dtype)
     G = case.num_q_heads // case.num_kv_heads
@@ -90,7 +90,7 @@ def identical_keys_error(case, decode=None) -> float:
         L = int(case.context_lens[s])
         if L == 0:
             continue
-        V = np.stack([O.to_f64(case.v_cache[case.block_tables[s, t // B], t % B], case.dtype)
+        V = np.stack([O.to_f64(case.v_cache[case.block_tables[s, t // B], :, t % B], case.dtype)
                       for t in range(L)])  # [L, Hkv, D]
         mean = V.mean(axis=0)
         for h in range(case.num_q_heads):

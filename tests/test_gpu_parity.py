@@ -59,7 +59,7 @@ def test_config0_fp32_all_outputs(ps):
     out, ref, _ = run_and_compare(make_case(0), "cfg0", ps)
     # one-token sequence returns its V row exactly
     c = make_case(0)
-    v = c.v_cache[c.block_tables[0, 0], 0]  # [Hkv, D]
+    v = c.v_cache[c.block_tables[0, 0], :, 0]  # [Hkv, D]
     assert np.array_equal(out[0], v.astype(np.float32))
 
 
@@ -183,14 +183,14 @@ def test_identical_keys_give_mean_of_v():
     c = make_private_case("idk", [1, 33, 500], 4, 2, 128, 16, "bf16", 4)
     kc = c.k_cache.copy()
     for s, L in enumerate(c.context_lens.tolist()):
-        row = kc[c.block_tables[s, 0], 0].copy()
+        row = kc[c.block_tables[s, 0], :, 0].copy()
         for t in range(L):
-            kc[c.block_tables[s, t // 16], t % 16] = row
+            kc[c.block_tables[s, t // 16], :, t % 16] = row
     say("identical keys")
     dc = DeviceCase(c, k_cache=kc)
     out = dc.run_decode(0).cpu().numpy()
     for s, L in enumerate(c.context_lens.tolist()):
-        V = np.stack([O.to_f64(c.v_cache[c.block_tables[s, t // 16], t % 16], "bf16")
+        V = np.stack([O.to_f64(c.v_cache[c.block_tables[s, t // 16], :, t % 16], "bf16")
                       for t in range(L)]).mean(axis=0)
         for h in range(4):
             assert np.abs(out[s, h] - V[h // 2]).max() <= TOL["bf16"]

@@ -18,7 +18,7 @@ def _decode_with(gather=None, kv_head_of=None, scale_mul=1.0, swap_kv=False, neg
                  row_shift=0):
     def decode(q, kc, vc, tables, lens, scale, B, dtype):
         S, Hq, D = q.shape
-        Hkv = kc.shape[2]
+        Hkv = kc.shape[1]
         G = Hq // Hkv
         qf = O.to_f64(q, dtype)
         out = np.zeros((S, Hq, D))
@@ -49,7 +49,7 @@ def _gather_shifted_offset(kc, vc, row, L, B, dtype):
     pos = np.arange(L)
     phys = np.asarray(row)[pos // B]
     off = (pos + 1) % B
-    return O.to_f64(kc[phys, off], dtype), O.to_f64(vc[phys, off], dtype)
+    return O.to_f64(kc[phys, :, off], dtype), O.to_f64(vc[phys, :, off], dtype)
 
 
 MUTANTS = {
@@ -101,4 +101,4 @@ def test_write_mutant_is_caught():
     s, L = 4, int(c.context_lens[4])
     pos = np.arange(L)
     phys = c.block_tables[s][pos // c.block_size]
-    assert not np.array_equal(kc[phys, pos % c.block_size], c.logical_k[s])
+    assert not np.array_equal(kc[phys, :, pos % c.block_size], c.logical_k[s])

@@ -72,12 +72,12 @@ def test_page3_pool_picture_gather_order():
     pool = g["pool"]
     NB = len(pool)
     # each block's K rows encode (request, ordinal, offset); free blocks are NaN
-    kc = np.full((NB, B, 1, 3), np.nan, np.float32)
+    kc = np.full((NB, 1, B, 3), np.nan, np.float32)
     for p, tag in enumerate(pool):
         if tag is None:
             continue
         for o in range(B):
-            kc[p, o, 0] = [ord(tag[0]), int(tag[1:]), o]
+            kc[p, 0, o] = [ord(tag[0]), int(tag[1:]), o]
     for req, table in g["tables"].items():
         assert [pool[p] for p in table] == [f"{req}{i + 1}" for i in range(len(table))]
         L = len(table) * B - 3  # last block partly used
@@ -225,19 +225,20 @@ def test_copy_then_write_rebuilds_logical_tokens(maker):
         L = int(c.context_lens[s])
         pos = np.arange(L)
         phys = c.block_tables[s][pos // c.block_size]
-        assert np.array_equal(kc[phys, pos % c.block_size], c.logical_k[s])
-        assert np.array_equal(vc[phys, pos % c.block_size], c.logical_v[s])
+        assert np.array_equal(kc[phys, :, pos % c.block_size], c.logical_k[s])
+        assert np.array_equal(vc[phys, :, pos % c.block_size], c.logical_v[s])
 
 
 def test_write_skips_negative_slots_and_is_bitwise():
-    kc = np.arange(2 * 4 * 1 * 2, dtype=np.uint16).reshape(2, 4, 1, 2)
+    # pool [blocks=2][kv_heads=1][block_size=4][head_dim=2]; slot 5 = block 1, offset 1
+    kc = np.arange(2 * 1 * 4 * 2, dtype=np.uint16).reshape(2, 1, 4, 2)
     k = np.array([[[0x7FC1, 0xFFFF]], [[1, 2]], [[3, 4]]], np.uint16)
     out_k, out_v = O.kv_cache_write(k, k, np.array([5, -1, 0]), kc, kc, 4)
     want = kc.copy()
-    want[1, 1] = k[0]
-    want[0, 0] = k[2]
+    want[1, :, 1] = k[0]
+    want[0, :, 0] = k[2]
     assert np.array_equal(out_k, want) and np.array_equal(out_v, want)
-    assert np.array_equal(kc, np.arange(16, dtype=np.uint16).reshape(2, 4, 1, 2))  # input untouched
+    assert np.array_equal(kc, np.arange(16, dtype=np.uint16).reshape(2, 1, 4, 2))  # input untouched
 
 
 def test_copy_blocks_in_list_order():

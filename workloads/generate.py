@@ -3,7 +3,7 @@
 Every workload is a *decode step* over a paged KV pool:
 
 * a pool of physical blocks, ``k_cache``/``v_cache`` of shape
-  ``[num_blocks, block_size, num_kv_heads, head_dim]`` (head_dim contiguous),
+  ``[num_blocks, num_kv_heads, block_size, head_dim]`` (head_dim contiguous),
   stored as float32 or as raw bfloat16 bit patterns (``uint16``);
 * per-sequence block tables (logical block -> physical block id) and context
   lengths;
@@ -84,7 +84,7 @@ class Case:
     block_size: int
     context_lens: np.ndarray  # int32 [S]; counts every token attended, incl. the new one
     block_tables: np.ndarray  # int32 [S, MB]; table used by decode (after copy-on-write)
-    k_cache: np.ndarray  # [NB, B, Hkv, D] pool before the step's edits
+    k_cache: np.ndarray  # [NB, Hkv, B, D] pool before the step's edits
     v_cache: np.ndarray
     q: np.ndarray  # [S, Hq, D]
     scale: np.float32
@@ -122,7 +122,7 @@ class Case:
 class _Pool:
     def __init__(self, nb: int, B: int, hkv: int, d: int, dtype: str, poison: bool):
         st = _storage(dtype)
-        shape = (nb, B, hkv, d)
+        shape = (nb, hkv, B, d)
         if poison:
             fill = F32_QNAN_BITS if dtype == "f32" else BF16_QNAN
             if dtype == "f32":
@@ -144,8 +144,8 @@ class _Pool:
         t = np.arange(start, start + len(k))
         phys = blocks[t // self.B]
         off = t % self.B
-        self.k[phys, off] = k
-        self.v[phys, off] = v
+        self.k[phys, :, off] = k  # k is [len, Hkv, D]
+        self.v[phys, :, off] = v
 
 
 def _cdiv(a: int, b: int) -> int:
