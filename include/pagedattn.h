@@ -54,7 +54,10 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = -4, /* valid but not compiled in (head_dim, group size) */
   PA_ERR_WORKSPACE = -5,   /* split-K workspace missing or too small */
   PA_ERR_ALIAS = -6,       /* copy pairs overlap (checked only when requested) */
-  PA_ERR_LAUNCH = -7       /* the HIP runtime refused the launch */
+  PA_ERR_LAUNCH = -7,      /* the HIP runtime refused the launch */
+  PA_ERR_OOM = -8,         /* block manager: no free block left */
+  PA_ERR_NO_SEQ = -9,      /* block manager: unknown sequence id */
+  PA_ERR_SEQ_EXISTS = -10  /* block manager: sequence id already in use */
 } pa_status;
 
 typedef enum pa_dtype {

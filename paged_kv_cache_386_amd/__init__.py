@@ -5,6 +5,8 @@ The Python names mirror the C entry points in ``include/pagedattn.h``; they
 only marshal arguments (torch supplies device memory and the stream).
 """
 from ._lib import (  # noqa: F401
+    BlockManager,
+    BlockStats,
     PA_BF16,
     PA_F32,
     PagedAttnError,

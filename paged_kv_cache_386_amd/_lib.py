@@ -20,6 +20,7 @@ PA_OK = 0
 STATUS_NAMES = {
     0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
     -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_ALIAS", -7: "PA_ERR_LAUNCH",
+    -8: "PA_ERR_OOM", -9: "PA_ERR_NO_SEQ", -10: "PA_ERR_SEQ_EXISTS",
 }
 
 # exported symbol -> (restype, argtypes)
@@ -35,6 +36,19 @@ SIGNATURES = {
     "kv_cache_write": (_I32, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
     "copy_blocks": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
     "pagedattn_status_string": (ctypes.c_char_p, [_I32]),
+    # block manager (include/pagedattn_blocks.h)
+    "pa_bm_create": (_VP, [_I32, _I32]),
+    "pa_bm_destroy": (None, [_VP]),
+    "pa_bm_num_free_blocks": (_I32, [_VP]),
+    "pa_bm_can_allocate": (_I32, [_VP, _I32]),
+    "pa_bm_add_sequence": (_I32, [_VP, ctypes.c_int64, _I32, _VP]),
+    "pa_bm_fork": (_I32, [_VP, ctypes.c_int64, ctypes.c_int64]),
+    "pa_bm_append_slot": (_I32, [_VP, ctypes.c_int64, _VP, _VP, _VP]),
+    "pa_bm_free_sequence": (_I32, [_VP, ctypes.c_int64]),
+    "pa_bm_context_len": (_I32, [_VP, ctypes.c_int64]),
+    "pa_bm_block_table": (_I32, [_VP, ctypes.c_int64, _VP, _I32]),
+    "pa_bm_prepare_decode": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "pa_bm_stats": (_I32, [_VP, _VP]),
     "pagedattn_version": (ctypes.c_char_p, []),
 }
 
@@ -166,3 +180,100 @@ def copy_blocks(src_dst_pairs, k_cache, v_cache, *, host_pairs=None, stream=None
                            _dtype_code(k_cache), hp, _stream(stream))
     del keep
     _check("copy_blocks", st)
+
+
+# ---------------------------------------------------------------- block manager
+
+class BlockStats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("shared_blocks", ctypes.c_int32), ("num_sequences", ctypes.c_int32),
+                ("tokens_logical", ctypes.c_int64), ("tokens_stored", ctypes.c_int64),
+                ("slots_allocated", ctypes.c_int64), ("utilisation", ctypes.c_double)]
+
+
+class BlockManager:
+    """The host block manager of libpagedattn (include/pagedattn_blocks.h):
+    pool, block tables, reference-counted forks with copy-on-write, and the
+    index arrays of a decode step.  Argument marshalling only."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+        self._h = lib().pa_bm_create(num_blocks, block_size)
+        if not self._h:
+            raise ValueError(f"bad block manager sizes ({num_blocks}, {block_size})")
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free_blocks(self) -> int:
+        return int(lib().pa_bm_num_free_blocks(self._h))
+
+    def can_allocate(self, num_tokens: int) -> bool:
+        return bool(lib().pa_bm_can_allocate(self._h, num_tokens))
+
+    def add_sequence(self, seq_id: int, num_tokens: int):
+        """Admit a sequence holding num_tokens tokens; returns their slots (int32)."""
+        import numpy as np
+        slots = np.zeros(max(num_tokens, 1), np.int32)
+        _check("pa_bm_add_sequence", lib().pa_bm_add_sequence(
+            self._h, seq_id, num_tokens, slots.ctypes.data_as(ctypes.c_void_p)))
+        return slots[:num_tokens]
+
+    def fork(self, parent: int, child: int) -> None:
+        _check("pa_bm_fork", lib().pa_bm_fork(self._h, parent, child))
+
+    def append_slot(self, seq_id: int):
+        """Returns (slot, copy_src, copy_dst); the copy pair is (-1, -1) when none."""
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_bm_append_slot", lib().pa_bm_append_slot(
+            self._h, seq_id, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def free_sequence(self, seq_id: int) -> None:
+        _check("pa_bm_free_sequence", lib().pa_bm_free_sequence(self._h, seq_id))
+
+    def context_len(self, seq_id: int) -> int:
+        n = int(lib().pa_bm_context_len(self._h, seq_id))
+        if n < 0:
+            raise PagedAttnError("pa_bm_context_len", n)
+        return n
+
+    def block_table(self, seq_id: int):
+        import numpy as np
+        n = int(lib().pa_bm_block_table(self._h, seq_id, None, 0))
+        if n < 0:
+            raise PagedAttnError("pa_bm_block_table", n)
+        t = np.zeros(max(n, 1), np.int32)
+        lib().pa_bm_block_table(self._h, seq_id, t.ctypes.data_as(ctypes.c_void_p), n)
+        return t[:n]
+
+    def prepare_decode(self, seq_ids, max_blocks: int, pad_block: int = 0):
+        """One decode step: returns (slot_mapping [n], copy_pairs [P, 2],
+        block_tables [n, max_blocks], context_lens [n]) as int32 numpy arrays."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, np.int64))
+        n = len(ids)
+        slots = np.zeros(max(n, 1), np.int32)
+        pairs = np.zeros((max(n, 1), 2), np.int32)
+        tables = np.zeros((max(n, 1), max(max_blocks, 1)), np.int32)
+        lens = np.zeros(max(n, 1), np.int32)
+        npairs = ctypes.c_int32(0)
+        vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+        _check("pa_bm_prepare_decode", lib().pa_bm_prepare_decode(
+            self._h, vp(ids), n, max_blocks, pad_block, vp(slots), vp(pairs),
+            ctypes.byref(npairs), vp(tables), vp(lens)))
+        return slots[:n], pairs[:npairs.value].copy(), tables[:n, :max_blocks], lens[:n]
+
+    def stats(self) -> BlockStats:
+        st = BlockStats()
+        _check("pa_bm_stats", lib().pa_bm_stats(self._h, ctypes.byref(st)))
+        return st

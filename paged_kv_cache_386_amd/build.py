@@ -40,7 +40,9 @@ def _hipcc() -> str:
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    """HIP translation units (device code) and plain C++ ones (host only)."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
@@ -49,7 +51,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-c", src, "-o", obj]
+        lang = ["-x", "c++"] if src.endswith(".cpp") else []
+        cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, *lang, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -84,6 +84,9 @@ const char *pagedattn_status_string(int32_t status) {
     case PA_ERR_WORKSPACE: return "split-K workspace missing or too small";
     case PA_ERR_ALIAS: return "copy pairs overlap (a dst repeats or is also a src)";
     case PA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case PA_ERR_OOM: return "no free KV block left";
+    case PA_ERR_NO_SEQ: return "unknown sequence id";
+    case PA_ERR_SEQ_EXISTS: return "sequence id already in use";
     default: return "unknown status";
   }
 }

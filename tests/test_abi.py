@@ -11,14 +11,14 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pagedattn.h", "pagedattn_blocks.h")]
 LIB = os.path.join(ROOT, "paged_kv_cache_386_amd", "libpagedattn.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpagedattn.so not built")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     for want in ("paged_attention_decode", "kv_cache_write", "copy_blocks",
                  "paged_attention_workspace_size", "paged_attention_num_partitions",
                  "paged_attention_partition_tokens",
-                 "pagedattn_status_string", "pagedattn_version"):
+                 "pagedattn_status_string", "pagedattn_version", "pa_bm_create",
+                 "pa_bm_prepare_decode", "pa_bm_append_slot", "pa_bm_fork", "pa_bm_stats"):
         assert want in names
 
 

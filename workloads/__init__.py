@@ -8,6 +8,7 @@ from .generate import (  # noqa: F401
     Case,
     CONFIG_NAMES,
     bf16_bits_from_f32,
+    draw_values,
     make_aliased_case,
     make_case,
     make_fork_case,

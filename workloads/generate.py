@@ -68,6 +68,13 @@ def _draw(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return x if dtype == "f32" else bf16_bits_from_f32(x)
 
 
+def draw_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """N(0, 1) values in the storage form of ``dtype`` (float32, or the
+    bfloat16 bit patterns of the rounded values), for callers that build
+    their own sequences token by token."""
+    return _draw(rng, shape, dtype)
+
+
 def _storage(dtype: str):
     return np.float32 if dtype == "f32" else np.uint16
 
