@@ -7,6 +7,9 @@ only marshal arguments (torch supplies device memory and the stream).
 from ._lib import (  # noqa: F401
     BlockManager,
     BlockStats,
+    Engine,
+    EngineConfig,
+    StepInfo,
     PA_BF16,
     PA_F32,
     PagedAttnError,

@@ -49,6 +49,14 @@ SIGNATURES = {
     "pa_bm_block_table": (_I32, [_VP, ctypes.c_int64, _VP, _I32]),
     "pa_bm_prepare_decode": (_I32, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
     "pa_bm_stats": (_I32, [_VP, _VP]),
+    # engine (include/pagedattn_engine.h)
+    "pa_engine_create": (_I32, [_VP, _VP, _VP, _VP]),
+    "pa_engine_destroy": (None, [_VP]),
+    "pa_engine_submit": (_I32, [_VP, ctypes.c_int64, _I32, _I32, _I32]),
+    "pa_engine_step": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, _VP, _VP]),
+    "pa_engine_num_waiting": (_I32, [_VP]),
+    "pa_engine_num_running": (_I32, [_VP]),
+    "pa_engine_blocks": (_VP, [_VP]),
     "pagedattn_version": (ctypes.c_char_p, []),
 }
 
@@ -277,3 +285,133 @@ class BlockManager:
         st = BlockStats()
         _check("pa_bm_stats", lib().pa_bm_stats(self._h, ctypes.byref(st)))
         return st
+
+
+# ---------------------------------------------------------------- engine
+
+class EngineConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_blocks", "block_size", "num_q_heads", "num_kv_heads", "head_dim", "dtype",
+        "max_batch", "max_context_len", "max_prompt_rows", "partition_size", "device")]
+
+
+class _StepInfo(ctypes.Structure):
+    _P64 = ctypes.POINTER(ctypes.c_int64)
+    _P32 = ctypes.POINTER(ctypes.c_int32)
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("admitted", ctypes.c_int32),
+        ("prompt_rows", ctypes.c_int32), ("preempted", ctypes.c_int32),
+        ("finished", ctypes.c_int32), ("num_copies", ctypes.c_int32),
+        ("max_context_len", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+        ("context_tokens", ctypes.c_int64),
+        ("batch_seq_ids", _P64), ("context_lens", _P32), ("slot_mapping", _P32),
+        ("block_tables", _P32), ("copy_pairs", _P32), ("admitted_seq_ids", _P64),
+        ("admitted_rows", _P32), ("prompt_slots", _P32), ("preempted_seq_ids", _P64),
+        ("finished_seq_ids", _P64), ("max_blocks_per_seq", ctypes.c_int32),
+    ]
+
+
+class StepInfo:
+    """What one engine step did, copied out of the engine's host arrays (the
+    counts only when ``arrays`` is false)."""
+
+    def __init__(self, raw: _StepInfo, arrays: bool = True):
+        for k in ("batch", "admitted", "prompt_rows", "preempted", "finished", "num_copies",
+                  "max_context_len", "free_blocks", "context_tokens"):
+            setattr(self, k, int(getattr(raw, k)))
+        if not arrays:
+            return
+        import numpy as np
+
+        def arr(p, n, dt, shape=None):
+            if n == 0:
+                return np.zeros(shape or (0,), dt)
+            a = np.ctypeslib.as_array(p, shape=(n,)).copy()
+            return a.reshape(shape) if shape else a
+
+        n = raw.batch
+        mb = raw.max_blocks_per_seq
+        self.batch_seq_ids = arr(raw.batch_seq_ids, n, np.int64)
+        self.context_lens = arr(raw.context_lens, n, np.int32)
+        self.slot_mapping = arr(raw.slot_mapping, n, np.int32)
+        self.block_tables = arr(raw.block_tables, n * mb, np.int32, (n, mb))
+        self.copy_pairs = arr(raw.copy_pairs, 2 * raw.num_copies, np.int32,
+                              (raw.num_copies, 2))
+        self.admitted_seq_ids = arr(raw.admitted_seq_ids, raw.admitted, np.int64)
+        self.admitted_rows = arr(raw.admitted_rows, raw.admitted, np.int32)
+        self.prompt_slots = arr(raw.prompt_slots, raw.prompt_rows, np.int32)
+        self.preempted_seq_ids = arr(raw.preempted_seq_ids, raw.preempted, np.int64)
+        self.finished_seq_ids = arr(raw.finished_seq_ids, raw.finished, np.int64)
+
+
+class Engine:
+    """The continuously batched decode engine of libpagedattn
+    (include/pagedattn_engine.h).  Argument marshalling only.
+
+    ``k_cache``/``v_cache`` (torch tensors [NB, Hkv, B, D]) give the pool;
+    with ``k_cache=None`` the engine only plans (no GPU use), and then the
+    pool sizes come from the keyword arguments."""
+
+    def __init__(self, k_cache=None, v_cache=None, *, num_q_heads: int, max_batch: int,
+                 max_context_len: int, max_prompt_rows: int = 0, partition_size: int = 0,
+                 num_blocks: int = 0, block_size: int = 0, num_kv_heads: int = 0,
+                 head_dim: int = 0, dtype: int = PA_BF16):
+        device = k_cache is not None
+        if device:
+            num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+            dtype = _dtype_code(k_cache)
+            if tuple(v_cache.shape) != tuple(k_cache.shape) or not k_cache.is_contiguous() \
+                    or not v_cache.is_contiguous():
+                raise ValueError("k_cache/v_cache must be contiguous and of one shape")
+        self.cfg = EngineConfig(num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
+                                dtype, max_batch, max_context_len,
+                                max_prompt_rows or max_context_len, partition_size,
+                                1 if device else 0)
+        self._pool = (k_cache, v_cache)
+        h = ctypes.c_void_p()
+        _check("pa_engine_create", lib().pa_engine_create(
+            ctypes.byref(self.cfg), _ptr(k_cache), _ptr(v_cache), ctypes.byref(h)))
+        self._h = h.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().pa_engine_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, request_id: int, prompt_len: int, max_new_tokens: int,
+               num_samples: int = 1) -> None:
+        _check("pa_engine_submit", lib().pa_engine_submit(
+            self._h, request_id, prompt_len, max_new_tokens, num_samples))
+
+    def step(self, q=None, k_new=None, v_new=None, prompt_k=None, prompt_v=None,
+             scale: float = 1.0, out=None, *, stream=None, arrays: bool = True) -> StepInfo:
+        raw = _StepInfo()
+        st = _stream(stream) if self.cfg.device else 0
+        _check("pa_engine_step", lib().pa_engine_step(
+            self._h, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(prompt_k), _ptr(prompt_v),
+            float(scale), _ptr(out), st, ctypes.byref(raw)))
+        return StepInfo(raw, arrays)
+
+    def num_waiting(self) -> int:
+        return int(lib().pa_engine_num_waiting(self._h))
+
+    def num_running(self) -> int:
+        return int(lib().pa_engine_num_running(self._h))
+
+    def block_stats(self) -> BlockStats:
+        st = BlockStats()
+        _check("pa_bm_stats", lib().pa_bm_stats(lib().pa_engine_blocks(self._h),
+                                                 ctypes.byref(st)))
+        return st
+
+    def context_len(self, seq_id: int) -> int:
+        n = int(lib().pa_bm_context_len(lib().pa_engine_blocks(self._h), seq_id))
+        if n < 0:
+            raise PagedAttnError("pa_bm_context_len", n)
+        return n

@@ -312,3 +312,96 @@ def test_serving_loop_on_the_oracle(dtype, Hq, Hkv, D, B, NB, seed):
     assert loop.copies > 0 and loop.steps == 16
     if NB < 100:
         assert loop.preempted > 0
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,B,NB,max_batch,seed", [
+    ("bf16", 4, 2, 64, 4, 300, 16, 1),
+    ("f32", 2, 1, 64, 8, 120, 32, 2),
+    ("bf16", 4, 2, 64, 4, 60, 12, 3),   # small pool: preemption
+])
+def test_engine_plans_on_the_oracle(dtype, Hq, Hkv, D, B, NB, max_batch, seed):
+    """The engine's scheduler and planning (plan-only mode) drive the oracle's
+    edits and decode: FCFS admission, forks for parallel samples, finishes,
+    preemption with recompute; every request gets exactly its tokens."""
+    from serving_loop import EngineHarness, drive_engine
+    h = EngineHarness("oracle", dtype, Hq, Hkv, D, B, NB, max_batch, max_ctx=96, seed=seed)
+    drive_engine(h, num_requests=40, seed=seed, max_prompt=60, max_new=30)
+    assert h.copies > 0 and h.admitted >= 40
+    if NB < 100:
+        assert h.preempted > 0
+
+
+def _plan_engine(**kw):
+    import paged_kv_cache_386_amd as pa
+    args = dict(num_q_heads=4, max_batch=8, max_context_len=64, num_blocks=40, block_size=4,
+                num_kv_heads=2, head_dim=64)
+    args.update(kw)
+    return pa.Engine(**args)
+
+
+def test_engine_submit_checks():
+    from paged_kv_cache_386_amd import PagedAttnError
+    e = _plan_engine()
+    e.submit(1, 10, 5)
+    for args, status in [((1, 10, 5), -10),        # id in use
+                         ((-1, 10, 5), -10),       # id out of range
+                         ((2, 0, 5), -2),          # empty prompt
+                         ((2, 60, 5), -2),         # longer than max_context_len
+                         ((2, 10, 0), -2),         # no decode step
+                         ((2, 10, 5, 9), -2),      # more samples than max_batch
+                         ((2, 8, 56, 8), -2)]:     # cannot run alone: 2 + 8*14 blocks
+        with pytest.raises(PagedAttnError) as ex:
+            e.submit(*args)
+        assert _status(ex) == status, args
+    assert e.num_waiting() == 1
+
+
+def test_engine_admits_first_come_first_served():
+    e = _plan_engine(max_batch=4)
+    e.submit(7, 5, 3)
+    e.submit(3, 5, 3, 2)
+    e.submit(9, 5, 3, 2)   # does not fit the batch beside the first two
+    e.submit(4, 1, 3)      # would fit, but admission stops at the first miss
+    info = e.step()
+    assert info.admitted_seq_ids.tolist() == [7 << 8, 3 << 8]
+    assert info.batch_seq_ids.tolist() == [7 << 8, 3 << 8, (3 << 8) | 1]
+    assert e.num_waiting() == 2
+    # the fork copies the shared partial prompt block once (5 % 4 != 0)
+    assert info.num_copies == 1
+    for _ in range(2):
+        info = e.step()
+    assert sorted(info.finished_seq_ids.tolist()) == [3 << 8, (3 << 8) | 1, 7 << 8]
+    info = e.step()
+    assert info.admitted_seq_ids.tolist() == [9 << 8, 4 << 8]
+
+
+def test_engine_preemption_requeues_the_newest_and_admits_nothing():
+    # 12 blocks of 4 (watermark 0); two requests of 8 + 20 tokens (7 blocks
+    # each at the end) run together until their 25th tokens need 14 blocks
+    e = _plan_engine(num_blocks=12, max_batch=4, max_context_len=40)
+    e.submit(1, 8, 20)
+    e.submit(2, 8, 20)
+    preempt_step = readmit = None
+    last_len = {}
+    for step in range(200):
+        if step == 10:
+            e.submit(3, 1, 1)  # waits behind nothing, admitted at once
+        info = e.step()
+        for sid, L in zip(info.batch_seq_ids.tolist(), info.context_lens.tolist()):
+            last_len[sid] = L
+        if info.preempted:
+            assert preempt_step is None
+            preempt_step = step
+            assert info.preempted_seq_ids.tolist() == [2 << 8]
+            assert info.admitted == 0
+            assert info.batch_seq_ids.tolist() == [1 << 8]
+            held = last_len[2 << 8]
+        if preempt_step is not None and (2 << 8) in info.admitted_seq_ids.tolist():
+            readmit = step
+            rows = info.admitted_rows[info.admitted_seq_ids.tolist().index(2 << 8)]
+            assert rows == held  # recomputed whole
+        if e.num_running() == 0 and e.num_waiting() == 0:
+            break
+    assert preempt_step == 16 and readmit is not None and readmit > preempt_step
+    assert last_len == {1 << 8: 28, 2 << 8: 28, 3 << 8: 2}
+    assert e.block_stats().free_blocks == 12

@@ -80,3 +80,25 @@ def test_serving_loop_preempts_when_the_pool_is_full():
     drive(loop, steps=20, partition_size=0, max_prompt=200, admit_p=0.8,
           sync=torch.cuda.synchronize)
     assert loop.preempted > 0
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,B,NB,ps", [
+    ("bf16", 32, 8, 128, 16, 800, 0),   # matrix-core decode, automatic partitions
+    ("bf16", 16, 2, 128, 16, 800, 64),  # groups of 8, forced 64-token partitions
+    ("f32", 8, 2, 64, 16, 800, 0),      # vector decode
+    ("bf16", 32, 8, 128, 16, 90, 0),    # small pool: preemption and recompute
+])
+def test_engine_steps_match_oracle(dtype, Hq, Hkv, D, B, NB, ps):
+    """The native engine (scheduler, block manager, one index copy and four
+    device calls per step) over a stream of requests with parallel samples:
+    after every step the pool holds each batch row's tokens bit for bit and
+    decode matches dense attention over them."""
+    from serving_loop import EngineHarness, drive_engine
+    say(f"engine {dtype} Hq={Hq} Hkv={Hkv} D={D} B={B} NB={NB} ps={ps}")
+    h = EngineHarness("device", dtype, Hq, Hkv, D, B, NB, max_batch=48, max_ctx=400,
+                      seed=NB + D, partition_size=ps)
+    drive_engine(h, num_requests=36, seed=NB + D, max_prompt=300, max_new=40)
+    assert h.copies > 0
+    if NB < 100:
+        assert h.preempted > 0
+    h.eng.close()
