@@ -56,9 +56,12 @@
  * Sequence ids: sample s of request r is (r << 8) | s.  A preempted sample
  * keeps its id when it is re-admitted.
  *
- * Unlike the calls of pagedattn.h, an engine owns memory: its device index
- * buffers, a split-K workspace and two pinned host staging buffers, allocated
- * once by pa_engine_create (nothing is allocated per step).  The pool
+ * Unlike the calls of pagedattn.h, an engine owns memory and a stream: two
+ * pinned host staging buffers and two device index buffers (steps alternate
+ * between them), a split-K workspace, and a copy stream (default priority)
+ * on which a step's index copy runs while the previous step's kernels still
+ * run on the caller's stream, which then waits for it through an event.
+ * Everything is allocated once by pa_engine_create; nothing per step.  The pool
  * (k_cache, v_cache) stays the caller's.  Calls on one engine must not
  * overlap, and every step of an engine must use the same stream (or streams
  * the caller orders): a step's device work reads index buffers the next step

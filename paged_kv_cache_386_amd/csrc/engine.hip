@@ -69,9 +69,15 @@ struct pa_engine {
   // index arrays, int32: [slots maxb][lens maxb][pairs 2 maxb][prompt slots R][tables maxb*MB]
   size_t off_lens = 0, off_pairs = 0, off_prompt = 0, off_tables = 0, words = 0;
   int32_t *staging[2] = {nullptr, nullptr};  // pinned host (device mode) or heap
-  hipEvent_t staged[2] = {nullptr, nullptr};
+  // double buffering: step t uses staging[t % 2] and dev_index[t % 2]; the
+  // index copy runs on the engine's own copy stream, so that it overlaps the
+  // previous step's kernels, and the caller's stream waits for it
+  hipEvent_t copied[2] = {nullptr, nullptr};    // copy stream: staging -> device done
+  hipEvent_t consumed[2] = {nullptr, nullptr};  // caller's stream: the step's kernels done
   bool pending[2] = {false, false};
-  int32_t *dev_index = nullptr;
+  bool used[2] = {false, false};
+  int32_t *dev_index[2] = {nullptr, nullptr};
+  hipStream_t copy_stream = nullptr;
   void *workspace = nullptr;
   size_t workspace_bytes = 0;
   int parity = 0;
@@ -86,12 +92,11 @@ namespace {
 void release(pa_engine *e) {
   if (!e) return;
   // device work of earlier steps may still read the index buffers
-  if (e->cfg.device && e->dev_index) (void)hipDeviceSynchronize();
+  if (e->cfg.device) (void)hipDeviceSynchronize();
   for (int b = 0; b < 2; ++b) {
-    if (e->staged[b]) {
-      if (e->pending[b]) (void)hipEventSynchronize(e->staged[b]);
-      (void)hipEventDestroy(e->staged[b]);
-    }
+    if (e->copied[b]) (void)hipEventDestroy(e->copied[b]);
+    if (e->consumed[b]) (void)hipEventDestroy(e->consumed[b]);
+    if (e->dev_index[b]) (void)hipFree(e->dev_index[b]);
     if (e->staging[b]) {
       if (e->cfg.device)
         (void)hipHostFree(e->staging[b]);
@@ -99,7 +104,7 @@ void release(pa_engine *e) {
         delete[] e->staging[b];
     }
   }
-  if (e->dev_index) (void)hipFree(e->dev_index);
+  if (e->copy_stream) (void)hipStreamDestroy(e->copy_stream);
   if (e->workspace) (void)hipFree(e->workspace);
   if (e->bm) pa_bm_destroy(e->bm);
   delete e;
@@ -197,10 +202,20 @@ int32_t pa_engine_create(const pa_engine_config *cfg, void *k_cache, void *v_cac
         release(e);
         return PA_ERR_OOM;
       }
-      if (hipEventCreateWithFlags(&e->staged[b], hipEventDisableTiming) != hipSuccess) {
-        e->staged[b] = nullptr;
+      if (hipEventCreateWithFlags(&e->copied[b], hipEventDisableTiming) != hipSuccess) {
+        e->copied[b] = nullptr;
         release(e);
         return PA_ERR_LAUNCH;
+      }
+      if (hipEventCreateWithFlags(&e->consumed[b], hipEventDisableTiming) != hipSuccess) {
+        e->consumed[b] = nullptr;
+        release(e);
+        return PA_ERR_LAUNCH;
+      }
+      if (hipMalloc((void **)&e->dev_index[b], bytes) != hipSuccess) {
+        e->dev_index[b] = nullptr;
+        release(e);
+        return PA_ERR_OOM;
       }
     } else {
       e->staging[b] = new (std::nothrow) int32_t[e->words];
@@ -211,10 +226,12 @@ int32_t pa_engine_create(const pa_engine_config *cfg, void *k_cache, void *v_cac
     }
   }
   if (c.device) {
-    if (hipMalloc((void **)&e->dev_index, bytes) != hipSuccess) {
-      e->dev_index = nullptr;
+    // default priority; non-blocking so that it never waits on the legacy
+    // default stream implicitly (every dependency is an explicit event)
+    if (hipStreamCreateWithFlags(&e->copy_stream, hipStreamNonBlocking) != hipSuccess) {
+      e->copy_stream = nullptr;
       release(e);
-      return PA_ERR_OOM;
+      return PA_ERR_LAUNCH;
     }
     // the split-K workspace of the largest step: for a fixed batch the
     // partition count grows with the longest context, so the longest one
@@ -286,7 +303,7 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
   // the staging buffer of this step was last copied from two steps ago
   const int buf = e->parity;
   if (e->pending[buf]) {
-    if (hipEventSynchronize(e->staged[buf]) != hipSuccess) return PA_ERR_LAUNCH;
+    if (hipEventSynchronize(e->copied[buf]) != hipSuccess) return PA_ERR_LAUNCH;
     e->pending[buf] = false;
   }
   int32_t *hs = e->staging[buf];
@@ -375,15 +392,20 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
     //    copy-on-write copies, new-token writes and decode, in stream order
     if (c.device && n > 0) {
       const size_t words = e->off_tables + (size_t)n * MB;
-      if (hipMemcpyAsync(e->dev_index, hs, words * sizeof(int32_t), hipMemcpyHostToDevice,
-                         st) != hipSuccess ||
-          hipEventRecord(e->staged[buf], st) != hipSuccess)
+      int32_t *dix = e->dev_index[buf];
+      // the copy may overwrite dix only once the kernels of two steps ago,
+      // which read it, are done
+      if ((e->used[buf] && hipStreamWaitEvent(e->copy_stream, e->consumed[buf], 0) != hipSuccess) ||
+          hipMemcpyAsync(dix, hs, words * sizeof(int32_t), hipMemcpyHostToDevice,
+                         e->copy_stream) != hipSuccess ||
+          hipEventRecord(e->copied[buf], e->copy_stream) != hipSuccess ||
+          hipStreamWaitEvent(st, e->copied[buf], 0) != hipSuccess)
         return PA_ERR_LAUNCH;
       e->pending[buf] = true;
-      const int32_t *d_slots = e->dev_index, *d_lens = e->dev_index + e->off_lens;
-      const int32_t *d_pairs = e->dev_index + e->off_pairs;
-      const int32_t *d_prompt = e->dev_index + e->off_prompt;
-      const int32_t *d_tables = e->dev_index + e->off_tables;
+      const int32_t *d_slots = dix, *d_lens = dix + e->off_lens;
+      const int32_t *d_pairs = dix + e->off_pairs;
+      const int32_t *d_prompt = dix + e->off_prompt;
+      const int32_t *d_tables = dix + e->off_tables;
       int32_t rc;
       if (rows_used) {
         rc = kv_cache_write(prompt_k, prompt_v, d_prompt, rows_used, e->k_cache, e->v_cache,
@@ -403,6 +425,8 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
                                   MB, max_ctx, c.dtype, c.partition_size, e->workspace,
                                   e->workspace_bytes, stream);
       if (rc != PA_OK) return rc;
+      if (hipEventRecord(e->consumed[buf], st) != hipSuccess) return PA_ERR_LAUNCH;
+      e->used[buf] = true;
       e->parity ^= 1;
     }
 
