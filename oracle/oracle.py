@@ -36,6 +36,14 @@ notes):
   skipped by the write;
 * the split-K merge (not on the pages) is the log-sum-exp combination of
   per-partition maxima, sums and normalised outputs.
+* multi-query attention (a chunk of prompt tokens, or tokens to verify, per
+  sequence: the chenxutan.com page, sections 2.3 (prefill computes the KV of
+  all input tokens at once), 4.3 and 5.1 (chunked prefill slices a long
+  prompt into pieces run beside decode) and 5.4 (speculative decoding: the
+  main model checks several guessed tokens in one pass)): the chunk's tokens
+  are the sequence's last ``n`` cached positions, and chunk token i, at
+  position ``p = L - n + i``, attends positions ``[0, p]`` (causal, as in
+  standard attention); nothing else changes.
 
 Parity is pinned (``tests/test_oracle_pins.py``) against: the library SDPA on
 the densely gathered tokens, pure-Python brute force, block-id permutation
@@ -219,3 +227,39 @@ def copy_blocks(pairs: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray
         kc[dst] = kc[src]
         vc[dst] = vc[src]
     return kc, vc
+
+
+def paged_attention_multi_query(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                                block_tables: np.ndarray, context_lens: np.ndarray,
+                                query_start: np.ndarray, scale: float, block_size: int,
+                                dtype: str) -> np.ndarray:
+    """Several query tokens per sequence over the paged pool, causal.
+
+    ``q`` is ``[T, Hq, D]``: sequence s owns rows ``query_start[s] ..
+    query_start[s+1] - 1`` (n_s of them), which are its last n_s cached
+    positions.  Row ``query_start[s] + i`` sits at position
+    ``p = context_lens[s] - n_s + i`` and attends positions ``[0, p]``
+    through the block table, each query head h reading KV head h // G.
+    Returns float64 ``[T, Hq, D]``."""
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = _group(Hq, Hkv)
+    qf = to_f64(q, dtype)
+    sc = np.float64(np.float32(scale))
+    out = np.zeros((T, Hq, D), np.float64)
+    starts = np.asarray(query_start).tolist()
+    for s in range(len(starts) - 1):
+        n = starts[s + 1] - starts[s]
+        if n == 0:
+            continue
+        L = int(context_lens[s])
+        if n > L:
+            raise ValueError("a chunk is longer than its sequence's context")
+        K, V = gather_sequence(k_cache, v_cache, block_tables[s], L, block_size, dtype)
+        for i in range(n):
+            p = L - n + i
+            row = starts[s] + i
+            for g in range(Hkv):
+                out[row, g * G:(g + 1) * G] = dense_attention(
+                    qf[row, g * G:(g + 1) * G], K[:p + 1, g], V[:p + 1, g], sc)
+    return out

@@ -7,11 +7,15 @@ lengths, slot mapping, copy pairs); it holds none of the attention arithmetic.
 from .generate import (  # noqa: F401
     Case,
     CONFIG_NAMES,
+    MULTI_QUERY_NAMES,
+    MultiQueryCase,
     bf16_bits_from_f32,
     draw_values,
     make_aliased_case,
     make_case,
     make_fork_case,
+    make_multi_query_case,
+    make_multi_query_workload,
     make_prefix_case,
     make_private_case,
 )

@@ -482,3 +482,117 @@ def permute_pool(case: Case, seed: int) -> Tuple[np.ndarray, np.ndarray, np.ndar
     sm = case.slot_mapping
     sm2 = np.where(sm >= 0, pi[np.maximum(sm, 0) // B] * B + np.maximum(sm, 0) % B, sm).astype(np.int32)
     return k2, v2, t2, tp2, pairs2, sm2
+
+
+# ---------------------------------------------------------------- multi-query
+
+def settle_step(case: Case) -> Case:
+    """The same workload with its step already taken: the copy pairs applied
+    (whole blocks, in list order) and each new token placed at its slot, so
+    that the pool holds every position [0, L) of every sequence."""
+    if not case.has_step:
+        return case
+    k, v = case.k_cache.copy(), case.v_cache.copy()
+    for src, dst in case.copy_pairs.reshape(-1, 2).tolist():
+        k[dst] = k[src]
+        v[dst] = v[src]
+    B = case.block_size
+    for i, slot in enumerate(case.slot_mapping.tolist()):
+        if slot >= 0:
+            k[slot // B, :, slot % B] = case.k_new[i]
+            v[slot // B, :, slot % B] = case.v_new[i]
+    return Case(name=case.name, dtype=case.dtype, num_q_heads=case.num_q_heads,
+                num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, block_size=B,
+                context_lens=case.context_lens, block_tables=case.block_tables, k_cache=k,
+                v_cache=v, q=case.q, scale=case.scale, poison_block=case.poison_block,
+                logical_k=case.logical_k, logical_v=case.logical_v,
+                description=case.description)
+
+
+def subset_sequences(case: Case, keep) -> Case:
+    """The workload restricted to the sequences ``keep`` (same pool)."""
+    keep = np.asarray(keep)
+    return Case(name=case.name, dtype=case.dtype, num_q_heads=case.num_q_heads,
+                num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                block_size=case.block_size, context_lens=case.context_lens[keep],
+                block_tables=case.block_tables[keep], k_cache=case.k_cache,
+                v_cache=case.v_cache, q=case.q[keep], scale=case.scale,
+                poison_block=case.poison_block,
+                logical_k=[case.logical_k[i] for i in keep] if case.logical_k else None,
+                logical_v=[case.logical_v[i] for i in keep] if case.logical_v else None,
+                description=case.description)
+
+
+@dataclass
+class MultiQueryCase:
+    """Several query tokens per sequence (a prompt chunk, or tokens to verify)
+    over the pool of ``base``: sequence s owns query rows ``query_start[s] ..
+    query_start[s+1] - 1``, which are its last cached positions.  ``base.q``
+    is not used."""
+
+    name: str
+    base: Case
+    q: np.ndarray             # [T, Hq, D]
+    query_start: np.ndarray   # int32 [S + 1]
+    description: str = ""
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start)
+
+    @property
+    def max_query_len(self) -> int:
+        ql = self.query_lens
+        return int(ql.max()) if ql.size else 0
+
+
+def make_multi_query_case(base: Case, q_lens, seed: int, name: str = "",
+                          description: str = "") -> MultiQueryCase:
+    """Chunks of ``q_lens[s]`` query tokens (each at most the sequence's
+    context length) drawn N(0, 1) from ``default_rng([seed, 2])``."""
+    q_lens = np.asarray(q_lens, np.int64)
+    if q_lens.shape != base.context_lens.shape or (q_lens < 0).any() or \
+            (q_lens > base.context_lens).any():
+        raise ValueError("each chunk must fit in its sequence's context")
+    qs = np.zeros(len(q_lens) + 1, np.int32)
+    qs[1:] = np.cumsum(q_lens)
+    vrng = np.random.default_rng([seed, 2])
+    q = _draw(vrng, (int(qs[-1]), base.num_q_heads, base.head_dim), base.dtype)
+    return MultiQueryCase(name=name or base.name, base=base, q=q, query_start=qs,
+                          description=description)
+
+
+MULTI_QUERY_NAMES = {
+    "chunked-prefill": ("chunked-prefill-bf16 (16 seqs, contexts U[1024,8192], a 512-token "
+                        "prompt chunk each, 32q/8kv, d128, B16)"),
+    "spec-verify": ("spec-verify-bf16 (256 seqs, lognormal contexts median 1024 cap 8192, "
+                    "5 tokens to verify each, 32q/8kv, d128, B16, 16-seq groups share a "
+                    "1024-token prefix)"),
+}
+
+
+def make_multi_query_workload(name: str, *, seed: int = 7, poison: bool = True,
+                              scale_down: int = 1) -> MultiQueryCase:
+    """The two multi-query workloads at full size (``scale_down`` > 1 keeps
+    every ``scale_down``-th sequence, for quick checks)."""
+    rng = np.random.default_rng(seed)
+    if name == "chunked-prefill":
+        lens = rng.integers(1024, 8192 + 1, size=16)[::scale_down]
+        base = make_private_case(name, lens, 32, 8, 128, 16, "bf16", seed, poison=poison,
+                                 rng=rng)
+        q_lens = np.full(len(lens), 512)
+    elif name == "spec-verify":
+        lens = np.minimum(np.round(np.exp(rng.normal(np.log(1024.0), 1.0, size=256))), 8192)
+        lens = np.maximum(lens, 5).astype(np.int64)
+        keep = np.arange(0, 256, scale_down)
+        base = settle_step(make_prefix_case(name, lens, 16, 1024, 32, 8, 128, 16, "bf16", seed,
+                                            poison=poison, rng=rng))
+        base = subset_sequences(base, keep)
+        q_lens = np.full(len(keep), 5)
+    else:
+        raise ValueError(name)
+    return make_multi_query_case(base, q_lens, seed, name, MULTI_QUERY_NAMES[name])
