@@ -143,6 +143,46 @@ int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                          int32_t max_context_len, int32_t partition_size);
 
 /*
+ * paged_attention_multi_query -- causal attention of several query tokens per
+ * sequence over the paged pool: a slice of a long prompt (chunked prefill) or
+ * tokens to verify (speculative decoding) ([P1] sections 2.3, 4.3, 5.1, 5.4).
+ *
+ * Sequence s owns query rows query_start[s] .. query_start[s+1]-1; with n of
+ * them and L = context_lens[s], they are the sequence's last n cached
+ * positions (their K/V must already be in the pool, e.g. by kv_cache_write).
+ * Row query_start[s] + i sits at position p = L - n + i, and for each query
+ * head h (KV head g = h / G):
+ *   out[row][h] = sum_{t <= p} exp(x_t - max) V_t / sum_{t <= p} exp(x_t - max),
+ *   x_t = scale * dot(q[row][h], K_t)
+ * with K_t, V_t read through block_tables[s] as in paged_attention_decode.
+ *
+ *   q              device, [num_tokens][num_q_heads][head_dim], dtype
+ *   query_start    device int32 [num_seqs + 1], non-decreasing, starting at 0
+ *   context_lens,
+ *   block_tables   as in paged_attention_decode
+ *   out            device float32 [num_tokens][num_q_heads][head_dim]; rows
+ *                  that belong to no sequence are not written
+ *   max_query_len  host: at least every sequence's n (rows past it are not
+ *                  computed)
+ * Chunks longer than their context, or reaching past num_tokens, are cut to
+ * fit; the numbers are then unspecified but every access stays in bounds.
+ * The products run on bfloat16 matrix instructions with fp32 accumulation;
+ * probabilities enter them as a pair of bfloat16 values (about 16
+ * significant bits).
+ * Supported: dtype PA_BF16; head_dim 64 or 128; any G; block_size a power of
+ * two in [1, 1024].
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
+ * PA_ERR_LAUNCH.
+ */
+int32_t paged_attention_multi_query(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *context_lens,
+                                    const int32_t *query_start, float scale, float *out,
+                                    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_blocks_per_seq,
+                                    int32_t max_query_len, int32_t dtype, void *stream);
+
+/*
  * kv_cache_write -- store each new token's K and V rows in the pool.
  *
  * For i in [0, num_tokens) with slot = slot_mapping[i] >= 0: copies

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     lib,
     num_partitions,
     paged_attention_decode,
+    paged_attention_multi_query,
     partition_tokens,
     workspace_size,
 )

@@ -30,6 +30,9 @@ SIGNATURES = {
     "paged_attention_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                       _VP, ctypes.c_size_t, _VP]),
+    "paged_attention_multi_query": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
+                                           _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                           _I32, _VP]),
     "paged_attention_workspace_size": (ctypes.c_size_t, [_I32] * 6),
     "paged_attention_num_partitions": (_I32, [_I32] * 4),
     "paged_attention_partition_tokens": (_I32, [_I32] * 4),
@@ -157,6 +160,29 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         float(scale), _ptr(out), S, Hq, Hkv, D, B, NB, MB, int(max_context_len),
         _dtype_code(q), int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
     _check("paged_attention_decode", st)
+
+
+def paged_attention_multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start,
+                                scale: float, out, *, max_query_len: int, stream=None) -> None:
+    """Causal attention of several query tokens per sequence (see
+    include/pagedattn.h).  q: [T, Hq, D] bfloat16; query_start: int32 [S+1];
+    out: float32 [T, Hq, D]."""
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q/k_cache/v_cache shapes disagree")
+    S = context_lens.shape[0]
+    if query_start.shape[0] != S + 1:
+        raise ValueError("query_start must have num_seqs + 1 entries")
+    MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    for t in (q, k_cache, v_cache, block_tables, context_lens, query_start, out):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    st = lib().paged_attention_multi_query(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start), float(scale), _ptr(out), S, T, Hq, Hkv, D, B, NB, MB,
+        int(max_query_len), _dtype_code(q), _stream(stream))
+    _check("paged_attention_multi_query", st)
 
 
 def kv_cache_write(k, v, slot_mapping, k_cache, v_cache, *, stream=None) -> None:

@@ -183,6 +183,55 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
+int32_t paged_attention_multi_query(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *context_lens,
+                                    const int32_t *query_start, float scale, float *out,
+                                    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_blocks_per_seq,
+                                    int32_t max_query_len, int32_t dtype, void *stream) {
+  if (!known_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0)
+    return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if ((int64_t)num_blocks * block_size * num_kv_heads * head_dim >= (int64_t(1) << 40))
+    return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
+  if (!pa::multi_query_supported(dtype, head_dim)) return PA_ERR_UNSUPPORTED;
+  const int64_t G = num_q_heads / num_kv_heads;
+  const int64_t rows = (int64_t)max_query_len * G;
+  const int64_t tiles = (rows + 63) / 64;
+  if ((int64_t)num_seqs * num_kv_heads * tiles + 8 >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  if ((int64_t)num_tokens * num_q_heads * head_dim >= (int64_t(1) << 40)) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+    return PA_ERR_NULL;
+  pa::MultiQueryArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.out = out;
+  a.scale = scale;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.log2_block_size = log2_exact(block_size);
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.dtype = dtype;
+  const hipError_t e = pa::launch_multi_query(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                        int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
                        int32_t block_size, int32_t num_kv_heads, int32_t head_dim,

@@ -38,6 +38,24 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 // Merge of the per-partition partials into `out` (P > 1 only).
 hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream);
 
+struct MultiQueryArgs {
+  const void *q;             // [num_tokens][Hq][D]
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start;  // [num_seqs + 1]
+  float *out;                // [num_tokens][Hq][D]
+  float scale;
+  int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim;
+  int32_t log2_block_size, num_blocks, max_blocks_per_seq, max_query_len;
+  int32_t dtype;
+};
+
+// Causal multi-query attention (multi_query.hip): bfloat16, head_dim 64 or 128.
+bool multi_query_supported(int32_t dtype, int32_t head_dim);
+hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream);
+
 hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                                  int32_t num_tokens, void *k_cache, void *v_cache,
                                  int64_t num_slots, int32_t log2_block_size, int32_t num_kv_heads,

@@ -1,0 +1,367 @@
+// Causal multi-query paged attention on the matrix cores of gfx950: several
+// query tokens per sequence (a chunk of a long prompt, or tokens to verify),
+// the chunk being the sequence's last cached positions, each token attending
+// every cached position up to its own ("vLLM 深度拆解..." at chenxutan.com,
+// sections 2.3, 4.3, 5.1 and 5.4; the attention itself is the one of the
+// "核心代码拆解" section of the devpress.csdn.net/amd walkthrough).
+//
+// Here the query side is a real dense tile: the chunk's tokens times the G
+// query heads of a KV head.  One workgroup (4 waves) takes 64 * RS query rows
+// of one (sequence, KV head) -- rows ordered token-major, row R being token
+// R / G, head R % G -- and walks the sequence's K/V in 64-token tiles through
+// the block table, up to the last position its rows attend.  Each tile is
+// staged in LDS once and shared by the 4 waves, each of which owns 16 * RS
+// rows (RS row sets of 16):
+//
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 K rows from LDS (lane n
+//    = lane%16 reads token n, elements 32s + 8g .. +7 with g = lane/16),
+//    B = the 16 query rows of a row set, kept in registers (column n = query
+//    row n).  Lane (g, n) receives the scores of query row n with tokens
+//    4g .. 4g+3 of each 16-token block.
+//  * O^T += V^T P^T on the same instruction: B = the probabilities as they
+//    sit after the first product (a 32-token k-step takes lane (g, n)'s
+//    tokens 4g .. 4g+3 of two 16-token blocks, the k order being any
+//    permutation shared by A and B), A = the same tokens of V for 16 head_dim
+//    elements, read from a transposed copy of the V tile in LDS.  So all of a
+//    lane's accumulators belong to its own query row, whose running maximum
+//    and sum the lane holds: the online softmax needs no shuffles beyond the
+//    two that combine a row's four lane groups per tile.
+//  * The probabilities (fp32) enter the product as a bfloat16 pair hi + lo
+//    (hi = p rounded, lo = the rest rounded), two MFMAs sharing one A
+//    operand: the pair carries p to about 2^-16 relative, so the bfloat16
+//    matrix cores give fp32-grade weights.
+//  * The causal mask is applied to scores (token t > the row's position
+//    gets -inf) only in tiles that reach past the workgroup's first row.
+//
+// Workgroups are mapped to the 8 XCDs so that all row tiles of one
+// (sequence, KV head), which read the same K/V, run on one XCD and share its
+// L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTk = 64;          // tokens per tile
+constexpr int kVtStride = kTk + 4;  // transposed V tile row (elements), padded
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+template <int D>
+struct TileRegs {
+  // K: chunk c = threadIdx + 256 j of the tile (token c / (D/8), elements
+  // 8 (c % (D/8)) .. +7); V: token quad and element chunk of this thread
+  static constexpr int kKChunks = kTk * D / 8 / kThreads;  // 4 (D=128) or 2 (D=64)
+  static constexpr int kVQuads = kTk / 4 * (D / 8);          // 256 (D=128) or 128
+  u32x4 k[kKChunks];
+  u32x4 v[4];
+};
+
+template <int D, int RS>
+__global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
+    float *__restrict__ out, float sl2, int num_tokens, int hkv, int G, int lgB, int nb, int mb,
+    int max_q, int row_tiles, int items) {
+  constexpr int kRows = 64 * RS;  // query rows per workgroup
+  constexpr int kKs = kTk == 64 ? D + 8 : D;  // K tile row stride (elements), padded
+  constexpr int kSteps = D / 32;              // k-steps of q.K
+  constexpr int kDb = D / 16;                 // 16-element blocks of the output
+  using Regs = TileRegs<D>;
+
+  // XCD-aware order: workgroup b runs on XCD b % 8; consecutive items (the
+  // row tiles of one sequence and KV head) go to one XCD
+  const int per = gridDim.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (item >= items) return;
+  const int rt = item % row_tiles;
+  const int kvh = (item / row_tiles) % hkv;
+  const int s = item / (row_tiles * hkv);
+  const int hq = hkv * G;
+
+  int L = context_lens[s];
+  L = max(0, min(L, mb << lgB));
+  const int qs = max(0, min(query_start[s], num_tokens));
+  int n = query_start[s + 1] - qs;
+  n = max(0, min(min(n, L), min(max_q, num_tokens - qs)));
+  const int rows = n * G;
+  const int row0 = rt * kRows;
+  if (row0 >= rows) return;
+  const int row_end = min(row0 + kRows, rows);
+  // positions attended by the workgroup: [0, pos_last]; tiles wholly below
+  // pos_first need no mask
+  const int pos_first = L - n + row0 / G;
+  const int pos_last = L - n + (row_end - 1) / G;
+  const int ntiles = pos_last / kTk + 1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
+  const int32_t *tbl = block_tables + (int64_t)s * mb;
+  const int bm1 = (1 << lgB) - 1;
+  const int64_t head_off = (int64_t)kvh * (D << lgB);
+  const int64_t block_elems = ((int64_t)hkv * D) << lgB;
+
+  // this lane's query rows (one per row set), their positions and the B
+  // operand of q.K
+  int pos[RS];
+  bf16x8 qb[RS][kSteps];
+  int wave_last = -1;
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    const int R = row0 + (wave * RS + r) * 16 + c16;
+    const bool active = R < rows;
+    const int tok = R / G;
+    pos[r] = active ? L - n + tok : -1;
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k) qb[r][k] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    if (active) {
+      const uint16_t *qrow = q + ((int64_t)(qs + tok) * hq + kvh * G + R % G) * D + 8 * g4;
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k)
+        qb[r][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * k));
+    }
+    // the wave's last attended position (rows are ascending in position)
+    const int Rw = min(row0 + (wave * RS + r) * 16 + 15, row_end - 1);
+    if (row0 + (wave * RS + r) * 16 < row_end) wave_last = max(wave_last, L - n + Rw / G);
+  }
+
+  __shared__ __attribute__((aligned(16))) uint16_t sk[kTk * kKs];
+  __shared__ __attribute__((aligned(16))) uint16_t svt[D * kVtStride];
+
+  // global -> registers for the tile at k0 (tokens past pos_last are zero)
+  auto load_tile = [&](Regs &T, int k0) {
+#pragma unroll
+    for (int j = 0; j < Regs::kKChunks; ++j) {
+      const int c = threadIdx.x + kThreads * j;
+      const int tok = k0 + c / (D / 8);
+      const int dc = c % (D / 8);
+      T.k[j] = u32x4{0, 0, 0, 0};
+      if (tok <= pos_last) {
+        const uint32_t bid = min((uint32_t)tbl[tok >> lgB], (uint32_t)(nb - 1));
+        T.k[j] = *reinterpret_cast<const u32x4 *>(kc + bid * block_elems + head_off +
+                                                  (int64_t)(tok & bm1) * D + 8 * dc);
+      }
+    }
+    if (threadIdx.x < Regs::kVQuads) {
+      const int tq = threadIdx.x / (D / 8);
+      const int dc = threadIdx.x % (D / 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = k0 + 4 * tq + i;
+        T.v[i] = u32x4{0, 0, 0, 0};
+        if (tok <= pos_last) {
+          const uint32_t bid = min((uint32_t)tbl[tok >> lgB], (uint32_t)(nb - 1));
+          T.v[i] = *reinterpret_cast<const u32x4 *>(vc + bid * block_elems + head_off +
+                                                    (int64_t)(tok & bm1) * D + 8 * dc);
+        }
+      }
+    }
+  };
+  // registers -> LDS: K row-major, V transposed (element-major, tokens
+  // contiguous)
+  auto store_tile = [&](const Regs &T) {
+#pragma unroll
+    for (int j = 0; j < Regs::kKChunks; ++j) {
+      const int c = threadIdx.x + kThreads * j;
+      *reinterpret_cast<u32x4 *>(&sk[(c / (D / 8)) * kKs + 8 * (c % (D / 8))]) = T.k[j];
+    }
+    if (threadIdx.x < Regs::kVQuads) {
+      const int tq = threadIdx.x / (D / 8);
+      const int dc = threadIdx.x % (D / 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        const uint32_t a0 = (T.v[0][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t a1 = (T.v[1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t a2 = (T.v[2][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t a3 = (T.v[3][e >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<u32x2 *>(&svt[(8 * dc + e) * kVtStride + 4 * tq]) =
+            u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
+      }
+    }
+  };
+
+  f32x4 acc[RS][kDb];
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+#pragma unroll
+    for (int b = 0; b < kDb; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[RS], lsum[RS];
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    m[r] = neg_inf();
+    lsum[r] = 0.f;
+  }
+
+  Regs T;
+  load_tile(T, 0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = it * kTk;
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile(T);
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(T, k0 + kTk);  // in flight during the products
+    if (k0 > wave_last) continue;                  // all of this wave's rows end earlier
+    const bool masked = k0 + kTk - 1 > pos_first;
+
+    // S^T for each 16-token block tb and row set r
+    f32x4 sc[RS][4];
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) sc[r][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4 *>(&sk[(16 * tb + c16) * kKs + 32 * k + 8 * g4]));
+#pragma unroll
+        for (int r = 0; r < RS; ++r)
+          sc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[r][k], sc[r][tb], 0, 0, 0);
+      }
+    }
+
+    // online softmax per row set; then the hi/lo probability operands
+    bf16x8 phi[RS][2], plo[RS][2];
+#pragma unroll
+    for (int r = 0; r < RS; ++r) {
+      float x[4][4];
+      float cm = neg_inf();
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = k0 + 16 * tb + 4 * g4 + i;
+          x[tb][i] = (!masked || t <= pos[r]) ? sc[r][tb][i] * sl2 : neg_inf();
+          cm = fmaxf(cm, x[tb][i]);
+        }
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      if (cm > m[r] + kSlack) {  // false while both are -inf
+        const float alpha = __builtin_amdgcn_exp2f(m[r] - cm);  // 0 when m was -inf
+        lsum[r] *= alpha;
+#pragma unroll
+        for (int b = 0; b < kDb; ++b) acc[r][b] *= alpha;
+        m[r] = cm;
+      }
+      const float mu = (m[r] == neg_inf()) ? 0.f : m[r];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          float pr[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int jj = j + u;
+            const int tb = 2 * kk + (jj >> 2);
+            pr[u] = __builtin_amdgcn_exp2f(x[tb][jj & 3] - mu);
+            lsum[r] += pr[u];
+          }
+          const uint32_t h0 = bf16_bits(pr[0]), h1 = bf16_bits(pr[1]);
+          const float r0 = pr[0] - __uint_as_float(h0 << 16);
+          const float r1 = pr[1] - __uint_as_float(h1 << 16);
+          hw[j >> 1] = h0 | (h1 << 16);
+          lw[j >> 1] = bf16_bits(r0) | (bf16_bits(r1) << 16);
+        }
+        phi[r][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+        plo[r][kk] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int b = 0; b < kDb; ++b) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint16_t *vr = &svt[(16 * b + c16) * kVtStride + 32 * kk + 4 * g4];
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+          acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[r][kk], acc[r][b], 0, 0, 0);
+          acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[r][kk], acc[r][b], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // normalise and write: lane (g4, c16) holds row c16 of each row set,
+  // elements 16 b + 4 g4 .. +3
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    float l = lsum[r];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int R = row0 + (wave * RS + r) * 16 + c16;
+    if (R < row_end) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float *orow = out + ((int64_t)(qs + R / G) * hq + kvh * G + R % G) * D + 4 * g4;
+#pragma unroll
+      for (int b = 0; b < kDb; ++b)
+        *reinterpret_cast<f32x4 *>(orow + 16 * b) = acc[r][b] * inv;
+    }
+  }
+}
+
+template <int D, int RS>
+hipError_t launch_typed(const MultiQueryArgs &a, hipStream_t stream) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int64_t rows = (int64_t)a.max_query_len * G;
+  const int row_tiles = (int)((rows + 64 * RS - 1) / (64 * RS));
+  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * row_tiles;
+  if (items <= 0) return hipSuccess;
+  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((paged_multi_query_kernel<D, RS>), dim3((uint32_t)grid), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t *>(a.q),
+                     static_cast<const uint16_t *>(a.k_cache),
+                     static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
+                     a.query_start, a.out, a.scale * kLog2e, a.num_tokens, a.num_kv_heads, G,
+                     a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.max_query_len,
+                     row_tiles, (int)items);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const MultiQueryArgs &a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.max_query_len * (a.num_q_heads / a.num_kv_heads);
+  if (rows > 64) return launch_typed<D, 2>(a, stream);
+  return launch_typed<D, 1>(a, stream);
+}
+
+}  // namespace
+
+bool multi_query_supported(int32_t dtype, int32_t head_dim) {
+  return dtype == 1 && (head_dim == 64 || head_dim == 128);
+}
+
+hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_d<64>(a, stream);
+    case 128: return launch_d<128>(a, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace pa

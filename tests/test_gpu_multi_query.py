@@ -1,0 +1,153 @@
+"""Causal multi-query paged attention (chunked prefill, speculative
+verification) through the C ABI against the oracle (needs an MI355X).
+
+Every output element at sizes the oracle finishes in seconds (chunks from 0
+tokens to whole prompts, tiles of 64 tokens with ragged tails, every block
+size, G from 1 to 8, both row-tile widths), and sampled sequences of the two
+full-size workloads.  Also bitwise determinism, invariance under relabelling
+physical blocks, rows outside every chunk left untouched, and NaN-poisoned
+unused slots never reaching the output."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from workloads import make_multi_query_case, make_multi_query_workload, make_private_case
+from workloads.generate import permute_pool, subset_sequences, make_multi_query_case as mqc
+
+from gpu_helpers import TOL, max_err, say, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_386_amd as pa
+    pa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _check_indices(c):
+    b = c.base
+    NB, B = b.num_blocks, b.block_size
+    qs = c.query_start
+    assert qs[0] == 0 and (np.diff(qs) >= 0).all()
+    for s, L in enumerate(b.context_lens.tolist()):
+        nb = -(-L // B)
+        assert nb <= b.max_blocks_per_seq
+        assert ((b.block_tables[s, :nb] >= 0) & (b.block_tables[s, :nb] < NB)).all()
+        assert qs[s + 1] - qs[s] <= L
+
+
+def run_gpu(c, tables=None, kc=None, vc=None, fill=0.0):
+    import paged_kv_cache_386_amd as pa
+    _check_indices(c)
+    b = c.base
+    T = c.num_tokens
+    out = torch.full((T, b.num_q_heads, b.head_dim), fill, dtype=torch.float32, device="cuda")
+    pa.paged_attention_multi_query(
+        to_torch(c.q, b.dtype), to_torch(b.k_cache if kc is None else kc, b.dtype),
+        to_torch(b.v_cache if vc is None else vc, b.dtype),
+        torch.from_numpy(np.ascontiguousarray(b.block_tables if tables is None else tables)).cuda(),
+        torch.from_numpy(b.context_lens).cuda(), torch.from_numpy(c.query_start).cuda(),
+        float(b.scale), out, max_query_len=c.max_query_len)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle(c):
+    b = c.base
+    return O.paged_attention_multi_query(c.q, b.k_cache, b.v_cache, b.block_tables,
+                                         b.context_lens, c.query_start, b.scale, b.block_size,
+                                         b.dtype)
+
+
+def compare(c, name):
+    say(f"{name}: S={c.base.num_seqs} T={c.num_tokens} Hq={c.base.num_q_heads} "
+        f"Hkv={c.base.num_kv_heads} D={c.base.head_dim} B={c.base.block_size} "
+        f"max_q={c.max_query_len}")
+    got = run_gpu(c)
+    ref = oracle(c)
+    err = max_err(got, ref)
+    assert err <= TOL["bf16"], f"{name}: max abs err {err}"
+    return got, ref
+
+
+LENS = [1, 5, 16, 63, 64, 65, 130, 200, 300, 520]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 2), (8, 1)])
+def test_chunks_of_every_length(D, G, Hkv):
+    # chunk lengths: 0, 1, whole prompt, a tile and a bit, long chunks
+    q_lens = [1, 5, 0, 63, 1, 65, 130, 17, 300, 100]
+    base = make_private_case(f"mq-{D}-{G}", LENS, G * Hkv, Hkv, D, 16, "bf16", 40 + D + G)
+    compare(make_multi_query_case(base, q_lens, 40 + D + G), f"mq D={D} G={G}")
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64, 128, 512, 1024])
+def test_block_sizes(B):
+    base = make_private_case(f"mq-B{B}", [1, 33, 97, 300, 700], 8, 2, 128, B, "bf16", B)
+    compare(make_multi_query_case(base, [1, 33, 20, 150, 64], B), f"mq B={B}")
+
+
+@pytest.mark.parametrize("max_q", [16, 17, 33, 200])
+def test_row_tile_widths(max_q):
+    """Rows per (sequence, KV head) below and above one 64-row tile, with a
+    16-token chunk per row set and ragged tails."""
+    lens = [max_q, max_q + 7, 3 * max_q, 900]
+    base = make_private_case(f"mq-rows{max_q}", lens, 16, 4, 128, 16, "bf16", max_q)
+    compare(make_multi_query_case(base, [max_q, max_q - 1, max_q, max_q // 2], max_q),
+            f"mq max_q={max_q}")
+
+
+def test_whole_prompt_first_token_is_its_v_row():
+    base = make_private_case("mq-prompt", [40, 129], 8, 2, 128, 16, "bf16", 9,
+                             keep_logical=True)
+    c = make_multi_query_case(base, [40, 129], 9)
+    got, _ = compare(c, "mq whole prompt")
+    for s in range(2):
+        v0 = O.to_f64(base.logical_v[s][0], "bf16")  # [Hkv, D]
+        assert np.array_equal(got[c.query_start[s]], np.repeat(v0, 4, axis=0))
+
+
+def test_determinism_and_relabelling():
+    base = make_private_case("mq-perm", [77, 300, 129], 8, 2, 128, 16, "bf16", 21)
+    c = make_multi_query_case(base, [77, 64, 100], 21)
+    a = run_gpu(c)
+    assert np.array_equal(a, run_gpu(c))
+    kc, vc, tables, _, _, _ = permute_pool(base, 5)
+    assert np.array_equal(a, run_gpu(c, tables=tables, kc=kc, vc=vc))
+
+
+def test_rows_outside_every_chunk_are_untouched():
+    base = make_private_case("mq-gap", [50, 60], 8, 2, 128, 16, "bf16", 3)
+    c = make_multi_query_case(base, [10, 20], 3)
+    # 8 extra rows after the last chunk
+    c.q = np.concatenate([c.q, c.q[:8]])
+    got = run_gpu(c, fill=7.0)
+    assert (got[30:] == 7.0).all()
+    assert max_err(got[:30], oracle(make_multi_query_case(base, [10, 20], 3))) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name,every,sample", [("chunked-prefill", 1, [0, 5, 11, 15]),
+                                               ("spec-verify", 1, list(range(0, 256, 9)))])
+def test_full_size_workloads(name, every, sample):
+    """The two multi-query workloads at full size on the GPU; the oracle on a
+    sample of their sequences (same pool, same tables)."""
+    c = make_multi_query_workload(name, scale_down=every)
+    say(f"{name} full size: S={c.base.num_seqs} T={c.num_tokens} max_q={c.max_query_len}")
+    got = run_gpu(c)
+    assert np.isfinite(got).all()
+    sub = subset_sequences(c.base, sample)
+    qs = c.query_start
+    q_sub = np.concatenate([c.q[qs[s]:qs[s + 1]] for s in sample])
+    rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in sample])
+    cs = mqc(sub, [int(qs[s + 1] - qs[s]) for s in sample], 0)
+    cs.q = q_sub
+    ref = oracle(cs)
+    err = max_err(got[rows], ref)
+    assert err <= TOL["bf16"], f"{name}: max abs err {err}"
