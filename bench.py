@@ -444,6 +444,118 @@ def serving_bench(args) -> int:
     return 0
 
 
+# ---------------------------------------------------------------- multi-query
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+
+
+def multi_query_bench(args) -> int:
+    """Causal multi-query paged attention on one of its two workloads:
+    chunked prefill (16 sequences, contexts U[1024, 8192], a 512-token chunk
+    each) is bound by the matrix cores and priced in bf16 TFLOP/s (4 * D
+    flops per query head and attended position: q.K and p.V); speculative
+    verification (256 sequences, 5 tokens each, prefix-shared lognormal
+    contexts) is bound by HBM and priced in GB/s of K/V read once per
+    (sequence, KV head)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_386_amd as pa
+    from workloads import make_multi_query_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.lib()
+    c = make_multi_query_workload(args.multi_query, poison=False)
+    b = c.base
+    q = to_dev(c.q, dev)
+    kc, vc = to_dev(b.k_cache, dev), to_dev(b.v_cache, dev)
+    tables = torch.from_numpy(b.block_tables).to(dev)
+    lens = torch.from_numpy(b.context_lens).to(dev)
+    qs = torch.from_numpy(c.query_start).to(dev)
+    out = torch.empty((c.num_tokens, b.num_q_heads, b.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    max_ctx = int(b.context_lens.max())
+    P = pa.multi_query_partitions(b.num_seqs, b.num_q_heads, b.num_kv_heads, c.max_query_len,
+                                  max_ctx, args.partition_size)
+    ws = torch.empty(max(pa.multi_query_workspace_size(
+        b.num_seqs, c.num_tokens, b.num_q_heads, b.num_kv_heads, b.head_dim, c.max_query_len,
+        max_ctx, args.partition_size), 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        pa.paged_attention_multi_query(q, kc, vc, tables, lens, qs, float(b.scale), out,
+                                       max_query_len=c.max_query_len, max_context_len=max_ctx,
+                                       partition_size=args.partition_size, workspace=ws,
+                                       stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+
+    Hq, Hkv, D = b.num_q_heads, b.num_kv_heads, b.head_dim
+    attended = 0  # (query token, position) pairs
+    kv_tokens = 0  # positions read per (sequence, KV head) group
+    for s in range(b.num_seqs):
+        n = int(c.query_start[s + 1] - c.query_start[s])
+        L = int(b.context_lens[s])
+        attended += sum(L - n + i + 1 for i in range(n))
+        kv_tokens += L if n else 0
+    flops = attended * Hq * 4 * D
+    kv_bytes = kv_tokens * Hkv * D * 2 * 2
+    io_bytes = c.num_tokens * Hq * D * (2 + 4) + b.block_tables.nbytes + 8 * b.num_seqs
+    tflops = flops / (us * 1e-6) / 1e12
+    gbps = (kv_bytes + io_bytes) / (us * 1e-6) / 1e9
+    mfma_bound = args.multi_query == "chunked-prefill"
+    from workloads import MULTI_QUERY_NAMES
+    rec = {
+        "metric": ("multi-query paged attention: achieved bf16 TFLOP/s" if mfma_bound else
+                   "multi-query paged attention: achieved HBM GB/s"),
+        "value": round(tflops if mfma_bound else gbps, 2),
+        "unit": "TFLOP/s" if mfma_bound else "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V; lengths as described)",
+        "config": {"workload": f"{args.multi_query}: {MULTI_QUERY_NAMES[args.multi_query]}",
+                   "num_seqs": b.num_seqs, "num_tokens": c.num_tokens,
+                   "max_query_len": c.max_query_len, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": b.block_size,
+                   "total_context_tokens": int(b.context_lens.sum()), "num_partitions": P},
+        "attended_pairs_per_s": round(attended * Hq / (us * 1e-6), 1),
+        "query_tokens_per_s": round(c.num_tokens / (us * 1e-6), 1),
+        "kernel_us": round(us, 2),
+        "roofline": {
+            "bound": "mfma" if mfma_bound else "hbm",
+            "kernel": "paged_multi_query_kernel",
+            "achieved": round(tflops if mfma_bound else gbps, 2),
+            "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBPS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round((tflops / PEAK_BF16_TFLOPS) if mfma_bound else (gbps / PEAK_HBM_GBPS), 4),
+            "traffic": None,
+            "algorithmic_flops_per_call": flops,
+            "algorithmic_bytes_per_call": kv_bytes + io_bytes,
+            "other": {"tflops": round(tflops, 2), "gbps": round(gbps, 1)},
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(rec))
+    return 0
+
+
 # ---------------------------------------------------------------- main
 
 def main() -> int:
@@ -455,6 +567,8 @@ def main() -> int:
                     help="untimed steps first (default 10; 200 with --serving)")
     ap.add_argument("--serving", action="store_true",
                     help="time the continuously batched engine over a request stream instead")
+    ap.add_argument("--multi-query", choices=["chunked-prefill", "spec-verify"], default=None,
+                    help="time causal multi-query attention on one of its workloads instead")
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4],
                     help="workload (default 2: the GQA prefix-sharing batch)")
     ap.add_argument("--block-size", type=int, default=None, help="config 3 only: 512 or 16")
@@ -476,6 +590,8 @@ def main() -> int:
     workload = f"cfg{args.config}" + (f"-B{args.block_size or 512}" if args.config == 3 else "")
     if args.serving:
         workload = "serving"
+    if args.multi_query:
+        workload = args.multi_query
     if args.summarize_counters:
         print(json.dumps(summarize_counters(*args.summarize_counters, workload), indent=1))
         return 0
@@ -497,6 +613,8 @@ def main() -> int:
         return 1
     if args.serving:
         return serving_bench(args)
+    if args.multi_query:
+        return multi_query_bench(args)
 
     t_gen = time.perf_counter()
     case = make_case(args.config, poison=False, block_size=args.block_size)

@@ -164,6 +164,18 @@ int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *                  that belong to no sequence are not written
  *   max_query_len  host: at least every sequence's n (rows past it are not
  *                  computed)
+ *   max_context_len host: at least every context_lens[s]; sets the number of
+ *                  partitions
+ *   partition_size split-K partition in tokens: 0 = automatic (chunks of at
+ *                  most 64 query rows per KV head are split like decode,
+ *                  rounded up to whole 64-token tiles; longer chunks are not
+ *                  split), negative = never, positive = that many tokens (a
+ *                  multiple of 64).  With more than one partition the
+ *                  partials go to the workspace and a second kernel merges
+ *                  them in ascending order.
+ *   workspace      device scratch of workspace_bytes bytes, at least
+ *                  paged_attention_multi_query_workspace_size(...); may be
+ *                  NULL when that is 0
  * Chunks longer than their context, or reaching past num_tokens, are cut to
  * fit; the numbers are then unspecified but every access stays in bounds.
  * The products run on bfloat16 matrix instructions with fp32 accumulation;
@@ -172,7 +184,7 @@ int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  * Supported: dtype PA_BF16; head_dim 64 or 128; any G; block_size a power of
  * two in [1, 1024].
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
- * PA_ERR_LAUNCH.
+ * PA_ERR_WORKSPACE, PA_ERR_LAUNCH.
  */
 int32_t paged_attention_multi_query(const void *q, const void *k_cache, const void *v_cache,
                                     const int32_t *block_tables, const int32_t *context_lens,
@@ -180,7 +192,22 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
                                     int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                     int32_t num_blocks, int32_t max_blocks_per_seq,
-                                    int32_t max_query_len, int32_t dtype, void *stream);
+                                    int32_t max_query_len, int32_t max_context_len,
+                                    int32_t dtype, int32_t partition_size, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/* Partitions paged_attention_multi_query will use for these arguments (1 = no
+ * split), or a negative pa_status for a partition_size it rejects. */
+int32_t paged_attention_multi_query_partitions(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t max_query_len,
+                                               int32_t max_context_len, int32_t partition_size);
+
+/* Workspace bytes paged_attention_multi_query needs (0 when it will not split). */
+size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t max_query_len,
+                                                  int32_t max_context_len,
+                                                  int32_t partition_size);
 
 /*
  * kv_cache_write -- store each new token's K and V rows in the pool.

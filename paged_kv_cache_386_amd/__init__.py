@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     copy_blocks,
     kv_cache_write,
     lib,
+    multi_query_partitions,
+    multi_query_workspace_size,
     num_partitions,
     paged_attention_decode,
     paged_attention_multi_query,

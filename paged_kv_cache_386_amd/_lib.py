@@ -32,7 +32,9 @@ SIGNATURES = {
                                       _VP, ctypes.c_size_t, _VP]),
     "paged_attention_multi_query": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
                                            _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
-                                           _I32, _VP]),
+                                           _I32, _I32, _I32, _VP, ctypes.c_size_t, _VP]),
+    "paged_attention_multi_query_partitions": (_I32, [_I32] * 6),
+    "paged_attention_multi_query_workspace_size": (ctypes.c_size_t, [_I32] * 8),
     "paged_attention_workspace_size": (ctypes.c_size_t, [_I32] * 6),
     "paged_attention_num_partitions": (_I32, [_I32] * 4),
     "paged_attention_partition_tokens": (_I32, [_I32] * 4),
@@ -162,11 +164,29 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
     _check("paged_attention_decode", st)
 
 
+def multi_query_partitions(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                           max_query_len: int, max_context_len: int,
+                           partition_size: int = 0) -> int:
+    return int(lib().paged_attention_multi_query_partitions(
+        num_seqs, num_q_heads, num_kv_heads, max_query_len, max_context_len, partition_size))
+
+
+def multi_query_workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int,
+                               num_kv_heads: int, head_dim: int, max_query_len: int,
+                               max_context_len: int, partition_size: int = 0) -> int:
+    return int(lib().paged_attention_multi_query_workspace_size(
+        num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len,
+        max_context_len, partition_size))
+
+
 def paged_attention_multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start,
-                                scale: float, out, *, max_query_len: int, stream=None) -> None:
+                                scale: float, out, *, max_query_len: int, max_context_len: int,
+                                partition_size: int = 0, workspace=None, stream=None) -> None:
     """Causal attention of several query tokens per sequence (see
     include/pagedattn.h).  q: [T, Hq, D] bfloat16; query_start: int32 [S+1];
-    out: float32 [T, Hq, D]."""
+    out: float32 [T, Hq, D].  ``workspace`` (a uint8 device tensor) is
+    allocated here when needed and not given."""
+    import torch
     T, Hq, D = q.shape
     NB, Hkv, B, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -178,10 +198,16 @@ def paged_attention_multi_query(q, k_cache, v_cache, block_tables, context_lens,
     for t in (q, k_cache, v_cache, block_tables, context_lens, query_start, out):
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
+    need = multi_query_workspace_size(S, T, Hq, Hkv, D, max_query_len, max_context_len,
+                                      partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().paged_attention_multi_query(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(query_start), float(scale), _ptr(out), S, T, Hq, Hkv, D, B, NB, MB,
-        int(max_query_len), _dtype_code(q), _stream(stream))
+        int(max_query_len), int(max_context_len), _dtype_code(q), int(partition_size),
+        _ptr(workspace), ws_bytes, _stream(stream))
     _check("paged_attention_multi_query", st)
 
 

@@ -70,9 +70,58 @@ int32_t resolve_partitions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_c
   return (int32_t)(((int64_t)max_context_len + want - 1) / want);
 }
 
+// Multi-query partitions: the row tiles of one (sequence, KV head) already
+// give the chip work when chunks are long, so only chunks of at most 64 query
+// rows per KV head are split, by the decode policy rounded up to whole
+// 64-token tiles; an explicit size must be a multiple of 64.
+int32_t resolve_mq_partitions(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t max_query_len, int32_t max_context_len,
+                              int32_t partition_size, int32_t *ps) {
+  if (max_context_len < 0 || max_query_len < 0 || num_kv_heads <= 0) return PA_ERR_SHAPE;
+  const int64_t rows = (int64_t)max_query_len * (num_q_heads / num_kv_heads);
+  int32_t want = partition_size;
+  if (want == 0) {
+    want = -1;
+    if (rows <= 64) {
+      int32_t dps = 0;
+      const int32_t dp = resolve_partitions(num_seqs, num_kv_heads, max_context_len, 0, &dps);
+      if (dp > 1) want = (dps + 63) / 64 * 64;
+    }
+  }
+  if (want > 0 && want % 64 != 0) return PA_ERR_SHAPE;
+  if (want < 0 || max_context_len <= want) {
+    *ps = 1 << 30;
+    return 1;
+  }
+  *ps = want;
+  return (int32_t)(((int64_t)max_context_len + want - 1) / want);
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t paged_attention_multi_query_partitions(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t max_query_len,
+                                               int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return PA_ERR_SHAPE;
+  int32_t ps = 0;
+  return resolve_mq_partitions(num_seqs, num_q_heads, num_kv_heads, max_query_len,
+                               max_context_len, partition_size, &ps);
+}
+
+size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_tokens,
+                                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t max_query_len,
+                                                  int32_t max_context_len,
+                                                  int32_t partition_size) {
+  if (num_tokens < 0 || head_dim <= 0) return 0;
+  const int32_t P = paged_attention_multi_query_partitions(
+      num_seqs, num_q_heads, num_kv_heads, max_query_len, max_context_len, partition_size);
+  if (P <= 1) return 0;
+  return (size_t)num_tokens * num_q_heads * P * (head_dim + 2) * sizeof(float);
+}
 
 const char *pagedattn_status_string(int32_t status) {
   switch (status) {
@@ -189,11 +238,15 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
                                     int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                     int32_t num_blocks, int32_t max_blocks_per_seq,
-                                    int32_t max_query_len, int32_t dtype, void *stream) {
+                                    int32_t max_query_len, int32_t max_context_len,
+                                    int32_t dtype, int32_t partition_size, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
   if (!known_dtype(dtype)) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      head_dim <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0)
+      head_dim <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0 ||
+      max_context_len < 0)
     return PA_ERR_SHAPE;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
   if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size * num_kv_heads * head_dim >= (int64_t(1) << 40))
@@ -203,11 +256,23 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
   const int64_t G = num_q_heads / num_kv_heads;
   const int64_t rows = (int64_t)max_query_len * G;
   const int64_t tiles = (rows + 63) / 64;
-  if ((int64_t)num_seqs * num_kv_heads * tiles + 8 >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  int32_t ps = 0;
+  const int32_t P = resolve_mq_partitions(num_seqs, num_q_heads, num_kv_heads, max_query_len,
+                                          max_context_len, partition_size, &ps);
+  if (P < 0) return P;
+  if ((int64_t)num_seqs * num_kv_heads * tiles * P + 8 >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
   if ((int64_t)num_tokens * num_q_heads * head_dim >= (int64_t(1) << 40)) return PA_ERR_SHAPE;
+  if ((int64_t)num_tokens * num_q_heads >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
     return PA_ERR_NULL;
+  float *ws_o = nullptr, *ws_ml = nullptr;
+  if (P > 1) {
+    const size_t need = (size_t)num_tokens * num_q_heads * P * (head_dim + 2) * sizeof(float);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    ws_o = static_cast<float *>(workspace);
+    ws_ml = ws_o + (size_t)num_tokens * num_q_heads * P * head_dim;
+  }
   pa::MultiQueryArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -227,6 +292,10 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_query_len = max_query_len;
   a.dtype = dtype;
+  a.partition_size = ps;
+  a.num_partitions = P;
+  a.ws_o = ws_o;
+  a.ws_ml = ws_ml;
   const hipError_t e = pa::launch_multi_query(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

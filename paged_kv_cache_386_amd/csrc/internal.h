@@ -50,6 +50,10 @@ struct MultiQueryArgs {
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim;
   int32_t log2_block_size, num_blocks, max_blocks_per_seq, max_query_len;
   int32_t dtype;
+  int32_t partition_size;  // tokens per partition (a multiple of 64) when P > 1
+  int32_t num_partitions;  // P
+  float *ws_o;             // [num_tokens][Hq][P][D] (P > 1 only)
+  float *ws_ml;            // [num_tokens][Hq][P][2]
 };
 
 // Causal multi-query attention (multi_query.hip): bfloat16, head_dim 64 or 128.

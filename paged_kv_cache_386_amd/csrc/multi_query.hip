@@ -39,6 +39,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <climits>
+
 #include "internal.h"
 
 namespace pa {
@@ -78,8 +81,9 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
-    float *__restrict__ out, float sl2, int num_tokens, int hkv, int G, int lgB, int nb, int mb,
-    int max_q, int row_tiles, int items) {
+    float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
+    int num_tokens, int hkv, int G, int lgB, int nb, int mb, int max_q, int row_tiles, int items,
+    int ps, int P) {
   constexpr int kRows = 64 * RS;  // query rows per workgroup
   constexpr int kKs = kTk == 64 ? D + 8 : D;  // K tile row stride (elements), padded
   constexpr int kSteps = D / 32;              // k-steps of q.K
@@ -91,9 +95,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   const int per = gridDim.x / kXcds;
   const int item = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
   if (item >= items) return;
-  const int rt = item % row_tiles;
-  const int kvh = (item / row_tiles) % hkv;
-  const int s = item / (row_tiles * hkv);
+  // partitions from the last down (long contexts' tails start first), then
+  // (sequence, KV head, row tile)
+  const int per_part = items / P;
+  const int part = (P - 1) - item / per_part;
+  const int rt = (item % per_part) % row_tiles;
+  const int kvh = ((item % per_part) / row_tiles) % hkv;
+  const int s = (item % per_part) / (row_tiles * hkv);
   const int hq = hkv * G;
 
   int L = context_lens[s];
@@ -109,7 +117,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   // pos_first need no mask
   const int pos_first = L - n + row0 / G;
   const int pos_last = L - n + (row_end - 1) / G;
-  const int ntiles = pos_last / kTk + 1;
+  // this partition's tiles: [k_begin, k_end) (ps is a multiple of the tile)
+  const int k_begin = part * ps;
+  if (k_begin > pos_last) return;
+  const int k_end = min(k_begin + ps, pos_last + 1);
+  const int ntiles = (k_end - k_begin + kTk - 1) / kTk;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -146,33 +158,40 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t sk[kTk * kKs];
   __shared__ __attribute__((aligned(16))) uint16_t svt[D * kVtStride];
+  // physical block of each token of the next tiles, two slots: the table is
+  // read one tile ahead of the K/V rows it locates, so that the two reads
+  // never wait on each other
+  __shared__ uint32_t sbid[2][kTk];
+
+  auto table_entry = [&](int k0) -> uint32_t {  // token k0 + threadIdx.x (< 64 threads)
+    const int tok = k0 + (int)threadIdx.x;
+    return tok <= pos_last ? min((uint32_t)tbl[tok >> lgB], (uint32_t)(nb - 1)) : 0u;
+  };
 
   // global -> registers for the tile at k0 (tokens past pos_last are zero)
-  auto load_tile = [&](Regs &T, int k0) {
+  auto load_tile = [&](Regs &T, int k0, const uint32_t *ids) {
 #pragma unroll
     for (int j = 0; j < Regs::kKChunks; ++j) {
       const int c = threadIdx.x + kThreads * j;
-      const int tok = k0 + c / (D / 8);
+      const int tt = c / (D / 8);
+      const int tok = k0 + tt;
       const int dc = c % (D / 8);
       T.k[j] = u32x4{0, 0, 0, 0};
-      if (tok <= pos_last) {
-        const uint32_t bid = min((uint32_t)tbl[tok >> lgB], (uint32_t)(nb - 1));
-        T.k[j] = *reinterpret_cast<const u32x4 *>(kc + bid * block_elems + head_off +
+      if (tok <= pos_last)
+        T.k[j] = *reinterpret_cast<const u32x4 *>(kc + ids[tt] * block_elems + head_off +
                                                   (int64_t)(tok & bm1) * D + 8 * dc);
-      }
     }
     if (threadIdx.x < Regs::kVQuads) {
       const int tq = threadIdx.x / (D / 8);
       const int dc = threadIdx.x % (D / 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = k0 + 4 * tq + i;
+        const int tt = 4 * tq + i;
+        const int tok = k0 + tt;
         T.v[i] = u32x4{0, 0, 0, 0};
-        if (tok <= pos_last) {
-          const uint32_t bid = min((uint32_t)tbl[tok >> lgB], (uint32_t)(nb - 1));
-          T.v[i] = *reinterpret_cast<const u32x4 *>(vc + bid * block_elems + head_off +
+        if (tok <= pos_last)
+          T.v[i] = *reinterpret_cast<const u32x4 *>(vc + ids[tt] * block_elems + head_off +
                                                     (int64_t)(tok & bm1) * D + 8 * dc);
-        }
       }
     }
   };
@@ -213,14 +232,20 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   }
 
   Regs T;
-  load_tile(T, 0);
+  uint32_t id_next = 0;
+  if (threadIdx.x < kTk) sbid[0][threadIdx.x] = table_entry(k_begin);
+  __syncthreads();
+  load_tile(T, k_begin, sbid[0]);
+  if (threadIdx.x < kTk && ntiles > 1) id_next = table_entry(k_begin + kTk);
   for (int it = 0; it < ntiles; ++it) {
-    const int k0 = it * kTk;
+    const int k0 = k_begin + it * kTk;
     __syncthreads();  // every wave is done with the previous tile
     store_tile(T);
+    if (threadIdx.x < kTk) sbid[(it + 1) & 1][threadIdx.x] = id_next;
     __syncthreads();
-    if (it + 1 < ntiles) load_tile(T, k0 + kTk);  // in flight during the products
-    if (k0 > wave_last) continue;                  // all of this wave's rows end earlier
+    if (it + 1 < ntiles) load_tile(T, k0 + kTk, sbid[(it + 1) & 1]);  // during the products
+    if (threadIdx.x < kTk && it + 2 < ntiles) id_next = table_entry(k0 + 2 * kTk);
+    if (k0 > wave_last) continue;  // all of this wave's rows end earlier
     const bool masked = k0 + kTk - 1 > pos_first;
 
     // S^T for each 16-token block tb and row set r
@@ -317,12 +342,59 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     const int R = row0 + (wave * RS + r) * 16 + c16;
     if (R < row_end) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      float *orow = out + ((int64_t)(qs + R / G) * hq + kvh * G + R % G) * D + 4 * g4;
+      const int64_t orow = (int64_t)(qs + R / G) * hq + kvh * G + R % G;
+      float *o = P > 1 ? ws_o + (orow * P + part) * D : out + orow * D;
 #pragma unroll
       for (int b = 0; b < kDb; ++b)
-        *reinterpret_cast<f32x4 *>(orow + 16 * b) = acc[r][b] * inv;
+        *reinterpret_cast<f32x4 *>(o + 16 * b + 4 * g4) = acc[r][b] * inv;
+      if (P > 1 && g4 == 0) {
+        ws_ml[(orow * P + part) * 2 + 0] = m[r];
+        ws_ml[(orow * P + part) * 2 + 1] = l;
+      }
     }
   }
+}
+
+// Merge of the partition partials of each (query token, head) row: the
+// row's sequence is found by binary search over query_start, and only the
+// partitions its position reaches are combined (log-sum-exp, ascending).
+template <int D>
+__global__ __launch_bounds__(D) void paged_multi_query_merge_kernel(
+    const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
+    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
+    int num_seqs, int num_tokens, int hq, int cap, int max_q, int ps, int P) {
+  const int64_t row = blockIdx.x;  // token * hq + h
+  const int tok = (int)(row / hq);
+  // last sequence whose first row is <= tok
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (max(0, min(query_start[mid], num_tokens)) <= tok) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = lo;
+  int L = context_lens[s];
+  L = max(0, min(L, cap));
+  const int qs = max(0, min(query_start[s], num_tokens));
+  int n = query_start[s + 1] - qs;
+  n = max(0, min(min(n, L), min(max_q, num_tokens - qs)));
+  const int i = tok - qs;
+  if (i < 0 || i >= n) return;  // a row no chunk owns
+  const int pos = L - n + i;
+  const int np = min(pos / ps + 1, P);
+  const float *ml = ws_ml + row * P * 2;
+  const float *o = ws_o + row * P * D;
+  float M = ml[0];
+  for (int j = 1; j < np; ++j) M = fmaxf(M, ml[2 * j]);
+  const int d = threadIdx.x;
+  float num = 0.f, den = 0.f;
+  for (int j = 0; j < np; ++j) {
+    const float w = ml[2 * j] == neg_inf() ? 0.f
+                                           : ml[2 * j + 1] * __builtin_amdgcn_exp2f(ml[2 * j] - M);
+    num = fmaf(w, o[(int64_t)j * D + d], num);
+    den += w;
+  }
+  out[row * D + d] = den > 0.f ? num / den : 0.f;
 }
 
 template <int D, int RS>
@@ -330,16 +402,25 @@ hipError_t launch_typed(const MultiQueryArgs &a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t rows = (int64_t)a.max_query_len * G;
   const int row_tiles = (int)((rows + 64 * RS - 1) / (64 * RS));
-  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * row_tiles;
+  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * row_tiles * a.num_partitions;
   if (items <= 0) return hipSuccess;
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((paged_multi_query_kernel<D, RS>), dim3((uint32_t)grid), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t *>(a.q),
                      static_cast<const uint16_t *>(a.k_cache),
                      static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
-                     a.query_start, a.out, a.scale * kLog2e, a.num_tokens, a.num_kv_heads, G,
-                     a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.max_query_len,
-                     row_tiles, (int)items);
+                     a.query_start, a.out, a.ws_o, a.ws_ml, a.scale * kLog2e, a.num_tokens,
+                     a.num_kv_heads, G, a.log2_block_size, a.num_blocks, a.max_blocks_per_seq,
+                     a.max_query_len, row_tiles, (int)items, a.partition_size, a.num_partitions);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_partitions <= 1) return e;
+  const int64_t mrows = (int64_t)a.num_tokens * a.num_q_heads;
+  const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
+                                         INT32_MAX);
+  hipLaunchKernelGGL((paged_multi_query_merge_kernel<D>), dim3((uint32_t)mrows), dim3(D), 0,
+                     stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out, a.num_seqs,
+                     a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
+                     a.num_partitions);
   return hipGetLastError();
 }
 

@@ -164,3 +164,18 @@ def test_engine_create_rejects_bad_configs():
     assert create(partition_size=24) == -2
     assert create(device=1) == -1                 # no pool given
     assert lib.pa_engine_create(None, None, None, None) == -1
+
+
+def test_multi_query_partition_policy():
+    import paged_kv_cache_386_amd as pa
+    P = pa.multi_query_partitions
+    assert P(256, 32, 8, 5, 8192) == 4        # 20 rows per KV head: decode's 2048 tokens
+    assert P(16, 32, 8, 512, 8192) == 1       # long chunks: row tiles give the work
+    assert P(8, 32, 8, 4, 32768) == 8         # few pairs: 4096-token partitions
+    assert P(256, 32, 8, 5, 2048) == 1        # short contexts do not split
+    assert P(16, 32, 8, 512, 8192, -1) == 1
+    assert P(16, 32, 8, 512, 8192, 128) == 64
+    assert P(16, 32, 8, 512, 8192, 100) == -2  # not a multiple of the 64-token tile
+    assert pa.multi_query_workspace_size(256, 1280, 32, 8, 128, 5, 8192) == \
+        1280 * 32 * 4 * 130 * 4
+    assert pa.multi_query_workspace_size(16, 8192, 32, 8, 128, 512, 8192) == 0

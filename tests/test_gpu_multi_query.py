@@ -42,7 +42,7 @@ def _check_indices(c):
         assert qs[s + 1] - qs[s] <= L
 
 
-def run_gpu(c, tables=None, kc=None, vc=None, fill=0.0):
+def run_gpu(c, tables=None, kc=None, vc=None, fill=0.0, ps=0):
     import paged_kv_cache_386_amd as pa
     _check_indices(c)
     b = c.base
@@ -53,7 +53,8 @@ def run_gpu(c, tables=None, kc=None, vc=None, fill=0.0):
         to_torch(b.v_cache if vc is None else vc, b.dtype),
         torch.from_numpy(np.ascontiguousarray(b.block_tables if tables is None else tables)).cuda(),
         torch.from_numpy(b.context_lens).cuda(), torch.from_numpy(c.query_start).cuda(),
-        float(b.scale), out, max_query_len=c.max_query_len)
+        float(b.scale), out, max_query_len=c.max_query_len,
+        max_context_len=int(b.context_lens.max()), partition_size=ps)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -65,11 +66,11 @@ def oracle(c):
                                          b.dtype)
 
 
-def compare(c, name):
+def compare(c, name, ps=0):
     say(f"{name}: S={c.base.num_seqs} T={c.num_tokens} Hq={c.base.num_q_heads} "
         f"Hkv={c.base.num_kv_heads} D={c.base.head_dim} B={c.base.block_size} "
-        f"max_q={c.max_query_len}")
-    got = run_gpu(c)
+        f"max_q={c.max_query_len} ps={ps}")
+    got = run_gpu(c, ps=ps)
     ref = oracle(c)
     err = max_err(got, ref)
     assert err <= TOL["bf16"], f"{name}: max abs err {err}"
@@ -85,7 +86,17 @@ def test_chunks_of_every_length(D, G, Hkv):
     # chunk lengths: 0, 1, whole prompt, a tile and a bit, long chunks
     q_lens = [1, 5, 0, 63, 1, 65, 130, 17, 300, 100]
     base = make_private_case(f"mq-{D}-{G}", LENS, G * Hkv, Hkv, D, 16, "bf16", 40 + D + G)
-    compare(make_multi_query_case(base, q_lens, 40 + D + G), f"mq D={D} G={G}")
+    for ps in (0, -1, 64, 192):
+        compare(make_multi_query_case(base, q_lens, 40 + D + G), f"mq D={D} G={G}", ps)
+
+
+@pytest.mark.parametrize("ps", [0, 64, 128, 2048])
+def test_partitions_of_short_chunks(ps):
+    """Few query rows per KV head (the split case): 1 to 8 tokens per
+    sequence over contexts up to 5000, every partition size."""
+    lens = [1, 8, 64, 65, 700, 2049, 5000, 4096]
+    base = make_private_case(f"mq-ps{ps}", lens, 32, 8, 128, 16, "bf16", 77)
+    compare(make_multi_query_case(base, [1, 8, 5, 3, 8, 2, 7, 4], 77), f"mq ps={ps}", ps)
 
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64, 128, 512, 1024])
