@@ -11,6 +11,9 @@ from .generate import (  # noqa: F401
     MultiQueryCase,
     bf16_bits_from_f32,
     draw_values,
+    draw_e4m3_codes,
+    Fp8Case,
+    make_fp8_case,
     make_aliased_case,
     make_case,
     make_fork_case,

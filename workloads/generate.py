@@ -596,3 +596,51 @@ def make_multi_query_workload(name: str, *, seed: int = 7, poison: bool = True,
     else:
         raise ValueError(name)
     return make_multi_query_case(base, q_lens, seed, name, MULTI_QUERY_NAMES[name])
+
+
+# ---------------------------------------------------------------- FP8 pools
+
+E4M3_QNAN = 0x7F
+
+
+@dataclass
+class Fp8Case:
+    """A workload whose pool holds FP8 (E4M3) codes: ``base`` gives the
+    structure (tables, lengths, copy pairs, slots), the bfloat16 queries and
+    the bfloat16 new tokens (to be quantised by the write); ``k8``/``v8``
+    replace its pool, with one fp32 scale per cache."""
+
+    base: Case
+    k8: np.ndarray  # uint8 [NB, Hkv, B, D]
+    v8: np.ndarray
+    k_scale: np.float32
+    v_scale: np.float32
+
+    @property
+    def name(self) -> str:
+        return self.base.name
+
+
+def draw_e4m3_codes(rng: np.random.Generator, shape, max_exponent_field: int = 9) -> np.ndarray:
+    """Random E4M3 codes: random sign and mantissa, exponent field uniform in
+    [0, max_exponent_field] (so never the NaN code; magnitudes below
+    2^(max_exponent_field - 6))."""
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    e = rng.integers(0, max_exponent_field + 1, size=shape, dtype=np.uint8) << 3
+    m = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign | e | m).astype(np.uint8)
+
+
+def make_fp8_case(base: Case, seed: int, k_scale: float = 0.25, v_scale: float = 0.5) -> Fp8Case:
+    """The same workload over an FP8 pool: every slot gets a random code from
+    ``default_rng([seed, 3])``, except the slots that hold the NaN poison in
+    ``base`` (never read), which get the E4M3 NaN code."""
+    if base.dtype != "bf16":
+        raise ValueError("FP8 workloads take bfloat16 queries and new tokens")
+    rng = np.random.default_rng([seed, 3])
+    k8 = draw_e4m3_codes(rng, base.k_cache.shape)
+    v8 = draw_e4m3_codes(rng, base.v_cache.shape)
+    k8[base.k_cache == BF16_QNAN] = E4M3_QNAN
+    v8[base.v_cache == BF16_QNAN] = E4M3_QNAN
+    return Fp8Case(base=base, k8=k8, v8=v8, k_scale=np.float32(k_scale),
+                   v_scale=np.float32(v_scale))
