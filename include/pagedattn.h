@@ -61,8 +61,10 @@ typedef enum pa_status {
 } pa_status;
 
 typedef enum pa_dtype {
-  PA_F32 = 0,  /* IEEE binary32 */
-  PA_BF16 = 1  /* bfloat16 (the high half of a binary32), stored as 16-bit words */
+  PA_F32 = 0,      /* IEEE binary32 */
+  PA_BF16 = 1,     /* bfloat16 (the high half of a binary32), stored as 16-bit words */
+  PA_FP8_E4M3 = 2  /* pools only: OCP 8-bit float E4M3 (bias 7, no infinities, max 448),
+                      one code per byte, meaning code value * the cache's scale */
 } pa_dtype;
 
 /*
@@ -118,6 +120,31 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
                                int32_t max_blocks_per_seq, int32_t max_context_len,
                                int32_t dtype, int32_t partition_size,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode_fp8 -- paged_attention_decode over an FP8 (E4M3)
+ * pool ([P3] architecture figure: FP8/INT8 quantisation in the kernel layer;
+ * [P1] section 5.3: FP8 trades a little precision for memory and bandwidth).
+ *
+ * k_cache and v_cache hold one E4M3 code per element in the layout above; an
+ * element's value is e4m3(code) * k_scale (K) or * v_scale (V), so the
+ * result is that of paged_attention_decode on the dequantised pool.  q is
+ * bfloat16.  Codes are widened exactly to bfloat16 for q.K on the matrix
+ * cores and to fp32 for p.V; k_scale joins the softmax scale and v_scale
+ * multiplies the output.  Every other argument, the workspace (same size as
+ * paged_attention_decode's) and the partition policy are those of
+ * paged_attention_decode.
+ * Supported: head_dim 128, G in {4, 8}; k_scale and v_scale finite and > 0.
+ * Errors: as paged_attention_decode.
+ */
+int32_t paged_attention_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *block_tables, const int32_t *context_lens,
+                                   float scale, float k_scale, float v_scale, float *out,
+                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len,
+                                   int32_t partition_size, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of workspace paged_attention_decode needs for these arguments (0 when
@@ -224,13 +251,35 @@ size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_
  *   slot_mapping   device int32 [num_tokens]
  *   k_cache,
  *   v_cache        device pool (layout above), modified in place
- * head_dim must be a multiple of 8.
+ * dtype may also be PA_FP8_E4M3 (codes copied as bytes).  A head row
+ * (head_dim elements) must be a multiple of 16 bytes.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH.
  */
 int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                        int32_t num_tokens, void *k_cache, void *v_cache,
                        int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                        int32_t head_dim, int32_t dtype, void *stream);
+
+/*
+ * kv_cache_write_fp8 -- kv_cache_write into an FP8 (E4M3) pool: each element
+ * x of k (v) is stored as the code of y = x / k_scale (x / v_scale), the
+ * division done in fp32 (correctly rounded), y clamped to [-448, 448] and
+ * rounded to the nearest E4M3 value, ties to the even mantissa; NaN is
+ * stored as NaN.
+ *
+ *   k, v           device, [num_tokens][num_kv_heads][head_dim], src_dtype
+ *                  (PA_F32 or PA_BF16)
+ *   slot_mapping   device int32 [num_tokens] (negative or out-of-pool slots
+ *                  are skipped; two tokens must not share a slot)
+ *   k_cache,
+ *   v_cache        device FP8 pool (layout above), modified in place
+ * head_dim must be a multiple of 16; scales finite and > 0.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH.
+ */
+int32_t kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
+                           int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t src_dtype, float k_scale, float v_scale, void *stream);
 
 /*
  * copy_blocks -- copy-on-write block copies.
@@ -247,7 +296,8 @@ int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping
  *
  *   src_dst_pairs  device int32 [num_pairs][2]
  *   host_pairs     optional host copy of the same pairs for the alias check
- * head_dim must be a multiple of 8.
+ * dtype is that of the pool (PA_FP8_E4M3 included); a head row must be a
+ * multiple of 16 bytes.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIAS, PA_ERR_LAUNCH.
  */
 int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cache,

@@ -27,9 +27,19 @@ int log2_exact(int64_t x) {
   return n;
 }
 
-int64_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+int64_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
 
 bool known_dtype(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
+
+// pools may also hold FP8 codes (moved as raw bytes by the edits)
+bool known_pool_dtype(int32_t dtype) { return known_dtype(dtype) || dtype == PA_FP8_E4M3; }
+
+// head rows must be whole 16-byte vectors for the edit kernels
+bool head_row_ok(int32_t head_dim, int32_t dtype) {
+  return head_dim > 0 && ((int64_t)head_dim * elem_bytes(dtype)) % 16 == 0;
+}
+
+bool valid_scale(float x) { return x > 0.f && x < __builtin_huge_valf(); }
 
 // Partition policy.  Returns the number of partitions (>= 1) and the partition
 // size through *ps, or a negative pa_status.
@@ -168,13 +178,19 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
   return (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
 }
 
-int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v_cache,
-                               const int32_t *block_tables, const int32_t *context_lens,
-                               float scale, float *out, int32_t num_seqs, int32_t num_q_heads,
-                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                               int32_t num_blocks, int32_t max_blocks_per_seq,
-                               int32_t max_context_len, int32_t dtype, int32_t partition_size,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode over a pool of kv_dtype (dtype for a bf16/fp32 pool, PA_FP8_E4M3
+// with bf16 queries); the checks and launch shared by both entry points.
+int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, float scale,
+                    float *out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+                    int32_t kv_dtype, float k_scale, float v_scale, int32_t partition_size,
+                    void *workspace, size_t workspace_bytes, void *stream) {
   if (!known_dtype(dtype)) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
@@ -183,12 +199,17 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
   // byte offsets inside one block are 32-bit in the kernels
-  if ((int64_t)block_size * num_kv_heads * head_dim * elem_bytes(dtype) >= (int64_t(1) << 31))
+  if ((int64_t)block_size * num_kv_heads * head_dim * elem_bytes(kv_dtype) >= (int64_t(1) << 31))
     return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
-  if (!pa::decode_supported(dtype, head_dim, num_q_heads / num_kv_heads))
+  if (kv_dtype == PA_FP8_E4M3) {
+    if (!pa::decode_mfma_supported(dtype, head_dim, num_q_heads / num_kv_heads))
+      return PA_ERR_UNSUPPORTED;
+    if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_SHAPE;
+  } else if (!pa::decode_supported(dtype, head_dim, num_q_heads / num_kv_heads)) {
     return PA_ERR_UNSUPPORTED;
+  }
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
 
@@ -217,6 +238,9 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_partitions = P;
   a.dtype = dtype;
+  a.kv_dtype = kv_dtype;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   if (P > 1) {
     const size_t need = (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
@@ -229,6 +253,58 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
   }
   const hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v_cache,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               float scale, float *out, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int32_t dtype, int32_t partition_size,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, dtype, dtype, 1.f, 1.f, partition_size,
+                     workspace, workspace_bytes, stream);
+}
+
+int32_t paged_attention_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *block_tables, const int32_t *context_lens,
+                                   float scale, float k_scale, float v_scale, float *out,
+                                   int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len,
+                                   int32_t partition_size, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, PA_BF16, PA_FP8_E4M3, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+int32_t kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
+                           int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t src_dtype, float k_scale, float v_scale, void *stream) {
+  if (!known_dtype(src_dtype)) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 ||
+      !head_row_ok(head_dim, PA_FP8_E4M3))
+    return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
+  if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_SHAPE;
+  if ((int64_t)num_kv_heads * head_dim / 16 > (int64_t)128 * 65535) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  const hipError_t e = pa::launch_kv_cache_write_fp8(
+      k, v, slot_mapping, num_tokens, k_cache, v_cache, (int64_t)num_blocks * block_size,
+      log2_exact(block_size), num_kv_heads, head_dim, src_dtype, k_scale, v_scale,
+      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -305,9 +381,8 @@ int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping
                        int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
                        int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                        int32_t dtype, void *stream) {
-  if (!known_dtype(dtype)) return PA_ERR_DTYPE;
-  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      head_dim % 8 != 0)
+  if (!known_pool_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || !head_row_ok(head_dim, dtype))
     return PA_ERR_SHAPE;
   if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
@@ -327,9 +402,8 @@ int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cac
                     void *v_cache, int32_t num_blocks, int32_t block_size,
                     int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                     const int32_t *host_pairs, void *stream) {
-  if (!known_dtype(dtype)) return PA_ERR_DTYPE;
-  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      head_dim % 8 != 0)
+  if (!known_pool_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || !head_row_ok(head_dim, dtype))
     return PA_ERR_SHAPE;
   if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;

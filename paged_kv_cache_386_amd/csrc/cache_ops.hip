@@ -5,6 +5,11 @@
 //    its head's slab of the slot's block) are stored at its slot ("3.1" and "3.3" sections of the chenxutan.com vLLM
 //    deep-dive: the generated token's K/V goes back into the cache, appended
 //    into the sequence's current block);
+//  * kv_cache_write_fp8: the same store into an FP8 (E4M3) pool, each element
+//    divided by its cache's fp32 scale and rounded to the nearest E4M3 value
+//    (the FP8 quantisation named in the kernel layer of the
+//    devpress.csdn.net/amd walkthrough's architecture figure; the format and
+//    the per-cache scale are this library's choice, as the pages give none);
 //  * copy_blocks: whole physical blocks copied onto others, the copy-on-write
 //    step taken before a forked sequence appends to a shared block
 //    ("关键设计二：Copy-on-Write" section of the devpress.csdn.net/amd vLLM
@@ -51,6 +56,74 @@ __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(
   vc[dst] = vx;
 }
 
+// E4M3 code of y: saturate to +-448, nearest value, ties to the even
+// mantissa; NaN gives the NaN code.  (OCP 8-bit floating point, E4M3: bias
+// 7, subnormals m/8 * 2^-6, the all-ones code is NaN, no infinities.)
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // 448 and above: saturate
+  if (a >= 0x3C800000u) {                     // 2^-6 and above: normal
+    const uint32_t keep = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xFFFFFu;
+    uint32_t code = (((a >> 23) - 120u) << 3) | keep;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++code;  // may carry
+    return sign | code;
+  }
+  // below 2^-6: multiples of 2^-9 (codes 0..8), rounded half to even
+  return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.f);
+}
+
+template <typename T>
+__device__ __forceinline__ float widen(T x);
+template <>
+__device__ __forceinline__ float widen<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ float widen<uint16_t>(uint16_t x) {
+  return __uint_as_float((uint32_t)x << 16);
+}
+
+// grid.x = token, grid.y = stripe of the token's 16-element groups (hkv heads
+// of head_vecs groups each).  Group j of head h = j / head_vecs is divided by
+// the cache's scale, encoded, and stored as one 16-byte vector in that head's
+// slab of the slot's block.
+template <typename T>
+__global__ __launch_bounds__(kWriteThreads) void kv_cache_write_fp8_kernel(
+    const T *__restrict__ k, const T *__restrict__ v, const int32_t *__restrict__ slot_mapping,
+    u32x4 *__restrict__ kc, u32x4 *__restrict__ vc, float k_scale, float v_scale,
+    int64_t num_slots, int lgB, int hkv, int head_vecs) {
+  const int64_t i = blockIdx.x;
+  const int row_vecs = hkv * head_vecs;
+  const int j = blockIdx.y * kWriteThreads + threadIdx.x;
+  if (j >= row_vecs) return;
+  const int32_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int h = j / head_vecs;
+  const int jj = j - h * head_vecs;
+  const int64_t blk = slot >> lgB;
+  const int off = slot & ((1 << lgB) - 1);
+  const int64_t dst = (((blk * hkv + h) << lgB) + off) * head_vecs + jj;
+  const int64_t src = (i * row_vecs + j) * 16;  // elements
+  u32x4 ko, vo;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t kw = 0, vw = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      kw |= e4m3_encode(widen<T>(k[src + 4 * w + b]) / k_scale) << (8 * b);
+      vw |= e4m3_encode(widen<T>(v[src + 4 * w + b]) / v_scale) << (8 * b);
+    }
+    ko[w] = kw;
+    vo[w] = vw;
+  }
+  kc[dst] = ko;
+  vc[dst] = vo;
+}
+
 // grid.x = pair, grid.y = stripe of kCopyThreads*kCopyVecsPerThread vectors of
 // the block, grid.z = 0 for K, 1 for V.
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
@@ -91,6 +164,31 @@ hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *sl
                      static_cast<const u32x4 *>(v), slot_mapping, static_cast<u32x4 *>(k_cache),
                      static_cast<u32x4 *>(v_cache), num_slots, (int)log2_block_size,
                      (int)num_kv_heads, (int)head_vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
+                                     int32_t num_tokens, void *k_cache, void *v_cache,
+                                     int64_t num_slots, int32_t log2_block_size,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
+                                     float k_scale, float v_scale, hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  const int head_vecs = head_dim / 16;
+  const int64_t row_vecs = (int64_t)head_vecs * num_kv_heads;
+  const int64_t stripes = (row_vecs + kWriteThreads - 1) / kWriteThreads;
+  const dim3 grid((uint32_t)num_tokens, (uint32_t)stripes);
+  if (src_dtype == 0)
+    hipLaunchKernelGGL(kv_cache_write_fp8_kernel<float>, grid, dim3(kWriteThreads), 0, stream,
+                       static_cast<const float *>(k), static_cast<const float *>(v),
+                       slot_mapping, static_cast<u32x4 *>(k_cache),
+                       static_cast<u32x4 *>(v_cache), k_scale, v_scale, num_slots,
+                       (int)log2_block_size, (int)num_kv_heads, head_vecs);
+  else
+    hipLaunchKernelGGL(kv_cache_write_fp8_kernel<uint16_t>, grid, dim3(kWriteThreads), 0, stream,
+                       static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
+                       slot_mapping, static_cast<u32x4 *>(k_cache),
+                       static_cast<u32x4 *>(v_cache), k_scale, v_scale, num_slots,
+                       (int)log2_block_size, (int)num_kv_heads, head_vecs);
   return hipGetLastError();
 }
 

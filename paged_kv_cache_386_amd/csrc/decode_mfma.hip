@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace pa {
@@ -78,13 +80,75 @@ __device__ __forceinline__ float quad_bcast(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), R * 0x55, 0xF, 0xF, false));
 }
 
-struct Tile {
-  u32x4 k[4];  // token n of the tile, elements 32s + 8g .. +7 (s = 0..3)
-  u32x4 v[4];  // token 4g + j of the tile, elements 8n .. 8n+7 (j = 0..3)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight K or V elements: 16 bytes of bfloat16, or 8 bytes of FP8 (E4M3).
+template <bool FP8>
+struct Vec8 {
+  using type = u32x4;
+};
+template <>
+struct Vec8<true> {
+  using type = u32x2;
 };
 
-template <int G, bool SMALLB>
+template <bool FP8>
+struct Tile {
+  typename Vec8<FP8>::type k[4];  // token n of the tile, elements 32s + 8g .. +7 (s = 0..3)
+  typename Vec8<FP8>::type v[4];  // token 4g + j of the tile, elements 8n .. 8n+7 (j = 0..3)
+};
+
+template <int POLICY>
+__device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY));
+}
+
+// Four E4M3 codes (one dword) to fp32 with the hardware conversion (OCP
+// E4M3 on gfx950; every code is exact in fp32).
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
+
+// Eight E4M3 codes to the bfloat16 MFMA operand (exact: an E4M3 value has at
+// most 4 significant bits, so the high half of its fp32 form is the value).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float f[4];
+    e4m3x4_to_f32(w[h], f);
+    r[2 * h] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+    r[2 * h + 1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int G, bool SMALLB, bool FP8>
 struct MfmaDecode {
+  using KV = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+  using V8 = typename Vec8<FP8>::type;
+  using TileT = Tile<FP8>;
+  static constexpr int kElem = FP8 ? 1 : 2;  // bytes per element
+  template <int POLICY>
+  static __device__ __forceinline__ V8 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (FP8)
+      return buffer_load8<POLICY>(r, off);
+    else
+      return buffer_load<POLICY>(r, off);
+  }
+  static __device__ __forceinline__ V8 zero8() { return V8{}; }
+  static __device__ __forceinline__ bf16x8 k_operand(const V8 &w) {
+    if constexpr (FP8)
+      return e4m3x8_to_bf16(w);
+    else
+      return __builtin_bit_cast(bf16x8, w);
+  }
   // WIDE: p.V on 16x16x4 with a wave-shared running maximum (G = 8);
   // otherwise 4x4x1 blocks with one running maximum per lane group (G = 4).
   static constexpr bool WIDE = G > 4;
@@ -92,8 +156,8 @@ struct MfmaDecode {
   // Issue the loads of the tile starting at token cs.  Rows of tokens at or
   // past t1 are not read (their registers are zero) when MASK is set.
   template <bool MASK>
-  static __device__ __forceinline__ void load(Tile &T, const uint16_t *__restrict__ kc,
-                                              const uint16_t *__restrict__ vc,
+  static __device__ __forceinline__ void load(TileT &T, const KV *__restrict__ kc,
+                                              const KV *__restrict__ vc,
                                               const int32_t *__restrict__ tbl, int ent,
                                               bool stream_v, int cs, int t1,
                                               int lgB, int nb, int g, int n, int row_elems,
@@ -104,53 +168,53 @@ struct MfmaDecode {
       // ahead of time (ent); its rows are read through buffer descriptors
       // spanning the block (reads past it return zeros)
       const uint32_t pid = min((uint32_t)ent, (uint32_t)(nb - 1));
-      const uint32_t bbytes = (uint32_t)(block_elems * 2);
+      const uint32_t bbytes = (uint32_t)(block_elems * kElem);
       const auto rk = block_rsrc(kc + (int64_t)pid * block_elems, bbytes);
       const auto rv = block_rsrc(vc + (int64_t)pid * block_elems, bbytes);
       const int o = cs & bm1;
-      const uint32_t koff = (uint32_t)(((o + n) * row_elems + head_off + 8 * g) * 2);
+      const uint32_t koff = (uint32_t)(((o + n) * row_elems + head_off + 8 * g) * kElem);
       const bool okk = !MASK || cs + n < t1;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        T.k[s] = okk ? buffer_load<kCacheNormal>(rk, koff + 64 * s) : u32x4{0, 0, 0, 0};
+        T.k[s] = okk ? bload<kCacheNormal>(rk, koff + 32 * kElem * s) : zero8();
       uint32_t voff[4];
       bool ok[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        voff[j] = (uint32_t)(((o + 4 * g + j) * row_elems + head_off + 8 * n) * 2);
+        voff[j] = (uint32_t)(((o + 4 * g + j) * row_elems + head_off + 8 * n) * kElem);
         ok[j] = !MASK || cs + 4 * g + j < t1;
       }
       if (stream_v) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          T.v[j] = ok[j] ? buffer_load<kCacheStream>(rv, voff[j]) : u32x4{0, 0, 0, 0};
+          T.v[j] = ok[j] ? bload<kCacheStream>(rv, voff[j]) : zero8();
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          T.v[j] = ok[j] ? buffer_load<kCacheNormal>(rv, voff[j]) : u32x4{0, 0, 0, 0};
+          T.v[j] = ok[j] ? bload<kCacheNormal>(rv, voff[j]) : zero8();
       }
     } else {
       // blocks shorter than a tile: each token row looks up its own block
       const int tk = cs + n;
       if (!MASK || tk < t1) {
         const uint32_t pid = min((uint32_t)tbl[tk >> lgB], (uint32_t)(nb - 1));
-        const u32x4 *kp = reinterpret_cast<const u32x4 *>(
+        const V8 *kp = reinterpret_cast<const V8 *>(
             kc + (int64_t)pid * block_elems + head_off + (tk & bm1) * row_elems + 8 * g);
 #pragma unroll
         for (int s = 0; s < 4; ++s) T.k[s] = kp[4 * s];
       } else {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) T.k[s] = u32x4{0, 0, 0, 0};
+        for (int s = 0; s < 4; ++s) T.k[s] = zero8();
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tv = cs + 4 * g + j;
         if (!MASK || tv < t1) {
           const uint32_t pid = min((uint32_t)tbl[tv >> lgB], (uint32_t)(nb - 1));
-          T.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+          T.v[j] = __builtin_nontemporal_load(reinterpret_cast<const V8 *>(
               vc + (int64_t)pid * block_elems + head_off + (tv & bm1) * row_elems + 8 * n));
         } else {
-          T.v[j] = u32x4{0, 0, 0, 0};
+          T.v[j] = zero8();
         }
       }
     }
@@ -159,18 +223,30 @@ struct MfmaDecode {
   }
 
   // acc[i] += p (x) V elements 8n + i of one token row, for i = 0..7.
-  static __device__ __forceinline__ void pv(const u32x4 &w, float p, f32x4 (&acc)[8]) {
+  static __device__ __forceinline__ void pv(const V8 &w, float p, f32x4 (&acc)[8]) {
+    float e[8];
+    if constexpr (FP8) {
+      float a[4], b[4];
+      e4m3x4_to_f32(w[0], a);
+      e4m3x4_to_f32(w[1], b);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = __uint_as_float(w[e] << 16);
-      const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
-      if constexpr (WIDE) {
-        acc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, lo, acc[2 * e], 0, 0, 0);
-        acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, hi, acc[2 * e + 1], 0, 0, 0);
-      } else {
-        acc[2 * e] = __builtin_amdgcn_mfma_f32_4x4x1f32(p, lo, acc[2 * e], 0, 0, 0);
-        acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(p, hi, acc[2 * e + 1], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        e[i] = a[i];
+        e[4 + i] = b[i];
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[2 * i] = __uint_as_float(w[i] << 16);
+        e[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (WIDE)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, e[i], acc[i], 0, 0, 0);
+      else
+        acc[i] = __builtin_amdgcn_mfma_f32_4x4x1f32(p, e[i], acc[i], 0, 0, 0);
     }
   }
 
@@ -178,14 +254,13 @@ struct MfmaDecode {
   // lane's query head's running maximum: of its lane group (G = 4) or of the
   // wave (WIDE); lsum covers the lane group's tokens in both cases.
   template <bool MASK>
-  static __device__ __forceinline__ void compute(const Tile &T, const bf16x8 (&qb)[4],
+  static __device__ __forceinline__ void compute(const TileT &T, const bf16x8 (&qb)[4],
                                                  f32x4 (&acc)[8], float &m, float &lsum, int cs,
                                                  int t1, int g, float sl2) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T.k[s]), qb[s], c, 0,
-                                                   0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(T.k[s]), qb[s], c, 0, 0, 0);
     float x[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) x[j] = (!MASK || cs + 4 * g + j < t1) ? c[j] * sl2 : neg_inf();
@@ -232,14 +307,16 @@ struct MfmaDecode {
   }
 };
 
-template <int G, bool SMALLB>
+template <int G, bool SMALLB, bool FP8>
 __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ context_lens, float *__restrict__ out, float *__restrict__ ws_o,
-    float *__restrict__ ws_ml, float sl2, int num_seqs, int hkv, int lgB, int nb, int mb, int ps,
-    int P) {
-  using K = MfmaDecode<G, SMALLB>;
+    const uint16_t *__restrict__ q,
+    const typename MfmaDecode<G, SMALLB, FP8>::KV *__restrict__ kc,
+    const typename MfmaDecode<G, SMALLB, FP8>::KV *__restrict__ vc,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+    float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
+    float v_scale, int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P) {
+  using K = MfmaDecode<G, SMALLB, FP8>;
+  using TileT = typename K::TileT;
   constexpr bool WIDE = K::WIDE;
 
   const int id = blockIdx.x;
@@ -331,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     return __builtin_amdgcn_readlane(ent_cur, j & 63);
   };
   {
-    Tile A, Bt;
+    TileT A, Bt;
     bool sv = true;
     int ent = 0;
     if (nw > 0) {
@@ -440,9 +517,9 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     }
     const int64_t row = (int64_t)s * hq + kvh * G + h;
     if (final_out) {
-      out[row * kD + d] = ls > 0.f ? o / ls : 0.f;
+      out[row * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
     } else {
-      ws_o[(row * P + p) * kD + d] = o / ls;
+      ws_o[(row * P + p) * kD + d] = v_scale * (o / ls);
       if (d == 0) {
         ws_ml[(row * P + p) * 2 + 0] = M;
         ws_ml[(row * P + p) * 2 + 1] = ls;
@@ -451,26 +528,28 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   }
 }
 
-template <int G, bool SMALLB>
+template <int G, bool SMALLB, bool FP8>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+  using KV = typename MfmaDecode<G, SMALLB, FP8>::KV;
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
   if (grid <= 0) return hipSuccess;
-  const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<G, SMALLB>), dim3((uint32_t)grid), dim3(kThreads),
-                     0, stream, static_cast<const uint16_t *>(a.q),
-                     static_cast<const uint16_t *>(a.k_cache),
-                     static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
-                     a.out, a.ws_o, a.ws_ml, sl2, a.num_seqs, a.num_kv_heads, a.log2_block_size,
+  // the K scale multiplies every score, so it joins the softmax scale
+  const float sl2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<G, SMALLB, FP8>), dim3((uint32_t)grid),
+                     dim3(kThreads), 0, stream, static_cast<const uint16_t *>(a.q),
+                     static_cast<const KV *>(a.k_cache), static_cast<const KV *>(a.v_cache),
+                     a.block_tables, a.context_lens, a.out, a.ws_o, a.ws_ml, sl2,
+                     FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads, a.log2_block_size,
                      a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions <= 1) return e;
   return launch_partition_merge(a, stream);
 }
 
-template <int G>
+template <int G, bool FP8>
 hipError_t launch_b(const DecodeArgs &a, hipStream_t stream) {
-  if (a.log2_block_size >= 4) return launch_typed<G, false>(a, stream);
-  return launch_typed<G, true>(a, stream);
+  if (a.log2_block_size >= 4) return launch_typed<G, false, FP8>(a, stream);
+  return launch_typed<G, true, FP8>(a, stream);
 }
 
 }  // namespace
@@ -480,9 +559,10 @@ bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+  const bool fp8 = a.kv_dtype == 2;
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 4: return launch_b<4>(a, stream);
-    case 8: return launch_b<8>(a, stream);
+    case 4: return fp8 ? launch_b<4, true>(a, stream) : launch_b<4, false>(a, stream);
+    case 8: return fp8 ? launch_b<8, true>(a, stream) : launch_b<8, false>(a, stream);
     default: return hipErrorNotSupported;
   }
 }

@@ -22,7 +22,10 @@ struct DecodeArgs {
   int32_t log2_block_size, num_blocks, max_blocks_per_seq;
   int32_t partition_size;  // tokens per partition (>= every context when P == 1)
   int32_t num_partitions;  // P
-  int32_t dtype;           // 0 = f32, 1 = bf16
+  int32_t dtype;           // of q and, unless kv_dtype says otherwise, of the pool: 0 = f32, 1 = bf16
+  int32_t kv_dtype = -1;   // 2 = FP8 E4M3 pool (bf16 q, matrix-core kernel only); -1 = dtype
+  float k_scale = 1.f;     // FP8 pool: stored code c means e4m3(c) * scale
+  float v_scale = 1.f;
 };
 
 // Enqueues decode (and the partition merge when P > 1).  Returns hipSuccess or
@@ -64,6 +67,12 @@ hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *sl
                                  int32_t num_tokens, void *k_cache, void *v_cache,
                                  int64_t num_slots, int32_t log2_block_size, int32_t num_kv_heads,
                                  int64_t head_row_bytes, hipStream_t stream);
+
+hipError_t launch_kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
+                                     int32_t num_tokens, void *k_cache, void *v_cache,
+                                     int64_t num_slots, int32_t log2_block_size,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
+                                     float k_scale, float v_scale, hipStream_t stream);
 
 hipError_t launch_copy_blocks(const int32_t *pairs, int32_t num_pairs, void *k_cache,
                               void *v_cache, int32_t num_blocks, int64_t block_bytes,
