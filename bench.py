@@ -66,8 +66,10 @@ CAL_WRITE_BYTES = CAL_READ_BYTES
 # ---------------------------------------------------------------- byte model
 
 def kv_row_bytes(case) -> int:
-    """Bytes of one token's K (or V) row over all KV heads."""
-    return case.num_kv_heads * case.head_dim * (4 if case.dtype == "f32" else 2)
+    """Bytes of one token's K (or V) row over all KV heads, as stored in the
+    pool (one byte per element for an FP8 pool)."""
+    el = getattr(case, "kv_elem_bytes", None) or (4 if case.dtype == "f32" else 2)
+    return case.num_kv_heads * case.head_dim * el
 
 
 def unique_slots(case) -> int:
@@ -111,7 +113,8 @@ def edit_bytes(case) -> int:
     blk = case.block_size * kv_row_bytes(case)
     copies = 2 * 2 * blk * len(case.copy_pairs)
     T = len(case.slot_mapping)
-    writes = 2 * 2 * kv_row_bytes(case) * T + 4 * T + 8 * len(case.copy_pairs)
+    src_row = case.num_kv_heads * case.head_dim * (4 if case.dtype == "f32" else 2)
+    writes = 2 * (src_row + kv_row_bytes(case)) * T + 4 * T + 8 * len(case.copy_pairs)
     return copies + writes
 
 
@@ -577,6 +580,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=25.0,
                     help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="configs 2-4 over an FP8 (E4M3) pool: quantising write and FP8 decode")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -588,6 +593,13 @@ def main() -> int:
         args.steps = 50 if args.steps is None else args.steps
         args.warmup = 10 if args.warmup is None else args.warmup
     workload = f"cfg{args.config}" + (f"-B{args.block_size or 512}" if args.config == 3 else "")
+    if args.kv_fp8:
+        if args.config == 1:
+            print("the FP8 pool runs on the matrix-core decode (G = 4 or 8): configs 2-4",
+                  file=sys.stderr)
+            return 2
+        workload += "-fp8"
+        args.no_cpu_baseline = True
     if args.serving:
         workload = "serving"
     if args.multi_query:
@@ -640,9 +652,14 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(dev)
 
+    c8 = None
+    if args.kv_fp8:
+        from workloads import make_fp8_case
+        c8 = make_fp8_case(case, args.config)
+        case.kv_elem_bytes = 1
     q = to_dev(case.q, dev)
-    kc = to_dev(case.k_cache, dev)
-    vc = to_dev(case.v_cache, dev)
+    kc = to_dev(case.k_cache if c8 is None else c8.k8, dev)
+    vc = to_dev(case.v_cache if c8 is None else c8.v8, dev)
     tables = torch.from_numpy(case.block_tables).to(dev)
     lens = torch.from_numpy(case.context_lens).to(dev)
     out = torch.empty(case.q.shape, dtype=torch.float32, device=dev)
@@ -662,12 +679,24 @@ def main() -> int:
 
     def edits():
         pa.copy_blocks(pairs, kc, vc, stream=stream)
-        pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
+        if c8 is None:
+            pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
+        else:
+            pa.kv_cache_write_fp8(k_new, v_new, slots, kc, vc, float(c8.k_scale),
+                                  float(c8.v_scale), stream=stream)
 
     def decode():
-        pa.paged_attention_decode(q, kc, vc, tables, lens, float(case.scale), out,
-                                  max_context_len=max_ctx, partition_size=args.partition_size,
-                                  workspace=ws, stream=stream)
+        if c8 is None:
+            pa.paged_attention_decode(q, kc, vc, tables, lens, float(case.scale), out,
+                                      max_context_len=max_ctx,
+                                      partition_size=args.partition_size, workspace=ws,
+                                      stream=stream)
+        else:
+            pa.paged_attention_decode_fp8(q, kc, vc, tables, lens, float(case.scale),
+                                          float(c8.k_scale), float(c8.v_scale), out,
+                                          max_context_len=max_ctx,
+                                          partition_size=args.partition_size, workspace=ws,
+                                          stream=stream)
 
     for _ in range(args.warmup):
         if has_step:
@@ -717,8 +746,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.dtype,
-        "data": "synthetic (seeded N(0,1) q/K/V; lengths, prefix groups and forks as described)",
+        "dtype": case.dtype if c8 is None else "fp8-e4m3 (bf16 q)",
+        "data": "synthetic (seeded N(0,1) q/K/V; lengths, prefix groups and forks as described)"
+                + ("; K/V as random E4M3 codes, k_scale 0.25, v_scale 0.5" if c8 else ""),
         "config": {
             "workload": f"{workload}: {case.description}",
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,

@@ -93,11 +93,29 @@ struct Vec8<true> {
   using type = u32x2;
 };
 
+// K rows are fetched 16 bytes per lane: for bfloat16, lane group g takes
+// elements 32s + 8g .. +7 of k-step s (s = 0..3); for FP8 a 16-byte load
+// holds two k-steps, so lane group g takes elements 16(4i + g) .. +15 in load
+// i (i = 0, 1), giving k-step 2i + u its elements 16(4i + g) + 8u .. +7.  The
+// dot product sums over all 128 elements either way; q's operand is loaded
+// with the same assignment.  Each load instruction then covers 64
+// contiguous bytes of every token row it touches.
 template <bool FP8>
 struct Tile {
-  typename Vec8<FP8>::type k[4];  // token n of the tile, elements 32s + 8g .. +7 (s = 0..3)
+  u32x4 k[FP8 ? 2 : 4];           // token n of the tile (see above)
   typename Vec8<FP8>::type v[4];  // token 4g + j of the tile, elements 8n .. 8n+7 (j = 0..3)
 };
+
+// First element of lane group g's part of K load i (see Tile).
+template <bool FP8>
+__device__ __forceinline__ int k_load_elem(int g, int i) {
+  return FP8 ? 16 * (4 * i + g) : 32 * i + 8 * g;
+}
+// First element of lane group g's part of k-step s.
+template <bool FP8>
+__device__ __forceinline__ int k_step_elem(int g, int s) {
+  return FP8 ? 16 * (4 * (s >> 1) + g) + 8 * (s & 1) : 32 * s + 8 * g;
+}
 
 template <int POLICY>
 __device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -142,12 +160,16 @@ struct MfmaDecode {
     else
       return buffer_load<POLICY>(r, off);
   }
+  static constexpr int kKLoads = FP8 ? 2 : 4;
   static __device__ __forceinline__ V8 zero8() { return V8{}; }
-  static __device__ __forceinline__ bf16x8 k_operand(const V8 &w) {
-    if constexpr (FP8)
-      return e4m3x8_to_bf16(w);
-    else
-      return __builtin_bit_cast(bf16x8, w);
+  // the A operand of k-step s
+  static __device__ __forceinline__ bf16x8 k_operand(const TileT &T, int s) {
+    if constexpr (FP8) {
+      const u32x4 &w = T.k[s >> 1];
+      return e4m3x8_to_bf16((s & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+    } else {
+      return __builtin_bit_cast(bf16x8, T.k[s]);
+    }
   }
   // WIDE: p.V on 16x16x4 with a wave-shared running maximum (G = 8);
   // otherwise 4x4x1 blocks with one running maximum per lane group (G = 4).
@@ -172,11 +194,12 @@ struct MfmaDecode {
       const auto rk = block_rsrc(kc + (int64_t)pid * block_elems, bbytes);
       const auto rv = block_rsrc(vc + (int64_t)pid * block_elems, bbytes);
       const int o = cs & bm1;
-      const uint32_t koff = (uint32_t)(((o + n) * row_elems + head_off + 8 * g) * kElem);
+      const uint32_t krow = (uint32_t)(((o + n) * row_elems + head_off) * kElem);
       const bool okk = !MASK || cs + n < t1;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        T.k[s] = okk ? bload<kCacheNormal>(rk, koff + 32 * kElem * s) : zero8();
+      for (int i = 0; i < kKLoads; ++i)
+        T.k[i] = okk ? buffer_load<kCacheNormal>(rk, krow + k_load_elem<FP8>(g, i) * kElem)
+                     : u32x4{0, 0, 0, 0};
       uint32_t voff[4];
       bool ok[4];
 #pragma unroll
@@ -198,13 +221,13 @@ struct MfmaDecode {
       const int tk = cs + n;
       if (!MASK || tk < t1) {
         const uint32_t pid = min((uint32_t)tbl[tk >> lgB], (uint32_t)(nb - 1));
-        const V8 *kp = reinterpret_cast<const V8 *>(
-            kc + (int64_t)pid * block_elems + head_off + (tk & bm1) * row_elems + 8 * g);
+        const KV *krow = kc + (int64_t)pid * block_elems + head_off + (tk & bm1) * row_elems;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) T.k[s] = kp[4 * s];
+        for (int i = 0; i < kKLoads; ++i)
+          T.k[i] = *reinterpret_cast<const u32x4 *>(krow + k_load_elem<FP8>(g, i));
       } else {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) T.k[s] = zero8();
+        for (int i = 0; i < kKLoads; ++i) T.k[i] = u32x4{0, 0, 0, 0};
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -260,7 +283,7 @@ struct MfmaDecode {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(T.k[s]), qb[s], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(T, s), qb[s], c, 0, 0, 0);
     float x[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) x[j] = (!MASK || cs + 4 * g + j < t1) ? c[j] * sl2 : neg_inf();
@@ -343,10 +366,11 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   // B operand of q.K: column n is query head n % G of this KV head
   bf16x8 qb[4];
   {
-    const uint16_t *qrow = q + ((int64_t)s * hq + kvh * G + n % G) * kD + 8 * g;
+    const uint16_t *qrow = q + ((int64_t)s * hq + kvh * G + n % G) * kD;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      qb[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * k));
+      qb[k] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(qrow + k_step_elem<FP8>(g, k)));
   }
 
   f32x4 acc[8];
