@@ -50,7 +50,9 @@ if ROOT not in sys.path:
 METRIC = "paged decode achieved HBM GB/s (% of peak) and attended KV tokens/s, 1 GPU"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "paged_kv_cache_386_amd", "csrc")
-DECODE_SOURCES = ["api.hip", "decode.hip", "decode_mfma.hip", "internal.h"]
+# what decides the decode kernels' memory traffic: their sources and the
+# partition policy (the text of resolve_partitions in api.hip)
+DECODE_SOURCES = ["decode.hip", "decode_mfma.hip"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_counters.json")
 DECODE_KERNELS = ("paged_decode_mfma_kernel", "paged_decode_kernel", "paged_decode_merge_kernel")
 
@@ -125,6 +127,10 @@ def decode_source_hash() -> str:
     for name in DECODE_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(CSRC, "api.hip"), "rb") as f:
+        api = f.read()
+    start = api.index(b"int32_t resolve_partitions(")
+    h.update(api[start:api.index(b"\n}\n", start)])
     return h.hexdigest()[:16]
 
 
