@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
 #include <type_traits>
 
 #include "internal.h"
@@ -52,6 +53,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.f;  // allowed growth of scores over the running max (log2)
+constexpr int kMqMaxRows = 64;  // multi-query rows per KV head taken by this kernel
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -276,17 +278,22 @@ struct MfmaDecode {
   // Fold one tile into the running (max, sum, accumulators).  m is this
   // lane's query head's running maximum: of its lane group (G = 4) or of the
   // wave (WIDE); lsum covers the lane group's tokens in both cases.
+  // cpos: this lane's column's last attended position (multi-query: a
+  // causal mask per column; decode passes INT_MAX)
   template <bool MASK>
   static __device__ __forceinline__ void compute(const TileT &T, const bf16x8 (&qb)[4],
                                                  f32x4 (&acc)[8], float &m, float &lsum, int cs,
-                                                 int t1, int g, float sl2) {
+                                                 int t1, int g, float sl2, int cpos) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(T, s), qb[s], c, 0, 0, 0);
     float x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = (!MASK || cs + 4 * g + j < t1) ? c[j] * sl2 : neg_inf();
+    for (int j = 0; j < 4; ++j) {
+      const int t = cs + 4 * g + j;
+      x[j] = ((!MASK || t < t1) && t <= cpos) ? c[j] * sl2 : neg_inf();
+    }
     float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     if constexpr (WIDE) {
       cm = fmaxf(cm, __shfl_xor(cm, 16));
@@ -330,28 +337,52 @@ struct MfmaDecode {
   }
 };
 
-template <int G, bool SMALLB, bool FP8>
+// Multi-query mode (MQ, G = 16 columns): the same walk for a few query tokens
+// per sequence (at most 16 (token, head) rows per KV head), column n being
+// token n / gh and head n % gh of the KV head's gh query heads; the chunk is
+// the sequence's last nq positions and column n attends positions up to
+// L - nq + n / gh (the causal mask of multi_query.hip).
+template <int G, bool SMALLB, bool FP8, bool MQ>
 __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     const uint16_t *__restrict__ q,
     const typename MfmaDecode<G, SMALLB, FP8>::KV *__restrict__ kc,
     const typename MfmaDecode<G, SMALLB, FP8>::KV *__restrict__ vc,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
-    float v_scale, int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P) {
+    float v_scale, int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P,
+    const int32_t *__restrict__ query_start, int num_tokens, int gh, int max_q, int csets) {
   using K = MfmaDecode<G, SMALLB, FP8>;
   using TileT = typename K::TileT;
   constexpr bool WIDE = K::WIDE;
 
-  const int id = blockIdx.x;
+  int id = blockIdx.x;
+  // multi-query with more than 16 rows per KV head: column set cset takes
+  // rows 16 cset .. 16 cset + 15.  The sets of one item are 8 workgroups
+  // apart, so they run on the same XCD (workgroup b runs on XCD b % 8) and
+  // the second set's K/V reads hit its L2.
+  int cset = 0;
+  if constexpr (MQ) {
+    const int t = id / 8;
+    cset = t % csets;
+    id = (t / csets) * 8 + id % 8;
+    if (id >= num_seqs * hkv * P) return;
+  }
   // work item: KV head fastest, then sequence, then partition from the last
   // down (as in decode.hip)
   const int kvh = id % hkv;
   const int s = (id / hkv) % num_seqs;
   const int p = (P - 1) - id / (hkv * num_seqs);
-  const int hq = hkv * G;
+  const int hq = hkv * (MQ ? gh : G);
 
   int L = context_lens[s];
   L = max(0, min(L, mb << lgB));
+  int qs = 0, nq = 0, ncols = G;
+  if constexpr (MQ) {
+    qs = max(0, min(query_start[s], num_tokens));
+    nq = max(0, min(min(query_start[s + 1] - qs, L), min(max_q, num_tokens - qs)));
+    ncols = min(nq * gh - G * cset, G);
+    if (ncols <= 0) return;
+  }
   const int nparts = min((L + ps - 1) / ps, P);
   if (p >= max(nparts, 1)) return;
   const int t0 = p * ps;
@@ -363,9 +394,24 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   const int n = lane & 15;
   const int32_t *tbl = block_tables + (int64_t)s * mb;
 
-  // B operand of q.K: column n is query head n % G of this KV head
+  // B operand of q.K: column n is query head n % G of this KV head (decode),
+  // or row n of the chunk (multi-query; columns past the chunk are zero and
+  // fully masked)
   bf16x8 qb[4];
-  {
+  int cpos = INT_MAX;
+  if constexpr (MQ) {
+    const int R = G * cset + n;  // this column's row of the chunk
+    cpos = n < ncols ? L - nq + R / gh : -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qb[k] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    if (n < ncols) {
+      const uint16_t *qrow = q + ((int64_t)(qs + R / gh) * hq + kvh * gh + R % gh) * kD;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        qb[k] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4 *>(qrow + k_step_elem<FP8>(g, k)));
+    }
+  } else {
     const uint16_t *qrow = q + ((int64_t)s * hq + kvh * G + n % G) * kD;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -444,20 +490,20 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
         ent = entry(j + 1, sv);
         K::template load<false>(Bt, kc, vc, tbl, ent, sv, cstart(j + 1), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
+        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2, cpos);
         ent = entry(j + 2, sv);
         K::template load<false>(A, kc, vc, tbl, ent, sv, cstart(j + 2), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2);
+        K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2, cpos);
       }
       if (j + 2 == nw) {
         ent = entry(j + 1, sv);
         K::template load<false>(Bt, kc, vc, tbl, ent, sv, cstart(j + 1), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
-        K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2);
+        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2, cpos);
+        K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2, cpos);
       } else {
-        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2);
+        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2, cpos);
       }
     }
     if (t0 + nfull * kTile < t1 && nfull % kWaves == wave) {
@@ -465,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
       ent = entry(nw, sv);
       K::template load<true>(A, kc, vc, tbl, ent, sv, cs, t1, lgB, nb, g, n, row_elems,
                              head_off, block_elems);
-      K::template compute<true>(A, qb, acc, m, lsum, cs, t1, g, sl2);
+      K::template compute<true>(A, qb, acc, m, lsum, cs, t1, g, sl2, cpos);
     }
   }
 
@@ -524,7 +570,9 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     }
   }
   __syncthreads();
-  const bool final_out = nparts <= 1;
+  // decode writes a sequence with one partition straight to out (its merge
+  // skips it); the multi-query merge combines every row whenever P > 1
+  const bool final_out = MQ ? P <= 1 : nparts <= 1;
   for (int i = threadIdx.x; i < G * kD; i += kThreads) {
     const int h = i / kD;
     const int d = i % kD;
@@ -539,11 +587,18 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
       ls = fmaf(sm_l[w][h], f, ls);
       o = fmaf(sm_acc[w][h][d], f, o);
     }
-    const int64_t row = (int64_t)s * hq + kvh * G + h;
+    int64_t row;
+    if constexpr (MQ) {
+      if (h >= ncols) continue;
+      const int R = G * cset + h;
+      row = (int64_t)(qs + R / gh) * hq + kvh * gh + R % gh;
+    } else {
+      row = (int64_t)s * hq + kvh * G + h;
+    }
     if (final_out) {
       out[row * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
     } else {
-      ws_o[(row * P + p) * kD + d] = v_scale * (o / ls);
+      ws_o[(row * P + p) * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
       if (d == 0) {
         ws_ml[(row * P + p) * 2 + 0] = M;
         ws_ml[(row * P + p) * 2 + 1] = ls;
@@ -559,12 +614,13 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   // the K scale multiplies every score, so it joins the softmax scale
   const float sl2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<G, SMALLB, FP8>), dim3((uint32_t)grid),
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<G, SMALLB, FP8, false>), dim3((uint32_t)grid),
                      dim3(kThreads), 0, stream, static_cast<const uint16_t *>(a.q),
                      static_cast<const KV *>(a.k_cache), static_cast<const KV *>(a.v_cache),
                      a.block_tables, a.context_lens, a.out, a.ws_o, a.ws_ml, sl2,
                      FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads, a.log2_block_size,
-                     a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions);
+                     a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions,
+                     nullptr, 0, 0, 0, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions <= 1) return e;
   return launch_partition_merge(a, stream);
@@ -576,7 +632,34 @@ hipError_t launch_b(const DecodeArgs &a, hipStream_t stream) {
   return launch_typed<G, true, FP8>(a, stream);
 }
 
+template <bool SMALLB>
+hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
+  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
+  if (items <= 0) return hipSuccess;
+  const int gh = a.num_q_heads / a.num_kv_heads;
+  const int csets = (int)(((int64_t)a.max_query_len * gh + 15) / 16);
+  const int64_t grid = (items + 7) / 8 * 8 * csets;
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<16, SMALLB, false, true>), dim3((uint32_t)grid),
+                     dim3(kThreads), 0, stream, static_cast<const uint16_t *>(a.q),
+                     static_cast<const uint16_t *>(a.k_cache),
+                     static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
+                     a.out, a.ws_o, a.ws_ml, a.scale * kLog2e, 1.f, a.num_seqs, a.num_kv_heads,
+                     a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.partition_size,
+                     a.num_partitions, a.query_start, a.num_tokens, gh, a.max_query_len, csets);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool multi_query_few_rows_supported(const MultiQueryArgs &a) {
+  return a.dtype == 1 && a.head_dim == kD &&
+         (int64_t)a.max_query_len * (a.num_q_heads / a.num_kv_heads) <= kMqMaxRows;
+}
+
+hipError_t launch_multi_query_few_rows(const MultiQueryArgs &a, hipStream_t stream) {
+  if (a.log2_block_size >= 4) return launch_mq<false>(a, stream);
+  return launch_mq<true>(a, stream);
+}
 
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
   return dtype == 1 && head_dim == kD && (group == 4 || group == 8);

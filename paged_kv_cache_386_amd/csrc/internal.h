@@ -59,6 +59,13 @@ struct MultiQueryArgs {
   float *ws_ml;            // [num_tokens][Hq][P][2]
 };
 
+// Multi-query attention on the decode kernel (decode_mfma.hip) when every KV
+// head has at most 64 (token, head) rows, in sets of 16: bfloat16, head_dim
+// 128.  Writes
+// out, or the partition partials that the multi-query merge combines.
+bool multi_query_few_rows_supported(const struct MultiQueryArgs &a);
+hipError_t launch_multi_query_few_rows(const struct MultiQueryArgs &a, hipStream_t stream);
+
 // Causal multi-query attention (multi_query.hip): bfloat16, head_dim 64 or 128.
 bool multi_query_supported(int32_t dtype, int32_t head_dim);
 hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream);

@@ -397,6 +397,23 @@ __global__ __launch_bounds__(D) void paged_multi_query_merge_kernel(
   out[row * D + d] = den > 0.f ? num / den : 0.f;
 }
 
+hipError_t launch_merge(const MultiQueryArgs &a, hipStream_t stream) {
+  const int64_t mrows = (int64_t)a.num_tokens * a.num_q_heads;
+  const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
+                                         INT32_MAX);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL((paged_multi_query_merge_kernel<64>), dim3((uint32_t)mrows), dim3(64), 0,
+                       stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out, a.num_seqs,
+                       a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
+                       a.num_partitions);
+  else
+    hipLaunchKernelGGL((paged_multi_query_merge_kernel<128>), dim3((uint32_t)mrows), dim3(128), 0,
+                       stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out, a.num_seqs,
+                       a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
+                       a.num_partitions);
+  return hipGetLastError();
+}
+
 template <int D, int RS>
 hipError_t launch_typed(const MultiQueryArgs &a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -414,14 +431,7 @@ hipError_t launch_typed(const MultiQueryArgs &a, hipStream_t stream) {
                      a.max_query_len, row_tiles, (int)items, a.partition_size, a.num_partitions);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions <= 1) return e;
-  const int64_t mrows = (int64_t)a.num_tokens * a.num_q_heads;
-  const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
-                                         INT32_MAX);
-  hipLaunchKernelGGL((paged_multi_query_merge_kernel<D>), dim3((uint32_t)mrows), dim3(D), 0,
-                     stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out, a.num_seqs,
-                     a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
-                     a.num_partitions);
-  return hipGetLastError();
+  return launch_merge(a, stream);
 }
 
 template <int D>
@@ -438,6 +448,12 @@ bool multi_query_supported(int32_t dtype, int32_t head_dim) {
 }
 
 hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream) {
+  if (multi_query_few_rows_supported(a)) {
+    // a few rows per KV head: the decode walk, one wave per 16-token tile
+    hipError_t e = launch_multi_query_few_rows(a, stream);
+    if (e != hipSuccess || a.num_partitions <= 1) return e;
+    return launch_merge(a, stream);
+  }
   switch (a.head_dim) {
     case 64: return launch_d<64>(a, stream);
     case 128: return launch_d<128>(a, stream);

@@ -162,3 +162,17 @@ def test_full_size_workloads(name, every, sample):
     ref = oracle(cs)
     err = max_err(got[rows], ref)
     assert err <= TOL["bf16"], f"{name}: max abs err {err}"
+
+
+@pytest.mark.parametrize("G,Hkv,maxq", [(4, 8, 4), (8, 4, 2), (1, 8, 16), (2, 4, 8),
+                                         (4, 8, 5), (8, 4, 8), (2, 2, 17), (1, 4, 64)])
+@pytest.mark.parametrize("ps", [0, -1, 64, 2048])
+@pytest.mark.parametrize("B", [4, 16, 512])
+def test_few_rows_per_kv_head(G, Hkv, maxq, ps, B):
+    """At most 64 (token, head) rows per KV head: the decode-shaped kernel
+    with a causal mask per column, in sets of 16 columns, every partition
+    size and block size."""
+    lens = [1, 3, 16, 17, 64, 65, 700, 2049, 5000, 4096]
+    q_lens = [min(L, maxq - (i % 2)) for i, L in enumerate(lens)]
+    base = make_private_case(f"mq-few-{G}-{B}", lens, G * Hkv, Hkv, 128, B, "bf16", G + B)
+    compare(make_multi_query_case(base, q_lens, G + B), f"mq few rows G={G} B={B}", ps)
