@@ -14,6 +14,8 @@ from .generate import (  # noqa: F401
     draw_e4m3_codes,
     Fp8Case,
     make_fp8_case,
+    Int8Case,
+    make_int8_case,
     make_aliased_case,
     make_case,
     make_fork_case,

@@ -644,3 +644,37 @@ def make_fp8_case(base: Case, seed: int, k_scale: float = 0.25, v_scale: float =
     v8[base.v_cache == BF16_QNAN] = E4M3_QNAN
     return Fp8Case(base=base, k8=k8, v8=v8, k_scale=np.float32(k_scale),
                    v_scale=np.float32(v_scale))
+
+
+# ---------------------------------------------------------------- INT8 pools
+
+@dataclass
+class Int8Case:
+    """A workload over an INT8 pool (signed codes in [-127, 127], one fp32
+    scale per cache); ``base`` as for Fp8Case."""
+
+    base: Case
+    k8: np.ndarray  # int8 [NB, Hkv, B, D]
+    v8: np.ndarray
+    k_scale: np.float32
+    v_scale: np.float32
+
+    @property
+    def name(self) -> str:
+        return self.base.name
+
+
+def make_int8_case(base: Case, seed: int, k_scale: float = 0.02,
+                   v_scale: float = 0.03) -> Int8Case:
+    """The same workload over an INT8 pool: every slot gets a code uniform in
+    [-127, 127] from ``default_rng([seed, 4])``; slots that ``base`` poisons
+    (never read) get -128, a code no write produces."""
+    if base.dtype != "bf16":
+        raise ValueError("INT8 workloads take bfloat16 queries and new tokens")
+    rng = np.random.default_rng([seed, 4])
+    k8 = rng.integers(-127, 128, size=base.k_cache.shape, dtype=np.int8)
+    v8 = rng.integers(-127, 128, size=base.v_cache.shape, dtype=np.int8)
+    k8[base.k_cache == BF16_QNAN] = -128
+    v8[base.v_cache == BF16_QNAN] = -128
+    return Int8Case(base=base, k8=k8, v8=v8, k_scale=np.float32(k_scale),
+                    v_scale=np.float32(v_scale))
