@@ -588,6 +588,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-fp8", action="store_true",
                     help="configs 2-4 over an FP8 (E4M3) pool: quantising write and FP8 decode")
+    ap.add_argument("--kv-int8", action="store_true",
+                    help="configs 2-4 over an INT8 pool: quantising write and INT8 decode")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -599,12 +601,12 @@ def main() -> int:
         args.steps = 50 if args.steps is None else args.steps
         args.warmup = 10 if args.warmup is None else args.warmup
     workload = f"cfg{args.config}" + (f"-B{args.block_size or 512}" if args.config == 3 else "")
-    if args.kv_fp8:
-        if args.config == 1:
-            print("the FP8 pool runs on the matrix-core decode (G = 4 or 8): configs 2-4",
-                  file=sys.stderr)
+    if args.kv_fp8 or args.kv_int8:
+        if args.config == 1 or (args.kv_fp8 and args.kv_int8):
+            print("8-bit pools run on the matrix-core decode (G = 4 or 8): configs 2-4, "
+                  "one of --kv-fp8 / --kv-int8", file=sys.stderr)
             return 2
-        workload += "-fp8"
+        workload += "-fp8" if args.kv_fp8 else "-int8"
         args.no_cpu_baseline = True
     if args.serving:
         workload = "serving"
@@ -663,6 +665,10 @@ def main() -> int:
         from workloads import make_fp8_case
         c8 = make_fp8_case(case, args.config)
         case.kv_elem_bytes = 1
+    elif args.kv_int8:
+        from workloads import make_int8_case
+        c8 = make_int8_case(case, args.config)
+        case.kv_elem_bytes = 1
     q = to_dev(case.q, dev)
     kc = to_dev(case.k_cache if c8 is None else c8.k8, dev)
     vc = to_dev(case.v_cache if c8 is None else c8.v8, dev)
@@ -688,8 +694,9 @@ def main() -> int:
         if c8 is None:
             pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
         else:
-            pa.kv_cache_write_fp8(k_new, v_new, slots, kc, vc, float(c8.k_scale),
-                                  float(c8.v_scale), stream=stream)
+            write = pa.kv_cache_write_fp8 if args.kv_fp8 else pa.kv_cache_write_int8
+            write(k_new, v_new, slots, kc, vc, float(c8.k_scale), float(c8.v_scale),
+                  stream=stream)
 
     def decode():
         if c8 is None:
@@ -698,11 +705,10 @@ def main() -> int:
                                       partition_size=args.partition_size, workspace=ws,
                                       stream=stream)
         else:
-            pa.paged_attention_decode_fp8(q, kc, vc, tables, lens, float(case.scale),
-                                          float(c8.k_scale), float(c8.v_scale), out,
-                                          max_context_len=max_ctx,
-                                          partition_size=args.partition_size, workspace=ws,
-                                          stream=stream)
+            dec = pa.paged_attention_decode_fp8 if args.kv_fp8 else pa.paged_attention_decode_int8
+            dec(q, kc, vc, tables, lens, float(case.scale), float(c8.k_scale),
+                float(c8.v_scale), out, max_context_len=max_ctx,
+                partition_size=args.partition_size, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         if has_step:
@@ -752,9 +758,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.dtype if c8 is None else "fp8-e4m3 (bf16 q)",
+        "dtype": case.dtype if c8 is None else
+                 ("fp8-e4m3 (bf16 q)" if args.kv_fp8 else "int8 (bf16 q)"),
         "data": "synthetic (seeded N(0,1) q/K/V; lengths, prefix groups and forks as described)"
-                + ("; K/V as random E4M3 codes, k_scale 0.25, v_scale 0.5" if c8 else ""),
+                + ("" if c8 is None else
+                   f"; K/V as random {'E4M3' if args.kv_fp8 else 'INT8'} codes, k_scale "
+                   f"{float(c8.k_scale)}, v_scale {float(c8.v_scale)}"),
         "config": {
             "workload": f"{workload}: {case.description}",
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,

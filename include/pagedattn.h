@@ -63,8 +63,10 @@ typedef enum pa_status {
 typedef enum pa_dtype {
   PA_F32 = 0,      /* IEEE binary32 */
   PA_BF16 = 1,     /* bfloat16 (the high half of a binary32), stored as 16-bit words */
-  PA_FP8_E4M3 = 2  /* pools only: OCP 8-bit float E4M3 (bias 7, no infinities, max 448),
+  PA_FP8_E4M3 = 2, /* pools only: OCP 8-bit float E4M3 (bias 7, no infinities, max 448),
                       one code per byte, meaning code value * the cache's scale */
+  PA_INT8 = 3      /* pools only: signed byte codes in [-127, 127], meaning code * the
+                      cache's scale */
 } pa_dtype;
 
 /*
@@ -145,6 +147,22 @@ int32_t paged_attention_decode_fp8(const void *q, const void *k_cache, const voi
                                    int32_t max_blocks_per_seq, int32_t max_context_len,
                                    int32_t partition_size, void *workspace,
                                    size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode_int8 -- paged_attention_decode_fp8 over an INT8
+ * pool ([P3] architecture figure: FP8/INT8 quantisation): an element's value
+ * is code * k_scale (K) or * v_scale (V), the code a signed byte.  Codes are
+ * widened exactly to bfloat16 for q.K and to fp32 for p.V.  Arguments,
+ * support and errors are those of paged_attention_decode_fp8.
+ */
+int32_t paged_attention_decode_int8(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *context_lens,
+                                    float scale, float k_scale, float v_scale, float *out,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    int32_t partition_size, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of workspace paged_attention_decode needs for these arguments (0 when
@@ -251,7 +269,7 @@ size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_
  *   slot_mapping   device int32 [num_tokens]
  *   k_cache,
  *   v_cache        device pool (layout above), modified in place
- * dtype may also be PA_FP8_E4M3 (codes copied as bytes).  A head row
+ * dtype may also be PA_FP8_E4M3 or PA_INT8 (codes copied as bytes).  A head row
  * (head_dim elements) must be a multiple of 16 bytes.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH.
  */
@@ -282,6 +300,18 @@ int32_t kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_map
                            int32_t src_dtype, float k_scale, float v_scale, void *stream);
 
 /*
+ * kv_cache_write_int8 -- kv_cache_write into an INT8 pool: each element x of
+ * k (v) is stored as round(x / k_scale) (x / v_scale), the division done in
+ * fp32 (correctly rounded), rounded to the nearest integer with ties to
+ * even and clamped to [-127, 127]; NaN is stored as 0.  Arguments and errors
+ * are those of kv_cache_write_fp8.
+ */
+int32_t kv_cache_write_int8(const void *k, const void *v, const int32_t *slot_mapping,
+                            int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
+                            int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t src_dtype, float k_scale, float v_scale, void *stream);
+
+/*
  * copy_blocks -- copy-on-write block copies.
  *
  * For each pair i, copies physical block src = pairs[2i] onto dst = pairs[2i+1]
@@ -296,7 +326,7 @@ int32_t kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_map
  *
  *   src_dst_pairs  device int32 [num_pairs][2]
  *   host_pairs     optional host copy of the same pairs for the alias check
- * dtype is that of the pool (PA_FP8_E4M3 included); a head row must be a
+ * dtype is that of the pool (8-bit kinds included); a head row must be a
  * multiple of 16 bytes.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIAS, PA_ERR_LAUNCH.
  */

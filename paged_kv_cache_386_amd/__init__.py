@@ -13,16 +13,19 @@ from ._lib import (  # noqa: F401
     PA_BF16,
     PA_F32,
     PA_FP8_E4M3,
+    PA_INT8,
     PagedAttnError,
     copy_blocks,
     kv_cache_write,
     kv_cache_write_fp8,
+    kv_cache_write_int8,
     lib,
     multi_query_partitions,
     multi_query_workspace_size,
     num_partitions,
     paged_attention_decode,
     paged_attention_decode_fp8,
+    paged_attention_decode_int8,
     paged_attention_multi_query,
     partition_tokens,
     workspace_size,

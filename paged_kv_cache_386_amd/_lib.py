@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libpagedattn.so")
 PA_F32 = 0
 PA_BF16 = 1
 PA_FP8_E4M3 = 2
+PA_INT8 = 3
 
 PA_OK = 0
 STATUS_NAMES = {
@@ -42,6 +43,12 @@ SIGNATURES = {
                                           ctypes.c_size_t, _VP]),
     "kv_cache_write_fp8": (_I32, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                                   ctypes.c_float, ctypes.c_float, _VP]),
+    "paged_attention_decode_int8": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_float, _VP, _I32, _I32, _I32,
+                                           _I32, _I32, _I32, _I32, _I32, _I32, _VP,
+                                           ctypes.c_size_t, _VP]),
+    "kv_cache_write_int8": (_I32, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
+                                   ctypes.c_float, ctypes.c_float, _VP]),
     "paged_attention_workspace_size": (ctypes.c_size_t, [_I32] * 6),
     "paged_attention_num_partitions": (_I32, [_I32] * 4),
     "paged_attention_partition_tokens": (_I32, [_I32] * 4),
@@ -107,6 +114,8 @@ def _dtype_code(t) -> int:
         return PA_BF16
     if t.dtype == torch.uint8:
         return PA_FP8_E4M3  # pools of E4M3 codes
+    if t.dtype == torch.int8:
+        return PA_INT8  # pools of INT8 codes
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -220,18 +229,15 @@ def paged_attention_multi_query(q, k_cache, v_cache, block_tables, context_lens,
     _check("paged_attention_multi_query", st)
 
 
-def paged_attention_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float,
-                               k_scale: float, v_scale: float, out, *, max_context_len: int,
-                               partition_size: int = 0, workspace=None, stream=None) -> None:
-    """Decode over an FP8 pool (uint8 tensors of E4M3 codes [NB, Hkv, B, D]);
-    q: bfloat16 [S, Hq, D]; out: float32 [S, Hq, D]."""
+def _decode_q8(fn: str, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+               v_scale, out, max_context_len, partition_size, workspace, stream, dtype) -> None:
     import torch
     S, Hq, D = q.shape
     NB, Hkv, B, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("q/k_cache/v_cache shapes disagree")
-    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
-        raise TypeError("FP8 pools are uint8 tensors of E4M3 codes")
+    if k_cache.dtype != dtype or v_cache.dtype != dtype:
+        raise TypeError(f"{fn} takes pools of {dtype}")
     MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
     need = workspace_size(S, Hq, Hkv, D, max_context_len, partition_size)
     if need and workspace is None:
@@ -240,26 +246,59 @@ def paged_attention_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, 
     for t in (q, k_cache, v_cache, block_tables, context_lens, out):
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-    st = lib().paged_attention_decode_fp8(
+    st = getattr(lib(), fn)(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         float(scale), float(k_scale), float(v_scale), _ptr(out), S, Hq, Hkv, D, B, NB, MB,
         int(max_context_len), int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
-    _check("paged_attention_decode_fp8", st)
+    _check(fn, st)
+
+
+def paged_attention_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                               k_scale: float, v_scale: float, out, *, max_context_len: int,
+                               partition_size: int = 0, workspace=None, stream=None) -> None:
+    """Decode over an FP8 pool (uint8 tensors of E4M3 codes [NB, Hkv, B, D]);
+    q: bfloat16 [S, Hq, D]; out: float32 [S, Hq, D]."""
+    import torch
+    _decode_q8("paged_attention_decode_fp8", q, k_cache, v_cache, block_tables, context_lens,
+               scale, k_scale, v_scale, out, max_context_len, partition_size, workspace, stream,
+               torch.uint8)
+
+
+def paged_attention_decode_int8(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                                k_scale: float, v_scale: float, out, *, max_context_len: int,
+                                partition_size: int = 0, workspace=None, stream=None) -> None:
+    """Decode over an INT8 pool (int8 tensors [NB, Hkv, B, D])."""
+    import torch
+    _decode_q8("paged_attention_decode_int8", q, k_cache, v_cache, block_tables, context_lens,
+               scale, k_scale, v_scale, out, max_context_len, partition_size, workspace, stream,
+               torch.int8)
+
+
+def _write_q8(fn, k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream) -> None:
+    T = k.shape[0]
+    NB, Hkv, B, D = k_cache.shape
+    for t in (k, v, slot_mapping, k_cache, v_cache):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    st = getattr(lib(), fn)(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
+                            _ptr(v_cache), NB, B, Hkv, D, _dtype_code(k), float(k_scale),
+                            float(v_scale), _stream(stream))
+    _check(fn, st)
 
 
 def kv_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale: float, v_scale: float, *,
                        stream=None) -> None:
     """Quantise k[i], v[i] ([T, Hkv, D], float32 or bfloat16) into the FP8
     pool (uint8 [NB, Hkv, B, D]) at slot slot_mapping[i]."""
-    T = k.shape[0]
-    NB, Hkv, B, D = k_cache.shape
-    for t in (k, v, slot_mapping, k_cache, v_cache):
-        if not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
-    st = lib().kv_cache_write_fp8(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache),
-                                  _ptr(v_cache), NB, B, Hkv, D, _dtype_code(k), float(k_scale),
-                                  float(v_scale), _stream(stream))
-    _check("kv_cache_write_fp8", st)
+    _write_q8("kv_cache_write_fp8", k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+              stream)
+
+
+def kv_cache_write_int8(k, v, slot_mapping, k_cache, v_cache, k_scale: float, v_scale: float, *,
+                        stream=None) -> None:
+    """Quantise k[i], v[i] into the INT8 pool (int8 [NB, Hkv, B, D])."""
+    _write_q8("kv_cache_write_int8", k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+              stream)
 
 
 def kv_cache_write(k, v, slot_mapping, k_cache, v_cache, *, stream=None) -> None:

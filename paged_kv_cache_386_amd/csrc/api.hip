@@ -29,10 +29,12 @@ int log2_exact(int64_t x) {
 
 int64_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
 
+bool is_q8(int32_t dtype) { return dtype == PA_FP8_E4M3 || dtype == PA_INT8; }
+
 bool known_dtype(int32_t dtype) { return dtype == PA_F32 || dtype == PA_BF16; }
 
 // pools may also hold FP8 codes (moved as raw bytes by the edits)
-bool known_pool_dtype(int32_t dtype) { return known_dtype(dtype) || dtype == PA_FP8_E4M3; }
+bool known_pool_dtype(int32_t dtype) { return known_dtype(dtype) || is_q8(dtype); }
 
 // head rows must be whole 16-byte vectors for the edit kernels
 bool head_row_ok(int32_t head_dim, int32_t dtype) {
@@ -203,7 +205,7 @@ int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
     return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
-  if (kv_dtype == PA_FP8_E4M3) {
+  if (is_q8(kv_dtype)) {
     if (!pa::decode_mfma_supported(dtype, head_dim, num_q_heads / num_kv_heads))
       return PA_ERR_UNSUPPORTED;
     if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_SHAPE;
@@ -287,13 +289,30 @@ int32_t paged_attention_decode_fp8(const void *q, const void *k_cache, const voi
                      partition_size, workspace, workspace_bytes, stream);
 }
 
-int32_t kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
-                           int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
-                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t src_dtype, float k_scale, float v_scale, void *stream) {
+int32_t paged_attention_decode_int8(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *context_lens,
+                                    float scale, float k_scale, float v_scale, float *out,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    int32_t partition_size, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, PA_BF16, PA_INT8, k_scale, v_scale,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t write_q8(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+                 void *k_cache, void *v_cache, int32_t num_blocks, int32_t block_size,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype, int32_t kv_dtype,
+                 float k_scale, float v_scale, void *stream) {
   if (!known_dtype(src_dtype)) return PA_ERR_DTYPE;
-  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 ||
-      !head_row_ok(head_dim, PA_FP8_E4M3))
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || !head_row_ok(head_dim, kv_dtype))
     return PA_ERR_SHAPE;
   if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
@@ -301,11 +320,31 @@ int32_t kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_map
   if ((int64_t)num_kv_heads * head_dim / 16 > (int64_t)128 * 65535) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
-  const hipError_t e = pa::launch_kv_cache_write_fp8(
+  const hipError_t e = pa::launch_kv_cache_write_q8(
       k, v, slot_mapping, num_tokens, k_cache, v_cache, (int64_t)num_blocks * block_size,
-      log2_exact(block_size), num_kv_heads, head_dim, src_dtype, k_scale, v_scale,
+      log2_exact(block_size), num_kv_heads, head_dim, src_dtype, kv_dtype, k_scale, v_scale,
       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
+                           int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t src_dtype, float k_scale, float v_scale, void *stream) {
+  return write_q8(k, v, slot_mapping, num_tokens, k_cache, v_cache, num_blocks, block_size,
+                  num_kv_heads, head_dim, src_dtype, PA_FP8_E4M3, k_scale, v_scale, stream);
+}
+
+int32_t kv_cache_write_int8(const void *k, const void *v, const int32_t *slot_mapping,
+                            int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
+                            int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t src_dtype, float k_scale, float v_scale, void *stream) {
+  return write_q8(k, v, slot_mapping, num_tokens, k_cache, v_cache, num_blocks, block_size,
+                  num_kv_heads, head_dim, src_dtype, PA_INT8, k_scale, v_scale, stream);
 }
 
 int32_t paged_attention_multi_query(const void *q, const void *k_cache, const void *v_cache,

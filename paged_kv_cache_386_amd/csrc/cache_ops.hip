@@ -5,11 +5,12 @@
 //    its head's slab of the slot's block) are stored at its slot ("3.1" and "3.3" sections of the chenxutan.com vLLM
 //    deep-dive: the generated token's K/V goes back into the cache, appended
 //    into the sequence's current block);
-//  * kv_cache_write_fp8: the same store into an FP8 (E4M3) pool, each element
-//    divided by its cache's fp32 scale and rounded to the nearest E4M3 value
-//    (the FP8 quantisation named in the kernel layer of the
-//    devpress.csdn.net/amd walkthrough's architecture figure; the format and
-//    the per-cache scale are this library's choice, as the pages give none);
+//  * kv_cache_write_fp8 / _int8: the same store into an FP8 (E4M3) or INT8
+//    pool, each element divided by its cache's fp32 scale and rounded to the
+//    nearest E4M3 value or integer (the FP8/INT8 quantisation named in the
+//    kernel layer of the devpress.csdn.net/amd walkthrough's architecture
+//    figure; the formats and the per-cache scale are this library's choice,
+//    as the pages give none);
 //  * copy_blocks: whole physical blocks copied onto others, the copy-on-write
 //    step taken before a forked sequence appends to a shared block
 //    ("关键设计二：Copy-on-Write" section of the devpress.csdn.net/amd vLLM
@@ -76,6 +77,22 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.f);
 }
 
+// INT8 code of y: nearest integer, ties to even, clamped to [-127, 127];
+// NaN gives 0.
+__device__ __forceinline__ uint32_t int8_encode(float y) {
+  if (y != y) return 0u;
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f);
+  return (uint32_t)(uint8_t)(int8_t)(int32_t)r;
+}
+
+template <int Q8>
+__device__ __forceinline__ uint32_t encode8(float y) {
+  if constexpr (Q8 == 1)
+    return e4m3_encode(y);
+  else
+    return int8_encode(y);
+}
+
 template <typename T>
 __device__ __forceinline__ float widen(T x);
 template <>
@@ -91,8 +108,8 @@ __device__ __forceinline__ float widen<uint16_t>(uint16_t x) {
 // of head_vecs groups each).  Group j of head h = j / head_vecs is divided by
 // the cache's scale, encoded, and stored as one 16-byte vector in that head's
 // slab of the slot's block.
-template <typename T>
-__global__ __launch_bounds__(kWriteThreads) void kv_cache_write_fp8_kernel(
+template <typename T, int Q8>
+__global__ __launch_bounds__(kWriteThreads) void kv_cache_write_q8_kernel(
     const T *__restrict__ k, const T *__restrict__ v, const int32_t *__restrict__ slot_mapping,
     u32x4 *__restrict__ kc, u32x4 *__restrict__ vc, float k_scale, float v_scale,
     int64_t num_slots, int lgB, int hkv, int head_vecs) {
@@ -114,8 +131,8 @@ __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_fp8_kernel(
     uint32_t kw = 0, vw = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      kw |= e4m3_encode(widen<T>(k[src + 4 * w + b]) / k_scale) << (8 * b);
-      vw |= e4m3_encode(widen<T>(v[src + 4 * w + b]) / v_scale) << (8 * b);
+      kw |= encode8<Q8>(widen<T>(k[src + 4 * w + b]) / k_scale) << (8 * b);
+      vw |= encode8<Q8>(widen<T>(v[src + 4 * w + b]) / v_scale) << (8 * b);
     }
     ko[w] = kw;
     vo[w] = vw;
@@ -167,28 +184,47 @@ hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *sl
   return hipGetLastError();
 }
 
-hipError_t launch_kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
-                                     int32_t num_tokens, void *k_cache, void *v_cache,
-                                     int64_t num_slots, int32_t log2_block_size,
-                                     int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
-                                     float k_scale, float v_scale, hipStream_t stream) {
-  if (num_tokens <= 0) return hipSuccess;
-  const int head_vecs = head_dim / 16;
+namespace {
+
+template <typename T, int Q8>
+void launch_q8(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+               void *k_cache, void *v_cache, int64_t num_slots, int32_t log2_block_size,
+               int32_t num_kv_heads, int head_vecs, float k_scale, float v_scale,
+               hipStream_t stream) {
   const int64_t row_vecs = (int64_t)head_vecs * num_kv_heads;
   const int64_t stripes = (row_vecs + kWriteThreads - 1) / kWriteThreads;
-  const dim3 grid((uint32_t)num_tokens, (uint32_t)stripes);
-  if (src_dtype == 0)
-    hipLaunchKernelGGL(kv_cache_write_fp8_kernel<float>, grid, dim3(kWriteThreads), 0, stream,
-                       static_cast<const float *>(k), static_cast<const float *>(v),
-                       slot_mapping, static_cast<u32x4 *>(k_cache),
-                       static_cast<u32x4 *>(v_cache), k_scale, v_scale, num_slots,
-                       (int)log2_block_size, (int)num_kv_heads, head_vecs);
-  else
-    hipLaunchKernelGGL(kv_cache_write_fp8_kernel<uint16_t>, grid, dim3(kWriteThreads), 0, stream,
-                       static_cast<const uint16_t *>(k), static_cast<const uint16_t *>(v),
-                       slot_mapping, static_cast<u32x4 *>(k_cache),
-                       static_cast<u32x4 *>(v_cache), k_scale, v_scale, num_slots,
-                       (int)log2_block_size, (int)num_kv_heads, head_vecs);
+  hipLaunchKernelGGL((kv_cache_write_q8_kernel<T, Q8>),
+                     dim3((uint32_t)num_tokens, (uint32_t)stripes), dim3(kWriteThreads), 0,
+                     stream, static_cast<const T *>(k), static_cast<const T *>(v), slot_mapping,
+                     static_cast<u32x4 *>(k_cache), static_cast<u32x4 *>(v_cache), k_scale,
+                     v_scale, num_slots, (int)log2_block_size, (int)num_kv_heads, head_vecs);
+}
+
+}  // namespace
+
+hipError_t launch_kv_cache_write_q8(const void *k, const void *v, const int32_t *slot_mapping,
+                                    int32_t num_tokens, void *k_cache, void *v_cache,
+                                    int64_t num_slots, int32_t log2_block_size,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
+                                    int32_t kv_dtype, float k_scale, float v_scale,
+                                    hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  const int hv = head_dim / 16;
+  if (src_dtype == 0) {
+    if (kv_dtype == 2)
+      launch_q8<float, 1>(k, v, slot_mapping, num_tokens, k_cache, v_cache, num_slots,
+                          log2_block_size, num_kv_heads, hv, k_scale, v_scale, stream);
+    else
+      launch_q8<float, 2>(k, v, slot_mapping, num_tokens, k_cache, v_cache, num_slots,
+                          log2_block_size, num_kv_heads, hv, k_scale, v_scale, stream);
+  } else {
+    if (kv_dtype == 2)
+      launch_q8<uint16_t, 1>(k, v, slot_mapping, num_tokens, k_cache, v_cache, num_slots,
+                             log2_block_size, num_kv_heads, hv, k_scale, v_scale, stream);
+    else
+      launch_q8<uint16_t, 2>(k, v, slot_mapping, num_tokens, k_cache, v_cache, num_slots,
+                             log2_block_size, num_kv_heads, hv, k_scale, v_scale, stream);
+  }
   return hipGetLastError();
 }
 

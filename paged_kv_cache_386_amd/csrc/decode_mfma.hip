@@ -135,22 +135,41 @@ __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
   f[3] = hi[1];
 }
 
-// Eight E4M3 codes to the bfloat16 MFMA operand (exact: an E4M3 value has at
-// most 4 significant bits, so the high half of its fp32 form is the value).
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 w) {
+// Four signed 8-bit codes (one dword) to fp32 (exact).
+__device__ __forceinline__ void i8x4_to_f32(uint32_t w, float (&f)[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) f[b] = (float)((int32_t)(w << (24 - 8 * b)) >> 24);
+}
+
+template <int Q8>
+__device__ __forceinline__ void codes4_to_f32(uint32_t w, float (&f)[4]) {
+  if constexpr (Q8 == 1)
+    e4m3x4_to_f32(w, f);
+  else
+    i8x4_to_f32(w, f);
+}
+
+// Eight 8-bit codes to the bfloat16 MFMA operand (exact: an E4M3 value has
+// at most 4 significant bits and an INT8 code at most 7, so the high half of
+// the fp32 form is the value).
+template <int Q8>
+__device__ __forceinline__ bf16x8 codes8_to_bf16(u32x2 w) {
   u32x4 r;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float f[4];
-    e4m3x4_to_f32(w[h], f);
+    codes4_to_f32<Q8>(w[h], f);
     r[2 * h] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
     r[2 * h + 1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xFFFF0000u);
   }
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int G, bool SMALLB, bool FP8>
+// Q8: the pool's element kind -- 0 bfloat16, 1 FP8 (E4M3), 2 INT8 (signed
+// codes); the two 8-bit kinds share every load and differ only in widening.
+template <int G, bool SMALLB, int Q8>
 struct MfmaDecode {
+  static constexpr bool FP8 = Q8 != 0;  // one byte per element
   using KV = typename std::conditional<FP8, uint8_t, uint16_t>::type;
   using V8 = typename Vec8<FP8>::type;
   using TileT = Tile<FP8>;
@@ -168,7 +187,7 @@ struct MfmaDecode {
   static __device__ __forceinline__ bf16x8 k_operand(const TileT &T, int s) {
     if constexpr (FP8) {
       const u32x4 &w = T.k[s >> 1];
-      return e4m3x8_to_bf16((s & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+      return codes8_to_bf16<Q8>((s & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
     } else {
       return __builtin_bit_cast(bf16x8, T.k[s]);
     }
@@ -252,8 +271,8 @@ struct MfmaDecode {
     float e[8];
     if constexpr (FP8) {
       float a[4], b[4];
-      e4m3x4_to_f32(w[0], a);
-      e4m3x4_to_f32(w[1], b);
+      codes4_to_f32<Q8>(w[0], a);
+      codes4_to_f32<Q8>(w[1], b);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         e[i] = a[i];
@@ -342,18 +361,19 @@ struct MfmaDecode {
 // token n / gh and head n % gh of the KV head's gh query heads; the chunk is
 // the sequence's last nq positions and column n attends positions up to
 // L - nq + n / gh (the causal mask of multi_query.hip).
-template <int G, bool SMALLB, bool FP8, bool MQ>
+template <int G, bool SMALLB, int Q8, bool MQ>
 __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     const uint16_t *__restrict__ q,
-    const typename MfmaDecode<G, SMALLB, FP8>::KV *__restrict__ kc,
-    const typename MfmaDecode<G, SMALLB, FP8>::KV *__restrict__ vc,
+    const typename MfmaDecode<G, SMALLB, Q8>::KV *__restrict__ kc,
+    const typename MfmaDecode<G, SMALLB, Q8>::KV *__restrict__ vc,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
     float v_scale, int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P,
     const int32_t *__restrict__ query_start, int num_tokens, int gh, int max_q, int csets) {
-  using K = MfmaDecode<G, SMALLB, FP8>;
+  using K = MfmaDecode<G, SMALLB, Q8>;
   using TileT = typename K::TileT;
   constexpr bool WIDE = K::WIDE;
+  constexpr bool FP8 = K::FP8;
 
   int id = blockIdx.x;
   // multi-query with more than 16 rows per KV head: column set cset takes
@@ -607,14 +627,15 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   }
 }
 
-template <int G, bool SMALLB, bool FP8>
+template <int G, bool SMALLB, int Q8>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
-  using KV = typename MfmaDecode<G, SMALLB, FP8>::KV;
+  using KV = typename MfmaDecode<G, SMALLB, Q8>::KV;
+  constexpr bool FP8 = Q8 != 0;  // scaled 8-bit codes
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
   if (grid <= 0) return hipSuccess;
   // the K scale multiplies every score, so it joins the softmax scale
   const float sl2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<G, SMALLB, FP8, false>), dim3((uint32_t)grid),
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<G, SMALLB, Q8, false>), dim3((uint32_t)grid),
                      dim3(kThreads), 0, stream, static_cast<const uint16_t *>(a.q),
                      static_cast<const KV *>(a.k_cache), static_cast<const KV *>(a.v_cache),
                      a.block_tables, a.context_lens, a.out, a.ws_o, a.ws_ml, sl2,
@@ -626,10 +647,10 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
   return launch_partition_merge(a, stream);
 }
 
-template <int G, bool FP8>
+template <int G, int Q8>
 hipError_t launch_b(const DecodeArgs &a, hipStream_t stream) {
-  if (a.log2_block_size >= 4) return launch_typed<G, false, FP8>(a, stream);
-  return launch_typed<G, true, FP8>(a, stream);
+  if (a.log2_block_size >= 4) return launch_typed<G, false, Q8>(a, stream);
+  return launch_typed<G, true, Q8>(a, stream);
 }
 
 template <bool SMALLB>
@@ -639,7 +660,7 @@ hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
   const int gh = a.num_q_heads / a.num_kv_heads;
   const int csets = (int)(((int64_t)a.max_query_len * gh + 15) / 16);
   const int64_t grid = (items + 7) / 8 * 8 * csets;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<16, SMALLB, false, true>), dim3((uint32_t)grid),
+  hipLaunchKernelGGL((paged_decode_mfma_kernel<16, SMALLB, 0, true>), dim3((uint32_t)grid),
                      dim3(kThreads), 0, stream, static_cast<const uint16_t *>(a.q),
                      static_cast<const uint16_t *>(a.k_cache),
                      static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
@@ -665,11 +686,19 @@ bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
   return dtype == 1 && head_dim == kD && (group == 4 || group == 8);
 }
 
+template <int G>
+hipError_t launch_kind(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.kv_dtype) {
+    case 2: return launch_b<G, 1>(a, stream);  // FP8 E4M3
+    case 3: return launch_b<G, 2>(a, stream);  // INT8
+    default: return launch_b<G, 0>(a, stream);
+  }
+}
+
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
-  const bool fp8 = a.kv_dtype == 2;
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 4: return fp8 ? launch_b<4, true>(a, stream) : launch_b<4, false>(a, stream);
-    case 8: return fp8 ? launch_b<8, true>(a, stream) : launch_b<8, false>(a, stream);
+    case 4: return launch_kind<4>(a, stream);
+    case 8: return launch_kind<8>(a, stream);
     default: return hipErrorNotSupported;
   }
 }

@@ -23,8 +23,9 @@ struct DecodeArgs {
   int32_t partition_size;  // tokens per partition (>= every context when P == 1)
   int32_t num_partitions;  // P
   int32_t dtype;           // of q and, unless kv_dtype says otherwise, of the pool: 0 = f32, 1 = bf16
-  int32_t kv_dtype = -1;   // 2 = FP8 E4M3 pool (bf16 q, matrix-core kernel only); -1 = dtype
-  float k_scale = 1.f;     // FP8 pool: stored code c means e4m3(c) * scale
+  int32_t kv_dtype = -1;   // 2 = FP8 E4M3, 3 = INT8 pool (bf16 q, matrix-core kernel only);
+                           // -1 = dtype
+  float k_scale = 1.f;     // 8-bit pools: stored code c means value(c) * scale
   float v_scale = 1.f;
 };
 
@@ -75,11 +76,13 @@ hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *sl
                                  int64_t num_slots, int32_t log2_block_size, int32_t num_kv_heads,
                                  int64_t head_row_bytes, hipStream_t stream);
 
-hipError_t launch_kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
-                                     int32_t num_tokens, void *k_cache, void *v_cache,
-                                     int64_t num_slots, int32_t log2_block_size,
-                                     int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
-                                     float k_scale, float v_scale, hipStream_t stream);
+// Quantising write into an 8-bit pool: kv_dtype 2 = FP8 E4M3, 3 = INT8.
+hipError_t launch_kv_cache_write_q8(const void *k, const void *v, const int32_t *slot_mapping,
+                                    int32_t num_tokens, void *k_cache, void *v_cache,
+                                    int64_t num_slots, int32_t log2_block_size,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
+                                    int32_t kv_dtype, float k_scale, float v_scale,
+                                    hipStream_t stream);
 
 hipError_t launch_copy_blocks(const int32_t *pairs, int32_t num_pairs, void *k_cache,
                               void *v_cache, int32_t num_blocks, int64_t block_bytes,

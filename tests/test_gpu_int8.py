@@ -1,0 +1,155 @@
+"""INT8 KV cache through the C ABI against the oracle (needs an MI355X): the
+quantising write bit for bit (ties, clamping, NaN, negative slots), every
+code read back exactly through decode, INT8 decode against the oracle on
+private, prefix-shared and forked pools at several block and partition
+sizes, and the full-size GQA prefix workload on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import int8
+from oracle import oracle as O
+from workloads import make_case, make_fork_case, make_int8_case, make_prefix_case, \
+    make_private_case
+from workloads.generate import bf16_bits_from_f32, settle_step
+
+from gpu_helpers import TOL, max_err, say, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_386_amd as pa
+    pa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_decode_int8(c8, ps=0):
+    import paged_kv_cache_386_amd as pa
+    b = c8.base
+    NB, B = b.num_blocks, b.block_size
+    for s, L in enumerate(b.context_lens.tolist()):
+        nb = -(-L // B)
+        assert ((b.block_tables[s, :nb] >= 0) & (b.block_tables[s, :nb] < NB)).all()
+    out = torch.empty(b.q.shape, dtype=torch.float32, device="cuda")
+    pa.paged_attention_decode_int8(
+        to_torch(b.q, "bf16"), _dev(c8.k8), _dev(c8.v8),
+        torch.from_numpy(b.block_tables).cuda(), torch.from_numpy(b.context_lens).cuda(),
+        float(b.scale), float(c8.k_scale), float(c8.v_scale), out,
+        max_context_len=b.max_context_len, partition_size=ps)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_decode(c8, rows=None):
+    b = c8.base
+    return int8.paged_attention_decode_int8(b.q, c8.k8, c8.v8, b.block_tables, b.context_lens,
+                                            b.scale, b.block_size, "bf16", c8.k_scale,
+                                            c8.v_scale, rows=rows)
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 0.02, 0.37])
+def test_write_rounds_like_the_oracle(src, scale):
+    import paged_kv_cache_386_amd as pa
+    rng = np.random.default_rng(5)
+    Hkv, D, B, NB = 2, 128, 16, 12
+    halves = (np.arange(-140, 140) + 0.5).astype(np.float32)
+    vals = np.concatenate([halves * np.float32(scale), np.nextafter(halves, 0) * np.float32(scale),
+                           [0.0, -0.0, 1e30, -1e30, np.inf, -np.inf, np.nan],
+                           rng.standard_normal(4000).astype(np.float32) * 100 * scale])
+    T = -(-len(vals) // (Hkv * D))
+    flat = np.resize(vals, T * Hkv * D).astype(np.float32)
+    k = flat.reshape(T, Hkv, D)
+    v = np.roll(flat, 7).reshape(T, Hkv, D)
+    if src == "bf16":
+        k, v = bf16_bits_from_f32(k), bf16_bits_from_f32(v)
+    slots = rng.permutation(NB * B)[:T].astype(np.int32)
+    slots[3] = -1
+    kc = np.full((NB, Hkv, B, D), -128, np.int8)
+    vc = kc.copy()
+    say(f"int8 write src={src} scale={scale} T={T}")
+    dk, dv = _dev(kc), _dev(vc)
+    pa.kv_cache_write_int8(to_torch(k, src), to_torch(v, src), torch.from_numpy(slots).cuda(),
+                           dk, dv, scale, scale * 2)
+    torch.cuda.synchronize()
+    wk, wv = int8.kv_cache_write_int8(k, v, slots, kc, vc, B, src, scale, scale * 2)
+    assert np.array_equal(dk.cpu().numpy(), wk)
+    assert np.array_equal(dv.cpu().numpy(), wv)
+
+
+def test_raw_byte_edits_on_int8_pools():
+    import paged_kv_cache_386_amd as pa
+    rng = np.random.default_rng(6)
+    kc = rng.integers(-128, 128, size=(10, 2, 16, 128), dtype=np.int8)
+    vc = rng.integers(-128, 128, size=kc.shape, dtype=np.int8)
+    k = rng.integers(-128, 128, size=(5, 2, 128), dtype=np.int8)
+    v = rng.integers(-128, 128, size=(5, 2, 128), dtype=np.int8)
+    slots = np.array([3, 17, -1, 100, 159], np.int32)
+    pairs = np.array([[1, 7], [2, 8]], np.int32)
+    dk, dv = _dev(kc), _dev(vc)
+    pa.copy_blocks(torch.from_numpy(pairs).cuda(), dk, dv, host_pairs=pairs)
+    pa.kv_cache_write(_dev(k), _dev(v), torch.from_numpy(slots).cuda(), dk, dv)
+    torch.cuda.synchronize()
+    wk, wv = O.copy_blocks(pairs, kc, vc)
+    wk, wv = O.kv_cache_write(k, v, slots, wk, wv, 16)
+    assert np.array_equal(dk.cpu().numpy(), wk) and np.array_equal(dv.cpu().numpy(), wv)
+
+
+def test_every_code_reads_back_exactly():
+    codes = np.arange(-127, 128, dtype=np.int8)
+    S = 2
+    base = make_private_case("i8-codes", [1] * S, 8, 2, 128, 16, "bf16", 8)
+    c8 = make_int8_case(base, 8, v_scale=0.25)
+    row = np.resize(codes, S * 2 * 128).reshape(S, 2, 128)
+    for s in range(S):
+        c8.v8[base.block_tables[s, 0], :, 0] = row[s]
+    got = run_decode_int8(c8)
+    for s in range(S):
+        want = row[s].astype(np.float64) * 0.25
+        assert np.array_equal(got[s], np.repeat(want, 4, axis=0).astype(np.float32))
+
+
+@pytest.mark.parametrize("G,Hkv", [(4, 2), (8, 1)])
+@pytest.mark.parametrize("B", [1, 4, 16, 64, 512])
+def test_decode_matches_oracle(G, Hkv, B):
+    lens = [1, 15, 16, 17, 63, 64, 65, 200, 513, 1030]
+    base = make_private_case(f"i8-{G}-{B}", lens, G * Hkv, Hkv, 128, B, "bf16", G + B)
+    c8 = make_int8_case(base, G + B)
+    ref = oracle_decode(c8)
+    for ps in (0, -1, 64):
+        say(f"int8 decode G={G} B={B} ps={ps}")
+        err = max_err(run_decode_int8(c8, ps), ref)
+        assert err <= TOL["bf16"], f"G={G} B={B} ps={ps}: {err}"
+
+
+def test_decode_prefix_and_forked_pools():
+    lens = [1, 5, 9, 16, 17, 18, 20, 33, 3, 40, 12, 300, 64, 65, 70, 1000]
+    for base in (settle_step(make_prefix_case("i8-prefix", lens, 8, 32, 16, 2, 128, 16, "bf16",
+                                              31)),
+                 settle_step(make_fork_case("i8-fork", [9, 9, 9, 9, 60, 60, 60, 60, 1, 130, 4, 300],
+                                            2, 4, 32, 8, 128, 16, "bf16", 12))):
+        c8 = make_int8_case(base, 31)
+        err = max_err(run_decode_int8(c8), oracle_decode(c8))
+        assert err <= TOL["bf16"], (base.name, err)
+
+
+def test_full_size_prefix_workload_sampled():
+    base = settle_step(make_case(2))
+    c8 = make_int8_case(base, 2)
+    say("int8 decode, GQA prefix-sharing batch at full size")
+    got = run_decode_int8(c8)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(0)
+    rows = [(int(s), int(h)) for s, h in zip(rng.integers(0, 256, 48), rng.integers(0, 32, 48))]
+    ref = oracle_decode(c8, rows=rows)
+    err = max_err(np.array([got[s, h] for s, h in rows]), ref)
+    assert err <= TOL["bf16"], err
