@@ -22,7 +22,8 @@
 //    sit after the first product (a 32-token k-step takes lane (g, n)'s
 //    tokens 4g .. 4g+3 of two 16-token blocks, the k order being any
 //    permutation shared by A and B), A = the same tokens of V for 16 head_dim
-//    elements, read from a transposed copy of the V tile in LDS.  So all of a
+//    elements, read from the row-major V tile with gfx950's transposing LDS
+//    reads (ds_read_b64_tr_b16).  So all of a
 //    lane's accumulators belong to its own query row, whose running maximum
 //    and sum the lane holds: the online softmax needs no shuffles beyond the
 //    two that combine a row's four lane groups per tile.
@@ -50,7 +51,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTk = 64;          // tokens per tile
-constexpr int kVtStride = kTk + 4;  // transposed V tile row (elements), padded
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.f;
@@ -68,12 +70,11 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
 
 template <int D>
 struct TileRegs {
-  // K: chunk c = threadIdx + 256 j of the tile (token c / (D/8), elements
-  // 8 (c % (D/8)) .. +7); V: token quad and element chunk of this thread
+  // K and V: chunk c = threadIdx + 256 j of the tile (token c / (D/8),
+  // elements 8 (c % (D/8)) .. +7)
   static constexpr int kKChunks = kTk * D / 8 / kThreads;  // 4 (D=128) or 2 (D=64)
-  static constexpr int kVQuads = kTk / 4 * (D / 8);          // 256 (D=128) or 128
   u32x4 k[kKChunks];
-  u32x4 v[4];
+  u32x4 v[kKChunks];
 };
 
 template <int D, int RS>
@@ -156,8 +157,12 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     if (row0 + (wave * RS + r) * 16 < row_end) wave_last = max(wave_last, L - n + Rw / G);
   }
 
+  // both tiles row-major; V rows are padded differently from K rows so that
+  // the transposing reads of V (4 rows x 32 bytes per 16 lanes) and the
+  // 16-row reads of K are both free of bank conflicts
+  constexpr int kVs = D + 16;
   __shared__ __attribute__((aligned(16))) uint16_t sk[kTk * kKs];
-  __shared__ __attribute__((aligned(16))) uint16_t svt[D * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[kTk * kVs];
   // physical block of each token of the next tiles, two slots: the table is
   // read one tile ahead of the K/V rows it locates, so that the two reads
   // never wait on each other
@@ -181,41 +186,25 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
         T.k[j] = *reinterpret_cast<const u32x4 *>(kc + ids[tt] * block_elems + head_off +
                                                   (int64_t)(tok & bm1) * D + 8 * dc);
     }
-    if (threadIdx.x < Regs::kVQuads) {
-      const int tq = threadIdx.x / (D / 8);
-      const int dc = threadIdx.x % (D / 8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tt = 4 * tq + i;
-        const int tok = k0 + tt;
-        T.v[i] = u32x4{0, 0, 0, 0};
-        if (tok <= pos_last)
-          T.v[i] = *reinterpret_cast<const u32x4 *>(vc + ids[tt] * block_elems + head_off +
-                                                    (int64_t)(tok & bm1) * D + 8 * dc);
-      }
+    for (int j = 0; j < Regs::kKChunks; ++j) {
+      const int c = threadIdx.x + kThreads * j;
+      const int tt = c / (D / 8);
+      const int tok = k0 + tt;
+      const int dc = c % (D / 8);
+      T.v[j] = u32x4{0, 0, 0, 0};
+      if (tok <= pos_last)
+        T.v[j] = *reinterpret_cast<const u32x4 *>(vc + ids[tt] * block_elems + head_off +
+                                                  (int64_t)(tok & bm1) * D + 8 * dc);
     }
   };
-  // registers -> LDS: K row-major, V transposed (element-major, tokens
-  // contiguous)
+  // registers -> LDS, both row-major
   auto store_tile = [&](const Regs &T) {
 #pragma unroll
     for (int j = 0; j < Regs::kKChunks; ++j) {
       const int c = threadIdx.x + kThreads * j;
       *reinterpret_cast<u32x4 *>(&sk[(c / (D / 8)) * kKs + 8 * (c % (D / 8))]) = T.k[j];
-    }
-    if (threadIdx.x < Regs::kVQuads) {
-      const int tq = threadIdx.x / (D / 8);
-      const int dc = threadIdx.x % (D / 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        const uint32_t a0 = (T.v[0][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t a1 = (T.v[1][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t a2 = (T.v[2][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t a3 = (T.v[3][e >> 1] >> sh) & 0xFFFFu;
-        *reinterpret_cast<u32x2 *>(&svt[(8 * dc + e) * kVtStride + 4 * tq]) =
-            u32x2{a0 | (a1 << 16), a2 | (a3 << 16)};
-      }
+      *reinterpret_cast<u32x4 *>(&sv[(c / (D / 8)) * kVs + 8 * (c % (D / 8))]) = T.v[j];
     }
   };
 
@@ -319,9 +308,15 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     for (int b = 0; b < kDb; ++b) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t *vr = &svt[(16 * b + c16) * kVtStride + 32 * kk + 4 * g4];
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16);
+        // gfx950's transposing LDS read: within each 16-lane group, lane c
+        // points at 4 elements of row (base + c / 4) and receives, from the
+        // rows base .. base + 3, the element in its own column -- here
+        // element 16 b + c16 of tokens 32 kk + 4 g4 + 0..3 (and + 16)
+        const uint16_t *vr = &sv[(32 * kk + 4 * g4 + c16 / 4) * kVs + 16 * b + 4 * (c16 % 4)];
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vr)));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vr + 16 * kVs)));
         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int r = 0; r < RS; ++r) {
