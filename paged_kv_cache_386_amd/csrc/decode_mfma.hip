@@ -83,7 +83,14 @@ __device__ __forceinline__ float quad_bcast(float x) {
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 bits of x, rounded to nearest even (hardware conversion)
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
 
 // Eight K or V elements: 16 bytes of bfloat16, or 8 bytes of FP8 (E4M3).
 template <bool FP8>
@@ -266,43 +273,86 @@ struct MfmaDecode {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // acc[i] += p (x) V elements 8n + i of one token row, for i = 0..7.
-  static __device__ __forceinline__ void pv(const V8 &w, float p, f32x4 (&acc)[8]) {
-    float e[8];
+  // p.V runs on v_mfma_f32_16x16x32_bf16 over pairs of tiles (32 tokens per
+  // k-step): O^T += V^T P^T.  B = the probabilities as the q.K product left
+  // them (lane (g, n): column n, tokens 4g .. 4g+3 of each tile of the pair),
+  // as a bfloat16 pair hi + lo (about 16 significant bits); A = the same
+  // tokens of V for 16 head_dim elements.  V rows are staged in the wave's
+  // LDS slice, 32 rows in the order row(slot, t) = 8 (t / 4) + 4 slot + t % 4
+  // (slot = tile of the pair), so that the transposing LDS reads of gfx950
+  // deliver V^T directly: for bfloat16 two ds_read_b64_tr_b16 (rows
+  // 8g .. 8g+3 and 8g+4 .. 8g+7, lane n receiving element 16 b + n of each),
+  // for 8-bit codes one ds_read_b64_tr_b8 (rows 8g .. 8g+7), widened exactly
+  // to bfloat16.  The result leaves lane (g, n) with column n, elements
+  // 16 b + 4 g + i: all of a lane's accumulators belong to its own column.
+  static constexpr int kVRow = kD + 16;  // LDS row (elements); padded against bank conflicts
+  static constexpr int kSliceBytes = 32 * kVRow * kElem;
+
+  static __device__ __forceinline__ void stage_v(const TileT &T, KV *slice, int slot, int g,
+                                                 int n) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<V8 *>(slice + (8 * g + 4 * slot + j) * kVRow + 8 * n) = T.v[j];
+  }
+  static __device__ __forceinline__ void zero_v(KV *slice, int slot, int g, int n) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<V8 *>(slice + (8 * g + 4 * slot + j) * kVRow + 8 * n) = zero8();
+  }
+  static __device__ __forceinline__ bf16x8 v_operand(const KV *slice, int b, int g, int n) {
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     if constexpr (FP8) {
-      float a[4], b[4];
-      codes4_to_f32<Q8>(w[0], a);
-      codes4_to_f32<Q8>(w[1], b);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[i] = a[i];
-        e[4 + i] = b[i];
-      }
+      const KV *pa = slice + (8 * g + n / 2) * kVRow + 16 * b + 8 * (n % 2);
+      const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(pa));
+      return codes8_to_bf16<Q8>(__builtin_bit_cast(u32x2, w));
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[2 * i] = __uint_as_float(w[i] << 16);
-        e[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (WIDE)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(p, e[i], acc[i], 0, 0, 0);
-      else
-        acc[i] = __builtin_amdgcn_mfma_f32_4x4x1f32(p, e[i], acc[i], 0, 0, 0);
+      const KV *pa = slice + (8 * g + n / 4) * kVRow + 16 * b + 4 * (n % 4);
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                     (lds_i16x4 *)(pa)));
+      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                     (lds_i16x4 *)(pa + 4 * kVRow)));
+      return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
   }
 
-  // Fold one tile into the running (max, sum, accumulators).  m is this
-  // lane's query head's running maximum: of its lane group (G = 4) or of the
-  // wave (WIDE); lsum covers the lane group's tokens in both cases.
+  // acc[b] += V^T P^T for the staged pair; p0: the first tile's
+  // probabilities, p1: the second's (zeros when the pair is incomplete).
+  static __device__ __forceinline__ void pv_pair(const KV *slice, const float (&p0)[4],
+                                                 const float (&p1)[4], f32x4 (&acc)[8], int g,
+                                                 int n) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float a = h < 2 ? p0[2 * h] : p1[2 * h - 4];
+      const float b = h < 2 ? p0[2 * h + 1] : p1[2 * h - 3];
+      const uint32_t ha = bf16_rne(a), hb = bf16_rne(b);
+      hw[h] = ha | (hb << 16);
+      lw[h] = bf16_rne(a - __uint_as_float(ha << 16)) |
+              (bf16_rne(b - __uint_as_float(hb << 16)) << 16);
+    }
+    const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+    const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bf16x8 a = v_operand(slice, b, g, n);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, acc[b], 0, 0, 0);
+    }
+  }
+
+  // Fold one tile into the running state: q.K, the online softmax (m: this
+  // lane's column's running maximum in log2 units, shared by the four lane
+  // groups; lsum: the lane's own tokens), the V rows staged into slot `slot`
+  // of the pair; with the pair complete, p.V.  p0 keeps the first tile's
+  // probabilities until then (and is rescaled with the accumulators).
   // cpos: this lane's column's last attended position (multi-query: a
-  // causal mask per column; decode passes INT_MAX)
+  // causal mask per column; decode passes INT_MAX).
   template <bool MASK>
   static __device__ __forceinline__ void compute(const TileT &T, const bf16x8 (&qb)[4],
-                                                 f32x4 (&acc)[8], float &m, float &lsum, int cs,
-                                                 int t1, int g, float sl2, int cpos) {
+                                                 f32x4 (&acc)[8], float &m, float &lsum,
+                                                 float (&p0)[4], int &slot, KV *slice, int cs,
+                                                 int t1, int g, int n, float sl2, int cpos) {
     f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -314,35 +364,16 @@ struct MfmaDecode {
       x[j] = ((!MASK || t < t1) && t <= cpos) ? c[j] * sl2 : neg_inf();
     }
     float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    if constexpr (WIDE) {
-      cm = fmaxf(cm, __shfl_xor(cm, 16));
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
-    }
-    const bool need = cm > m + kSlack;  // false while both are -inf
-    float alpha = 1.f;
-    if (need) {
-      alpha = __builtin_amdgcn_exp2f(m - cm);  // 0 when m was -inf
+    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    if (cm > m + kSlack) {  // false while both are -inf
+      const float alpha = __builtin_amdgcn_exp2f(m - cm);  // 0 when m was -inf
       lsum *= alpha;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) acc[b] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p0[j] *= alpha;
       m = cm;
-    }
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      float a[4];
-      if constexpr (WIDE) {
-        // accumulator row r of lane group g is query head (4g + r) % G, whose
-        // factor lane 4g + r holds
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = __shfl(alpha, 4 * g + r);
-      } else {
-        // accumulator row r is the query head of lane r of the quad
-        a[0] = quad_bcast<0>(alpha);
-        a[1] = quad_bcast<1>(alpha);
-        a[2] = quad_bcast<2>(alpha);
-        a[3] = quad_bcast<3>(alpha);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][r] *= a[r];
     }
     const float mu = (m == neg_inf()) ? 0.f : m;
     float p[4];
@@ -351,8 +382,25 @@ struct MfmaDecode {
       p[j] = __builtin_amdgcn_exp2f(x[j] - mu);
       lsum += p[j];
     }
+    stage_v(T, slice, slot, g, n);
+    if (slot == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pv(T.v[j], p[j], acc);
+      for (int j = 0; j < 4; ++j) p0[j] = p[j];
+      slot = 1;
+    } else {
+      pv_pair(slice, p0, p, acc, g, n);
+      slot = 0;
+    }
+  }
+
+  // Completes a half-filled pair with a zero tile.
+  static __device__ __forceinline__ void flush(const float (&p0)[4], int slot, KV *slice,
+                                               f32x4 (&acc)[8], int g, int n) {
+    if (slot == 1) {
+      zero_v(slice, 1, g, n);
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      pv_pair(slice, p0, z, acc, g, n);
+    }
   }
 };
 
@@ -443,6 +491,13 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = neg_inf(), lsum = 0.f;
+  float p0[4] = {0.f, 0.f, 0.f, 0.f};  // the pending first tile of a pair
+  int slot = 0;
+  // the wave's LDS slice: V rows of the pair in the loop, then its results
+  constexpr int kSlice =
+      K::kSliceBytes > G * kD * 4 ? K::kSliceBytes : G * kD * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves][kSlice];
+  typename K::KV *slice = reinterpret_cast<typename K::KV *>(smem[wave]);
 
   // pool layout [blocks][kv_heads][block_size][head_dim]: consecutive tokens of
   // one KV head are kD elements apart, a head's slab of a block is kD << lgB
@@ -510,20 +565,25 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
         ent = entry(j + 1, sv);
         K::template load<false>(Bt, kc, vc, tbl, ent, sv, cstart(j + 1), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2, cpos);
+        K::template compute<false>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g, n,
+                                   sl2, cpos);
         ent = entry(j + 2, sv);
         K::template load<false>(A, kc, vc, tbl, ent, sv, cstart(j + 2), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2, cpos);
+        K::template compute<false>(Bt, qb, acc, m, lsum, p0, slot, slice, cstart(j + 1), t1, g,
+                                   n, sl2, cpos);
       }
       if (j + 2 == nw) {
         ent = entry(j + 1, sv);
         K::template load<false>(Bt, kc, vc, tbl, ent, sv, cstart(j + 1), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2, cpos);
-        K::template compute<false>(Bt, qb, acc, m, lsum, cstart(j + 1), t1, g, sl2, cpos);
+        K::template compute<false>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g, n,
+                                   sl2, cpos);
+        K::template compute<false>(Bt, qb, acc, m, lsum, p0, slot, slice, cstart(j + 1), t1, g,
+                                   n, sl2, cpos);
       } else {
-        K::template compute<false>(A, qb, acc, m, lsum, cstart(j), t1, g, sl2, cpos);
+        K::template compute<false>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g, n,
+                                   sl2, cpos);
       }
     }
     if (t0 + nfull * kTile < t1 && nfull % kWaves == wave) {
@@ -531,62 +591,30 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
       ent = entry(nw, sv);
       K::template load<true>(A, kc, vc, tbl, ent, sv, cs, t1, lgB, nb, g, n, row_elems,
                              head_off, block_elems);
-      K::template compute<true>(A, qb, acc, m, lsum, cs, t1, g, sl2, cpos);
+      K::template compute<true>(A, qb, acc, m, lsum, p0, slot, slice, cs, t1, g, n, sl2,
+                                 cpos);
     }
   }
 
-  // This wave's maximum and sum per accumulator row, with the lane groups'
-  // shares combined.  Afterwards lane (g, n) holds, for row r, query head
-  //   WIDE: (4g + r) % G, elements 8n + i (the MFMA summed the lane groups);
-  //   G=4:  r, elements 8n + i (identical in every lane group).
-  float Mr[4], Lr[4];
-  if constexpr (WIDE) {
-    float l = lsum;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      Mr[r] = __shfl(m, 4 * g + r);
-      Lr[r] = __shfl(l, 4 * g + r);
-    }
-  } else {
-    const float mq[4] = {quad_bcast<0>(m), quad_bcast<1>(m), quad_bcast<2>(m), quad_bcast<3>(m)};
-    const float lq[4] = {quad_bcast<0>(lsum), quad_bcast<1>(lsum), quad_bcast<2>(lsum),
-                         quad_bcast<3>(lsum)};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float M = fmaxf(mq[r], __shfl_xor(mq[r], 16));
-      M = fmaxf(M, __shfl_xor(M, 32));
-      const float f = (mq[r] == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mq[r] - M);
-      float l = lq[r] * f;
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
-      Mr[r] = M;
-      Lr[r] = l;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float a = acc[i][r] * f;
-        a += __shfl_xor(a, 16);
-        a += __shfl_xor(a, 32);
-        acc[i][r] = a;
-      }
-    }
-  }
+  K::flush(p0, slot, slice, acc, g, n);
 
-  // Merge the waves through LDS.
-  __shared__ float sm_acc[kWaves][G][kD];
+  // This wave's results per column: the maximum m is already the column's;
+  // the sum combines the four lane groups; the accumulators (lane (g, n):
+  // column n, elements 16 b + 4 g + i) go to the wave's LDS slice, which its
+  // own loop no longer uses.  Columns past G repeat earlier ones (decode).
+  float lcol = lsum;
+  lcol += __shfl_xor(lcol, 16);
+  lcol += __shfl_xor(lcol, 32);
   __shared__ float sm_m[kWaves][G];
   __shared__ float sm_l[kWaves][G];
-  if (g < G / 4) {
+  float *wacc = reinterpret_cast<float *>(smem[wave]);  // [G][kD]
+  if (n < G) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qr = 4 * g + r;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm_acc[wave][qr][8 * n + i] = acc[i][r];
-      if (n == 0) {
-        sm_m[wave][qr] = Mr[r];
-        sm_l[wave][qr] = Lr[r];
-      }
+    for (int b = 0; b < 8; ++b)
+      *reinterpret_cast<f32x4 *>(wacc + n * kD + 16 * b + 4 * g) = acc[b];
+    if (g == 0) {
+      sm_m[wave][n] = m;
+      sm_l[wave][n] = lcol;
     }
   }
   __syncthreads();
@@ -605,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
       const float mw = sm_m[w][h];
       const float f = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       ls = fmaf(sm_l[w][h], f, ls);
-      o = fmaf(sm_acc[w][h][d], f, o);
+      o = fmaf(reinterpret_cast<const float *>(smem[w])[h * kD + d], f, o);
     }
     int64_t row;
     if constexpr (MQ) {
