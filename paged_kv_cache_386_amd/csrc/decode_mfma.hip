@@ -1,5 +1,7 @@
-// PagedAttention decode on the matrix cores of gfx950, for bfloat16 K/V with
-// head_dim 128 and a GQA group of 4 or 8 query heads per KV head.
+// PagedAttention decode on the matrix cores of gfx950, for head_dim 128 and
+// a GQA group of 4 or 8 query heads per KV head, over bfloat16, FP8 (E4M3)
+// or INT8 pools; also causal multi-query attention for chunks of at most 64
+// (token, head) rows per KV head.
 //
 // The operation is the one of decode.hip (the "核心代码拆解" section of the
 // devpress.csdn.net/amd vLLM walkthrough: table lookup per logical block, scaled
@@ -8,29 +10,22 @@
 // element are what bounds the kernel; here both products run on MFMA:
 //
 //  * q.K: v_mfma_f32_16x16x32_bf16.  A = 16 K rows of a 16-token tile (lane
-//    n = lane%16 loads token n, elements 32s + 8g .. +7 for k-step s, where
-//    g = lane/16), B = the G query rows repeated over the 16 columns
-//    (column n holds query n % G).  Products of bfloat16 values are exact and
-//    accumulate in fp32.  The result gives lane (g, n) the scores of query
-//    n % G with tokens 4g .. 4g+3 of the tile.
-//  * p.V, G = 4: v_mfma_f32_4x4x1f32 (16 independent 4x4 blocks, fp32
-//    operands).  Block b = lane/4 takes A = the probabilities of its 4 lanes
-//    (the 4 query heads, one token of the lane group) and B = one fp32 element
-//    of V per lane: lane (g, n) loads elements 8n .. 8n+7 of token 4g+j's V row
-//    and feeds them to 8 MFMAs.  Each lane group (16 lanes) keeps its own
-//    running maximum and sum, since its accumulators only ever see its own
-//    tokens, so the hot loop has no cross-lane traffic; the lane groups are
-//    merged once at the end.
-//  * p.V, G = 8: v_mfma_f32_16x16x4f32.  A = the probabilities of the 16
-//    columns (query n % G) for the 4 tokens 4g+j of step j, B = the same V
-//    elements as above; the MFMA sums over the 4 lane groups, so the running
-//    maximum is shared by the wave (two cross-lane max steps per tile) and half
-//    as many accumulators are live as a second 4x4 pass would need.
-//  * Probabilities stay fp32, so no precision is lost in p.V.  A running
-//    maximum is raised only when a tile's maximum exceeds it by more than 8
-//    (log2 units), so accumulators are rarely rescaled; probabilities stay
-//    below 2^8 and the result is the same ratio of sums.
-
+//    n = lane%16 loads token n; lane group g = lane/16 holds its share of the
+//    elements, see Tile), B = the query rows over the 16 columns (column n
+//    holds query n % G, or row n of a multi-query chunk).  Products of
+//    bfloat16 values are exact and accumulate in fp32; 8-bit codes are
+//    widened exactly to bfloat16 first.  The result gives lane (g, n) the
+//    scores of column n with tokens 4g .. 4g+3 of the tile.
+//  * p.V: the same instruction over pairs of tiles, O^T += V^T P^T (see
+//    MfmaDecode::pv_pair): the probabilities enter as a bfloat16 pair hi + lo
+//    (about 16 significant bits), V^T comes from the wave's LDS slice through
+//    gfx950's transposing LDS reads, and every accumulator of a lane belongs
+//    to its own column, so the online softmax needs two cross-lane max steps
+//    per tile and nothing else.
+//  * A running maximum is raised only when a tile's maximum exceeds it by
+//    more than 8 (log2 units), so accumulators are rarely rescaled;
+//    probabilities stay below 2^8 and the result is the same ratio of sums.
+//
 // Work split, tiles, partitions and the merge of partition partials are those
 // of decode.hip: one workgroup of 4 waves per (sequence, KV head, partition),
 // 16-token tiles round-robin over the waves, double-buffered in registers.
@@ -75,12 +70,6 @@ __device__ __forceinline__ u32x4 buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
 }
 
-// Broadcast lane R of each quad of 4 lanes to the whole quad.
-template <int R>
-__device__ __forceinline__ float quad_bcast(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), R * 0x55, 0xF, 0xF, false));
-}
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -199,9 +188,6 @@ struct MfmaDecode {
       return __builtin_bit_cast(bf16x8, T.k[s]);
     }
   }
-  // WIDE: p.V on 16x16x4 with a wave-shared running maximum (G = 8);
-  // otherwise 4x4x1 blocks with one running maximum per lane group (G = 4).
-  static constexpr bool WIDE = G > 4;
 
   // Issue the loads of the tile starting at token cs.  Rows of tokens at or
   // past t1 are not read (their registers are zero) when MASK is set.
@@ -420,7 +406,6 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     const int32_t *__restrict__ query_start, int num_tokens, int gh, int max_q, int csets) {
   using K = MfmaDecode<G, SMALLB, Q8>;
   using TileT = typename K::TileT;
-  constexpr bool WIDE = K::WIDE;
   constexpr bool FP8 = K::FP8;
 
   int id = blockIdx.x;
