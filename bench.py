@@ -587,9 +587,9 @@ def main() -> int:
                     help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-fp8", action="store_true",
-                    help="configs 2-4 over an FP8 (E4M3) pool: quantising write and FP8 decode")
+                    help="the workload over an FP8 (E4M3) pool: quantising write and FP8 decode")
     ap.add_argument("--kv-int8", action="store_true",
-                    help="configs 2-4 over an INT8 pool: quantising write and INT8 decode")
+                    help="the workload over an INT8 pool: quantising write and INT8 decode")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -602,9 +602,8 @@ def main() -> int:
         args.warmup = 10 if args.warmup is None else args.warmup
     workload = f"cfg{args.config}" + (f"-B{args.block_size or 512}" if args.config == 3 else "")
     if args.kv_fp8 or args.kv_int8:
-        if args.config == 1 or (args.kv_fp8 and args.kv_int8):
-            print("8-bit pools run on the matrix-core decode (G = 4 or 8): configs 2-4, "
-                  "one of --kv-fp8 / --kv-int8", file=sys.stderr)
+        if args.kv_fp8 and args.kv_int8:
+            print("one of --kv-fp8 / --kv-int8", file=sys.stderr)
             return 2
         workload += "-fp8" if args.kv_fp8 else "-int8"
         args.no_cpu_baseline = True

@@ -136,7 +136,8 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
  * multiplies the output.  Every other argument, the workspace (same size as
  * paged_attention_decode's) and the partition policy are those of
  * paged_attention_decode.
- * Supported: head_dim 128, G in {4, 8}; k_scale and v_scale finite and > 0.
+ * Supported: head_dim 128, G in {1, 2, 4, 8}; k_scale and v_scale finite and
+ * > 0.
  * Errors: as paged_attention_decode.
  */
 int32_t paged_attention_decode_fp8(const void *q, const void *k_cache, const void *v_cache,

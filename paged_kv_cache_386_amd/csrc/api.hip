@@ -206,7 +206,7 @@ int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
   if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
   if (is_q8(kv_dtype)) {
-    if (!pa::decode_mfma_supported(dtype, head_dim, num_q_heads / num_kv_heads))
+    if (dtype != PA_BF16 || !pa::decode_q8_supported(head_dim, num_q_heads / num_kv_heads))
       return PA_ERR_UNSUPPORTED;
     if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_SHAPE;
   } else if (!pa::decode_supported(dtype, head_dim, num_q_heads / num_kv_heads)) {

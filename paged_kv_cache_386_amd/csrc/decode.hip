@@ -539,7 +539,8 @@ hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  if (decode_mfma_supported(a.dtype, a.head_dim, a.num_q_heads / a.num_kv_heads))
+  if (a.kv_dtype == 2 || a.kv_dtype == 3 ||  // 8-bit pools: matrix-core kernel only
+      decode_mfma_supported(a.dtype, a.head_dim, a.num_q_heads / a.num_kv_heads))
     return launch_decode_mfma(a, stream);
   if (a.dtype == 0) return launch_d<float>(a, stream);
   if (a.dtype == 1) return launch_d<uint16_t>(a, stream);

@@ -696,7 +696,14 @@ hipError_t launch_multi_query_few_rows(const MultiQueryArgs &a, hipStream_t stre
 }
 
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
+  // bfloat16 pools with G < 4 stay on the vector kernel (decode.hip), measured
+  // faster there (Llama-7B-shaped layer, G = 1: 382 vs 387 us); 8-bit pools
+  // run only here, for every G
   return dtype == 1 && head_dim == kD && (group == 4 || group == 8);
+}
+
+bool decode_q8_supported(int32_t head_dim, int32_t group) {
+  return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 template <int G>
@@ -710,6 +717,8 @@ hipError_t launch_kind(const DecodeArgs &a, hipStream_t stream) {
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_kind<1>(a, stream);
+    case 2: return launch_kind<2>(a, stream);
     case 4: return launch_kind<4>(a, stream);
     case 8: return launch_kind<8>(a, stream);
     default: return hipErrorNotSupported;

@@ -37,6 +37,8 @@ bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group);
 
 // The matrix-core decode (decode_mfma.hip): bfloat16, head_dim 128, G in {4, 8}.
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
+// 8-bit (FP8 / INT8) pools with bfloat16 queries: head_dim 128, G in {1, 2, 4, 8}.
+bool decode_q8_supported(int32_t head_dim, int32_t group);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 
 // Merge of the per-partition partials into `out` (P > 1 only).

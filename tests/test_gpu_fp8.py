@@ -132,7 +132,7 @@ def test_every_code_reads_back_exactly():
         assert np.array_equal(got[s], np.repeat(want, 4, axis=0).astype(np.float32))
 
 
-@pytest.mark.parametrize("G,Hkv", [(4, 2), (8, 1)])
+@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2), (8, 1)])
 @pytest.mark.parametrize("B", [1, 4, 16, 64, 512])
 def test_decode_matches_oracle(G, Hkv, B):
     lens = [1, 15, 16, 17, 63, 64, 65, 200, 513, 1030]
