@@ -387,6 +387,11 @@ def serving_bench(args) -> int:
           for _ in range(K)]
     infos = []
     host = np.zeros(K)
+    # the Python loop around the engine is the harness, not the engine: keep
+    # the collector's pauses (milliseconds, leaving the GPU idle) out of it
+    import gc
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(K):
@@ -397,6 +402,7 @@ def serving_bench(args) -> int:
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     gpu_ms = np.array([a.elapsed_time(b) for a, b in ev])
     tokens = sum(x.batch for x in infos)
     ctx = sum(x.context_tokens for x in infos)
