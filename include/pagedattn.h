@@ -108,6 +108,13 @@ typedef enum pa_dtype {
  *                  paged_attention_workspace_size(...) for the same arguments;
  *                  may be NULL when that size is 0.  Its contents on entry do
  *                  not matter; it must not be used by other work in flight.
+ *                  It holds the split partials, then (for launches of more
+ *                  than 1024 workgroups, one per sequence, KV head and
+ *                  partition) a dispatch list: a first small kernel sorts
+ *                  the work longest first, so that short items, not long
+ *                  ones, finish the launch.  A workspace too small for the
+ *                  list but large enough for the partials still gives the
+ *                  same results, in a fixed order (slower on mixed lengths).
  *
  * Supported: head_dim 64 or 128; G in {1, 2, 4, 8}; block_size a power of two
  * in [1, 1024]; num_blocks * block_size < 2^31.
@@ -166,8 +173,11 @@ int32_t paged_attention_decode_int8(const void *q, const void *k_cache, const vo
                                     size_t workspace_bytes, void *stream);
 
 /*
- * Bytes of workspace paged_attention_decode needs for these arguments (0 when
- * the call will not split).  Returns 0 for arguments decode would reject.
+ * Bytes of workspace paged_attention_decode (and its FP8 / INT8 forms) needs
+ * for these arguments: 4 * num_seqs * num_q_heads * P * (head_dim + 2) for
+ * the partials when the call splits into P > 1 partitions, plus 4 * num_seqs
+ * * P for the dispatch list when num_seqs * num_kv_heads * P > 1024; 0 when
+ * neither applies.  Returns 0 for arguments decode would reject.
  */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
@@ -221,7 +231,10 @@ int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *                  them in ascending order.
  *   workspace      device scratch of workspace_bytes bytes, at least
  *                  paged_attention_multi_query_workspace_size(...); may be
- *                  NULL when that is 0
+ *                  NULL when that is 0.  As for decode, it holds the partials
+ *                  and then, for launches of more than 1024 workgroups, the
+ *                  longest-first dispatch list; with room for the partials
+ *                  only, the results are the same, in a fixed order.
  * Chunks longer than their context, or reaching past num_tokens, are cut to
  * fit; the numbers are then unspecified but every access stays in bounds.
  * The products run on bfloat16 matrix instructions with fp32 accumulation;
@@ -248,7 +261,10 @@ int32_t paged_attention_multi_query_partitions(int32_t num_seqs, int32_t num_q_h
                                                int32_t num_kv_heads, int32_t max_query_len,
                                                int32_t max_context_len, int32_t partition_size);
 
-/* Workspace bytes paged_attention_multi_query needs (0 when it will not split). */
+/* Workspace bytes paged_attention_multi_query needs: 4 * num_tokens *
+ * num_q_heads * P * (head_dim + 2) for the partials when it splits into P > 1
+ * partitions, plus 4 * num_seqs * P for the dispatch list when the launch has
+ * more than 1024 workgroups; 0 when neither applies. */
 size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_tokens,
                                                   int32_t num_q_heads, int32_t num_kv_heads,
                                                   int32_t head_dim, int32_t max_query_len,

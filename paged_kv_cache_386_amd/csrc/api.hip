@@ -109,6 +109,40 @@ int32_t resolve_mq_partitions(int32_t num_seqs, int32_t num_q_heads, int32_t num
   return (int32_t)(((int64_t)max_context_len + want - 1) / want);
 }
 
+// A decode call's workspace: the split-K partials ([S][Hq][P][D] outputs, then
+// [S][Hq][P][2] (max, sum); P > 1 only), followed by the longest-first
+// dispatch list (int32 [S * P]) when the launch is large enough to use one.
+struct DecodeWorkspace {
+  size_t partials, order;
+};
+DecodeWorkspace decode_workspace(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
+                                 int64_t head_dim, int64_t P) {
+  DecodeWorkspace w;
+  w.partials = P > 1 ? (size_t)(num_seqs * num_q_heads * P * (head_dim + 2)) * sizeof(float) : 0;
+  w.order = pa::schedule_wanted(num_seqs * num_kv_heads * P, num_seqs, P)
+                ? (size_t)(num_seqs * P) * sizeof(int32_t)
+                : 0;
+  return w;
+}
+
+// A multi-query call's workspace: the split partials ([T][Hq][P][D], then
+// [T][Hq][P][2]; P > 1 only), then the longest-first list (int32 [S * P])
+// when the launch is large enough to use one.
+struct MultiQueryWorkspace {
+  size_t partials, order;
+};
+MultiQueryWorkspace multi_query_workspace(int64_t num_seqs, int64_t num_tokens,
+                                          int64_t num_q_heads, int64_t num_kv_heads,
+                                          int64_t head_dim, int64_t max_query_len, int64_t P) {
+  MultiQueryWorkspace w;
+  w.partials =
+      P > 1 ? (size_t)(num_tokens * num_q_heads * P * (head_dim + 2)) * sizeof(float) : 0;
+  const int64_t wgs = pa::multi_query_workgroups(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 max_query_len, P);
+  w.order = pa::schedule_wanted(wgs, num_seqs, P) ? (size_t)(num_seqs * P) * sizeof(int32_t) : 0;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,8 +165,10 @@ size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_
   if (num_tokens < 0 || head_dim <= 0) return 0;
   const int32_t P = paged_attention_multi_query_partitions(
       num_seqs, num_q_heads, num_kv_heads, max_query_len, max_context_len, partition_size);
-  if (P <= 1) return 0;
-  return (size_t)num_tokens * num_q_heads * P * (head_dim + 2) * sizeof(float);
+  if (P < 1) return 0;
+  const MultiQueryWorkspace w = multi_query_workspace(num_seqs, num_tokens, num_q_heads,
+                                                      num_kv_heads, head_dim, max_query_len, P);
+  return w.partials + w.order;
 }
 
 const char *pagedattn_status_string(int32_t status) {
@@ -172,12 +208,12 @@ int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
   int32_t ps = 0;
   const int32_t P = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps);
-  (void)num_kv_heads;
-  if (P <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
+  if (P < 1) return 0;
+  const DecodeWorkspace w = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, P);
+  return w.partials + w.order;
 }
 
 }  // extern "C"
@@ -243,9 +279,9 @@ int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
   a.kv_dtype = kv_dtype;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  const DecodeWorkspace w = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, P);
   if (P > 1) {
-    const size_t need = (size_t)num_seqs * num_q_heads * P * (head_dim + 2) * sizeof(float);
-    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < w.partials) return PA_ERR_WORKSPACE;
     a.ws_o = static_cast<float *>(workspace);
     a.ws_ml = a.ws_o + (size_t)num_seqs * num_q_heads * P * head_dim;
     a.partition_size = ps;
@@ -253,6 +289,9 @@ int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
     // one partition covers any context the kernel will accept after clamping
     a.partition_size = (int32_t)((int64_t)max_blocks_per_seq * block_size);
   }
+  // with room for it, the longest-first list; else the fixed order
+  if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order)
+    a.order = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + w.partials);
   const hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -382,9 +421,10 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
     return PA_ERR_NULL;
   float *ws_o = nullptr, *ws_ml = nullptr;
+  const MultiQueryWorkspace w = multi_query_workspace(num_seqs, num_tokens, num_q_heads,
+                                                      num_kv_heads, head_dim, max_query_len, P);
   if (P > 1) {
-    const size_t need = (size_t)num_tokens * num_q_heads * P * (head_dim + 2) * sizeof(float);
-    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < w.partials) return PA_ERR_WORKSPACE;
     ws_o = static_cast<float *>(workspace);
     ws_ml = ws_o + (size_t)num_tokens * num_q_heads * P * head_dim;
   }
@@ -411,6 +451,9 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
   a.num_partitions = P;
   a.ws_o = ws_o;
   a.ws_ml = ws_ml;
+  // with room for it, the longest-first list; else the fixed order
+  if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order)
+    a.order = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + w.partials);
   const hipError_t e = pa::launch_multi_query(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

@@ -283,20 +283,23 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
-    int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P) {
+    int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P,
+    const int32_t *__restrict__ order) {
   using K = Decode<T, D, G, SMALLB>;
   constexpr int TPL = K::TPL, VPL = K::VPL, LPR = K::LPR, EPV = K::EPV, DPL = K::DPL;
   (void)TPL;
 
-  // Work item: KV head fastest, then sequence, then partition from the last
-  // down (long sequences' later partitions start first, short tails last).  With the
-  // hardware's round-robin placement of consecutive workgroups over the 8 XCDs,
-  // items that share a KV head (and so a prefix block's head slice) land on
-  // the same XCD whenever num_kv_heads is a multiple of 8.
-  const int id = blockIdx.x;
-  const int kvh = id % hkv;
-  const int s = (id / hkv) % num_seqs;
-  const int p = (P - 1) - id / (hkv * num_seqs);
+  // Work item: KV head fastest, then item = (sequence, partition), from
+  // the longest-first list when there is one, else the fixed order --
+  // sequence, then partition from the last down (long sequences' later
+  // partitions start first).  With the hardware's round-robin placement of
+  // consecutive workgroups over the 8 XCDs, items that share a KV head (and
+  // so a prefix block's head slice) land on the same XCD whenever
+  // num_kv_heads is a multiple of 8.
+  const int kvh = blockIdx.x % hkv;
+  const int item = order ? order[blockIdx.x / hkv] : (int)(blockIdx.x / hkv);
+  const int s = item % num_seqs;
+  const int p = (P - 1) - item / num_seqs;
   const int hq = hkv * G;
 
   int L = context_lens[s];
@@ -479,7 +482,8 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
                      0, stream, static_cast<const T *>(a.q), static_cast<const T *>(a.k_cache),
                      static_cast<const T *>(a.v_cache), a.block_tables, a.context_lens, a.out,
                      a.ws_o, a.ws_ml, sl2, a.num_seqs, a.num_kv_heads, a.log2_block_size,
-                     a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions);
+                     a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions,
+                     a.order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions <= 1) return e;
   return launch_partition_merge(a, stream);
@@ -539,6 +543,12 @@ hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (a.order) {
+    const hipError_t e =
+        launch_schedule(a.context_lens, a.order, a.num_seqs, a.num_partitions, a.partition_size,
+                        a.max_blocks_per_seq << a.log2_block_size, stream);
+    if (e != hipSuccess) return e;
+  }
   if (a.kv_dtype == 2 || a.kv_dtype == 3 ||  // 8-bit pools: matrix-core kernel only
       decode_mfma_supported(a.dtype, a.head_dim, a.num_q_heads / a.num_kv_heads))
     return launch_decode_mfma(a, stream);

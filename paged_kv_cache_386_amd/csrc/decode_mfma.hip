@@ -48,7 +48,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 8.f;  // allowed growth of scores over the running max (log2)
-constexpr int kMqMaxRows = 64;  // multi-query rows per KV head taken by this kernel
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -403,7 +402,8 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
     float v_scale, int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P,
-    const int32_t *__restrict__ query_start, int num_tokens, int gh, int max_q, int csets) {
+    const int32_t *__restrict__ query_start, int num_tokens, int gh, int max_q, int csets,
+    const int32_t *__restrict__ order) {
   using K = MfmaDecode<G, SMALLB, Q8>;
   using TileT = typename K::TileT;
   constexpr bool FP8 = K::FP8;
@@ -420,11 +420,12 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
     id = (t / csets) * 8 + id % 8;
     if (id >= num_seqs * hkv * P) return;
   }
-  // work item: KV head fastest, then sequence, then partition from the last
-  // down (as in decode.hip)
+  // work item: KV head fastest, then (sequence, partition) from the
+  // longest-first list or the fixed order (as in decode.hip)
   const int kvh = id % hkv;
-  const int s = (id / hkv) % num_seqs;
-  const int p = (P - 1) - id / (hkv * num_seqs);
+  const int item = order ? order[id / hkv] : id / hkv;
+  const int s = item % num_seqs;
+  const int p = (P - 1) - item / num_seqs;
   const int hq = hkv * (MQ ? gh : G);
 
   int L = context_lens[s];
@@ -654,7 +655,7 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
                      a.block_tables, a.context_lens, a.out, a.ws_o, a.ws_ml, sl2,
                      FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads, a.log2_block_size,
                      a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions,
-                     nullptr, 0, 0, 0, 1);
+                     nullptr, 0, 0, 0, 1, a.order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions <= 1) return e;
   return launch_partition_merge(a, stream);
@@ -679,7 +680,8 @@ hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
                      static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
                      a.out, a.ws_o, a.ws_ml, a.scale * kLog2e, 1.f, a.num_seqs, a.num_kv_heads,
                      a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.partition_size,
-                     a.num_partitions, a.query_start, a.num_tokens, gh, a.max_query_len, csets);
+                     a.num_partitions, a.query_start, a.num_tokens, gh, a.max_query_len, csets,
+                     a.order);
   return hipGetLastError();
 }
 
@@ -687,7 +689,7 @@ hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
 
 bool multi_query_few_rows_supported(const MultiQueryArgs &a) {
   return a.dtype == 1 && a.head_dim == kD &&
-         (int64_t)a.max_query_len * (a.num_q_heads / a.num_kv_heads) <= kMqMaxRows;
+         (int64_t)a.max_query_len * (a.num_q_heads / a.num_kv_heads) <= kMqFewRows;
 }
 
 hipError_t launch_multi_query_few_rows(const MultiQueryArgs &a, hipStream_t stream) {

@@ -27,7 +27,20 @@ struct DecodeArgs {
                            // -1 = dtype
   float k_scale = 1.f;     // 8-bit pools: stored code c means value(c) * scale
   float v_scale = 1.f;
+  int32_t *order = nullptr;  // [S * P] dispatch order of the (sequence, partition) items,
+                             // written by launch_decode_schedule; nullptr = fixed order
 };
+
+// Launches with more workgroups than this run their longest items first (a
+// smaller grid is resident at once, so its order does not matter).
+constexpr int64_t kScheduleMinWorkgroups = 1024;
+bool schedule_wanted(int64_t workgroups, int64_t num_seqs, int64_t P);
+// Writes order[0 .. S*P-1] (schedule.hip): the (sequence, partition) items
+// c (sequence c % S, partition P - 1 - c / S), longest first; ps = tokens
+// per partition, cap = the most tokens a sequence may have.  launch_decode
+// and launch_multi_query call it when their args carry an order buffer.
+hipError_t launch_schedule(const int32_t *context_lens, int32_t *order, int num_seqs, int P,
+                           int ps, int cap, hipStream_t stream);
 
 // Enqueues decode (and the partition merge when P > 1).  Returns hipSuccess or
 // the launch error; hipErrorNotSupported when no kernel is compiled for the
@@ -60,7 +73,17 @@ struct MultiQueryArgs {
   int32_t num_partitions;  // P
   float *ws_o;             // [num_tokens][Hq][P][D] (P > 1 only)
   float *ws_ml;            // [num_tokens][Hq][P][2]
+  int32_t *order = nullptr;  // [S * P] longest-first (sequence, partition) list, or nullptr
 };
+
+// Workgroups of a multi-query launch (either kernel), for the schedule
+// decision and the workspace size.
+int64_t multi_query_workgroups(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
+                               int64_t head_dim, int64_t max_query_len, int64_t P);
+
+// Multi-query launches with at most this many (token, head) rows per KV head
+// take the decode walk (decode_mfma.hip) when it supports them.
+constexpr int64_t kMqFewRows = 64;
 
 // Multi-query attention on the decode kernel (decode_mfma.hip) when every KV
 // head has at most 64 (token, head) rows, in sets of 16: bfloat16, head_dim

@@ -83,26 +83,30 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
-    int num_tokens, int hkv, int G, int lgB, int nb, int mb, int max_q, int row_tiles, int items,
-    int ps, int P) {
+    int num_tokens, int hkv, int G, int lgB, int nb, int mb, int max_q, int row_tiles, int units,
+    int ps, int P, const int32_t *__restrict__ order) {
   constexpr int kRows = 64 * RS;  // query rows per workgroup
   constexpr int kKs = kTk == 64 ? D + 8 : D;  // K tile row stride (elements), padded
   constexpr int kSteps = D / 32;              // k-steps of q.K
   constexpr int kDb = D / 16;                 // 16-element blocks of the output
   using Regs = TileRegs<D>;
 
-  // XCD-aware order: workgroup b runs on XCD b % 8; consecutive items (the
-  // row tiles of one sequence and KV head) go to one XCD
-  const int per = gridDim.x / kXcds;
-  const int item = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (item >= items) return;
-  // partitions from the last down (long contexts' tails start first), then
-  // (sequence, KV head, row tile)
-  const int per_part = items / P;
-  const int part = (P - 1) - item / per_part;
-  const int rt = (item % per_part) % row_tiles;
-  const int kvh = ((item % per_part) / row_tiles) % hkv;
-  const int s = (item % per_part) / (row_tiles * hkv);
+  // XCD-aware order.  A unit r is a KV head (r % hkv) of a (sequence,
+  // partition) item (r / hkv: from the longest-first list when there is one,
+  // else sequence r / hkv % S, partition from the last down); its row tiles
+  // read the same K/V.  Units are dealt round-robin to the XCDs (workgroup b
+  // runs on XCD b % 8), so each XCD gets every eighth unit of the list, and
+  // each XCD runs its units' row tiles back to back, sharing their reads in
+  // its L2.
+  const int j = blockIdx.x / kXcds;
+  const int r = (j / row_tiles) * kXcds + blockIdx.x % kXcds;
+  const int rt = j % row_tiles;
+  if (r >= units) return;
+  const int kvh = r % hkv;
+  const int num_seqs = units / (hkv * P);
+  const int item = order ? order[r / hkv] : r / hkv;
+  const int s = item % num_seqs;
+  const int part = (P - 1) - item / num_seqs;
   const int hq = hkv * G;
 
   int L = context_lens[s];
@@ -414,16 +418,17 @@ hipError_t launch_typed(const MultiQueryArgs &a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t rows = (int64_t)a.max_query_len * G;
   const int row_tiles = (int)((rows + 64 * RS - 1) / (64 * RS));
-  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * row_tiles * a.num_partitions;
-  if (items <= 0) return hipSuccess;
-  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
+  if (units <= 0 || row_tiles <= 0) return hipSuccess;
+  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds * row_tiles;
   hipLaunchKernelGGL((paged_multi_query_kernel<D, RS>), dim3((uint32_t)grid), dim3(kThreads), 0,
                      stream, static_cast<const uint16_t *>(a.q),
                      static_cast<const uint16_t *>(a.k_cache),
                      static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
                      a.query_start, a.out, a.ws_o, a.ws_ml, a.scale * kLog2e, a.num_tokens,
                      a.num_kv_heads, G, a.log2_block_size, a.num_blocks, a.max_blocks_per_seq,
-                     a.max_query_len, row_tiles, (int)items, a.partition_size, a.num_partitions);
+                     a.max_query_len, row_tiles, (int)units, a.partition_size, a.num_partitions,
+                     a.order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions <= 1) return e;
   return launch_merge(a, stream);
@@ -442,7 +447,24 @@ bool multi_query_supported(int32_t dtype, int32_t head_dim) {
   return dtype == 1 && (head_dim == 64 || head_dim == 128);
 }
 
+int64_t multi_query_workgroups(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
+                               int64_t head_dim, int64_t max_query_len, int64_t P) {
+  const int64_t rows = max_query_len * (num_q_heads / num_kv_heads);
+  const int64_t units = num_seqs * num_kv_heads * P;
+  if (head_dim == 128 && rows <= kMqFewRows)  // the decode walk: 16-row column sets
+    return (units + kXcds - 1) / kXcds * kXcds * ((rows + 15) / 16);
+  const int64_t rs = rows > 64 ? 2 : 1;
+  return (units + kXcds - 1) / kXcds * kXcds * ((rows + 64 * rs - 1) / (64 * rs));
+}
+
 hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream) {
+  if (a.order) {
+    const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
+                                           INT32_MAX);
+    const hipError_t e = launch_schedule(a.context_lens, a.order, a.num_seqs,
+                                         a.num_partitions, a.partition_size, cap, stream);
+    if (e != hipSuccess) return e;
+  }
   if (multi_query_few_rows_supported(a)) {
     // a few rows per KV head: the decode walk, one wave per 16-token tile
     hipError_t e = launch_multi_query_few_rows(a, stream);

@@ -66,7 +66,7 @@ int main(void) {
   /* size queries and argument checks of the device calls (nothing launched) */
   CHECK(paged_attention_num_partitions(256, 8, 8192, 0) == 4);
   CHECK(paged_attention_workspace_size(256, 32, 8, 128, 8192, 0) ==
-        (size_t)256 * 32 * 4 * 130 * 4);
+        (size_t)256 * 32 * 4 * 130 * 4 + (size_t)256 * 4 * 4); /* partials + dispatch list */
   CHECK(paged_attention_multi_query_partitions(256, 32, 8, 5, 8192, 0) == 4);
   CHECK(paged_attention_decode(NULL, NULL, NULL, NULL, NULL, 0.1f, NULL, 1, 4, 2, 96, 16, 8, 4,
                                64, PA_BF16, 0, NULL, 0, NULL) == PA_ERR_UNSUPPORTED);

@@ -106,8 +106,15 @@ def test_partition_policy():
     assert lib.paged_attention_partition_tokens(255, 1, 4096, 0) == 2048  # 2 parts
     assert lib.paged_attention_partition_tokens(8, 8, 1000, 0) == 512  # 512 minimum
     assert lib.paged_attention_partition_tokens(8, 8, 500, 0) == 500  # shorter: no split
-    assert lib.paged_attention_workspace_size(8, 64, 8, 128, 32768, 512) == 8 * 64 * 64 * 130 * 4
+    # partials, then the dispatch list (int32 per (sequence, partition)) once
+    # the launch has more than 1024 workgroups
+    assert lib.paged_attention_workspace_size(8, 64, 8, 128, 32768, 512) == \
+        8 * 64 * 64 * 130 * 4 + 8 * 64 * 4
     assert lib.paged_attention_workspace_size(8, 64, 8, 128, 500, 0) == 0
+    assert lib.paged_attention_workspace_size(128, 32, 8, 128, 2048, 0) == 0  # 1024 workgroups
+    assert lib.paged_attention_workspace_size(129, 32, 8, 128, 2048, 0) == 129 * 4  # 1032
+    assert lib.paged_attention_workspace_size(2, 4, 2, 128, 1024, 0) == 2 * 4 * 2 * 130 * 4
+    assert lib.paged_attention_workspace_size(2, 4, 0, 128, 1024, 0) == 0  # rejected
 
 
 def test_cache_ops_reject_bad_arguments_on_host():
@@ -176,6 +183,11 @@ def test_multi_query_partition_policy():
     assert P(16, 32, 8, 512, 8192, -1) == 1
     assert P(16, 32, 8, 512, 8192, 128) == 64
     assert P(16, 32, 8, 512, 8192, 100) == -2  # not a multiple of the 64-token tile
+    # partials (split calls), then the dispatch list once the launch has more
+    # than 1024 workgroups: 256 x 8 x 4 units x 2 column sets; 16 x 8 units x
+    # 16 row tiles of 128 rows
     assert pa.multi_query_workspace_size(256, 1280, 32, 8, 128, 5, 8192) == \
-        1280 * 32 * 4 * 130 * 4
-    assert pa.multi_query_workspace_size(16, 8192, 32, 8, 128, 512, 8192) == 0
+        1280 * 32 * 4 * 130 * 4 + 256 * 4 * 4
+    assert pa.multi_query_workspace_size(16, 8192, 32, 8, 128, 512, 8192) == 16 * 4
+    assert pa.multi_query_workspace_size(2, 10, 32, 8, 128, 5, 100) == 0
+    assert pa.multi_query_workspace_size(4, 2048, 32, 8, 128, 512, 8192) == 0  # 512 workgroups
