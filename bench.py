@@ -12,8 +12,9 @@ Inputs are seeded synthetic data resident in HBM before timing starts.
 Prints one JSON line.  `value` is the step's unique HBM bytes (each distinct
 KV slot read once -- the least HBM must deliver -- plus q, out, tables,
 partials and the edits) per second of step time.  `roofline` prices the decode
-call (decode kernel plus partition merge, timed with HIP events on the stream
-they run on) against the MI355X HBM peak with the attended algorithmic bytes
+call (the dispatch sort of large launches, the decode kernel and the partition
+merge, timed with HIP events on the stream they run on) against the MI355X HBM
+peak with the attended algorithmic bytes
 (K and V read once per sequence and KV head through its block table, 4 KiB per
 attended token here, plus q, out, tables and partials); `unique_gbps` is the
 same call priced with the unique bytes, and `traffic` the bytes the rocprofv3
@@ -50,11 +51,12 @@ if ROOT not in sys.path:
 METRIC = "paged decode achieved HBM GB/s (% of peak) and attended KV tokens/s, 1 GPU"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "paged_kv_cache_386_amd", "csrc")
-# what decides the decode kernels' memory traffic: their sources and the
-# partition policy (the text of resolve_partitions in api.hip)
-DECODE_SOURCES = ["decode.hip", "decode_mfma.hip"]
+# what decides the decode kernels' memory traffic: their sources (with the
+# dispatch-order sort) and the partition policy (the text of
+# resolve_partitions in api.hip)
+DECODE_SOURCES = ["decode.hip", "decode_mfma.hip", "schedule.hip"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_counters.json")
-DECODE_KERNELS = ("paged_decode_mfma_kernel", "paged_decode_kernel", "paged_decode_merge_kernel")
+SCHEDULE_MIN_WORKGROUPS = 1024  # launches above this sort their items first
 
 # calibration copy: CAL_PAIRS blocks of CAL_BLOCK_BYTES in each of two caches
 CAL_BLOCKS = 16384
@@ -89,8 +91,9 @@ def unique_slots(case) -> int:
 def decode_bytes(case, num_partitions: int, partition_size: int, unique: bool) -> int:
     """Algorithmic bytes of one decode call: K and V rows (each distinct slot
     once when ``unique``, else once per attending sequence), q, out, the used
-    block-table entries, context lengths and, for split sequences, the
-    partition partials written by decode and read by the merge."""
+    block-table entries, context lengths, for split sequences the partition
+    partials written by decode and read by the merge, and for large launches
+    the dispatch list (int32 per (sequence, partition), written and read)."""
     import numpy as np
     L = case.context_lens.astype(np.int64)
     S, Hq, D, B = case.num_seqs, case.num_q_heads, case.head_dim, case.block_size
@@ -104,7 +107,10 @@ def decode_bytes(case, num_partitions: int, partition_size: int, unique: bool) -
         n = np.minimum((L + partition_size - 1) // partition_size, num_partitions)
         split = n[n > 1].sum()
         partials = 2 * int(split) * Hq * (D + 2) * 4
-    return kv + qo + tables + partials
+    order = 0
+    if S * case.num_kv_heads * num_partitions > SCHEDULE_MIN_WORKGROUPS:
+        order = 2 * 4 * S * num_partitions + 4 * S  # the list, and the lengths it sorts by
+    return kv + qo + tables + partials + order
 
 
 def edit_bytes(case) -> int:
@@ -167,7 +173,8 @@ def _counter_rows(directory: str, counter: str):
 def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> dict:
     """Scale factors from the calibration copy (the first copy_blocks dispatch,
     whose grid covers CAL_PAIRS pairs) and measured bytes per decode call
-    (decode kernel plus merge, averaged over the calls after the first)."""
+    (dispatch sort, decode kernel and merge, averaged over the calls after
+    the first)."""
     out = {}
     for counter, directory, true_bytes in (("FETCH_SIZE", fetch_dir, CAL_READ_BYTES),
                                            ("WRITE_SIZE", write_dir, CAL_WRITE_BYTES)):
@@ -176,11 +183,16 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str) -> dict:
         if not cal:
             raise SystemExit("no calibration copy_blocks dispatch: run bench.py --copy-calibration")
         factor = true_bytes / (cal[0][3] * 1024.0)
-        # one decode call = one decode-kernel dispatch plus the merge that follows it
+        # one decode call = the dispatch sort (large launches), one
+        # decode-kernel dispatch and the merge that follows it
         calls = []
+        pending = 0.0
         for did, name, grid, kib in rows:
-            if "paged_decode_mfma_kernel" in name or "paged_decode_kernel" in name:
-                calls.append(kib)
+            if "decode_schedule_kernel" in name:
+                pending += kib
+            elif "paged_decode_mfma_kernel" in name or "paged_decode_kernel" in name:
+                calls.append(kib + pending)
+                pending = 0.0
             elif "paged_decode_merge_kernel" in name and calls:
                 calls[-1] += kib
         if len(calls) < 2:

@@ -12,11 +12,15 @@
 //
 // Item c (c < num_seqs * P) is sequence c % num_seqs and partition
 // P - 1 - c / num_seqs -- the fixed order's numbering.  Items are bucketed by
-// token count (1024 size classes of 2^shift tokens, longest class first; an
+// token count (512 size classes of 2^shift tokens, longest class first; an
 // item past the sequence's last partition, which does no work, sorts last)
-// with a counting sort in LDS.  Within a class the order is whatever the LDS
-// atomics give: every item computes the same result wherever it runs, so the
-// order changes timing only.
+// with a counting sort in LDS that keeps, within a class, the fixed order
+// between waves and rounds (and within a round, the order in which the LDS
+// serves one atomic's lanes): sequences that share prefix blocks and have
+// equal sizes then still run side by side and share those blocks' reads in
+// L2 (measured: a fully stable order made the GQA prefix batch's decode kernel
+// 3 us faster than one whose ties were in arbitrary order).  The order
+// changes timing only: every item computes the same result wherever it runs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,17 +29,34 @@
 namespace pa {
 namespace {
 
-constexpr int kSchedThreads = 1024;
-constexpr int kSizeClasses = 1024;  // + 1 for the empty items
-static_assert(kSchedThreads == kSizeClasses, "the scan gives each thread one size class");
+constexpr int kSchedWaves = 16;
+constexpr int kSchedThreads = 64 * kSchedWaves;
+constexpr int kSizeClasses = 512;     // + 1 for the empty items
+constexpr int kKeptClasses = 8192;    // item classes kept in LDS between passes
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Counting sort in three passes over the items, with wave w owning the
+// contiguous range [w * chunk, (w + 1) * chunk), 64 items a round:
+//  1. each wave counts its items per class (LDS atomics);
+//  2. start[k][w] = items of classes before k (all waves) + items of class k
+//     in waves before w;
+//  3. each wave places its items round by round through its own starts, so
+//     a class's items keep the order of the waves, and of the rounds within
+//     a wave.
 __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
     const int32_t *__restrict__ context_lens, int32_t *__restrict__ order, int num_seqs, int P,
     int ps, int cap, int shift) {
-  __shared__ int count[kSizeClasses + 1];
-  __shared__ int wave_total[kSchedThreads / 64];
+  // class-major, so one thread reads a class's 16 wave counts as 4 vectors
+  __shared__ __attribute__((aligned(16))) int start[kSizeClasses + 1][kSchedWaves];
+  __shared__ int wave_total[kSchedWaves];
+  __shared__ uint16_t kept[kKeptClasses];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int n = num_seqs * P;
+  const int chunk = ((n + kSchedWaves - 1) / kSchedWaves + 63) / 64 * 64;
+  const int begin = min(n, wave * chunk), end = min(n, begin + chunk);
 
   // the same clamps and partition bounds as the decode kernels
   auto size_class = [&](int c) -> int {
@@ -48,29 +69,55 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
     return (kSizeClasses - 1) - min(tokens >> shift, kSizeClasses - 1);
   };
 
-  for (int i = tid; i <= kSizeClasses; i += kSchedThreads) count[i] = 0;
+  for (int i = tid; i < (kSizeClasses + 1) * kSchedWaves / 4; i += kSchedThreads)
+    reinterpret_cast<i32x4 *>(&start[0][0])[i] = i32x4{0, 0, 0, 0};
   __syncthreads();
-  for (int c = tid; c < n; c += kSchedThreads) atomicAdd(&count[size_class(c)], 1);
+  for (int c = begin + lane; c < end; c += 64) {
+    const int k = size_class(c);
+    if (c < kKeptClasses) kept[c] = (uint16_t)k;
+    atomicAdd(&start[k][wave], 1);
+  }
   __syncthreads();
 
-  // exclusive prefix sum over the size classes: within each wave by lane
-  // shifts, then across the waves
-  const int v = count[tid];
-  int x = v;
-#pragma unroll
+  // thread k <= 512 owns class k: its total, an exclusive scan over the
+  // classes (the empty class, thread 512, comes after every other), then the
+  // per-wave starts
+  i32x4 cnt[kSchedWaves / 4];
+  int own = 0;
+  if (tid <= kSizeClasses) {
+    for (int v = 0; v < kSchedWaves / 4; ++v) {
+      cnt[v] = reinterpret_cast<const i32x4 *>(&start[tid][0])[v];
+      own += cnt[v][0] + cnt[v][1] + cnt[v][2] + cnt[v][3];
+    }
+    if (tid == kSizeClasses) own = 0;
+  }
+  int x = own;
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off);
-    if ((tid & 63) >= off) x += y;
+    if (lane >= off) x += y;
   }
-  if ((tid & 63) == 63) wave_total[tid >> 6] = x;
+  if (lane == 63) wave_total[wave] = x;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < (tid >> 6); ++w) base += wave_total[w];
-  count[tid] = base + x - v;
-  if (tid == kSizeClasses - 1) count[kSizeClasses] = base + x;
+  int run = x - own;
+  for (int w = 0; w < wave; ++w) run += wave_total[w];
+  if (tid <= kSizeClasses) {
+    for (int v = 0; v < kSchedWaves / 4; ++v) {
+      const i32x4 cv = cnt[v];
+      const i32x4 st = {run, run + cv[0], run + cv[0] + cv[1], run + cv[0] + cv[1] + cv[2]};
+      run += cv[0] + cv[1] + cv[2] + cv[3];
+      reinterpret_cast<i32x4 *>(&start[tid][0])[v] = st;
+    }
+  }
   __syncthreads();
 
-  for (int c = tid; c < n; c += kSchedThreads) order[atomicAdd(&count[size_class(c)], 1)] = c;
+  // each wave places its items in order: its own start per class, so items
+  // of one class keep the wave order; within a round, lanes that share a
+  // class take their slots through one LDS atomic (lane order as the
+  // hardware serves them)
+  for (int c = begin + lane; c < end; c += 64) {
+    const int k = c < kKeptClasses ? (int)kept[c] : size_class(c);
+    order[atomicAdd(&start[k][wave], 1)] = c;
+  }
 }
 
 }  // namespace
