@@ -301,101 +301,130 @@ struct MfmaDecode {
     }
   }
 
-  // acc[b] += V^T P^T for the staged pair; p0: the first tile's
-  // probabilities, p1: the second's (zeros when the pair is incomplete).
-  static __device__ __forceinline__ void pv_pair(const KV *slice, const float (&p0)[4],
-                                                 const float (&p1)[4], f32x4 (&acc)[8], int g,
-                                                 int n) {
-    uint32_t hw[4], lw[4];
+  // acc[c][b] += V^T P^T for the staged pair, for each of the NC column sets
+  // c; p0: the first tile's probabilities, p1: the second's (zeros when the
+  // pair is incomplete).  The V^T operands are read once for all sets.
+  template <int NC>
+  static __device__ __forceinline__ void pv_pair(const KV *slice, const float (&p0)[NC][4],
+                                                 const float (&p1)[NC][4], f32x4 (&acc)[NC][8],
+                                                 int g, int n) {
+    bf16x8 phi[NC], plo[NC];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float a = h < 2 ? p0[2 * h] : p1[2 * h - 4];
-      const float b = h < 2 ? p0[2 * h + 1] : p1[2 * h - 3];
-      const uint32_t ha = bf16_rne(a), hb = bf16_rne(b);
-      hw[h] = ha | (hb << 16);
-      lw[h] = bf16_rne(a - __uint_as_float(ha << 16)) |
-              (bf16_rne(b - __uint_as_float(hb << 16)) << 16);
+    for (int c = 0; c < NC; ++c) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float a = h < 2 ? p0[c][2 * h] : p1[c][2 * h - 4];
+        const float b = h < 2 ? p0[c][2 * h + 1] : p1[c][2 * h - 3];
+        const uint32_t ha = bf16_rne(a), hb = bf16_rne(b);
+        hw[h] = ha | (hb << 16);
+        lw[h] = bf16_rne(a - __uint_as_float(ha << 16)) |
+                (bf16_rne(b - __uint_as_float(hb << 16)) << 16);
+      }
+      phi[c] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+      plo[c] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
     }
-    const bf16x8 phi = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-    const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const bf16x8 a = v_operand(slice, b, g, n);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, acc[b], 0, 0, 0);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, acc[b], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        acc[c][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[c], acc[c][b], 0, 0, 0);
+        acc[c][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[c], acc[c][b], 0, 0, 0);
+      }
     }
   }
 
-  // Fold one tile into the running state: q.K, the online softmax (m: this
-  // lane's column's running maximum in log2 units, shared by the four lane
-  // groups; lsum: the lane's own tokens), the V rows staged into slot `slot`
-  // of the pair; with the pair complete, p.V.  p0 keeps the first tile's
+  // Fold one tile into the running state of NC column sets: q.K (the K
+  // operand read once for all sets), the online softmax (m: this lane's
+  // column's running maximum in log2 units, shared by the four lane groups;
+  // lsum: the lane's own tokens), the V rows staged into slot `slot` of the
+  // pair; with the pair complete, p.V.  p0 keeps the first tile's
   // probabilities until then (and is rescaled with the accumulators).
   // cpos: this lane's column's last attended position (multi-query: a
   // causal mask per column; decode passes INT_MAX).
-  template <bool MASK>
-  static __device__ __forceinline__ void compute(const TileT &T, const bf16x8 (&qb)[4],
-                                                 f32x4 (&acc)[8], float &m, float &lsum,
-                                                 float (&p0)[4], int &slot, KV *slice, int cs,
-                                                 int t1, int g, int n, float sl2, int cpos) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+  template <bool MASK, int NC>
+  static __device__ __forceinline__ void compute(const TileT &T, const bf16x8 (&qb)[NC][4],
+                                                 f32x4 (&acc)[NC][8], float (&m)[NC],
+                                                 float (&lsum)[NC], float (&p0)[NC][4],
+                                                 int &slot, KV *slice, int cs, int t1, int g,
+                                                 int n, float sl2, const int (&cpos)[NC]) {
+    f32x4 sc[NC];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(T, s), qb[s], c, 0, 0, 0);
-    float x[4];
+    for (int c = 0; c < NC; ++c) sc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = cs + 4 * g + j;
-      x[j] = ((!MASK || t < t1) && t <= cpos) ? c[j] * sl2 : neg_inf();
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 a = k_operand(T, s);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        sc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[c][s], sc[c], 0, 0, 0);
     }
-    float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
-    if (cm > m + kSlack) {  // false while both are -inf
-      const float alpha = __builtin_amdgcn_exp2f(m - cm);  // 0 when m was -inf
-      lsum *= alpha;
+    float p[NC][4];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[b] *= alpha;
+    for (int c = 0; c < NC; ++c) {
+      float x[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p0[j] *= alpha;
-      m = cm;
-    }
-    const float mu = (m == neg_inf()) ? 0.f : m;
-    float p[4];
+      for (int j = 0; j < 4; ++j) {
+        const int t = cs + 4 * g + j;
+        x[j] = ((!MASK || t < t1) && t <= cpos[c]) ? sc[c][j] * sl2 : neg_inf();
+      }
+      float cm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      if (cm > m[c] + kSlack) {  // false while both are -inf
+        const float alpha = __builtin_amdgcn_exp2f(m[c] - cm);  // 0 when m was -inf
+        lsum[c] *= alpha;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(x[j] - mu);
-      lsum += p[j];
+        for (int b = 0; b < 8; ++b) acc[c][b] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p0[c][j] *= alpha;
+        m[c] = cm;
+      }
+      const float mu = (m[c] == neg_inf()) ? 0.f : m[c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[c][j] = __builtin_amdgcn_exp2f(x[j] - mu);
+        lsum[c] += p[c][j];
+      }
     }
     stage_v(T, slice, slot, g, n);
     if (slot == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p0[j] = p[j];
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p0[c][j] = p[c][j];
       slot = 1;
     } else {
-      pv_pair(slice, p0, p, acc, g, n);
+      pv_pair<NC>(slice, p0, p, acc, g, n);
       slot = 0;
     }
   }
 
   // Completes a half-filled pair with a zero tile.
-  static __device__ __forceinline__ void flush(const float (&p0)[4], int slot, KV *slice,
-                                               f32x4 (&acc)[8], int g, int n) {
+  template <int NC>
+  static __device__ __forceinline__ void flush(const float (&p0)[NC][4], int slot, KV *slice,
+                                               f32x4 (&acc)[NC][8], int g, int n) {
     if (slot == 1) {
       zero_v(slice, 1, g, n);
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-      pv_pair(slice, p0, z, acc, g, n);
+      float z[NC][4];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[c][j] = 0.f;
+      pv_pair<NC>(slice, p0, z, acc, g, n);
     }
   }
 };
 
 // Multi-query mode (MQ, G = 16 columns): the same walk for a few query tokens
-// per sequence (at most 16 (token, head) rows per KV head), column n being
-// token n / gh and head n % gh of the KV head's gh query heads; the chunk is
-// the sequence's last nq positions and column n attends positions up to
-// L - nq + n / gh (the causal mask of multi_query.hip).
-template <int G, bool SMALLB, int Q8, bool MQ>
-__global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
+// per sequence (at most 64 (token, head) rows per KV head, in sets of 16),
+// column n of set c being row R = 16 c + n of the chunk: token R / gh and
+// head R % gh of the KV head's gh query heads.  The chunk is the sequence's
+// last nq positions and row R attends positions up to L - nq + R / gh (the
+// causal mask of multi_query.hip).  Each wave carries NC column sets, which
+// share every K/V load, the V staging and the V^T operand reads.
+template <int G, bool SMALLB, int Q8, bool MQ, int NC = 1>
+__global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_kernel(
     const uint16_t *__restrict__ q,
     const typename MfmaDecode<G, SMALLB, Q8>::KV *__restrict__ kc,
     const typename MfmaDecode<G, SMALLB, Q8>::KV *__restrict__ vc,
@@ -409,15 +438,16 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   constexpr bool FP8 = K::FP8;
 
   int id = blockIdx.x;
-  // multi-query with more than 16 rows per KV head: column set cset takes
-  // rows 16 cset .. 16 cset + 15.  The sets of one item are 8 workgroups
-  // apart, so they run on the same XCD (workgroup b runs on XCD b % 8) and
-  // the second set's K/V reads hit its L2.
-  int cset = 0;
+  // multi-query with more than 16 * NC rows per KV head: workgroup group cg
+  // takes column sets NC cg .. NC cg + NC - 1.  The groups of one item are 8
+  // workgroups apart, so they run on the same XCD (workgroup b runs on XCD
+  // b % 8) and the later groups' K/V reads hit its L2.
+  int cgroup = 0;
   if constexpr (MQ) {
+    const int cgroups = (csets + NC - 1) / NC;
     const int t = id / 8;
-    cset = t % csets;
-    id = (t / csets) * 8 + id % 8;
+    cgroup = t % cgroups;
+    id = (t / cgroups) * 8 + id % 8;
     if (id >= num_seqs * hkv * P) return;
   }
   // work item: KV head fastest, then (sequence, partition) from the
@@ -430,12 +460,15 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
 
   int L = context_lens[s];
   L = max(0, min(L, mb << lgB));
-  int qs = 0, nq = 0, ncols = G;
+  int qs = 0, nq = 0, ncols[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ncols[c] = G;
   if constexpr (MQ) {
     qs = max(0, min(query_start[s], num_tokens));
     nq = max(0, min(min(query_start[s + 1] - qs, L), min(max_q, num_tokens - qs)));
-    ncols = min(nq * gh - G * cset, G);
-    if (ncols <= 0) return;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ncols[c] = min(nq * gh - G * (NC * cgroup + c), G);
+    if (ncols[0] <= 0) return;
   }
   const int nparts = min((L + ps - 1) / ps, P);
   if (p >= max(nparts, 1)) return;
@@ -448,36 +481,47 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
   const int n = lane & 15;
   const int32_t *tbl = block_tables + (int64_t)s * mb;
 
-  // B operand of q.K: column n is query head n % G of this KV head (decode),
-  // or row n of the chunk (multi-query; columns past the chunk are zero and
-  // fully masked)
-  bf16x8 qb[4];
-  int cpos = INT_MAX;
-  if constexpr (MQ) {
-    const int R = G * cset + n;  // this column's row of the chunk
-    cpos = n < ncols ? L - nq + R / gh : -1;
+  // B operand of q.K for each column set: column n is query head n % G of
+  // this KV head (decode), or row 16 c + n of the chunk (multi-query; columns
+  // past the chunk are zero and fully masked)
+  bf16x8 qb[NC][4];
+  int cpos[NC];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qb[k] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-    if (n < ncols) {
-      const uint16_t *qrow = q + ((int64_t)(qs + R / gh) * hq + kvh * gh + R % gh) * kD;
+  for (int c = 0; c < NC; ++c) {
+    cpos[c] = INT_MAX;
+    if constexpr (MQ) {
+      const int R = G * (NC * cgroup + c) + n;  // this column's row of the chunk
+      cpos[c] = n < ncols[c] ? L - nq + R / gh : -1;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qb[c][k] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      if (n < ncols[c]) {
+        const uint16_t *qrow = q + ((int64_t)(qs + R / gh) * hq + kvh * gh + R % gh) * kD;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          qb[c][k] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4 *>(qrow + k_step_elem<FP8>(g, k)));
+      }
+    } else {
+      const uint16_t *qrow = q + ((int64_t)s * hq + kvh * G + n % G) * kD;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        qb[k] = __builtin_bit_cast(
+        qb[c][k] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4 *>(qrow + k_step_elem<FP8>(g, k)));
     }
-  } else {
-    const uint16_t *qrow = q + ((int64_t)s * hq + kvh * G + n % G) * kD;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      qb[k] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4 *>(qrow + k_step_elem<FP8>(g, k)));
   }
 
-  f32x4 acc[8];
+  f32x4 acc[NC][8];
+  float m[NC], lsum[NC];
+  float p0[NC][4];  // the pending first tile of a pair
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = neg_inf(), lsum = 0.f;
-  float p0[4] = {0.f, 0.f, 0.f, 0.f};  // the pending first tile of a pair
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[c] = neg_inf();
+    lsum[c] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p0[c][j] = 0.f;
+  }
   int slot = 0;
   // the wave's LDS slice: V rows of the pair in the loop, then its results
   constexpr int kSlice =
@@ -551,25 +595,25 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
         ent = entry(j + 1, sv);
         K::template load<false>(Bt, kc, vc, tbl, ent, sv, cstart(j + 1), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g, n,
-                                   sl2, cpos);
+        K::template compute<false, NC>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g,
+                                       n, sl2, cpos);
         ent = entry(j + 2, sv);
         K::template load<false>(A, kc, vc, tbl, ent, sv, cstart(j + 2), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(Bt, qb, acc, m, lsum, p0, slot, slice, cstart(j + 1), t1, g,
-                                   n, sl2, cpos);
+        K::template compute<false, NC>(Bt, qb, acc, m, lsum, p0, slot, slice, cstart(j + 1),
+                                       t1, g, n, sl2, cpos);
       }
       if (j + 2 == nw) {
         ent = entry(j + 1, sv);
         K::template load<false>(Bt, kc, vc, tbl, ent, sv, cstart(j + 1), t1, lgB, nb, g, n,
                                 row_elems, head_off, block_elems);
-        K::template compute<false>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g, n,
-                                   sl2, cpos);
-        K::template compute<false>(Bt, qb, acc, m, lsum, p0, slot, slice, cstart(j + 1), t1, g,
-                                   n, sl2, cpos);
+        K::template compute<false, NC>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g,
+                                       n, sl2, cpos);
+        K::template compute<false, NC>(Bt, qb, acc, m, lsum, p0, slot, slice, cstart(j + 1),
+                                       t1, g, n, sl2, cpos);
       } else {
-        K::template compute<false>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g, n,
-                                   sl2, cpos);
+        K::template compute<false, NC>(A, qb, acc, m, lsum, p0, slot, slice, cstart(j), t1, g,
+                                       n, sl2, cpos);
       }
     }
     if (t0 + nfull * kTile < t1 && nfull % kWaves == wave) {
@@ -577,65 +621,71 @@ __global__ __launch_bounds__(kThreads, 3) void paged_decode_mfma_kernel(
       ent = entry(nw, sv);
       K::template load<true>(A, kc, vc, tbl, ent, sv, cs, t1, lgB, nb, g, n, row_elems,
                              head_off, block_elems);
-      K::template compute<true>(A, qb, acc, m, lsum, p0, slot, slice, cs, t1, g, n, sl2,
-                                 cpos);
+      K::template compute<true, NC>(A, qb, acc, m, lsum, p0, slot, slice, cs, t1, g, n, sl2,
+                                     cpos);
     }
   }
 
-  K::flush(p0, slot, slice, acc, g, n);
+  K::template flush<NC>(p0, slot, slice, acc, g, n);
 
-  // This wave's results per column: the maximum m is already the column's;
-  // the sum combines the four lane groups; the accumulators (lane (g, n):
-  // column n, elements 16 b + 4 g + i) go to the wave's LDS slice, which its
-  // own loop no longer uses.  Columns past G repeat earlier ones (decode).
-  float lcol = lsum;
-  lcol += __shfl_xor(lcol, 16);
-  lcol += __shfl_xor(lcol, 32);
+  // This wave's results per column, one column set at a time: the maximum m
+  // is already the column's; the sum combines the four lane groups; the
+  // accumulators (lane (g, n): column n, elements 16 b + 4 g + i) go to the
+  // wave's LDS slice, which its own loop no longer uses.  Columns past G
+  // repeat earlier ones (decode).
   __shared__ float sm_m[kWaves][G];
   __shared__ float sm_l[kWaves][G];
   float *wacc = reinterpret_cast<float *>(smem[wave]);  // [G][kD]
-  if (n < G) {
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-      *reinterpret_cast<f32x4 *>(wacc + n * kD + 16 * b + 4 * g) = acc[b];
-    if (g == 0) {
-      sm_m[wave][n] = m;
-      sm_l[wave][n] = lcol;
-    }
-  }
-  __syncthreads();
   // decode writes a sequence with one partition straight to out (its merge
   // skips it); the multi-query merge combines every row whenever P > 1
   const bool final_out = MQ ? P <= 1 : nparts <= 1;
-  for (int i = threadIdx.x; i < G * kD; i += kThreads) {
-    const int h = i / kD;
-    const int d = i % kD;
-    float M = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float ls = 0.f, o = 0.f;
+  for (int c = 0; c < NC; ++c) {
+    if (ncols[c] <= 0) break;  // the group's later sets are empty too
+    if (c > 0) __syncthreads();  // every wave has read the previous set's slices
+    float lcol = lsum[c];
+    lcol += __shfl_xor(lcol, 16);
+    lcol += __shfl_xor(lcol, 32);
+    if (n < G) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_m[w][h];
-      const float f = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      ls = fmaf(sm_l[w][h], f, ls);
-      o = fmaf(reinterpret_cast<const float *>(smem[w])[h * kD + d], f, o);
+      for (int b = 0; b < 8; ++b)
+        *reinterpret_cast<f32x4 *>(wacc + n * kD + 16 * b + 4 * g) = acc[c][b];
+      if (g == 0) {
+        sm_m[wave][n] = m[c];
+        sm_l[wave][n] = lcol;
+      }
     }
-    int64_t row;
-    if constexpr (MQ) {
-      if (h >= ncols) continue;
-      const int R = G * cset + h;
-      row = (int64_t)(qs + R / gh) * hq + kvh * gh + R % gh;
-    } else {
-      row = (int64_t)s * hq + kvh * G + h;
-    }
-    if (final_out) {
-      out[row * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
-    } else {
-      ws_o[(row * P + p) * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
-      if (d == 0) {
-        ws_ml[(row * P + p) * 2 + 0] = M;
-        ws_ml[(row * P + p) * 2 + 1] = ls;
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * kD; i += kThreads) {
+      const int h = i / kD;
+      const int d = i % kD;
+      float M = sm_m[0][h];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+      float ls = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_m[w][h];
+        const float f = (mw == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        ls = fmaf(sm_l[w][h], f, ls);
+        o = fmaf(reinterpret_cast<const float *>(smem[w])[h * kD + d], f, o);
+      }
+      int64_t row;
+      if constexpr (MQ) {
+        if (h >= ncols[c]) continue;
+        const int R = G * (NC * cgroup + c) + h;
+        row = (int64_t)(qs + R / gh) * hq + kvh * gh + R % gh;
+      } else {
+        row = (int64_t)s * hq + kvh * G + h;
+      }
+      if (final_out) {
+        out[row * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
+      } else {
+        ws_o[(row * P + p) * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
+        if (d == 0) {
+          ws_ml[(row * P + p) * 2 + 0] = M;
+          ws_ml[(row * P + p) * 2 + 1] = ls;
+        }
       }
     }
   }
@@ -673,10 +723,13 @@ hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
   if (items <= 0) return hipSuccess;
   const int gh = a.num_q_heads / a.num_kv_heads;
   const int csets = (int)(((int64_t)a.max_query_len * gh + 15) / 16);
-  const int64_t grid = (items + 7) / 8 * 8 * csets;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<16, SMALLB, 0, true>), dim3((uint32_t)grid),
-                     dim3(kThreads), 0, stream, static_cast<const uint16_t *>(a.q),
-                     static_cast<const uint16_t *>(a.k_cache),
+  // two column sets per wave from 17 rows up (one pass over K/V for 32
+  // columns), one otherwise
+  const int64_t grid = (items + 7) / 8 * 8 * multi_query_few_rows_groups(csets);
+  auto kernel = csets >= 2 ? paged_decode_mfma_kernel<16, SMALLB, 0, true, 2>
+                           : paged_decode_mfma_kernel<16, SMALLB, 0, true, 1>;
+  hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k_cache),
                      static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
                      a.out, a.ws_o, a.ws_ml, a.scale * kLog2e, 1.f, a.num_seqs, a.num_kv_heads,
                      a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.partition_size,
@@ -686,6 +739,10 @@ hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int64_t multi_query_few_rows_groups(int64_t csets) {
+  return csets >= 2 ? (csets + 1) / 2 : 1;
+}
 
 bool multi_query_few_rows_supported(const MultiQueryArgs &a) {
   return a.dtype == 1 && a.head_dim == kD &&

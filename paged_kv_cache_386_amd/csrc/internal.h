@@ -90,6 +90,9 @@ constexpr int64_t kMqFewRows = 64;
 // 128.  Writes
 // out, or the partition partials that the multi-query merge combines.
 bool multi_query_few_rows_supported(const struct MultiQueryArgs &a);
+// Workgroups per (sequence, KV head, partition) of that path for csets sets
+// of 16 rows (a wave carries two sets when there are at least two).
+int64_t multi_query_few_rows_groups(int64_t csets);
 hipError_t launch_multi_query_few_rows(const struct MultiQueryArgs &a, hipStream_t stream);
 
 // Causal multi-query attention (multi_query.hip): bfloat16, head_dim 64 or 128.

@@ -452,7 +452,7 @@ int64_t multi_query_workgroups(int64_t num_seqs, int64_t num_q_heads, int64_t nu
   const int64_t rows = max_query_len * (num_q_heads / num_kv_heads);
   const int64_t units = num_seqs * num_kv_heads * P;
   if (head_dim == 128 && rows <= kMqFewRows)  // the decode walk: 16-row column sets
-    return (units + kXcds - 1) / kXcds * kXcds * ((rows + 15) / 16);
+    return (units + kXcds - 1) / kXcds * kXcds * multi_query_few_rows_groups((rows + 15) / 16);
   const int64_t rs = rows > 64 ? 2 : 1;
   return (units + kXcds - 1) / kXcds * kXcds * ((rows + 64 * rs - 1) / (64 * rs));
 }
