@@ -163,10 +163,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
 
   // both tiles row-major; V rows are padded differently from K rows so that
   // the transposing reads of V (4 rows x 32 bytes per 16 lanes) and the
-  // 16-row reads of K are both free of bank conflicts
+  // 16-row reads of K are both free of bank conflicts.  Two buffers of each:
+  // the next tile is stored into one while the waves compute on the other.
   constexpr int kVs = D + 16;
-  __shared__ __attribute__((aligned(16))) uint16_t sk[kTk * kKs];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[kTk * kVs];
+  __shared__ __attribute__((aligned(16))) uint16_t sk_buf[2][kTk * kKs];
+  __shared__ __attribute__((aligned(16))) uint16_t sv_buf[2][kTk * kVs];
   // physical block of each token of the next tiles, two slots: the table is
   // read one tile ahead of the K/V rows it locates, so that the two reads
   // never wait on each other
@@ -202,13 +203,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
                                                   (int64_t)(tok & bm1) * D + 8 * dc);
     }
   };
-  // registers -> LDS, both row-major
-  auto store_tile = [&](const Regs &T) {
+  // registers -> LDS buffer `buf`, both row-major
+  auto store_tile = [&](const Regs &T, int buf) {
 #pragma unroll
     for (int j = 0; j < Regs::kKChunks; ++j) {
       const int c = threadIdx.x + kThreads * j;
-      *reinterpret_cast<u32x4 *>(&sk[(c / (D / 8)) * kKs + 8 * (c % (D / 8))]) = T.k[j];
-      *reinterpret_cast<u32x4 *>(&sv[(c / (D / 8)) * kVs + 8 * (c % (D / 8))]) = T.v[j];
+      *reinterpret_cast<u32x4 *>(&sk_buf[buf][(c / (D / 8)) * kKs + 8 * (c % (D / 8))]) = T.k[j];
+      *reinterpret_cast<u32x4 *>(&sv_buf[buf][(c / (D / 8)) * kVs + 8 * (c % (D / 8))]) = T.v[j];
     }
   };
 
@@ -224,110 +225,129 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     lsum[r] = 0.f;
   }
 
+  // Pipeline, one barrier per tile.  In iteration it the waves compute on
+  // tile it (buffer it & 1) while the loads of tile it + 1 are in flight;
+  // then each wave stores tile it + 1 into the other buffer (last read by
+  // tile it - 1, before the previous barrier), writes the block ids of tile
+  // it + 2 into the id slot tile it used (read when tile it's loads were
+  // issued, before the previous barrier), and after the barrier issues the
+  // loads of tile it + 2.
   Regs T;
   uint32_t id_next = 0;
   if (threadIdx.x < kTk) sbid[0][threadIdx.x] = table_entry(k_begin);
   __syncthreads();
   load_tile(T, k_begin, sbid[0]);
   if (threadIdx.x < kTk && ntiles > 1) id_next = table_entry(k_begin + kTk);
+  store_tile(T, 0);
+  if (threadIdx.x < kTk) sbid[1][threadIdx.x] = id_next;
+  __syncthreads();
+  if (ntiles > 1) load_tile(T, k_begin + kTk, sbid[1]);
+  if (threadIdx.x < kTk && ntiles > 2) id_next = table_entry(k_begin + 2 * kTk);
   for (int it = 0; it < ntiles; ++it) {
     const int k0 = k_begin + it * kTk;
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile(T);
-    if (threadIdx.x < kTk) sbid[(it + 1) & 1][threadIdx.x] = id_next;
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(T, k0 + kTk, sbid[(it + 1) & 1]);  // during the products
-    if (threadIdx.x < kTk && it + 2 < ntiles) id_next = table_entry(k0 + 2 * kTk);
-    if (k0 > wave_last) continue;  // all of this wave's rows end earlier
-    const bool masked = k0 + kTk - 1 > pos_first;
+    if (k0 <= wave_last) {  // else all of this wave's rows end earlier
+      const uint16_t *sk = sk_buf[it & 1];
+      const uint16_t *sv = sv_buf[it & 1];
+      const bool masked = k0 + kTk - 1 > pos_first;
 
-    // S^T for each 16-token block tb and row set r
-    f32x4 sc[RS][4];
+      // S^T for each 16-token block tb and row set r
+      f32x4 sc[RS][4];
 #pragma unroll
-    for (int r = 0; r < RS; ++r)
+      for (int r = 0; r < RS; ++r)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) sc[r][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tb = 0; tb < 4; ++tb) sc[r][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+      for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-      for (int k = 0; k < kSteps; ++k) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4 *>(&sk[(16 * tb + c16) * kKs + 32 * k + 8 * g4]));
+        for (int k = 0; k < kSteps; ++k) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8,
+              *reinterpret_cast<const u32x4 *>(&sk[(16 * tb + c16) * kKs + 32 * k + 8 * g4]));
 #pragma unroll
-        for (int r = 0; r < RS; ++r)
-          sc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[r][k], sc[r][tb], 0, 0, 0);
-      }
-    }
-
-    // online softmax per row set; then the hi/lo probability operands
-    bf16x8 phi[RS][2], plo[RS][2];
-#pragma unroll
-    for (int r = 0; r < RS; ++r) {
-      float x[4][4];
-      float cm = neg_inf();
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = k0 + 16 * tb + 4 * g4 + i;
-          x[tb][i] = (!masked || t <= pos[r]) ? sc[r][tb][i] * sl2 : neg_inf();
-          cm = fmaxf(cm, x[tb][i]);
+          for (int r = 0; r < RS; ++r)
+            sc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[r][k], sc[r][tb], 0, 0, 0);
         }
-      cm = fmaxf(cm, __shfl_xor(cm, 16));
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
-      if (cm > m[r] + kSlack) {  // false while both are -inf
-        const float alpha = __builtin_amdgcn_exp2f(m[r] - cm);  // 0 when m was -inf
-        lsum[r] *= alpha;
-#pragma unroll
-        for (int b = 0; b < kDb; ++b) acc[r][b] *= alpha;
-        m[r] = cm;
       }
-      const float mu = (m[r] == neg_inf()) ? 0.f : m[r];
+
+      // online softmax per row set; then the hi/lo probability operands
+      bf16x8 phi[RS][2], plo[RS][2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint32_t hw[4], lw[4];
+      for (int r = 0; r < RS; ++r) {
+        float x[4][4];
+        float cm = neg_inf();
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          float pr[2];
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int jj = j + u;
-            const int tb = 2 * kk + (jj >> 2);
-            pr[u] = __builtin_amdgcn_exp2f(x[tb][jj & 3] - mu);
-            lsum[r] += pr[u];
+          for (int i = 0; i < 4; ++i) {
+            const int t = k0 + 16 * tb + 4 * g4 + i;
+            x[tb][i] = (!masked || t <= pos[r]) ? sc[r][tb][i] * sl2 : neg_inf();
+            cm = fmaxf(cm, x[tb][i]);
           }
-          const uint32_t h0 = bf16_bits(pr[0]), h1 = bf16_bits(pr[1]);
-          const float r0 = pr[0] - __uint_as_float(h0 << 16);
-          const float r1 = pr[1] - __uint_as_float(h1 << 16);
-          hw[j >> 1] = h0 | (h1 << 16);
-          lw[j >> 1] = bf16_bits(r0) | (bf16_bits(r1) << 16);
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        if (cm > m[r] + kSlack) {  // false while both are -inf
+          const float alpha = __builtin_amdgcn_exp2f(m[r] - cm);  // 0 when m was -inf
+          lsum[r] *= alpha;
+#pragma unroll
+          for (int b = 0; b < kDb; ++b) acc[r][b] *= alpha;
+          m[r] = cm;
         }
-        phi[r][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-        plo[r][kk] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+        const float mu = (m[r] == neg_inf()) ? 0.f : m[r];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            float pr[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int jj = j + u;
+              const int tb = 2 * kk + (jj >> 2);
+              pr[u] = __builtin_amdgcn_exp2f(x[tb][jj & 3] - mu);
+              lsum[r] += pr[u];
+            }
+            const uint32_t h0 = bf16_bits(pr[0]), h1 = bf16_bits(pr[1]);
+            const float r0 = pr[0] - __uint_as_float(h0 << 16);
+            const float r1 = pr[1] - __uint_as_float(h1 << 16);
+            hw[j >> 1] = h0 | (h1 << 16);
+            lw[j >> 1] = bf16_bits(r0) | (bf16_bits(r1) << 16);
+          }
+          phi[r][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+          plo[r][kk] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+        }
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int b = 0; b < kDb; ++b) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          // gfx950's transposing LDS read: within each 16-lane group, lane c
+          // points at 4 elements of row (base + c / 4) and receives, from the
+          // rows base .. base + 3, the element in its own column -- here
+          // element 16 b + c16 of tokens 32 kk + 4 g4 + 0..3 (and + 16)
+          const uint16_t *vr = &sv[(32 * kk + 4 * g4 + c16 / 4) * kVs + 16 * b + 4 * (c16 % 4)];
+          const u32x2 lo = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vr)));
+          const u32x2 hi = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vr + 16 * kVs)));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int r = 0; r < RS; ++r) {
+            acc[r][b] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[r][kk], acc[r][b], 0, 0, 0);
+            acc[r][b] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[r][kk], acc[r][b], 0, 0, 0);
+          }
+        }
       }
     }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int b = 0; b < kDb; ++b) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // gfx950's transposing LDS read: within each 16-lane group, lane c
-        // points at 4 elements of row (base + c / 4) and receives, from the
-        // rows base .. base + 3, the element in its own column -- here
-        // element 16 b + c16 of tokens 32 kk + 4 g4 + 0..3 (and + 16)
-        const uint16_t *vr = &sv[(32 * kk + 4 * g4 + c16 / 4) * kVs + 16 * b + 4 * (c16 % 4)];
-        const u32x2 lo = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vr)));
-        const u32x2 hi = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vr + 16 * kVs)));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-        for (int r = 0; r < RS; ++r) {
-          acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[r][kk], acc[r][b], 0, 0, 0);
-          acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[r][kk], acc[r][b], 0, 0, 0);
-        }
-      }
+    if (it + 1 < ntiles) {
+      store_tile(T, (it + 1) & 1);
+      if (threadIdx.x < kTk && it + 2 < ntiles) sbid[it & 1][threadIdx.x] = id_next;
+      __syncthreads();
+      if (it + 2 < ntiles) load_tile(T, k0 + 2 * kTk, sbid[it & 1]);  // during the products
+      if (threadIdx.x < kTk && it + 3 < ntiles) id_next = table_entry(k0 + 3 * kTk);
     }
   }
 
