@@ -101,9 +101,11 @@ typedef enum pa_dtype {
  *                  pairs) equal partitions per context, at least 512
  *                  tokens), negative = never split, positive = that many
  *                  tokens (a multiple of 16).  With
- *                  more than one partition, per-partition (max, sum, output)
- *                  partials go to the workspace and a second kernel merges them
- *                  in ascending partition order.
+ *                  more than one partition, the sequences whose context
+ *                  spans several partitions leave per-partition (max, sum,
+ *                  output) partials in the workspace and a second kernel
+ *                  merges them in ascending partition order; the others are
+ *                  written directly.
  *   workspace      device scratch of workspace_bytes bytes, at least
  *                  paged_attention_workspace_size(...) for the same arguments;
  *                  may be NULL when that size is 0.  Its contents on entry do
@@ -226,9 +228,10 @@ int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *                  most 64 query rows per KV head are split like decode,
  *                  rounded up to whole 64-token tiles; longer chunks are not
  *                  split), negative = never, positive = that many tokens (a
- *                  multiple of 64).  With more than one partition the
- *                  partials go to the workspace and a second kernel merges
- *                  them in ascending order.
+ *                  multiple of 64).  With more than one partition, the
+ *                  sequences whose context spans several partitions leave
+ *                  partials in the workspace and a second kernel merges them
+ *                  in ascending order; the others are written directly.
  *   workspace      device scratch of workspace_bytes bytes, at least
  *                  paged_attention_multi_query_workspace_size(...); may be
  *                  NULL when that is 0.  As for decode, it holds the partials

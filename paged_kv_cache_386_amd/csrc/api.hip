@@ -417,6 +417,9 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
   if ((int64_t)num_seqs * num_kv_heads * tiles * P + 8 >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
   if ((int64_t)num_tokens * num_q_heads * head_dim >= (int64_t(1) << 40)) return PA_ERR_SHAPE;
   if ((int64_t)num_tokens * num_q_heads >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  // the merge has one workgroup per (sequence, chunk token, head)
+  if (P > 1 && (int64_t)num_seqs * max_query_len * num_q_heads >= (int64_t(1) << 31))
+    return PA_ERR_SHAPE;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
     return PA_ERR_NULL;

@@ -636,9 +636,8 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   __shared__ float sm_m[kWaves][G];
   __shared__ float sm_l[kWaves][G];
   float *wacc = reinterpret_cast<float *>(smem[wave]);  // [G][kD]
-  // decode writes a sequence with one partition straight to out (its merge
-  // skips it); the multi-query merge combines every row whenever P > 1
-  const bool final_out = MQ ? P <= 1 : nparts <= 1;
+  // a sequence with one partition goes straight to out (its merge skips it)
+  const bool final_out = nparts <= 1;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (ncols[c] <= 0) break;  // the group's later sets are empty too

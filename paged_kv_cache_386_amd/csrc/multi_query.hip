@@ -352,7 +352,10 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   }
 
   // normalise and write: lane (g4, c16) holds row c16 of each row set,
-  // elements 16 b + 4 g4 .. +3
+  // elements 16 b + 4 g4 .. +3.  A sequence whose context fits in one
+  // partition goes straight to out (the merge skips it); the others leave
+  // (max, sum, output) partials for the merge.
+  const bool split = min((L + ps - 1) / ps, P) > 1;
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
     float l = lsum[r];
@@ -362,11 +365,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     if (R < row_end) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const int64_t orow = (int64_t)(qs + R / G) * hq + kvh * G + R % G;
-      float *o = P > 1 ? ws_o + (orow * P + part) * D : out + orow * D;
+      float *o = split ? ws_o + (orow * P + part) * D : out + orow * D;
 #pragma unroll
       for (int b = 0; b < kDb; ++b)
         *reinterpret_cast<f32x4 *>(o + 16 * b + 4 * g4) = acc[r][b] * inv;
-      if (P > 1 && g4 == 0) {
+      if (split && g4 == 0) {
         ws_ml[(orow * P + part) * 2 + 0] = m[r];
         ws_ml[(orow * P + part) * 2 + 1] = l;
       }
@@ -374,33 +377,29 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   }
 }
 
-// Merge of the partition partials of each (query token, head) row: the
-// row's sequence is found by binary search over query_start, and only the
-// partitions its position reaches are combined (log-sum-exp, ascending).
+// Merge of the partition partials of one (query token, head) row, D threads:
+// workgroup (s, i, h) takes head h of token i of sequence s's chunk, and,
+// when the sequence was split, combines the partitions the token's position
+// reaches (log-sum-exp weights, ascending partition order).  Rows of
+// sequences that fit in one partition were written to out directly.
 template <int D>
 __global__ __launch_bounds__(D) void paged_multi_query_merge_kernel(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
-    int num_seqs, int num_tokens, int hq, int cap, int max_q, int ps, int P) {
-  const int64_t row = blockIdx.x;  // token * hq + h
-  const int tok = (int)(row / hq);
-  // last sequence whose first row is <= tok
-  int lo = 0, hi = num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (max(0, min(query_start[mid], num_tokens)) <= tok) lo = mid;
-    else hi = mid - 1;
-  }
-  const int s = lo;
+    int num_tokens, int hq, int cap, int max_q, int ps, int P) {
+  const int h = blockIdx.x % hq;
+  const int i = (blockIdx.x / hq) % max_q;
+  const int s = blockIdx.x / (hq * max_q);
   int L = context_lens[s];
   L = max(0, min(L, cap));
+  if (min((L + ps - 1) / ps, P) <= 1) return;  // written to out directly
   const int qs = max(0, min(query_start[s], num_tokens));
   int n = query_start[s + 1] - qs;
   n = max(0, min(min(n, L), min(max_q, num_tokens - qs)));
-  const int i = tok - qs;
-  if (i < 0 || i >= n) return;  // a row no chunk owns
+  if (i >= n) return;  // no such token in the chunk
   const int pos = L - n + i;
   const int np = min(pos / ps + 1, P);
+  const int64_t row = (int64_t)(qs + i) * hq + h;
   const float *ml = ws_ml + row * P * 2;
   const float *o = ws_o + row * P * D;
   float M = ml[0];
@@ -417,17 +416,18 @@ __global__ __launch_bounds__(D) void paged_multi_query_merge_kernel(
 }
 
 hipError_t launch_merge(const MultiQueryArgs &a, hipStream_t stream) {
-  const int64_t mrows = (int64_t)a.num_tokens * a.num_q_heads;
+  const int64_t wgs = (int64_t)a.num_seqs * a.max_query_len * a.num_q_heads;
+  if (wgs <= 0) return hipSuccess;
   const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
                                          INT32_MAX);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((paged_multi_query_merge_kernel<64>), dim3((uint32_t)mrows), dim3(64), 0,
-                       stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out, a.num_seqs,
+    hipLaunchKernelGGL((paged_multi_query_merge_kernel<64>), dim3((uint32_t)wgs), dim3(64), 0,
+                       stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out,
                        a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
                        a.num_partitions);
   else
-    hipLaunchKernelGGL((paged_multi_query_merge_kernel<128>), dim3((uint32_t)mrows), dim3(128), 0,
-                       stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out, a.num_seqs,
+    hipLaunchKernelGGL((paged_multi_query_merge_kernel<128>), dim3((uint32_t)wgs), dim3(128), 0,
+                       stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out,
                        a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
                        a.num_partitions);
   return hipGetLastError();
