@@ -80,16 +80,6 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// Eight K or V elements: 16 bytes of bfloat16, or 8 bytes of FP8 (E4M3).
-template <bool FP8>
-struct Vec8 {
-  using type = u32x4;
-};
-template <>
-struct Vec8<true> {
-  using type = u32x2;
-};
-
 // K rows are fetched 16 bytes per lane: for bfloat16, lane group g takes
 // elements 32s + 8g .. +7 of k-step s (s = 0..3); for FP8 a 16-byte load
 // holds two k-steps, so lane group g takes elements 16(4i + g) .. +15 in load
@@ -99,8 +89,11 @@ struct Vec8<true> {
 // contiguous bytes of every token row it touches.
 template <bool FP8>
 struct Tile {
-  u32x4 k[FP8 ? 2 : 4];           // token n of the tile (see above)
-  typename Vec8<FP8>::type v[4];  // token 4g + j of the tile, elements 8n .. 8n+7 (j = 0..3)
+  u32x4 k[FP8 ? 2 : 4];  // token n of the tile (see above)
+  // V, 16 bytes per lane and load (see v_token / v_elem): bfloat16, token
+  // 4g + j of the tile, elements 8n .. 8n+7 (j = 0..3); 8-bit codes, token
+  // 8j + lane / 8, elements 16 (lane % 8) .. +15 (j = 0, 1)
+  u32x4 v[FP8 ? 2 : 4];
 };
 
 // First element of lane group g's part of K load i (see Tile).
@@ -112,11 +105,6 @@ __device__ __forceinline__ int k_load_elem(int g, int i) {
 template <bool FP8>
 __device__ __forceinline__ int k_step_elem(int g, int s) {
   return FP8 ? 16 * (4 * (s >> 1) + g) + 8 * (s & 1) : 32 * s + 8 * g;
-}
-
-template <int POLICY>
-__device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY));
 }
 
 // Four E4M3 codes (one dword) to fp32 with the hardware conversion (OCP
@@ -166,18 +154,19 @@ template <int G, bool SMALLB, int Q8>
 struct MfmaDecode {
   static constexpr bool FP8 = Q8 != 0;  // one byte per element
   using KV = typename std::conditional<FP8, uint8_t, uint16_t>::type;
-  using V8 = typename Vec8<FP8>::type;
   using TileT = Tile<FP8>;
   static constexpr int kElem = FP8 ? 1 : 2;  // bytes per element
-  template <int POLICY>
-  static __device__ __forceinline__ V8 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (FP8)
-      return buffer_load8<POLICY>(r, off);
-    else
-      return buffer_load<POLICY>(r, off);
-  }
   static constexpr int kKLoads = FP8 ? 2 : 4;
-  static __device__ __forceinline__ V8 zero8() { return V8{}; }
+  static constexpr int kVLoads = FP8 ? 2 : 4;
+  // tile token and first element of lane (g, n)'s V chunk j
+  static __device__ __forceinline__ int v_token(int j, int g, int n) {
+    return FP8 ? 8 * j + 2 * g + n / 8 : 4 * g + j;
+  }
+  static __device__ __forceinline__ int v_elem(int g, int n) { return FP8 ? 16 * (n % 8) : 8 * n; }
+  // LDS row of tile token t in slot `slot` of the pair (see below)
+  static __device__ __forceinline__ int v_row(int slot, int t) {
+    return 8 * (t / 4) + 4 * slot + t % 4;
+  }
   // the A operand of k-step s
   static __device__ __forceinline__ bf16x8 k_operand(const TileT &T, int s) {
     if constexpr (FP8) {
@@ -213,21 +202,22 @@ struct MfmaDecode {
       for (int i = 0; i < kKLoads; ++i)
         T.k[i] = okk ? buffer_load<kCacheNormal>(rk, krow + k_load_elem<FP8>(g, i) * kElem)
                      : u32x4{0, 0, 0, 0};
-      uint32_t voff[4];
-      bool ok[4];
+      uint32_t voff[kVLoads];
+      bool ok[kVLoads];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        voff[j] = (uint32_t)(((o + 4 * g + j) * row_elems + head_off + 8 * n) * kElem);
-        ok[j] = !MASK || cs + 4 * g + j < t1;
+      for (int j = 0; j < kVLoads; ++j) {
+        const int t = v_token(j, g, n);
+        voff[j] = (uint32_t)(((o + t) * row_elems + head_off + v_elem(g, n)) * kElem);
+        ok[j] = !MASK || cs + t < t1;
       }
       if (stream_v) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          T.v[j] = ok[j] ? bload<kCacheStream>(rv, voff[j]) : zero8();
+        for (int j = 0; j < kVLoads; ++j)
+          T.v[j] = ok[j] ? buffer_load<kCacheStream>(rv, voff[j]) : u32x4{0, 0, 0, 0};
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          T.v[j] = ok[j] ? bload<kCacheNormal>(rv, voff[j]) : zero8();
+        for (int j = 0; j < kVLoads; ++j)
+          T.v[j] = ok[j] ? buffer_load<kCacheNormal>(rv, voff[j]) : u32x4{0, 0, 0, 0};
       }
     } else {
       // blocks shorter than a tile: each token row looks up its own block
@@ -243,14 +233,15 @@ struct MfmaDecode {
         for (int i = 0; i < kKLoads; ++i) T.k[i] = u32x4{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tv = cs + 4 * g + j;
+      for (int j = 0; j < kVLoads; ++j) {
+        const int tv = cs + v_token(j, g, n);
         if (!MASK || tv < t1) {
           const uint32_t pid = min((uint32_t)tbl[tv >> lgB], (uint32_t)(nb - 1));
-          T.v[j] = __builtin_nontemporal_load(reinterpret_cast<const V8 *>(
-              vc + (int64_t)pid * block_elems + head_off + (tv & bm1) * row_elems + 8 * n));
+          T.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+              vc + (int64_t)pid * block_elems + head_off + (tv & bm1) * row_elems +
+              v_elem(g, n)));
         } else {
-          T.v[j] = zero8();
+          T.v[j] = u32x4{0, 0, 0, 0};
         }
       }
     }
@@ -276,13 +267,15 @@ struct MfmaDecode {
   static __device__ __forceinline__ void stage_v(const TileT &T, KV *slice, int slot, int g,
                                                  int n) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<V8 *>(slice + (8 * g + 4 * slot + j) * kVRow + 8 * n) = T.v[j];
+    for (int j = 0; j < kVLoads; ++j)
+      *reinterpret_cast<u32x4 *>(slice + v_row(slot, v_token(j, g, n)) * kVRow + v_elem(g, n)) =
+          T.v[j];
   }
   static __device__ __forceinline__ void zero_v(KV *slice, int slot, int g, int n) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<V8 *>(slice + (8 * g + 4 * slot + j) * kVRow + 8 * n) = zero8();
+    for (int j = 0; j < kVLoads; ++j)
+      *reinterpret_cast<u32x4 *>(slice + v_row(slot, v_token(j, g, n)) * kVRow + v_elem(g, n)) =
+          u32x4{0, 0, 0, 0};
   }
   static __device__ __forceinline__ bf16x8 v_operand(const KV *slice, int b, int g, int n) {
     typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
