@@ -75,9 +75,12 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// bfloat16 bits of x, rounded to nearest even (hardware conversion)
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 bits of a (low half) and b (high half), rounded to nearest even:
+// one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // K rows are fetched 16 bytes per lane: for bfloat16, lane group g takes
@@ -107,43 +110,36 @@ __device__ __forceinline__ int k_step_elem(int g, int s) {
   return FP8 ? 16 * (4 * (s >> 1) + g) + 8 * (s & 1) : 32 * s + 8 * g;
 }
 
-// Four E4M3 codes (one dword) to fp32 with the hardware conversion (OCP
-// E4M3 on gfx950; every code is exact in fp32).
-__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float (&f)[4]) {
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  f[0] = lo[0];
-  f[1] = lo[1];
-  f[2] = hi[0];
-  f[3] = hi[1];
-}
-
 // Four signed 8-bit codes (one dword) to fp32 (exact).
 __device__ __forceinline__ void i8x4_to_f32(uint32_t w, float (&f)[4]) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) f[b] = (float)((int32_t)(w << (24 - 8 * b)) >> 24);
 }
 
-template <int Q8>
-__device__ __forceinline__ void codes4_to_f32(uint32_t w, float (&f)[4]) {
-  if constexpr (Q8 == 1)
-    e4m3x4_to_f32(w, f);
-  else
-    i8x4_to_f32(w, f);
-}
-
-// Eight 8-bit codes to the bfloat16 MFMA operand (exact: an E4M3 value has
-// at most 4 significant bits and an INT8 code at most 7, so the high half of
-// the fp32 form is the value).
+// Eight 8-bit codes to the bfloat16 MFMA operand, exactly (an E4M3 value has
+// at most 4 significant bits and an INT8 code at most 7).  E4M3: gfx950's
+// scaled conversion with scale 1 turns the two codes of one 16-bit half into
+// two bfloat16, the low byte into the low half (OCP E4M3, as the hardware's
+// other FP8 conversions).  INT8: widened to fp32, whose high halves are the
+// bfloat16 values, paired with one byte permute.
 template <int Q8>
 __device__ __forceinline__ bf16x8 codes8_to_bf16(u32x2 w) {
   u32x4 r;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    float f[4];
-    codes4_to_f32<Q8>(w[h], f);
-    r[2 * h] = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
-    r[2 * h + 1] = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xFFFF0000u);
+    if constexpr (Q8 == 1) {
+      r[2 * h] = __builtin_bit_cast(uint32_t,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, false));
+      r[2 * h + 1] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, true));
+    } else {
+      float f[4];
+      i8x4_to_f32(w[h], f);
+      // (f0 >> 16) | (f1 & 0xffff0000): bytes 2, 3 of f0, then bytes 2, 3 of f1
+      r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+      r[2 * h + 1] =
+          __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
+    }
   }
   return __builtin_bit_cast(bf16x8, r);
 }
@@ -309,10 +305,9 @@ struct MfmaDecode {
       for (int h = 0; h < 4; ++h) {
         const float a = h < 2 ? p0[c][2 * h] : p1[c][2 * h - 4];
         const float b = h < 2 ? p0[c][2 * h + 1] : p1[c][2 * h - 3];
-        const uint32_t ha = bf16_rne(a), hb = bf16_rne(b);
-        hw[h] = ha | (hb << 16);
-        lw[h] = bf16_rne(a - __uint_as_float(ha << 16)) |
-                (bf16_rne(b - __uint_as_float(hb << 16)) << 16);
+        hw[h] = bf16x2_bits(a, b);
+        lw[h] = bf16x2_bits(a - __uint_as_float(hw[h] << 16),
+                            b - __uint_as_float(hw[h] & 0xFFFF0000u));
       }
       phi[c] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
       plo[c] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});

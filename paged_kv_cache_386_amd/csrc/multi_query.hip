@@ -64,8 +64,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 bits of a (low half) and b (high half), rounded to nearest even:
+// one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 template <int D>
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   const int64_t block_elems = ((int64_t)hkv * D) << lgB;
 
   // this lane's query rows (one per row set), their positions and the B
-  // operand of q.K
+  // operand of q.K; sl2 becomes |sl2| once q carries the scale's sign
   int pos[RS];
   bf16x8 qb[RS][kSteps];
   int wave_last = -1;
@@ -152,14 +157,19 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     for (int k = 0; k < kSteps; ++k) qb[r][k] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     if (active) {
       const uint16_t *qrow = q + ((int64_t)(qs + tok) * hq + kvh * G + R % G) * D + 8 * g4;
+      // a negative scale moves onto q (exact sign flips), so sl2 >= 0 below
+      const uint32_t flip = sl2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
       for (int k = 0; k < kSteps; ++k)
-        qb[r][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * k));
+        qb[r][k] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * k) ^ u32x4{flip, flip, flip, flip});
     }
     // the wave's last attended position (rows are ascending in position)
     const int Rw = min(row0 + (wave * RS + r) * 16 + 15, row_end - 1);
     if (row0 + (wave * RS + r) * 16 < row_end) wave_last = max(wave_last, L - n + Rw / G);
   }
+  sl2 = fmaxf(__builtin_fabsf(sl2), 1.17549435e-38f);
+  const float slack = kSlack / sl2;  // kSlack in raw score units (may be inf)
 
   // both tiles row-major; V rows are padded differently from K rows so that
   // the transposing reads of V (4 rows x 32 bytes per 16 lanes) and the
@@ -269,24 +279,32 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
         }
       }
 
-      // online softmax per row set; then the hi/lo probability operands
+      // online softmax per row set; then the hi/lo probability operands.
+      // The running maximum m is kept on the raw scores (sl2 > 0: q carries
+      // a negative scale's sign, and a zero scale is raised to the least
+      // normal float, which gives every unmasked p = 1 as zero does), and
+      // p = 2^((x - m) sl2): exactly 1 at the maximum.  Masked positions
+      // (only in tiles that reach past the workgroup's first row) become
+      // -inf, so p = 0.
       bf16x8 phi[RS][2], plo[RS][2];
 #pragma unroll
       for (int r = 0; r < RS; ++r) {
-        float x[4][4];
+        if (masked) {
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (k0 + 16 * tb + 4 * g4 + i > pos[r]) sc[r][tb][i] = neg_inf();
+        }
         float cm = neg_inf();
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = k0 + 16 * tb + 4 * g4 + i;
-            x[tb][i] = (!masked || t <= pos[r]) ? sc[r][tb][i] * sl2 : neg_inf();
-            cm = fmaxf(cm, x[tb][i]);
-          }
+          for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[r][tb][i]);
         cm = fmaxf(cm, __shfl_xor(cm, 16));
         cm = fmaxf(cm, __shfl_xor(cm, 32));
-        if (cm > m[r] + kSlack) {  // false while both are -inf
-          const float alpha = __builtin_amdgcn_exp2f(m[r] - cm);  // 0 when m was -inf
+        if (cm > m[r] + slack) {  // false while both are -inf
+          const float alpha = __builtin_amdgcn_exp2f((m[r] - cm) * sl2);  // 0 when m was -inf
           lsum[r] *= alpha;
 #pragma unroll
           for (int b = 0; b < kDb; ++b) acc[r][b] *= alpha;
@@ -303,14 +321,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
             for (int u = 0; u < 2; ++u) {
               const int jj = j + u;
               const int tb = 2 * kk + (jj >> 2);
-              pr[u] = __builtin_amdgcn_exp2f(x[tb][jj & 3] - mu);
-              lsum[r] += pr[u];
+              pr[u] = __builtin_amdgcn_exp2f((sc[r][tb][jj & 3] - mu) * sl2);
             }
-            const uint32_t h0 = bf16_bits(pr[0]), h1 = bf16_bits(pr[1]);
-            const float r0 = pr[0] - __uint_as_float(h0 << 16);
-            const float r1 = pr[1] - __uint_as_float(h1 << 16);
-            hw[j >> 1] = h0 | (h1 << 16);
-            lw[j >> 1] = bf16_bits(r0) | (bf16_bits(r1) << 16);
+            lsum[r] += pr[0] + pr[1];
+            const uint32_t h = bf16x2_bits(pr[0], pr[1]);
+            hw[j >> 1] = h;
+            lw[j >> 1] = bf16x2_bits(pr[0] - __uint_as_float(h << 16),
+                                     pr[1] - __uint_as_float(h & 0xFFFF0000u));
           }
           phi[r][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
           plo[r][kk] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
@@ -370,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
       for (int b = 0; b < kDb; ++b)
         *reinterpret_cast<f32x4 *>(o + 16 * b + 4 * g4) = acc[r][b] * inv;
       if (split && g4 == 0) {
-        ws_ml[(orow * P + part) * 2 + 0] = m[r];
+        ws_ml[(orow * P + part) * 2 + 0] = m[r] * sl2;  // log2 units
         ws_ml[(orow * P + part) * 2 + 1] = l;
       }
     }
