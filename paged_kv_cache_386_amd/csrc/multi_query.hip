@@ -169,7 +169,9 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     if (row0 + (wave * RS + r) * 16 < row_end) wave_last = max(wave_last, L - n + Rw / G);
   }
   sl2 = fmaxf(__builtin_fabsf(sl2), 1.17549435e-38f);
-  const float slack = kSlack / sl2;  // kSlack in raw score units (may be inf)
+  // kSlack in raw score units, kept finite so that the first tile with a
+  // finite maximum always sets m (-inf + slack stays -inf)
+  const float slack = fminf(kSlack / sl2, 3.40282347e38f);
 
   // both tiles row-major; V rows are padded differently from K rows so that
   // the transposing reads of V (4 rows x 32 bytes per 16 lanes) and the

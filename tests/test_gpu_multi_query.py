@@ -176,3 +176,17 @@ def test_few_rows_per_kv_head(G, Hkv, maxq, ps, B):
     q_lens = [min(L, maxq - (i % 2)) for i, L in enumerate(lens)]
     base = make_private_case(f"mq-few-{G}-{B}", lens, G * Hkv, Hkv, 128, B, "bf16", G + B)
     compare(make_multi_query_case(base, q_lens, G + B), f"mq few rows G={G} B={B}", ps)
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+@pytest.mark.parametrize("max_q", [40, 5])  # row tiles of 128 rows; the decode walk
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.5])
+def test_negative_zero_and_large_scale(scale, max_q, ps):
+    """The row-tile kernel keeps its running maximum on the raw scores (q
+    carries a negative scale's sign; a zero scale gives every attended
+    position the same weight), and split partials report the maximum in
+    scaled units to the merge."""
+    base = make_private_case("mq-scale", [77, 300, 129, 530], 8, 2, 128, 16, "bf16", 31,
+                             scale=scale)
+    c = make_multi_query_case(base, [max_q, max_q, 1, max_q], 31)
+    compare(c, f"mq scale={scale}", ps=ps)
