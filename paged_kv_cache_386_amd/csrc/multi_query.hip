@@ -64,6 +64,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
+// Maximum of x over the lanes n, n + 16, n + 32 and n + 48 (the four lane
+// groups of column n), with gfx950's lane-swap instructions: after
+// v_permlane16_swap on two copies of x, lane l of the pair holds x of lanes
+// l and l ^ 16; after v_permlane32_swap, x of lanes l and l ^ 32.
+__device__ __forceinline__ float group_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -303,14 +316,17 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[r][tb][i]);
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
-        if (cm > m[r] + slack) {  // false while both are -inf
-          const float alpha = __builtin_amdgcn_exp2f((m[r] - cm) * sl2);  // 0 when m was -inf
+        cm = group_max4(cm);
+        // wave-uniform branch (lanes that need no rescale scale by exactly
+        // 1), so the accumulators are updated in place
+        const bool up = cm > m[r] + slack;  // false while both are -inf
+        if (__builtin_amdgcn_ballot_w64(up)) {
+          const float alpha =
+              up ? __builtin_amdgcn_exp2f((m[r] - cm) * sl2) : 1.f;  // 0 when m was -inf
           lsum[r] *= alpha;
 #pragma unroll
           for (int b = 0; b < kDb; ++b) acc[r][b] *= alpha;
-          m[r] = cm;
+          m[r] = up ? cm : m[r];
         }
         const float mu = (m[r] == neg_inf()) ? 0.f : m[r];
 #pragma unroll
