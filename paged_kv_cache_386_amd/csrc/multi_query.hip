@@ -203,29 +203,31 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     return tok <= pos_last ? min((uint32_t)tbl[tok >> lgB], (uint32_t)(nb - 1)) : 0u;
   };
 
-  // global -> registers for the tile at k0 (tokens past pos_last are zero)
+  // global -> registers for the tile at k0.  Thread t takes head_dim chunk
+  // t % (D/8) of tokens t / (D/8) + kTokStep j; a token's K and V rows share
+  // one offset, and the block ids come from LDS in one batch.  Tokens past
+  // pos_last have table entry 0, so every address is a row of the pool;
+  // their V rows are zeroed (p = 0 there, and 0 * NaN would not vanish),
+  // their K rows only meet masked scores.
+  constexpr int kTokStep = kThreads / (D / 8);
   auto load_tile = [&](Regs &T, int k0, const uint32_t *ids) {
+    const int dc = (int)threadIdx.x % (D / 8);
+    const int tt0 = (int)threadIdx.x / (D / 8);
+    uint32_t id[Regs::kKChunks];
+#pragma unroll
+    for (int j = 0; j < Regs::kKChunks; ++j) id[j] = ids[tt0 + kTokStep * j];
+    int64_t off[Regs::kKChunks];
+#pragma unroll
+    for (int j = 0; j < Regs::kKChunks; ++j)
+      off[j] = (int64_t)id[j] * block_elems + head_off +
+               (int64_t)(((k0 + tt0 + kTokStep * j) & bm1) * D + 8 * dc);
+#pragma unroll
+    for (int j = 0; j < Regs::kKChunks; ++j)
+      T.k[j] = *reinterpret_cast<const u32x4 *>(kc + off[j]);
 #pragma unroll
     for (int j = 0; j < Regs::kKChunks; ++j) {
-      const int c = threadIdx.x + kThreads * j;
-      const int tt = c / (D / 8);
-      const int tok = k0 + tt;
-      const int dc = c % (D / 8);
-      T.k[j] = u32x4{0, 0, 0, 0};
-      if (tok <= pos_last)
-        T.k[j] = *reinterpret_cast<const u32x4 *>(kc + ids[tt] * block_elems + head_off +
-                                                  (int64_t)(tok & bm1) * D + 8 * dc);
-    }
-#pragma unroll
-    for (int j = 0; j < Regs::kKChunks; ++j) {
-      const int c = threadIdx.x + kThreads * j;
-      const int tt = c / (D / 8);
-      const int tok = k0 + tt;
-      const int dc = c % (D / 8);
-      T.v[j] = u32x4{0, 0, 0, 0};
-      if (tok <= pos_last)
-        T.v[j] = *reinterpret_cast<const u32x4 *>(vc + ids[tt] * block_elems + head_off +
-                                                  (int64_t)(tok & bm1) * D + 8 * dc);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(vc + off[j]);
+      T.v[j] = k0 + tt0 + kTokStep * j <= pos_last ? v : u32x4{0, 0, 0, 0};
     }
   };
   // registers -> LDS buffer `buf`, both row-major
