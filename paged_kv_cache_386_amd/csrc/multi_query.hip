@@ -277,7 +277,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
       const uint16_t *sv = sv_buf[it & 1];
       const bool masked = k0 + kTk - 1 > pos_first;
 
-      // S^T for each 16-token block tb and row set r
+      // S^T for each 16-token block tb and row set r.  Each product phase
+      // runs at raised wave priority, so that a wave with products to
+      // issue goes ahead of one in its softmax and the matrix cores of the
+      // SIMD stay fed.
+      __builtin_amdgcn_s_setprio(1);
       f32x4 sc[RS][4];
 #pragma unroll
       for (int r = 0; r < RS; ++r)
@@ -295,6 +299,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
             sc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[r][k], sc[r][tb], 0, 0, 0);
         }
       }
+
+      __builtin_amdgcn_s_setprio(0);
 
       // online softmax per row set; then the hi/lo probability operands.
       // The running maximum m is kept on the raw scores (sl2 > 0: q carries
@@ -355,6 +361,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
       }
 
       // O^T += V^T P^T
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int b = 0; b < kDb; ++b) {
 #pragma unroll
@@ -379,6 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (it + 1 < ntiles) {
       store_tile(T, (it + 1) & 1);
       if (threadIdx.x < kTk && it + 2 < ntiles) sbid[it & 1][threadIdx.x] = id_next;
