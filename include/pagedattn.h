@@ -57,7 +57,8 @@ typedef enum pa_status {
   PA_ERR_LAUNCH = -7,      /* the HIP runtime refused the launch */
   PA_ERR_OOM = -8,         /* block manager: no free block left */
   PA_ERR_NO_SEQ = -9,      /* block manager: unknown sequence id */
-  PA_ERR_SEQ_EXISTS = -10  /* block manager: sequence id already in use */
+  PA_ERR_SEQ_EXISTS = -10, /* block manager: sequence id already in use */
+  PA_ERR_INDEX = -11       /* a device index is out of range (only with index checking on) */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -121,7 +122,7 @@ typedef enum pa_dtype {
  * Supported: head_dim 64 or 128; G in {1, 2, 4, 8}; block_size a power of two
  * in [1, 1024]; num_blocks * block_size < 2^31.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
- * PA_ERR_WORKSPACE, PA_ERR_LAUNCH.
+ * PA_ERR_WORKSPACE, PA_ERR_LAUNCH; PA_ERR_INDEX with index checking on.
  */
 int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v_cache,
                                const int32_t *block_tables, const int32_t *context_lens,
@@ -246,7 +247,7 @@ int32_t paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  * Supported: dtype PA_BF16; head_dim 64 or 128; any G; block_size a power of
  * two in [1, 1024].
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED,
- * PA_ERR_WORKSPACE, PA_ERR_LAUNCH.
+ * PA_ERR_WORKSPACE, PA_ERR_LAUNCH; PA_ERR_INDEX with index checking on.
  */
 int32_t paged_attention_multi_query(const void *q, const void *k_cache, const void *v_cache,
                                     const int32_t *block_tables, const int32_t *context_lens,
@@ -291,7 +292,8 @@ size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_
  *   v_cache        device pool (layout above), modified in place
  * dtype may also be PA_FP8_E4M3 or PA_INT8 (codes copied as bytes).  A head row
  * (head_dim elements) must be a multiple of 16 bytes.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH; PA_ERR_INDEX
+ * with index checking on.
  */
 int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
                        int32_t num_tokens, void *k_cache, void *v_cache,
@@ -312,7 +314,8 @@ int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping
  *   k_cache,
  *   v_cache        device FP8 pool (layout above), modified in place
  * head_dim must be a multiple of 16; scales finite and > 0.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH; PA_ERR_INDEX
+ * with index checking on.
  */
 int32_t kv_cache_write_fp8(const void *k, const void *v, const int32_t *slot_mapping,
                            int32_t num_tokens, void *k_cache, void *v_cache, int32_t num_blocks,
@@ -348,12 +351,41 @@ int32_t kv_cache_write_int8(const void *k, const void *v, const int32_t *slot_ma
  *   host_pairs     optional host copy of the same pairs for the alias check
  * dtype is that of the pool (8-bit kinds included); a head row must be a
  * multiple of 16 bytes.
- * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIAS, PA_ERR_LAUNCH.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIAS, PA_ERR_LAUNCH;
+ * PA_ERR_INDEX with index checking on.
  */
 int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cache,
                     void *v_cache, int32_t num_blocks, int32_t block_size,
                     int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                     const int32_t *host_pairs, void *stream);
+
+/*
+ * Index checking -- a debug mode, off by default.  It is on when the
+ * environment variable PAGEDATTN_CHECK is "1" at the library's first call
+ * that consults it, or after pagedattn_set_index_check(1) (0 turns it off).
+ * While it is on, before launching anything:
+ *   paged_attention_decode (_fp8, _int8) and paged_attention_multi_query
+ *     check every context length in [0, max_context_len] and, for each
+ *     sequence, block_tables entries 0 .. ceil(L/block_size)-1 in
+ *     [0, num_blocks);
+ *   paged_attention_multi_query also checks query_start[0] == 0,
+ *     query_start non-decreasing, query_start[num_seqs] <= num_tokens and
+ *     every chunk at most its context length and max_query_len;
+ *   kv_cache_write (_fp8, _int8) checks every slot < num_blocks*block_size
+ *     (negative slots are padding);
+ *   copy_blocks checks both ids of every pair in [0, num_blocks).
+ * A check runs one small kernel on the call's stream, synchronises that
+ * stream and reads back one device word the library owns (one per device;
+ * calls that overlap on one device race on it); on a bad index the call
+ * returns PA_ERR_INDEX and launches nothing.  Not for graph capture.  With
+ * checking off, the kernels clamp block ids into the pool and skip slots and
+ * pairs outside it, so every access stays in bounds and the results for such
+ * inputs are unspecified ([P1] section 2.1: every logical block maps through
+ * the table to a physical block of the pool).
+ */
+void pagedattn_set_index_check(int32_t enable);
+/* 1 while index checking is on, else 0. */
+int32_t pagedattn_index_check(void);
 
 /* A static English description of a pa_status value. */
 const char *pagedattn_status_string(int32_t status);

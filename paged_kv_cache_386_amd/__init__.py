@@ -13,9 +13,11 @@ from ._lib import (  # noqa: F401
     PA_BF16,
     PA_F32,
     PA_FP8_E4M3,
+    PA_ERR_INDEX,
     PA_INT8,
     PagedAttnError,
     copy_blocks,
+    index_check,
     kv_cache_write,
     kv_cache_write_fp8,
     kv_cache_write_int8,
@@ -28,5 +30,6 @@ from ._lib import (  # noqa: F401
     paged_attention_decode_int8,
     paged_attention_multi_query,
     partition_tokens,
+    set_index_check,
     workspace_size,
 )

@@ -22,8 +22,9 @@ PA_OK = 0
 STATUS_NAMES = {
     0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
     -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_ALIAS", -7: "PA_ERR_LAUNCH",
-    -8: "PA_ERR_OOM", -9: "PA_ERR_NO_SEQ", -10: "PA_ERR_SEQ_EXISTS",
+    -8: "PA_ERR_OOM", -9: "PA_ERR_NO_SEQ", -10: "PA_ERR_SEQ_EXISTS", -11: "PA_ERR_INDEX",
 }
+PA_ERR_INDEX = -11
 
 # exported symbol -> (restype, argtypes)
 _VP = ctypes.c_void_p
@@ -55,6 +56,8 @@ SIGNATURES = {
     "kv_cache_write": (_I32, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
     "copy_blocks": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
     "pagedattn_status_string": (ctypes.c_char_p, [_I32]),
+    "pagedattn_set_index_check": (None, [_I32]),
+    "pagedattn_index_check": (_I32, []),
     # block manager (include/pagedattn_blocks.h)
     "pa_bm_create": (_VP, [_I32, _I32]),
     "pa_bm_destroy": (None, [_VP]),
@@ -133,6 +136,18 @@ def _ptr(t) -> int:
 def _check(fn: str, status: int) -> None:
     if status != PA_OK:
         raise PagedAttnError(fn, status)
+
+
+def set_index_check(enable: bool) -> None:
+    """Turn the library's index checking (a debug mode) on or off: while on,
+    calls check the indices their kernels would read and raise
+    PagedAttnError(PA_ERR_INDEX) instead of launching when one is out of
+    range."""
+    lib().pagedattn_set_index_check(1 if enable else 0)
+
+
+def index_check() -> bool:
+    return bool(lib().pagedattn_index_check())
 
 
 def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

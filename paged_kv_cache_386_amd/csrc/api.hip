@@ -180,6 +180,7 @@ const char *pagedattn_status_string(int32_t status) {
     case PA_ERR_UNSUPPORTED: return "head_dim or query-group size not compiled in";
     case PA_ERR_WORKSPACE: return "split-K workspace missing or too small";
     case PA_ERR_ALIAS: return "copy pairs overlap (a dst repeats or is also a src)";
+    case PA_ERR_INDEX: return "an index read on the device is out of range (index checking)";
     case PA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
     case PA_ERR_OOM: return "no free KV block left";
     case PA_ERR_NO_SEQ: return "unknown sequence id";
@@ -292,6 +293,12 @@ int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
   // with room for it, the longest-first list; else the fixed order
   if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order)
     a.order = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + w.partials);
+  if (pa::index_check_on()) {
+    const int32_t st = pa::check_tables(context_lens, block_tables, num_seqs, max_blocks_per_seq,
+                                        a.log2_block_size, num_blocks, max_context_len,
+                                        static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+  }
   const hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -359,6 +366,11 @@ int32_t write_q8(const void *k, const void *v, const int32_t *slot_mapping, int3
   if ((int64_t)num_kv_heads * head_dim / 16 > (int64_t)128 * 65535) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  if (pa::index_check_on()) {
+    const int32_t st = pa::check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size,
+                                       static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+  }
   const hipError_t e = pa::launch_kv_cache_write_q8(
       k, v, slot_mapping, num_tokens, k_cache, v_cache, (int64_t)num_blocks * block_size,
       log2_exact(block_size), num_kv_heads, head_dim, src_dtype, kv_dtype, k_scale, v_scale,
@@ -457,6 +469,15 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
   // with room for it, the longest-first list; else the fixed order
   if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order)
     a.order = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + w.partials);
+  if (pa::index_check_on()) {
+    const hipStream_t st_stream = static_cast<hipStream_t>(stream);
+    int32_t st = pa::check_tables(context_lens, block_tables, num_seqs, max_blocks_per_seq,
+                                  a.log2_block_size, num_blocks, max_context_len, st_stream);
+    if (st == PA_OK)
+      st = pa::check_queries(context_lens, query_start, num_seqs, num_tokens, max_query_len,
+                             st_stream);
+    if (st != PA_OK) return st;
+  }
   const hipError_t e = pa::launch_multi_query(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -477,6 +498,11 @@ int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping
   const int64_t row_bytes = (int64_t)num_kv_heads * head_row_bytes;
   // the grid covers a token's rows in stripes of 128 vectors
   if (row_bytes / 16 > (int64_t)128 * 65535) return PA_ERR_SHAPE;
+  if (pa::index_check_on()) {
+    const int32_t st = pa::check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size,
+                                       static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+  }
   const hipError_t e = pa::launch_kv_cache_write(
       k, v, slot_mapping, num_tokens, k_cache, v_cache, (int64_t)num_blocks * block_size,
       log2_exact(block_size), num_kv_heads, head_row_bytes, static_cast<hipStream_t>(stream));
@@ -518,6 +544,11 @@ int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cac
     delete[] is_dst;
     delete[] is_src;
     if (status != PA_OK) return status;
+  }
+  if (pa::index_check_on()) {
+    const int32_t st =
+        pa::check_pairs(src_dst_pairs, num_pairs, num_blocks, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
   }
   const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes(dtype);
   const hipError_t e = pa::launch_copy_blocks(src_dst_pairs, num_pairs, k_cache, v_cache,

@@ -112,6 +112,21 @@ hipError_t launch_kv_cache_write_q8(const void *k, const void *v, const int32_t 
                                     int32_t kv_dtype, float k_scale, float v_scale,
                                     hipStream_t stream);
 
+// Index checking (checks.hip): on when PAGEDATTN_CHECK=1 at first use or
+// after pagedattn_set_index_check(1).  Each check enqueues one workgroup on
+// `stream`, synchronises it and returns PA_OK, PA_ERR_INDEX or PA_ERR_LAUNCH.
+bool index_check_on();
+void set_index_check(bool on);
+int32_t check_tables(const int32_t *lens, const int32_t *tables, int32_t num_seqs,
+                     int32_t max_blocks_per_seq, int32_t log2_block_size, int32_t num_blocks,
+                     int32_t max_context_len, hipStream_t stream);
+int32_t check_queries(const int32_t *lens, const int32_t *query_start, int32_t num_seqs,
+                      int32_t num_tokens, int32_t max_query_len, hipStream_t stream);
+int32_t check_slots(const int32_t *slots, int32_t num_tokens, int64_t num_slots,
+                    hipStream_t stream);
+int32_t check_pairs(const int32_t *pairs, int32_t num_pairs, int32_t num_blocks,
+                    hipStream_t stream);
+
 hipError_t launch_copy_blocks(const int32_t *pairs, int32_t num_pairs, void *k_cache,
                               void *v_cache, int32_t num_blocks, int64_t block_bytes,
                               hipStream_t stream);

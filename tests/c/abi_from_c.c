@@ -73,6 +73,14 @@ int main(void) {
   CHECK(kv_cache_write_fp8(NULL, NULL, NULL, 1, NULL, NULL, 8, 16, 2, 128, PA_BF16, 0.f, 1.f,
                            NULL) == PA_ERR_SHAPE); /* a zero scale */
   CHECK(strncmp(pagedattn_version(), "libpagedattn", 12) == 0);
+  /* the index-checking switch (a debug mode; no call here reaches a check) */
+  pagedattn_set_index_check(1);
+  CHECK(pagedattn_index_check() == 1);
+  CHECK(kv_cache_write(NULL, NULL, NULL, 1, NULL, NULL, 8, 16, 2, 128, PA_BF16, NULL) ==
+        PA_ERR_NULL);
+  pagedattn_set_index_check(0);
+  CHECK(pagedattn_index_check() == 0);
+  CHECK(strcmp(pagedattn_status_string(PA_ERR_INDEX), "unknown status") != 0);
   printf("ok\n");
   return 0;
 }

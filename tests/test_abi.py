@@ -191,3 +191,30 @@ def test_multi_query_partition_policy():
     assert pa.multi_query_workspace_size(16, 8192, 32, 8, 128, 512, 8192) == 16 * 4
     assert pa.multi_query_workspace_size(2, 10, 32, 8, 128, 5, 100) == 0
     assert pa.multi_query_workspace_size(4, 2048, 32, 8, 128, 512, 8192) == 0  # 512 workgroups
+
+
+def test_index_check_switch():
+    """Index checking is off by default, follows pagedattn_set_index_check,
+    and starts on when PAGEDATTN_CHECK=1 (read in a fresh process)."""
+    import sys
+    from paged_kv_cache_386_amd import _lib
+    lib = _lib.lib()
+    was = lib.pagedattn_index_check()
+    try:
+        lib.pagedattn_set_index_check(1)
+        assert lib.pagedattn_index_check() == 1
+        lib.pagedattn_set_index_check(0)
+        assert lib.pagedattn_index_check() == 0
+    finally:
+        lib.pagedattn_set_index_check(was)
+    assert lib.pagedattn_status_string(_lib.PA_ERR_INDEX) != b"unknown status"
+    code = ("from paged_kv_cache_386_amd import _lib; "
+            "print(_lib.lib().pagedattn_index_check())")
+    for env, want in (("1", "1"), ("0", "0"), (None, "0")):
+        e = dict(os.environ)
+        e.pop("PAGEDATTN_CHECK", None)
+        if env is not None:
+            e["PAGEDATTN_CHECK"] = env
+        out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                             check=True, cwd=ROOT, env=e).stdout.strip()
+        assert out == want, (env, out)
