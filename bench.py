@@ -20,7 +20,10 @@ attended token here, plus q, out, tables and partials); `unique_gbps` is the
 same call priced with the unique bytes, and `traffic` the bytes the rocprofv3
 FETCH_SIZE/WRITE_SIZE counters saw per decode call, scaled by what the same
 counters read for a copy of known size (`--copy-calibration`), when the
-committed counter summary was taken on the current decode sources.
+committed counter summary was taken on the current decode sources;
+`traffic_gbps` and `traffic_frac` price the call with those measured bytes
+(the HBM side: with shared prefixes the attended rate counts re-reads that
+the caches serve and can approach or pass the HBM peak).
 
 Other modes:
   --copy-calibration      also run one copy_blocks call over a 1 GiB pool first
@@ -763,6 +766,7 @@ def main() -> int:
     # call over its duration; the unique-slot rate (the least HBM must
     # deliver) and the measured counter traffic sit beside it
     achieved = dec_attended / (dec_us * 1e-6) / 1e9
+    traffic = load_traffic(workload)
 
     rec = {
         "metric": METRIC,
@@ -801,10 +805,15 @@ def main() -> int:
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": load_traffic(workload),
+            "traffic": traffic,
             "algorithmic_bytes_per_call": dec_attended,
             "unique_bytes_per_call": dec_unique,
             "unique_gbps": round(dec_unique / (dec_us * 1e-6) / 1e9, 1),
+            # the HBM side: measured traffic per call over the same duration
+            # (attended bytes above it are re-reads served by the caches)
+            "traffic_gbps": None if traffic is None else round(traffic / (dec_us * 1e-6) / 1e9, 1),
+            "traffic_frac": None if traffic is None else
+                            round(traffic / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         },
         "wall_s_timed": round(wall, 3),
     }
