@@ -118,6 +118,17 @@ def test_longctx_small_both_block_sizes():
     assert np.abs(outs[0] - outs[1]).max() <= 2 * TOL["bf16"]
 
 
+@pytest.mark.parametrize("B,L,ps", [(16, 131072, 0), (1024, 131071, 0), (16, 131071, -1),
+                                     (64, 131072, 128)])
+def test_very_long_single_context(B, L, ps):
+    """One sequence of about 2^17 tokens (GQA group of 8 on one KV head): the
+    automatic policy cuts it into 256 partitions of 512 tokens, an explicit
+    128-token partition into 1024, and a ragged length ends mid-block; also
+    the whole context in one workgroup (never split)."""
+    c = make_private_case(f"long1-B{B}-L{L}", [L], 8, 1, 128, B, "bf16", 41)
+    run_and_compare(c, c.name, ps)
+
+
 # ---------------------------------------------------------------- shared blocks
 
 @pytest.mark.parametrize("ps", [0, 32, 64])
