@@ -298,6 +298,7 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
   // num_kv_heads is a multiple of 8.
   const int kvh = blockIdx.x % hkv;
   const int item = order ? order[blockIdx.x / hkv] : (int)(blockIdx.x / hkv);
+  if (item < 0) return;  // listed as empty (past the sequence's end)
   const int s = item % num_seqs;
   const int p = (P - 1) - item / num_seqs;
   const int hq = hkv * G;

@@ -442,6 +442,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   // longest-first list or the fixed order (as in decode.hip)
   const int kvh = id % hkv;
   const int item = order ? order[id / hkv] : id / hkv;
+  if (item < 0) return;  // listed as empty (past the sequence's end)
   const int s = item % num_seqs;
   const int p = (P - 1) - item / num_seqs;
   const int hq = hkv * (MQ ? gh : G);

@@ -36,7 +36,8 @@ struct DecodeArgs {
 constexpr int64_t kScheduleMinWorkgroups = 1024;
 bool schedule_wanted(int64_t workgroups, int64_t num_seqs, int64_t P);
 // Writes order[0 .. S*P-1] (schedule.hip): the (sequence, partition) items
-// c (sequence c % S, partition P - 1 - c / S), longest first; ps = tokens
+// c (sequence c % S, partition P - 1 - c / S), longest first, those past a
+// sequence's last partition last and as ~c (negative); ps = tokens
 // per partition, cap = the most tokens a sequence may have.  launch_decode
 // and launch_multi_query call it when their args carry an order buffer.
 hipError_t launch_schedule(const int32_t *context_lens, int32_t *order, int num_seqs, int P,

@@ -123,6 +123,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   const int kvh = r % hkv;
   const int num_seqs = units / (hkv * P);
   const int item = order ? order[r / hkv] : r / hkv;
+  if (item < 0) return;  // listed as empty (past the sequence's end)
   const int s = item % num_seqs;
   const int part = (P - 1) - item / num_seqs;
   const int hq = hkv * G;

@@ -11,7 +11,9 @@
 // consecutive workgroups, as in the fixed order.
 //
 // Item c (c < num_seqs * P) is sequence c % num_seqs and partition
-// P - 1 - c / num_seqs -- the fixed order's numbering.  Items are bucketed by
+// P - 1 - c / num_seqs -- the fixed order's numbering; an item past its
+// sequence's last partition is listed as ~c, so that its workgroups exit
+// without reading the context length.  Items are bucketed by
 // token count (512 size classes of 2^shift tokens, longest class first; an
 // item past the sequence's last partition, which does no work, sorts last)
 // with a counting sort in LDS that keeps, within a class, the fixed order
@@ -116,7 +118,9 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
   // hardware serves them)
   for (int c = begin + lane; c < end; c += 64) {
     const int k = c < kKeptClasses ? (int)kept[c] : size_class(c);
-    order[atomicAdd(&start[k][wave], 1)] = c;
+    // items with no tokens are listed as ~c (negative): their workgroups
+    // exit on the list entry alone
+    order[atomicAdd(&start[k][wave], 1)] = k == kSizeClasses ? ~c : c;
   }
 }
 

@@ -173,7 +173,8 @@ def test_list_is_longest_first_permutation(S, Hkv, ps, top):
     """The list in the workspace (after the partials) holds every (sequence,
     partition) item once, in non-increasing size class (tokens >> shift, the
     classes 2^shift tokens wide with fewer than 512 of them over a
-    partition), items past a sequence's last partition at the end."""
+    partition), items past a sequence's last partition at the end, listed
+    as ~c (negative) so that their workgroups exit at once."""
     import paged_kv_cache_386_amd as pa
     G, D = 4, 128
     lens = _mixed_lengths(S, 41 + S, top)
@@ -186,7 +187,8 @@ def test_list_is_longest_first_permutation(S, Hkv, ps, top):
     ws = torch.empty(full, dtype=torch.uint8, device="cuda")
     dc.run_decode(ps, workspace=ws)
     torch.cuda.synchronize()
-    order = ws[partial:].cpu().numpy().view(np.int32)
+    listed = ws[partial:].cpu().numpy().view(np.int32)
+    order = np.where(listed < 0, ~listed, listed)
     assert np.array_equal(np.sort(order), np.arange(S * P))
     cap = c.block_tables.shape[1] * c.block_size
     tokens_per_part = pa.partition_tokens(S, Hkv, c.max_context_len, ps) if P > 1 else cap
@@ -200,3 +202,4 @@ def test_list_is_longest_first_permutation(S, Hkv, ps, top):
     tok = np.minimum(L, (p + 1) * tokens_per_part) - p * tokens_per_part
     key = np.where(p < np.maximum(nparts, 1), tok >> shift, -1)
     assert (np.diff(key) <= 0).all(), "not longest first"
+    assert np.array_equal(listed < 0, key < 0), "empty items are the negative entries"
