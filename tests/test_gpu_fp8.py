@@ -145,6 +145,20 @@ def test_decode_matches_oracle(G, Hkv, B):
         assert err <= TOL["bf16"], f"G={G} B={B} ps={ps}: {err}"
 
 
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("ps", [-1, 0])
+def test_long_contexts_one_workgroup(G, Hkv, ps):
+    """Contexts of 9,000 and 20,001 tokens: unsplit, a wave walks more than
+    64 tiles, so its block ids come in several 64-tile chunks, with a ragged
+    last tile (for G <= 4 through the three-buffer walk of 8-bit pools)."""
+    base = make_private_case(f"f8-long-{G}", [9000, 20001], G * Hkv, Hkv, 128, 16, "bf16",
+                             50 + G)
+    c8 = make_fp8_case(base, 50 + G)
+    say(f"fp8 long contexts G={G} ps={ps}")
+    err = max_err(run_decode_fp8(c8, ps), oracle_decode(c8))
+    assert err <= TOL["bf16"], f"G={G} ps={ps}: {err}"
+
+
 def test_decode_large_codes_and_prefix_sharing():
     """Codes over the whole E4M3 range (to 448) on a prefix-shared pool."""
     from workloads import make_prefix_case
