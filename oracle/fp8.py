@@ -24,7 +24,9 @@ scale scheme, so this oracle fixes the plainest one:
 Pinned in ``tests/test_oracle_fp8.py`` against torch's float8_e4m3fn
 conversions (every code, and many fp32 values including every tie), against
 the bf16 decode oracle on pools whose dequantised values are exact in bf16,
-and against closed forms.
+and against closed forms; the multi-query function against the bf16
+multi-query oracle on such pools and against the FP8 decode for one token per
+sequence.
 """
 from __future__ import annotations
 
@@ -147,4 +149,37 @@ def paged_attention_decode_fp8(q: np.ndarray, k_cache: np.ndarray, v_cache: np.n
         for g in range(Hkv):
             out[s, g * G:(g + 1) * G] = dense_attention(qf[s, g * G:(g + 1) * G], K[:, g],
                                                         V[:, g], sc)
+    return out
+
+
+def paged_attention_multi_query_fp8(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                                    block_tables: np.ndarray, context_lens: np.ndarray,
+                                    query_start: np.ndarray, scale: float, block_size: int,
+                                    q_dtype: str, k_scale: float, v_scale: float) -> np.ndarray:
+    """Causal multi-query attention over an FP8 pool: the definition of
+    ``oracle.paged_attention_multi_query`` (sequence s's n rows are its last n
+    positions; row i attends positions [0, L - n + i]) with K/V read as the
+    dequantised codes e4m3(c) * scale.  Returns float64 ``[T, Hq, D]``."""
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    qf = to_f64(q, q_dtype)
+    sc = np.float64(np.float32(scale))
+    out = np.zeros((T, Hq, D), np.float64)
+    starts = np.asarray(query_start).tolist()
+    for s in range(len(starts) - 1):
+        n = starts[s + 1] - starts[s]
+        if n == 0:
+            continue
+        L = int(context_lens[s])
+        if n > L:
+            raise ValueError("a chunk is longer than its sequence's context")
+        K, V = gather_sequence_fp8(k_cache, v_cache, block_tables[s], L, block_size, k_scale,
+                                   v_scale)
+        for i in range(n):
+            p = L - n + i
+            row = starts[s] + i
+            for g in range(Hkv):
+                out[row, g * G:(g + 1) * G] = dense_attention(
+                    qf[row, g * G:(g + 1) * G], K[:p + 1, g], V[:p + 1, g], sc)
     return out

@@ -123,3 +123,29 @@ def test_identical_keys_and_one_token():
     # the one-token sequence returns its dequantised V row exactly
     v0 = fp8.dequantize(c8.v8[base.block_tables[0, 0], :, 0], c8.v_scale)
     assert np.array_equal(out[0], np.repeat(v0, 2, axis=0))
+
+
+def test_multi_query_fp8_pins():
+    """The FP8 multi-query oracle against two pinned oracles: on pools whose
+    dequantised values are exact in bf16 it equals the bf16 multi-query
+    oracle on those values, and one query token per sequence (attending the
+    whole context) equals the FP8 decode oracle."""
+    from workloads import make_multi_query_case
+    base = make_private_case("f8mq", [5, 17, 40, 100], 8, 2, 16, 4, "bf16", 6)
+    c8 = make_fp8_case(base, 6, k_scale=0.25, v_scale=2.0)
+    kb, vb = _bf16_twin(c8)
+    mq = make_multi_query_case(base, [5, 3, 0, 7], 6)
+    want = O.paged_attention_multi_query(mq.q, kb, vb, base.block_tables, base.context_lens,
+                                         mq.query_start, base.scale, base.block_size, "bf16")
+    got = fp8.paged_attention_multi_query_fp8(mq.q, c8.k8, c8.v8, base.block_tables,
+                                              base.context_lens, mq.query_start, base.scale,
+                                              base.block_size, "bf16", c8.k_scale, c8.v_scale)
+    assert np.abs(got - want).max() < 1e-12
+    one = make_multi_query_case(base, [1, 1, 1, 1], 7)
+    got1 = fp8.paged_attention_multi_query_fp8(one.q, c8.k8, c8.v8, base.block_tables,
+                                               base.context_lens, one.query_start, base.scale,
+                                               base.block_size, "bf16", c8.k_scale, c8.v_scale)
+    dec = fp8.paged_attention_decode_fp8(one.q, c8.k8, c8.v8, base.block_tables,
+                                         base.context_lens, base.scale, base.block_size, "bf16",
+                                         c8.k_scale, c8.v_scale)
+    assert np.array_equal(got1, dec)
