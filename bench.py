@@ -499,7 +499,21 @@ def multi_query_bench(args) -> int:
     c = make_multi_query_workload(args.multi_query, poison=False)
     b = c.base
     q = to_dev(c.q, dev)
-    kc, vc = to_dev(b.k_cache, dev), to_dev(b.v_cache, dev)
+    c8 = None
+    if args.kv_int8:
+        print("--kv-int8 is not available with --multi-query", file=sys.stderr)
+        return 2
+    if args.kv_fp8:
+        if args.multi_query != "spec-verify":
+            print("--kv-fp8 with --multi-query: spec-verify only (FP8 multi-query runs at most "
+                  "64 rows per KV head)", file=sys.stderr)
+            return 2
+        from workloads.generate import make_fp8_case
+        c8 = make_fp8_case(b, 71)
+        kc = torch.from_numpy(c8.k8).to(dev)
+        vc = torch.from_numpy(c8.v8).to(dev)
+    else:
+        kc, vc = to_dev(b.k_cache, dev), to_dev(b.v_cache, dev)
     tables = torch.from_numpy(b.block_tables).to(dev)
     lens = torch.from_numpy(b.context_lens).to(dev)
     qs = torch.from_numpy(c.query_start).to(dev)
@@ -513,10 +527,17 @@ def multi_query_bench(args) -> int:
         max_ctx, args.partition_size), 1), dtype=torch.uint8, device=dev)
 
     def call():
-        pa.paged_attention_multi_query(q, kc, vc, tables, lens, qs, float(b.scale), out,
-                                       max_query_len=c.max_query_len, max_context_len=max_ctx,
-                                       partition_size=args.partition_size, workspace=ws,
-                                       stream=stream)
+        if c8 is not None:
+            pa.paged_attention_multi_query_fp8(
+                q, kc, vc, tables, lens, qs, float(b.scale), float(c8.k_scale),
+                float(c8.v_scale), out, max_query_len=c.max_query_len, max_context_len=max_ctx,
+                partition_size=args.partition_size, workspace=ws, stream=stream)
+        else:
+            pa.paged_attention_multi_query(q, kc, vc, tables, lens, qs, float(b.scale), out,
+                                           max_query_len=c.max_query_len,
+                                           max_context_len=max_ctx,
+                                           partition_size=args.partition_size, workspace=ws,
+                                           stream=stream)
 
     for _ in range(args.warmup):
         call()
@@ -540,7 +561,7 @@ def multi_query_bench(args) -> int:
         attended += sum(L - n + i + 1 for i in range(n))
         kv_tokens += L if n else 0
     flops = attended * Hq * 4 * D
-    kv_bytes = kv_tokens * Hkv * D * 2 * 2
+    kv_bytes = kv_tokens * Hkv * D * 2 * (1 if c8 is not None else 2)
     io_bytes = c.num_tokens * Hq * D * (2 + 4) + b.block_tables.nbytes + 8 * b.num_seqs
     tflops = flops / (us * 1e-6) / 1e12
     gbps = (kv_bytes + io_bytes) / (us * 1e-6) / 1e9
@@ -558,9 +579,12 @@ def multi_query_bench(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) q/K/V; lengths as described)",
-        "config": {"workload": f"{args.multi_query}: {MULTI_QUERY_NAMES[args.multi_query]}",
+        "dtype": "bf16" if c8 is None else "fp8-e4m3 (bf16 q)",
+        "data": "synthetic (seeded N(0,1) q/K/V; lengths as described)" + (
+            "" if c8 is None else f"; K/V as random E4M3 codes, k_scale {float(c8.k_scale)}, "
+                                  f"v_scale {float(c8.v_scale)}"),
+        "config": {"workload": f"{args.multi_query}: {MULTI_QUERY_NAMES[args.multi_query]}"
+                               + (" over an FP8 pool" if c8 is not None else ""),
                    "num_seqs": b.num_seqs, "num_tokens": c.num_tokens,
                    "max_query_len": c.max_query_len, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": b.block_size,
@@ -681,6 +705,9 @@ def main() -> int:
         copy_calibration(dev)
 
     c8 = None
+    if args.kv_int8:
+        print("--kv-int8 is not available with --multi-query", file=sys.stderr)
+        return 2
     if args.kv_fp8:
         from workloads import make_fp8_case
         c8 = make_fp8_case(case, args.config)

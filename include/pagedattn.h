@@ -276,6 +276,29 @@ size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_
                                                   int32_t partition_size);
 
 /*
+ * paged_attention_multi_query_fp8 -- paged_attention_multi_query over an FP8
+ * (E4M3) pool, as paged_attention_decode_fp8 reads it: a stored code c means
+ * e4m3(c) * k_scale (K) or * v_scale (V), widened exactly to bfloat16 for the
+ * products ([P1] sections 5.3 and 5.4: FP8 KV cache, speculative decoding).
+ * Arguments as in paged_attention_multi_query, with q in bfloat16 and
+ * k_cache, v_cache one code per byte; k_scale, v_scale finite and > 0.
+ * Supported: head_dim 128 and at most 64 (token, head) rows per KV head
+ * (max_query_len * G <= 64: verification-sized chunks, on the decode
+ * kernel's walk); longer chunks give PA_ERR_UNSUPPORTED.
+ * Errors: as paged_attention_multi_query.
+ */
+int32_t paged_attention_multi_query_fp8(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *block_tables, const int32_t *context_lens,
+                                        const int32_t *query_start, float scale, float k_scale,
+                                        float v_scale, float *out, int32_t num_seqs,
+                                        int32_t num_tokens, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, int32_t max_blocks_per_seq,
+                                        int32_t max_query_len, int32_t max_context_len,
+                                        int32_t partition_size, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+/*
  * kv_cache_write -- store each new token's K and V rows in the pool.
  *
  * For i in [0, num_tokens) with slot = slot_mapping[i] >= 0: copies

@@ -398,15 +398,22 @@ int32_t kv_cache_write_int8(const void *k, const void *v, const int32_t *slot_ma
                   num_kv_heads, head_dim, src_dtype, PA_INT8, k_scale, v_scale, stream);
 }
 
-int32_t paged_attention_multi_query(const void *q, const void *k_cache, const void *v_cache,
-                                    const int32_t *block_tables, const int32_t *context_lens,
-                                    const int32_t *query_start, float scale, float *out,
-                                    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
-                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                    int32_t num_blocks, int32_t max_blocks_per_seq,
-                                    int32_t max_query_len, int32_t max_context_len,
-                                    int32_t dtype, int32_t partition_size, void *workspace,
-                                    size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Multi-query attention over a pool of kv_dtype (dtype for a bf16 pool,
+// PA_FP8_E4M3 with bf16 queries); the checks and launch shared by both entry
+// points.
+int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, const int32_t *context_lens,
+                         const int32_t *query_start, float scale, float *out, int32_t num_seqs,
+                         int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t max_query_len,
+                         int32_t max_context_len, int32_t dtype, int32_t kv_dtype, float k_scale,
+                         float v_scale, int32_t partition_size, void *workspace,
+                         size_t workspace_bytes, void *stream) {
   if (!known_dtype(dtype)) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0 ||
@@ -419,6 +426,14 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
     return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
   if (!pa::multi_query_supported(dtype, head_dim)) return PA_ERR_UNSUPPORTED;
+  if (kv_dtype == PA_FP8_E4M3) {
+    // the decode walk only: bf16 queries, head_dim 128, at most 64 (token,
+    // head) rows per KV head
+    if (dtype != PA_BF16 || head_dim != 128 ||
+        (int64_t)max_query_len * (num_q_heads / num_kv_heads) > pa::kMqFewRows)
+      return PA_ERR_UNSUPPORTED;
+    if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_SHAPE;
+  }
   const int64_t G = num_q_heads / num_kv_heads;
   const int64_t rows = (int64_t)max_query_len * G;
   const int64_t tiles = (rows + 63) / 64;
@@ -462,6 +477,9 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_query_len = max_query_len;
   a.dtype = dtype;
+  a.kv_dtype = kv_dtype;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.partition_size = ps;
   a.num_partitions = P;
   a.ws_o = ws_o;
@@ -481,6 +499,43 @@ int32_t paged_attention_multi_query(const void *q, const void *k_cache, const vo
   const hipError_t e = pa::launch_multi_query(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_attention_multi_query(const void *q, const void *k_cache, const void *v_cache,
+                                    const int32_t *block_tables, const int32_t *context_lens,
+                                    const int32_t *query_start, float scale, float *out,
+                                    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_blocks_per_seq,
+                                    int32_t max_query_len, int32_t max_context_len,
+                                    int32_t dtype, int32_t partition_size, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  return multi_query_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                          out, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_blocks_per_seq, max_query_len,
+                          max_context_len, dtype, dtype, 1.f, 1.f, partition_size, workspace,
+                          workspace_bytes, stream);
+}
+
+int32_t paged_attention_multi_query_fp8(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *block_tables, const int32_t *context_lens,
+                                        const int32_t *query_start, float scale, float k_scale,
+                                        float v_scale, float *out, int32_t num_seqs,
+                                        int32_t num_tokens, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, int32_t max_blocks_per_seq,
+                                        int32_t max_query_len, int32_t max_context_len,
+                                        int32_t partition_size, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+  return multi_query_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                          out, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_blocks_per_seq, max_query_len,
+                          max_context_len, PA_BF16, PA_FP8_E4M3, k_scale, v_scale,
+                          partition_size, workspace, workspace_bytes, stream);
 }
 
 int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,

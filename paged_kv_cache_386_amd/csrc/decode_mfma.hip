@@ -746,8 +746,10 @@ hipError_t launch_b(const DecodeArgs &a, hipStream_t stream) {
   return launch_typed<G, true, Q8>(a, stream);
 }
 
-template <bool SMALLB>
+template <bool SMALLB, int Q8>
 hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
+  using KV = typename MfmaDecode<16, SMALLB, Q8>::KV;
+  constexpr bool FP8 = Q8 != 0;
   const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
   if (items <= 0) return hipSuccess;
   const int gh = a.num_q_heads / a.num_kv_heads;
@@ -755,12 +757,14 @@ hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
   // two column sets per wave from 17 rows up (one pass over K/V for 32
   // columns), one otherwise
   const int64_t grid = (items + 7) / 8 * 8 * multi_query_few_rows_groups(csets);
-  auto kernel = csets >= 2 ? paged_decode_mfma_kernel<16, SMALLB, 0, true, 2>
-                           : paged_decode_mfma_kernel<16, SMALLB, 0, true, 1>;
+  auto kernel = csets >= 2 ? paged_decode_mfma_kernel<16, SMALLB, Q8, true, 2>
+                           : paged_decode_mfma_kernel<16, SMALLB, Q8, true, 1>;
+  // as in decode: the K scale joins the softmax scale, the V scale the output
+  const float sl2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
   hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k_cache),
-                     static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
-                     a.out, a.ws_o, a.ws_ml, a.scale * kLog2e, 1.f, a.num_seqs, a.num_kv_heads,
+                     static_cast<const uint16_t *>(a.q), static_cast<const KV *>(a.k_cache),
+                     static_cast<const KV *>(a.v_cache), a.block_tables, a.context_lens, a.out,
+                     a.ws_o, a.ws_ml, sl2, FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads,
                      a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.partition_size,
                      a.num_partitions, a.query_start, a.num_tokens, gh, a.max_query_len, csets,
                      a.order);
@@ -779,8 +783,12 @@ bool multi_query_few_rows_supported(const MultiQueryArgs &a) {
 }
 
 hipError_t launch_multi_query_few_rows(const MultiQueryArgs &a, hipStream_t stream) {
-  if (a.log2_block_size >= 4) return launch_mq<false>(a, stream);
-  return launch_mq<true>(a, stream);
+  if (a.kv_dtype == 2) {  // FP8 E4M3 pool
+    if (a.log2_block_size >= 4) return launch_mq<false, 1>(a, stream);
+    return launch_mq<true, 1>(a, stream);
+  }
+  if (a.log2_block_size >= 4) return launch_mq<false, 0>(a, stream);
+  return launch_mq<true, 0>(a, stream);
 }
 
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
