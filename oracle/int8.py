@@ -91,3 +91,48 @@ def paged_attention_decode_int8(q: np.ndarray, k_cache: np.ndarray, v_cache: np.
             out[s, g * G:(g + 1) * G] = dense_attention(qf[s, g * G:(g + 1) * G], K[:, g],
                                                         V[:, g], sc)
     return out
+
+
+def gather_sequence_int8(k_cache: np.ndarray, v_cache: np.ndarray, table_row: np.ndarray,
+                         context_len: int, block_size: int, k_scale: float,
+                         v_scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Dequantised K and V of one sequence in logical order (float64,
+    ``[L, Hkv, D]``)."""
+    L = int(context_len)
+    pos = np.arange(L)
+    phys = np.asarray(table_row)[pos // block_size]
+    off = pos % block_size
+    return dequantize(k_cache[phys, :, off], k_scale), dequantize(v_cache[phys, :, off], v_scale)
+
+
+def paged_attention_multi_query_int8(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                                     block_tables: np.ndarray, context_lens: np.ndarray,
+                                     query_start: np.ndarray, scale: float, block_size: int,
+                                     q_dtype: str, k_scale: float, v_scale: float) -> np.ndarray:
+    """Causal multi-query attention (the definition of
+    ``oracle.paged_attention_multi_query``: sequence s's n rows are its last n
+    positions, row i attends [0, L - n + i]) over an INT8 pool read as
+    code * scale.  Returns float64 ``[T, Hq, D]``."""
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    qf = to_f64(q, q_dtype)
+    sc = np.float64(np.float32(scale))
+    out = np.zeros((T, Hq, D), np.float64)
+    starts = np.asarray(query_start).tolist()
+    for s in range(len(starts) - 1):
+        n = starts[s + 1] - starts[s]
+        if n == 0:
+            continue
+        L = int(context_lens[s])
+        if n > L:
+            raise ValueError("a chunk is longer than its sequence's context")
+        K, V = gather_sequence_int8(k_cache, v_cache, block_tables[s], L, block_size, k_scale,
+                                    v_scale)
+        for i in range(n):
+            p = L - n + i
+            row = starts[s] + i
+            for g in range(Hkv):
+                out[row, g * G:(g + 1) * G] = dense_attention(
+                    qf[row, g * G:(g + 1) * G], K[:p + 1, g], V[:p + 1, g], sc)
+    return out

@@ -72,3 +72,31 @@ def test_one_token_returns_its_v_row():
                                            "bf16", c8.k_scale, c8.v_scale)
     v0 = int8.dequantize(c8.v8[base.block_tables[0, 0], :, 0], c8.v_scale)
     assert np.array_equal(out[0], np.repeat(v0, 2, axis=0))
+
+
+def test_multi_query_int8_pins():
+    """The INT8 multi-query oracle equals the bf16 multi-query oracle on the
+    dequantised values (exact in bf16 at power-of-two scales), and one token
+    per sequence equals the INT8 decode oracle."""
+    from workloads import make_multi_query_case
+    base = make_private_case("i8mq", [5, 17, 40, 100], 8, 2, 16, 4, "bf16", 8)
+    c8 = make_int8_case(base, 8, k_scale=2.0 ** -5, v_scale=2.0 ** -6)
+    kd, vd = int8.dequantize(c8.k8, c8.k_scale), int8.dequantize(c8.v8, c8.v_scale)
+    kb = bf16_bits_from_f32(kd.astype(np.float32))
+    vb = bf16_bits_from_f32(vd.astype(np.float32))
+    mq = make_multi_query_case(base, [5, 3, 0, 7], 8)
+    want = O.paged_attention_multi_query(mq.q, kb, vb, base.block_tables, base.context_lens,
+                                         mq.query_start, base.scale, base.block_size, "bf16")
+    got = int8.paged_attention_multi_query_int8(mq.q, c8.k8, c8.v8, base.block_tables,
+                                                base.context_lens, mq.query_start, base.scale,
+                                                base.block_size, "bf16", c8.k_scale, c8.v_scale)
+    assert np.abs(got - want).max() < 1e-12
+    one = make_multi_query_case(base, [1, 1, 1, 1], 9)
+    got1 = int8.paged_attention_multi_query_int8(one.q, c8.k8, c8.v8, base.block_tables,
+                                                 base.context_lens, one.query_start, base.scale,
+                                                 base.block_size, "bf16", c8.k_scale,
+                                                 c8.v_scale)
+    dec = int8.paged_attention_decode_int8(one.q, c8.k8, c8.v8, base.block_tables,
+                                           base.context_lens, base.scale, base.block_size,
+                                           "bf16", c8.k_scale, c8.v_scale)
+    assert np.array_equal(got1, dec)
