@@ -705,9 +705,6 @@ def main() -> int:
         copy_calibration(dev)
 
     c8 = None
-    if args.kv_int8:
-        print("--kv-int8 is not available with --multi-query", file=sys.stderr)
-        return 2
     if args.kv_fp8:
         from workloads import make_fp8_case
         c8 = make_fp8_case(case, args.config)

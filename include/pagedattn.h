@@ -299,6 +299,23 @@ int32_t paged_attention_multi_query_fp8(const void *q, const void *k_cache, cons
                                         size_t workspace_bytes, void *stream);
 
 /*
+ * paged_attention_multi_query_int8 -- the same over an INT8 pool (a stored
+ * signed code c means c * k_scale or c * v_scale, as in
+ * paged_attention_decode_int8).  Supported and errors as
+ * paged_attention_multi_query_fp8.
+ */
+int32_t paged_attention_multi_query_int8(const void *q, const void *k_cache, const void *v_cache,
+                                         const int32_t *block_tables, const int32_t *context_lens,
+                                         const int32_t *query_start, float scale, float k_scale,
+                                         float v_scale, float *out, int32_t num_seqs,
+                                         int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                         int32_t num_blocks, int32_t max_blocks_per_seq,
+                                         int32_t max_query_len, int32_t max_context_len,
+                                         int32_t partition_size, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/*
  * kv_cache_write -- store each new token's K and V rows in the pool.
  *
  * For i in [0, num_tokens) with slot = slot_mapping[i] >= 0: copies

@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     paged_attention_decode_int8,
     paged_attention_multi_query,
     paged_attention_multi_query_fp8,
+    paged_attention_multi_query_int8,
     partition_tokens,
     set_index_check,
     workspace_size,

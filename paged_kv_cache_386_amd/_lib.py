@@ -40,6 +40,10 @@ SIGNATURES = {
                                                ctypes.c_float, ctypes.c_float, _VP, _I32, _I32,
                                                _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                                _I32, _VP, ctypes.c_size_t, _VP]),
+    "paged_attention_multi_query_int8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float,
+                                                ctypes.c_float, ctypes.c_float, _VP, _I32, _I32,
+                                                _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                _I32, _VP, ctypes.c_size_t, _VP]),
     "paged_attention_multi_query_partitions": (_I32, [_I32] * 6),
     "paged_attention_multi_query_workspace_size": (ctypes.c_size_t, [_I32] * 8),
     "paged_attention_decode_fp8": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float,
@@ -257,12 +261,35 @@ def paged_attention_multi_query_fp8(q, k_cache, v_cache, block_tables, context_l
     codes [NB, Hkv, B, D]); q: bfloat16 [T, Hq, D]; at most 64 (token, head)
     rows per KV head."""
     import torch
+    _multi_query_q8("paged_attention_multi_query_fp8", torch.uint8, q, k_cache, v_cache,
+                    block_tables, context_lens, query_start, scale, k_scale, v_scale, out,
+                    max_query_len, max_context_len, partition_size, workspace, stream)
+
+
+def paged_attention_multi_query_int8(q, k_cache, v_cache, block_tables, context_lens,
+                                     query_start, scale: float, k_scale: float, v_scale: float,
+                                     out, *, max_query_len: int, max_context_len: int,
+                                     partition_size: int = 0, workspace=None,
+                                     stream=None) -> None:
+    """paged_attention_multi_query over an INT8 pool (int8 tensors
+    [NB, Hkv, B, D]); q: bfloat16 [T, Hq, D]; at most 64 (token, head) rows
+    per KV head."""
+    import torch
+    _multi_query_q8("paged_attention_multi_query_int8", torch.int8, q, k_cache, v_cache,
+                    block_tables, context_lens, query_start, scale, k_scale, v_scale, out,
+                    max_query_len, max_context_len, partition_size, workspace, stream)
+
+
+def _multi_query_q8(fn, pool_dtype, q, k_cache, v_cache, block_tables, context_lens,
+                    query_start, scale, k_scale, v_scale, out, max_query_len, max_context_len,
+                    partition_size, workspace, stream) -> None:
+    import torch
     T, Hq, D = q.shape
     NB, Hkv, B, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("q/k_cache/v_cache shapes disagree")
-    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
-        raise TypeError("paged_attention_multi_query_fp8 takes pools of E4M3 codes (uint8)")
+    if k_cache.dtype != pool_dtype or v_cache.dtype != pool_dtype:
+        raise TypeError(f"{fn} takes pools of {pool_dtype}")
     S = context_lens.shape[0]
     if query_start.shape[0] != S + 1:
         raise ValueError("query_start must have num_seqs + 1 entries")
@@ -275,12 +302,12 @@ def paged_attention_multi_query_fp8(q, k_cache, v_cache, block_tables, context_l
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().paged_attention_multi_query_fp8(
+    st = getattr(lib(), fn)(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(query_start), float(scale), float(k_scale), float(v_scale), _ptr(out), S, T, Hq,
         Hkv, D, B, NB, MB, int(max_query_len), int(max_context_len), int(partition_size),
         _ptr(workspace), ws_bytes, _stream(stream))
-    _check("paged_attention_multi_query_fp8", st)
+    _check(fn, st)
 
 
 def _decode_q8(fn: str, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,

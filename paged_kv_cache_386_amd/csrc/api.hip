@@ -403,8 +403,8 @@ int32_t kv_cache_write_int8(const void *k, const void *v, const int32_t *slot_ma
 namespace {
 
 // Multi-query attention over a pool of kv_dtype (dtype for a bf16 pool,
-// PA_FP8_E4M3 with bf16 queries); the checks and launch shared by both entry
-// points.
+// PA_FP8_E4M3 or PA_INT8 with bf16 queries); the checks and launch shared by
+// the entry points.
 int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache,
                          const int32_t *block_tables, const int32_t *context_lens,
                          const int32_t *query_start, float scale, float *out, int32_t num_seqs,
@@ -426,7 +426,7 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
     return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
   if (!pa::multi_query_supported(dtype, head_dim)) return PA_ERR_UNSUPPORTED;
-  if (kv_dtype == PA_FP8_E4M3) {
+  if (is_q8(kv_dtype)) {
     // the decode walk only: bf16 queries, head_dim 128, at most 64 (token,
     // head) rows per KV head
     if (dtype != PA_BF16 || head_dim != 128 ||
@@ -535,6 +535,23 @@ int32_t paged_attention_multi_query_fp8(const void *q, const void *k_cache, cons
                           out, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                           block_size, num_blocks, max_blocks_per_seq, max_query_len,
                           max_context_len, PA_BF16, PA_FP8_E4M3, k_scale, v_scale,
+                          partition_size, workspace, workspace_bytes, stream);
+}
+
+int32_t paged_attention_multi_query_int8(const void *q, const void *k_cache, const void *v_cache,
+                                         const int32_t *block_tables, const int32_t *context_lens,
+                                         const int32_t *query_start, float scale, float k_scale,
+                                         float v_scale, float *out, int32_t num_seqs,
+                                         int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                         int32_t num_blocks, int32_t max_blocks_per_seq,
+                                         int32_t max_query_len, int32_t max_context_len,
+                                         int32_t partition_size, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  return multi_query_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                          out, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_blocks_per_seq, max_query_len,
+                          max_context_len, PA_BF16, PA_INT8, k_scale, v_scale,
                           partition_size, workspace, workspace_bytes, stream);
 }
 

@@ -787,6 +787,10 @@ hipError_t launch_multi_query_few_rows(const MultiQueryArgs &a, hipStream_t stre
     if (a.log2_block_size >= 4) return launch_mq<false, 1>(a, stream);
     return launch_mq<true, 1>(a, stream);
   }
+  if (a.kv_dtype == 3) {  // INT8 pool
+    if (a.log2_block_size >= 4) return launch_mq<false, 2>(a, stream);
+    return launch_mq<true, 2>(a, stream);
+  }
   if (a.log2_block_size >= 4) return launch_mq<false, 0>(a, stream);
   return launch_mq<true, 0>(a, stream);
 }

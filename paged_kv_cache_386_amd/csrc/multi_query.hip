@@ -525,7 +525,8 @@ int64_t multi_query_workgroups(int64_t num_seqs, int64_t num_q_heads, int64_t nu
 
 hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream) {
   // 8-bit pools run only on the decode walk (at most 64 rows per KV head)
-  if (a.kv_dtype == 2 && !multi_query_few_rows_supported(a)) return hipErrorNotSupported;
+  if ((a.kv_dtype == 2 || a.kv_dtype == 3) && !multi_query_few_rows_supported(a))
+    return hipErrorNotSupported;
   if (a.order) {
     const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
                                            INT32_MAX);

@@ -60,3 +60,12 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_bench_option_guards():
+    """Option combinations the benchmark refuses before touching a GPU, and
+    the 8-bit decode modes reaching their own path (no multi-query guard)."""
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    body = src[src.index("def multi_query_bench"):src.index("def main")]
+    assert "--kv-int8 is not available with --multi-query" in body
+    assert src.count("--kv-int8 is not available with --multi-query") == 1

@@ -153,3 +153,34 @@ def test_full_size_prefix_workload_sampled():
     ref = oracle_decode(c8, rows=rows)
     err = max_err(np.array([got[s, h] for s, h in rows]), ref)
     assert err <= TOL["bf16"], err
+
+
+# ---------------------------------------------------------------- multi-query
+
+@pytest.mark.parametrize("G,Hkv,q_lens", [(4, 2, [5, 1, 0, 16]), (8, 1, [8, 3, 1, 5]),
+                                          (1, 4, [40, 64, 2, 17])])
+@pytest.mark.parametrize("B", [16, 4])
+@pytest.mark.parametrize("ps", [0, 64])
+def test_multi_query_matches_oracle(G, Hkv, q_lens, B, ps):
+    import paged_kv_cache_386_amd as pa
+    from workloads import make_multi_query_case
+    lens = [max(q, L) for q, L in zip(q_lens, [5, 40, 300, 1030])]
+    base = make_private_case(f"i8mq-{G}-{B}", lens, G * Hkv, Hkv, 128, B, "bf16", 80 + G + B)
+    c8 = make_int8_case(base, 80 + G + B)
+    mq = make_multi_query_case(base, q_lens, 80 + G)
+    say(f"int8 multi-query G={G} B={B} ps={ps} q_lens={q_lens}")
+    out = torch.full((mq.num_tokens, base.num_q_heads, base.head_dim), 7.0,
+                     dtype=torch.float32, device="cuda")
+    pa.paged_attention_multi_query_int8(
+        to_torch(mq.q, "bf16"), _dev(c8.k8), _dev(c8.v8),
+        torch.from_numpy(base.block_tables).cuda(), torch.from_numpy(base.context_lens).cuda(),
+        torch.from_numpy(mq.query_start).cuda(), float(base.scale), float(c8.k_scale),
+        float(c8.v_scale), out, max_query_len=mq.max_query_len,
+        max_context_len=int(base.context_lens.max()), partition_size=ps)
+    torch.cuda.synchronize()
+    ref = int8.paged_attention_multi_query_int8(mq.q, c8.k8, c8.v8, base.block_tables,
+                                                base.context_lens, mq.query_start, base.scale,
+                                                base.block_size, "bf16", c8.k_scale,
+                                                c8.v_scale)
+    err = max_err(out.cpu().numpy(), ref)
+    assert err <= TOL["bf16"], f"G={G} B={B} ps={ps}: {err}"
