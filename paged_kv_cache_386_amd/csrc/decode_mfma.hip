@@ -194,10 +194,20 @@ struct MfmaDecode {
       const int o = cs & bm1;
       const uint32_t krow = (uint32_t)(((o + n) * row_elems + head_off) * kElem);
       const bool okk = !MASK || cs + n < t1;
+      // bfloat16 K rows follow the V hint; 8-bit K rows always use ordinary
+      // loads (streaming them lost 9-10% on the FP8 pools, where each load
+      // instruction covers half of a row's 128 bytes)
+      if (!FP8 && stream_v) {
 #pragma unroll
-      for (int i = 0; i < kKLoads; ++i)
-        T.k[i] = okk ? buffer_load<kCacheNormal>(rk, krow + k_load_elem<FP8>(g, i) * kElem)
-                     : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < kKLoads; ++i)
+          T.k[i] = okk ? buffer_load<kCacheStream>(rk, krow + k_load_elem<FP8>(g, i) * kElem)
+                       : u32x4{0, 0, 0, 0};
+      } else {
+#pragma unroll
+        for (int i = 0; i < kKLoads; ++i)
+          T.k[i] = okk ? buffer_load<kCacheNormal>(rk, krow + k_load_elem<FP8>(g, i) * kElem)
+                       : u32x4{0, 0, 0, 0};
+      }
       uint32_t voff[kVLoads];
       bool ok[kVLoads];
 #pragma unroll
