@@ -546,9 +546,10 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   // between a tile's loads and the previous tile's.  With them, a cache hint
   // per tile: a block that the previous or next sequence holds at the same
   // logical position (a shared prefix, forked siblings) is likely to be read
-  // again soon, so its V rows are read normally; every other block's V rows
-  // are streamed with non-temporal loads.  (The hint only steers caching;
-  // entries past a neighbour's length may match by chance, which is harmless.)
+  // again soon, so its rows are read normally; every other block's V rows
+  // (and K rows, in bfloat16 pools) are streamed with non-temporal loads.
+  // (The hint only steers caching; entries past a neighbour's length may
+  // match by chance, which is harmless.)
   int ent_cur = 0, ent_next = 0;
   uint64_t nt_cur = 0, nt_next = 0;
   auto chunk_entries = [&](int c, uint64_t &ntmask) {
