@@ -822,6 +822,9 @@ def main() -> int:
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 2),
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "decode_us": round(dec_us, 2),
+        # per-call spread of the same HIP-event timings
+        "decode_us_pct": {k: round(float(np.percentile(dec_ms, q)) * 1e3, 2)
+                          for k, q in (("p10", 10), ("p50", 50), ("p90", 90))},
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_attention_decode (decode kernel + partition merge, one call)",
