@@ -14,16 +14,15 @@ KV slot read once -- the least HBM must deliver -- plus q, out, tables,
 partials and the edits) per second of step time.  `roofline` prices the decode
 call (the dispatch sort of large launches, the decode kernel and the partition
 merge, timed with HIP events on the stream they run on) against the MI355X HBM
-peak with the attended algorithmic bytes
-(K and V read once per sequence and KV head through its block table, 4 KiB per
-attended token here, plus q, out, tables and partials); `unique_gbps` is the
-same call priced with the unique bytes, and `traffic` the bytes the rocprofv3
+peak with the same unique algorithmic bytes: `frac` is the one "% of peak"
+figure of the line.  Beside it: `effective_gbps`, the same call priced with
+attended bytes (K and V once per sequence and KV head through its block
+table, which counts a shared prefix once per sequence that reads it: more
+than HBM has to deliver), and `traffic`, the bytes the rocprofv3
 FETCH_SIZE/WRITE_SIZE counters saw per decode call, scaled by what the same
 counters read for a copy of known size (`--copy-calibration`), when the
-committed counter summary was taken on the current decode sources;
-`traffic_gbps` and `traffic_frac` price the call with those measured bytes
-(the HBM side: with shared prefixes the attended rate counts re-reads that
-the caches serve and can approach or pass the HBM peak).
+committed counter summary was taken on the current decode sources, with
+`reread_ratio` = traffic / unique bytes (1.0 = every byte fetched once).
 
 Other modes:
   --copy-calibration      also run one copy_blocks call over a 1 GiB pool first
@@ -284,6 +283,7 @@ def cpu_baseline(case, budget_s: float):
 
 
 _POOL = {}
+CPU_WORKER_CAP = 16  # worker processes one GPU's job may run on a shared host
 
 
 def _pool_decode(seq_ids):
@@ -302,12 +302,15 @@ def _pool_decode(seq_ids):
 
 def _cpu_baseline_pool(case, kc, vc, num_seqs):
     """The same oracle decode over the same sequences, spread over the host's
-    cores by a fork-started process pool (one single-threaded worker per core,
-    at most 16: the CPU share of one GPU).  Must run before the process
-    touches the GPU: the workers are forked from it."""
+    cores by a fork-started process pool, one single-threaded worker per core
+    of the affinity set, capped at 16 worker processes: the host CPU share
+    one GPU's job is allowed on a shared multi-GPU host (the record states
+    both counts).  Must run before the process touches the GPU: the workers
+    are forked from it."""
     import multiprocessing as mp
 
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    available = len(os.sched_getaffinity(0))
+    cores = max(1, min(CPU_WORKER_CAP, available))
     _POOL.update(case=case, kc=kc, vc=vc)
     # longest first, dealt round-robin, so that the workers finish together
     order = sorted(range(num_seqs), key=lambda s: -int(case.context_lens[s]))
@@ -321,8 +324,8 @@ def _cpu_baseline_pool(case, kc, vc, num_seqs):
             t = time.perf_counter() - t0
     finally:
         _POOL.clear()
-    return {"cores": cores, "decode_seconds": t, "seqs": num_seqs,
-            "cpu": _cpu_model()}
+    return {"cores": cores, "cores_available": available, "decode_seconds": t,
+            "seqs": num_seqs, "cpu": _cpu_model()}
 
 
 def _cpu_model() -> str:
@@ -561,7 +564,11 @@ def multi_query_bench(args) -> int:
         attended += sum(L - n + i + 1 for i in range(n))
         kv_tokens += L if n else 0
     flops = attended * Hq * 4 * D
-    kv_bytes = kv_tokens * Hkv * D * 2 * (1 if c8 is not None else 2)
+    el = 1 if c8 is not None else 2
+    # K/V priced with each distinct slot once (a shared prefix block counts
+    # once, as for decode); attended (once per sequence and KV head) beside it
+    kv_bytes = unique_slots(b) * Hkv * D * 2 * el
+    kv_attended = kv_tokens * Hkv * D * 2 * el
     io_bytes = c.num_tokens * Hq * D * (2 + 4) + b.block_tables.nbytes + 8 * b.num_seqs
     tflops = flops / (us * 1e-6) / 1e12
     gbps = (kv_bytes + io_bytes) / (us * 1e-6) / 1e9
@@ -600,8 +607,15 @@ def multi_query_bench(args) -> int:
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": round((tflops / PEAK_BF16_TFLOPS) if mfma_bound else (gbps / PEAK_HBM_GBPS), 4),
             "traffic": None,
+            "frac_definition": (
+                "4 * head_dim flops per (query head, attended position) per call / mean call "
+                "time / 2.5 PFLOP/s dense bf16" if mfma_bound else
+                "unique algorithmic bytes per call (each distinct KV slot once, plus q, out, "
+                "tables, lengths) / mean call time / 8 TB/s"),
             "algorithmic_flops_per_call": flops,
             "algorithmic_bytes_per_call": kv_bytes + io_bytes,
+            "attended_bytes_per_call": kv_attended + io_bytes,
+            "effective_gbps": round((kv_attended + io_bytes) / (us * 1e-6) / 1e9, 1),
             "other": {"tflops": round(tflops, 2), "gbps": round(gbps, 1)},
         },
         "wall_s_timed": round(wall, 3),
@@ -785,11 +799,12 @@ def main() -> int:
     step_bytes = dec_unique + edit_bytes(case)
     tokens = int(case.context_lens.astype(np.int64).sum())
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    # roofline: the attended algorithmic bytes (K/V read once per sequence and
-    # KV head, as the method reads them through each block table) per decode
-    # call over its duration; the unique-slot rate (the least HBM must
-    # deliver) and the measured counter traffic sit beside it
-    achieved = dec_attended / (dec_us * 1e-6) / 1e9
+    # roofline: the unique algorithmic bytes of one decode call (each
+    # distinct KV slot once: what HBM must deliver at least) over the call's
+    # mean duration; attended bytes (a shared block once per sequence that
+    # reads it) give the "effective" rate beside it, and the committed
+    # counter traffic the measured bytes
+    achieved = dec_unique / (dec_us * 1e-6) / 1e9
     traffic = load_traffic(workload)
 
     rec = {
@@ -819,7 +834,6 @@ def main() -> int:
             "step": ("copy_blocks + kv_cache_write + " if has_step else "") +
                     "paged_attention_decode (+ split-K merge)",
         },
-        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 2),
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "decode_us": round(dec_us, 2),
         # per-call spread of the same HIP-event timings
@@ -833,14 +847,19 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_call": dec_attended,
-            "unique_bytes_per_call": dec_unique,
-            "unique_gbps": round(dec_unique / (dec_us * 1e-6) / 1e9, 1),
-            # the HBM side: measured traffic per call over the same duration
-            # (attended bytes above it are re-reads served by the caches)
+            "frac_definition": ("unique algorithmic bytes per decode call (each distinct KV "
+                                "slot once, plus q, out, used table entries, lengths, split "
+                                "partials and the dispatch list) / mean decode-call time / "
+                                "8 TB/s"),
+            "algorithmic_bytes_per_call": dec_unique,
+            "attended_bytes_per_call": dec_attended,
+            # a shared block counted once per sequence that reads it: above
+            # what HBM has to deliver when blocks are shared
+            "effective_gbps": round(dec_attended / (dec_us * 1e-6) / 1e9, 1),
+            # measured bytes (committed counters on these decode sources)
+            # over the same duration, and their ratio to the unique bytes
             "traffic_gbps": None if traffic is None else round(traffic / (dec_us * 1e-6) / 1e9, 1),
-            "traffic_frac": None if traffic is None else
-                            round(traffic / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "reread_ratio": None if traffic is None else round(traffic / dec_unique, 3),
         },
         "wall_s_timed": round(wall, 3),
     }
@@ -863,9 +882,12 @@ def main() -> int:
                 "value": round(step_bytes / ac_step / 1e9, 4),
                 "unit": "GB/s",
                 "cores": ac["cores"],
+                "cores_available": ac["cores_available"],
                 "cpu": ac["cpu"],
                 "sample": (f"the same oracle decode of the same {ac['seqs']} sequences over "
-                           f"{ac['cores']} single-threaded worker processes in "
+                           f"{ac['cores']} single-threaded worker processes "
+                           f"({ac['cores_available']} cores in the affinity set; at most "
+                           f"{CPU_WORKER_CAP} worker processes per GPU job on this host) in "
                            f"{ac['decode_seconds']:.2f}s, plus the single-threaded edits"),
                 "gpu_speedup": round(ac_step / (ms_step * 1e-3), 1),
             },

@@ -13,7 +13,12 @@
  * Conventions for every entry point:
  *  - Pointers marked "device" point to GPU memory on the current HIP device;
  *    the caller owns every buffer.  The library never allocates, frees or keeps
- *    a pointer after the call returns, and holds no mutable global state.
+ *    a pointer after the call returns.  Its only mutable global state is the
+ *    index-check mode (a process-wide flag) and, per device, the one word the
+ *    index check writes its verdict into (see "Index checking" below: calls
+ *    that overlap on one device with checking on race on that word); with
+ *    checking off, calls share nothing and may run concurrently on any
+ *    streams.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    asynchronously on it; nothing is synchronised.
  *  - Arguments are validated on the host before anything is enqueued.  A
@@ -82,13 +87,25 @@ typedef enum pa_dtype {
  * table, read K, take the scaled dot with q, then softmax and the weighted sum
  * of V; [P1] section 2.1 block table; [P1] section 2.3 decode reads the whole
  * KV cache per generated token).  L = 0 gives zeros.  Arithmetic is fp32 with
- * an online (running-maximum) softmax; bf16 inputs are read exactly.
+ * an online (running-maximum) softmax; bf16 inputs are read exactly.  Where
+ * the products run on the matrix cores (bf16 with G = 4 or 8), q.K is exact
+ * products with fp32 accumulation, and the probabilities enter p.V as a pair
+ * of bfloat16 values hi + lo (about 16 significant bits) with fp32
+ * accumulation; the vector-ALU path (fp32, and bf16 with G = 1 or 2) keeps
+ * every step in fp32.
  *
  *   q              device, [num_seqs][num_q_heads][head_dim], dtype
  *   k_cache,
  *   v_cache        device, the pool described above, dtype
  *   block_tables   device int32 [num_seqs][max_blocks_per_seq]; entries past
- *                  ceil(L/block_size) are never read
+ *                  ceil(L/block_size) never address the pool and may hold any
+ *                  value.  As a cache hint, the kernels also read the entries of
+ *                  the neighbouring rows s-1 and s+1 at the block indices row s
+ *                  uses (a block a neighbour holds at the same logical position
+ *                  is read with ordinary, cached loads, every other block with
+ *                  streaming ones); those reads stay inside the
+ *                  [num_seqs][max_blocks_per_seq] array, and their values only
+ *                  steer caching
  *   context_lens   device int32 [num_seqs]; must not exceed max_context_len
  *   scale          softmax scale applied to the dot product (e.g. 1/sqrt(d))
  *   out            device float32 [num_seqs][num_q_heads][head_dim]; written
@@ -141,9 +158,11 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
  * k_cache and v_cache hold one E4M3 code per element in the layout above; an
  * element's value is e4m3(code) * k_scale (K) or * v_scale (V), so the
  * result is that of paged_attention_decode on the dequantised pool.  q is
- * bfloat16.  Codes are widened exactly to bfloat16 for q.K on the matrix
- * cores and to fp32 for p.V; k_scale joins the softmax scale and v_scale
- * multiplies the output.  Every other argument, the workspace (same size as
+ * bfloat16.  Both products run on the bfloat16 matrix cores with fp32
+ * accumulation: K and V codes are widened exactly to bfloat16 (an E4M3 value
+ * has at most 4 significant bits), and the probabilities enter p.V as a pair
+ * of bfloat16 values hi + lo (about 16 significant bits); k_scale joins the
+ * softmax scale and v_scale multiplies the output.  Every other argument, the workspace (same size as
  * paged_attention_decode's) and the partition policy are those of
  * paged_attention_decode.
  * Supported: head_dim 128, G in {1, 2, 4, 8}; k_scale and v_scale finite and
@@ -163,8 +182,9 @@ int32_t paged_attention_decode_fp8(const void *q, const void *k_cache, const voi
  * paged_attention_decode_int8 -- paged_attention_decode_fp8 over an INT8
  * pool ([P3] architecture figure: FP8/INT8 quantisation): an element's value
  * is code * k_scale (K) or * v_scale (V), the code a signed byte.  Codes are
- * widened exactly to bfloat16 for q.K and to fp32 for p.V.  Arguments,
- * support and errors are those of paged_attention_decode_fp8.
+ * widened exactly to bfloat16 (at most 7 significant bits) for both products,
+ * with the probabilities entering p.V as a bfloat16 pair, as for FP8.
+ * Arguments, support and errors are those of paged_attention_decode_fp8.
  */
 int32_t paged_attention_decode_int8(const void *q, const void *k_cache, const void *v_cache,
                                     const int32_t *block_tables, const int32_t *context_lens,

@@ -10,6 +10,11 @@ import torch
 from oracle import oracle as O
 
 TOL = {"f32": 1e-5, "bf16": 2e-3}
+# Regression bound for the decode paths: the kernels' measured error is about
+# 1e-7 (fp32) and 1e-6 (bf16 inputs, fp32 accumulation), far inside TOL, so a
+# lost or repeated tile at long context (which moves the output by about
+# 1e-3 on N(0, 1) inputs) fails this bound even where it would pass TOL.
+REGRESS = {"f32": 1e-5, "bf16": 1e-4}
 
 
 def say(msg: str) -> None:

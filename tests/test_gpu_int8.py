@@ -2,7 +2,7 @@
 quantising write bit for bit (ties, clamping, NaN, negative slots), every
 code read back exactly through decode, INT8 decode against the oracle on
 private, prefix-shared and forked pools at several block and partition
-sizes, and the full-size GQA prefix workload on sampled rows."""
+sizes, and the full-size GQA prefix workload (every output element)."""
 import numpy as np
 import pytest
 import torch
@@ -142,16 +142,17 @@ def test_decode_prefix_and_forked_pools():
         assert err <= TOL["bf16"], (base.name, err)
 
 
-def test_full_size_prefix_workload_sampled():
+def test_full_size_prefix_workload():
+    """The GQA prefix-sharing batch at full size over an INT8 pool, in
+    the benchmark's launch configuration (automatic partitions, dispatch
+    list): every output element against the oracle."""
     base = settle_step(make_case(2))
     c8 = make_int8_case(base, 2)
     say("int8 decode, GQA prefix-sharing batch at full size")
     got = run_decode_int8(c8)
     assert np.isfinite(got).all()
-    rng = np.random.default_rng(0)
-    rows = [(int(s), int(h)) for s, h in zip(rng.integers(0, 256, 48), rng.integers(0, 32, 48))]
-    ref = oracle_decode(c8, rows=rows)
-    err = max_err(np.array([got[s, h] for s, h in rows]), ref)
+    err = max_err(got, oracle_decode(c8))
+    say(f"int8 cfg2 full size: all {got.size} outputs, max abs err {err:.3e}")
     assert err <= TOL["bf16"], err
 
 
