@@ -16,9 +16,10 @@
  *    a pointer after the call returns.  Its only mutable global state is the
  *    index-check mode (a process-wide flag) and, per device, the one word the
  *    index check writes its verdict into (see "Index checking" below: calls
- *    that overlap on one device with checking on race on that word); with
- *    checking off, calls share nothing and may run concurrently on any
- *    streams.
+ *    that overlap on one device with checking on race on that word), and the
+ *    static scratch array of paged_attention_decode_noalloc (calls of that
+ *    entry point that overlap on one device race on it); otherwise calls
+ *    share nothing and may run concurrently on any streams.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    asynchronously on it; nothing is synchronised.
  *  - Arguments are validated on the host before anything is enqueued.  A
@@ -63,7 +64,8 @@ typedef enum pa_status {
   PA_ERR_OOM = -8,         /* block manager: no free block left */
   PA_ERR_NO_SEQ = -9,      /* block manager: unknown sequence id */
   PA_ERR_SEQ_EXISTS = -10, /* block manager: sequence id already in use */
-  PA_ERR_INDEX = -11       /* a device index is out of range (only with index checking on) */
+  PA_ERR_INDEX = -11,      /* a device index is out of range (only with index checking on) */
+  PA_ERR_SCRATCH = -12     /* the call needs more than the library's static scratch holds */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -149,6 +151,37 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
                                int32_t max_blocks_per_seq, int32_t max_context_len,
                                int32_t dtype, int32_t partition_size,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode_noalloc -- paged_attention_decode without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It allocates nothing and calls no allocating routine; the
+ * split-K partials and the dispatch list go to a static device array of the
+ * library, paged_attention_noalloc_scratch_bytes() bytes (32 MiB) on each GPU
+ * it runs on, held from the library's load until the process ends.  Its
+ * device address is looked up on the first call on each device, so that
+ * call must find the device current.
+ *
+ * Arguments, results (bit for bit those of paged_attention_decode with a
+ * workspace of paged_attention_workspace_size bytes), support and errors are
+ * those of paged_attention_decode, plus PA_ERR_SCRATCH (nothing enqueued)
+ * when paged_attention_workspace_size for these arguments exceeds the static
+ * size.  Every call on one GPU uses that GPU's one array: calls that overlap
+ * on one GPU (other streams, other threads) race on it and must be ordered
+ * by the caller.  Nothing in it needs to start at zero: a call writes every
+ * byte of it that it reads.
+ */
+int32_t paged_attention_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                       const int32_t *block_tables, const int32_t *context_lens,
+                                       float scale, float *out, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       int32_t dtype, int32_t partition_size, void *stream);
+
+/* Bytes of the static scratch paged_attention_decode_noalloc uses per GPU. */
+size_t paged_attention_noalloc_scratch_bytes(void);
 
 /*
  * paged_attention_decode_fp8 -- paged_attention_decode over an FP8 (E4M3)

@@ -24,8 +24,10 @@ from ._lib import (  # noqa: F401
     lib,
     multi_query_partitions,
     multi_query_workspace_size,
+    noalloc_scratch_bytes,
     num_partitions,
     paged_attention_decode,
+    paged_attention_decode_noalloc,
     paged_attention_decode_fp8,
     paged_attention_decode_int8,
     paged_attention_multi_query,

@@ -23,6 +23,7 @@ STATUS_NAMES = {
     0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
     -4: "PA_ERR_UNSUPPORTED", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_ALIAS", -7: "PA_ERR_LAUNCH",
     -8: "PA_ERR_OOM", -9: "PA_ERR_NO_SEQ", -10: "PA_ERR_SEQ_EXISTS", -11: "PA_ERR_INDEX",
+    -12: "PA_ERR_SCRATCH",
 }
 PA_ERR_INDEX = -11
 
@@ -33,6 +34,10 @@ SIGNATURES = {
     "paged_attention_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                       _VP, ctypes.c_size_t, _VP]),
+    "paged_attention_decode_noalloc": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
+                                              _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                              _I32, _I32, _VP]),
+    "paged_attention_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "paged_attention_multi_query": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
                                            _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                            _I32, _I32, _I32, _VP, ctypes.c_size_t, _VP]),
@@ -203,6 +208,33 @@ def paged_attention_decode(q, k_cache, v_cache, block_tables, context_lens, scal
         float(scale), _ptr(out), S, Hq, Hkv, D, B, NB, MB, int(max_context_len),
         _dtype_code(q), int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
     _check("paged_attention_decode", st)
+
+
+def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens,
+                                   scale: float, out, *, max_context_len: int,
+                                   partition_size: int = 0, stream=None) -> None:
+    """paged_attention_decode with the workspace in the library's static
+    device scratch (include/pagedattn.h): nothing is allocated, here or in
+    the library.  Raises PagedAttnError(PA_ERR_SCRATCH) when the call needs
+    more than ``noalloc_scratch_bytes()``."""
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q/k_cache/v_cache shapes disagree")
+    MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    for t in (q, k_cache, v_cache, block_tables, context_lens, out):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    st = lib().paged_attention_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), _ptr(out), S, Hq, Hkv, D, B, NB, MB, int(max_context_len),
+        _dtype_code(q), int(partition_size), _stream(stream))
+    _check("paged_attention_decode_noalloc", st)
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static device scratch paged_attention_decode_noalloc uses."""
+    return int(lib().paged_attention_noalloc_scratch_bytes())
 
 
 def multi_query_partitions(num_seqs: int, num_q_heads: int, num_kv_heads: int,

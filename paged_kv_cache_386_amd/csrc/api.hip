@@ -185,6 +185,8 @@ const char *pagedattn_status_string(int32_t status) {
     case PA_ERR_OOM: return "no free KV block left";
     case PA_ERR_NO_SEQ: return "unknown sequence id";
     case PA_ERR_SEQ_EXISTS: return "sequence id already in use";
+    case PA_ERR_SCRATCH:
+      return "the call needs more workspace than the library's static scratch holds";
     default: return "unknown status";
   }
 }

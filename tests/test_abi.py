@@ -85,6 +85,26 @@ def test_decode_rejects_bad_arguments_on_host():
     assert _decode(lib, NB=1 << 27, B=16) == -2  # pool slots beyond int32
 
 
+def test_noalloc_decode_rejects_on_host():
+    """The allocation-free decode checks its workspace need against the
+    static scratch before touching any device: too large gives
+    PA_ERR_SCRATCH; arguments decode rejects (need 0) reach decode's own
+    checks."""
+    from paged_kv_cache_386_amd import _lib
+    lib = _lib.lib()
+    cap = lib.paged_attention_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    f = lib.paged_attention_decode_noalloc
+    # 4096 sequences of up to 65536 tokens: 32 partitions of partials, far
+    # beyond the scratch
+    need = lib.paged_attention_workspace_size(4096, 64, 8, 128, 65536, 0)
+    assert need > cap
+    assert f(1, 1, 1, 1, 1, 0.1, 1, 4096, 64, 8, 128, 16, 10, 4096, 65536, 1, 0, 0) == -12
+    assert lib.pagedattn_status_string(-12)
+    assert f(1, 1, 1, 1, 1, 0.1, 1, 2, 4, 2, 128, 16, 10, 4, 64, 7, 0, 0) == -3
+    assert f(1, 1, 1, 1, 1, 0.1, 1, 2, 4, 2, 128, 12, 10, 4, 64, 1, 0, 0) == -2
+
+
 def test_partition_policy():
     from paged_kv_cache_386_amd import _lib
     lib = _lib.lib()
