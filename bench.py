@@ -649,6 +649,10 @@ def main() -> int:
                     help="the workload over an FP8 (E4M3) pool: quantising write and FP8 decode")
     ap.add_argument("--kv-int8", action="store_true",
                     help="the workload over an INT8 pool: quantising write and INT8 decode")
+    ap.add_argument("--no-prefix", action="store_true",
+                    help="plain paged_attention_decode even where sequences share prefixes "
+                         "(default: paged_attention_decode_prefix with the groups "
+                         "pa_prefix_groups finds in the host tables)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -666,6 +670,8 @@ def main() -> int:
             return 2
         workload += "-fp8" if args.kv_fp8 else "-int8"
         args.no_cpu_baseline = True
+    if args.no_prefix:
+        workload += "-noprefix"
     if args.serving:
         workload = "serving"
     if args.multi_query:
@@ -742,9 +748,26 @@ def main() -> int:
     max_ctx = case.max_context_len
     S, Hq, Hkv, D = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
     P = pa.num_partitions(S, Hkv, max_ctx, args.partition_size)
-    ws_bytes = pa.workspace_size(S, Hq, Hkv, D, max_ctx, args.partition_size)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ps = pa.partition_tokens(S, Hkv, max_ctx, args.partition_size) if P > 1 else 0
+    # shared prefixes: the host finds them in the tables it built (the block
+    # manager's knowledge; not part of the timed step)
+    groups_np = np.zeros((0, 2), np.int32)
+    shared_np = np.zeros(S, np.int32)
+    if not args.no_prefix:
+        groups_np, shared_np = pa.prefix_groups(case.block_tables, case.context_lens,
+                                                case.block_size, Hq, Hkv, 16)
+    use_prefix = len(groups_np) > 0
+    kv_code = pa.PA_BF16 if c8 is None else (pa.PA_FP8_E4M3 if args.kv_fp8 else pa.PA_INT8)
+    if case.dtype == "f32":
+        kv_code = pa.PA_F32
+    if use_prefix:
+        groups_d = torch.from_numpy(groups_np).to(dev)
+        shared_d = torch.from_numpy(shared_np).to(dev)
+        ws_bytes = pa.prefix_workspace_size(S, Hq, Hkv, D, max_ctx, args.partition_size,
+                                            len(groups_np), kv_code)
+    else:
+        ws_bytes = pa.workspace_size(S, Hq, Hkv, D, max_ctx, args.partition_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def edits():
@@ -757,7 +780,13 @@ def main() -> int:
                   stream=stream)
 
     def decode():
-        if c8 is None:
+        if use_prefix:
+            pa.paged_attention_decode_prefix(
+                q, kc, vc, tables, lens, groups_d, shared_d, float(case.scale), out,
+                max_context_len=max_ctx, k_scale=1.0 if c8 is None else float(c8.k_scale),
+                v_scale=1.0 if c8 is None else float(c8.v_scale),
+                partition_size=args.partition_size, workspace=ws, stream=stream)
+        elif c8 is None:
             pa.paged_attention_decode(q, kc, vc, tables, lens, float(case.scale), out,
                                       max_context_len=max_ctx,
                                       partition_size=args.partition_size, workspace=ws,
@@ -831,8 +860,11 @@ def main() -> int:
             "total_context_tokens": tokens, "unique_kv_slots": unique_slots(case),
             "copy_pairs": int(len(case.copy_pairs)), "new_tokens": int(len(case.slot_mapping)),
             "partition_size": ps if P > 1 else None, "num_partitions": P,
+            "prefix_groups": int(len(groups_np)),
+            "shared_tokens": int(shared_np.sum()),
             "step": ("copy_blocks + kv_cache_write + " if has_step else "") +
-                    "paged_attention_decode (+ split-K merge)",
+                    ("paged_attention_decode_prefix (shared prefixes read once per group; "
+                     "+ merge)" if use_prefix else "paged_attention_decode (+ split-K merge)"),
         },
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "decode_us": round(dec_us, 2),
@@ -841,7 +873,9 @@ def main() -> int:
                           for k, q in (("p10", 10), ("p50", 50), ("p90", 90))},
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode (decode kernel + partition merge, one call)",
+            "kernel": ("paged_attention_decode_prefix (dispatch sort, decode kernel with the "
+                       "prefix items, merge; one call)" if use_prefix else
+                       "paged_attention_decode (decode kernel + partition merge, one call)"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

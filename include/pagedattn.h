@@ -115,8 +115,8 @@ typedef enum pa_dtype {
  *   max_context_len host upper bound of context_lens (sizes the launch);
  *                  must be <= max_blocks_per_seq * block_size
  *   dtype          element type of q, k_cache and v_cache
- *   partition_size split-K partition in tokens: 0 = automatic (2048-token
- *                  partitions for contexts above 2048 when there are at least
+ *   partition_size split-K partition in tokens: 0 = automatic (4096-token
+ *                  partitions for contexts above 4096 when there are at least
  *                  256 (sequence, KV head) pairs; with fewer, floor(512 /
  *                  pairs) equal partitions per context, at least 512
  *                  tokens), negative = never split, positive = that many
@@ -151,6 +151,65 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
                                int32_t max_blocks_per_seq, int32_t max_context_len,
                                int32_t dtype, int32_t partition_size,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode_prefix -- paged_attention_decode for a batch whose
+ * sequences share prefixes, reading each shared block once per group instead
+ * of once per sequence ([P1] section 5.2 prefix caching: requests with a
+ * common prompt prefix keep its blocks once and reuse them; [P3]
+ * "关键设计二：Copy-on-Write": forked sequences share their parent's
+ * blocks).  The result is that of paged_attention_decode (or of its FP8 /
+ * INT8 forms) on the same tables: the groups only change which reads are
+ * shared.
+ *
+ *   prefix_groups  device int32 [num_groups][2]: (first sequence, members)
+ *                  of each group, a run of consecutive sequences; groups in
+ *                  ascending order and disjoint; members in [1, 64 / G]
+ *   num_groups     host, 0 .. num_seqs (0: plain decode)
+ *   shared_lens    device int32 [num_seqs]: sequence s reads positions
+ *                  [0, shared_lens[s]) through its group (in [0, L]; 0 for a
+ *                  sequence in no group).  The rows of two members of one
+ *                  group must name the same blocks below the shorter of
+ *                  their two shared lengths.  Lengths are used rounded down
+ *                  to whole 16-token tiles.
+ *   kv_dtype       the pool's element type: PA_F32 or PA_BF16 (q the same),
+ *                  PA_FP8_E4M3 or PA_INT8 (q bfloat16; k_scale and v_scale as
+ *                  in paged_attention_decode_fp8; ignored otherwise)
+ *   workspace      at least paged_attention_prefix_workspace_size(...) bytes
+ * Every other argument is paged_attention_decode's.  With groups, the work
+ * items of each (group, KV head) attend the group's shared positions for
+ * all of its (member, query head) pairs, 16 pairs per item, on the matrix
+ * cores, and each sequence's own items attend only the rest of its context;
+ * a merge kernel then combines every member's prefix and private partials in
+ * ascending position order.
+ * Where this is not compiled (fp32 pools, head_dim 64) or num_groups is 0,
+ * the call is plain decode and the groups are ignored.
+ * Supported and errors: as paged_attention_decode (and its FP8 / INT8
+ * forms); PA_ERR_SHAPE for num_groups outside [0, num_seqs], PA_ERR_NULL for
+ * missing groups or shared lengths.  Groups and shared lengths that break the
+ * rules above give unspecified numbers, every access staying in bounds; with
+ * index checking on they give PA_ERR_INDEX.
+ */
+int32_t paged_attention_decode_prefix(const void *q, const void *k_cache, const void *v_cache,
+                                      const int32_t *block_tables, const int32_t *context_lens,
+                                      const int32_t *prefix_groups, int32_t num_groups,
+                                      const int32_t *shared_lens, float scale, float k_scale,
+                                      float v_scale, float *out, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      int32_t kv_dtype, int32_t partition_size, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of paged_attention_decode_prefix: with the prefix path,
+ * 4 * num_seqs * num_q_heads * (P + 1) * (head_dim + 2) for the partials plus
+ * 4 * (num_seqs * P + 4 * num_groups) for the dispatch list when the launch
+ * has more than 1024 workgroups; otherwise paged_attention_workspace_size's.
+ * 0 for arguments the call rejects. */
+size_t paged_attention_prefix_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t max_context_len, int32_t partition_size,
+                                             int32_t num_groups, int32_t kv_dtype);
 
 /*
  * paged_attention_decode_noalloc -- paged_attention_decode without a

@@ -115,6 +115,38 @@ int32_t pa_bm_prepare_decode(pa_block_manager *bm, const int64_t *seq_ids, int32
 /* Pool occupancy and utilisation. */
 int32_t pa_bm_stats(const pa_block_manager *bm, pa_block_stats *out);
 
+/*
+ * pa_prefix_groups -- the shared-prefix groups of a decode batch, for
+ * paged_attention_decode_prefix, found from the host copy of its block tables
+ * ([P1] section 5.2 prefix caching and [P3] "关键设计二": sequences that share
+ * a prompt prefix or were forked hold the same physical blocks at the same
+ * logical positions).
+ *
+ * Scans the sequences in order; a group is a run of at least two
+ * consecutive non-empty sequences, at most max_members long, whose rows start
+ * with the same block.  Its reference row is the member with the most blocks
+ * (the first of equals); every other member's shared length is
+ * min(L, B * (leading entries equal to the reference row's, among the used
+ * entries of both)), or 0 below min_shared_tokens, and the reference member's
+ * is min(L, the longest of the others').  Every member thus names the
+ * reference row's blocks below its shared length, and so every pair of
+ * members names the same blocks below the shorter of its two.  A run in
+ * which nobody shares min_shared_tokens is no group.  Sequences in no group
+ * get shared length 0.
+ *
+ *   block_tables   host int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens   host int32 [num_seqs]
+ *   max_members    most members per group: 64 / G for the decode kernel
+ *   groups         host int32 [num_seqs][2] out: (first sequence, members)
+ *                  per group, ascending
+ *   shared_lens    host int32 [num_seqs] out
+ * Returns the number of groups (>= 0), or PA_ERR_NULL / PA_ERR_SHAPE.
+ */
+int32_t pa_prefix_groups(const int32_t *block_tables, const int32_t *context_lens,
+                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                         int32_t max_members, int32_t min_shared_tokens, int32_t *groups,
+                         int32_t *shared_lens);
+
 #ifdef __cplusplus
 }
 #endif

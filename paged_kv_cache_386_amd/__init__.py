@@ -28,6 +28,9 @@ from ._lib import (  # noqa: F401
     num_partitions,
     paged_attention_decode,
     paged_attention_decode_noalloc,
+    paged_attention_decode_prefix,
+    prefix_groups,
+    prefix_workspace_size,
     paged_attention_decode_fp8,
     paged_attention_decode_int8,
     paged_attention_multi_query,

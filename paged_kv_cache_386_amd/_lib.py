@@ -34,6 +34,12 @@ SIGNATURES = {
     "paged_attention_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                       _VP, ctypes.c_size_t, _VP]),
+    "paged_attention_decode_prefix": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP,
+                                             ctypes.c_float, ctypes.c_float, ctypes.c_float, _VP,
+                                             _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                             _I32, _I32, _VP, ctypes.c_size_t, _VP]),
+    "paged_attention_prefix_workspace_size": (ctypes.c_size_t, [_I32] * 8),
+    "pa_prefix_groups": (_I32, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
     "paged_attention_decode_noalloc": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
                                               _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                               _I32, _I32, _VP]),
@@ -230,6 +236,72 @@ def paged_attention_decode_noalloc(q, k_cache, v_cache, block_tables, context_le
         float(scale), _ptr(out), S, Hq, Hkv, D, B, NB, MB, int(max_context_len),
         _dtype_code(q), int(partition_size), _stream(stream))
     _check("paged_attention_decode_noalloc", st)
+
+
+def prefix_groups(block_tables, context_lens, block_size: int, num_q_heads: int,
+                  num_kv_heads: int, min_shared_tokens: int = 16):
+    """The shared-prefix groups of a batch from host block tables
+    (pa_prefix_groups in include/pagedattn_blocks.h): numpy int32
+    ``groups [n, 2]`` and ``shared_lens [S]``.  At most 64 / G members per
+    group, as the decode kernel takes them."""
+    import numpy as np
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = int(lens.shape[0])
+    MB = int(tables.shape[1]) if tables.ndim == 2 and S else 1
+    groups = np.zeros((max(S, 1), 2), np.int32)
+    shared = np.zeros(max(S, 1), np.int32)
+    G = num_q_heads // num_kv_heads
+    n = lib().pa_prefix_groups(tables.ctypes.data, lens.ctypes.data, S, MB, int(block_size),
+                               max(1, 64 // G), int(min_shared_tokens), groups.ctypes.data,
+                               shared.ctypes.data)
+    if n < 0:
+        raise PagedAttnError("pa_prefix_groups", n)
+    return groups[:n].copy(), shared[:S].copy()
+
+
+def prefix_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          max_context_len: int, partition_size: int, num_groups: int,
+                          kv_dtype: int) -> int:
+    return int(lib().paged_attention_prefix_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size,
+        num_groups, kv_dtype))
+
+
+def paged_attention_decode_prefix(q, k_cache, v_cache, block_tables, context_lens, groups,
+                                  shared_lens, scale: float, out, *, max_context_len: int,
+                                  k_scale: float = 1.0, v_scale: float = 1.0,
+                                  partition_size: int = 0, workspace=None,
+                                  stream=None) -> None:
+    """Decode with shared prefixes read once per group (see
+    include/pagedattn.h).  ``groups``: device int32 [n, 2] (first sequence,
+    members); ``shared_lens``: device int32 [S].  The pool may be float32,
+    bfloat16, or 8-bit codes (uint8 = FP8 E4M3, int8 = INT8, with bfloat16 q
+    and the two scales)."""
+    import torch
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q/k_cache/v_cache shapes disagree")
+    MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    kv = _dtype_code(k_cache)
+    ng = int(groups.shape[0]) if groups is not None else 0
+    need = prefix_workspace_size(S, Hq, Hkv, D, max_context_len, partition_size, ng, kv)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    for t in (q, k_cache, v_cache, block_tables, context_lens, out):
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if ng and not (groups.is_contiguous() and shared_lens.is_contiguous()):
+        raise ValueError("groups and shared_lens must be contiguous")
+    st = lib().paged_attention_decode_prefix(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(groups) if ng else 0, ng, _ptr(shared_lens) if ng else 0, float(scale),
+        float(k_scale), float(v_scale), _ptr(out), S, Hq, Hkv, D, B, NB, MB,
+        int(max_context_len), kv, int(partition_size), _ptr(workspace), ws_bytes,
+        _stream(stream))
+    _check("paged_attention_decode_prefix", st)
 
 
 def noalloc_scratch_bytes() -> int:

@@ -91,6 +91,63 @@ __global__ __launch_bounds__(kCheckThreads) void check_pairs_kernel(
   publish(bad);
 }
 
+// Prefix groups: each (first, count) with count in [1, max_members] inside
+// [0, S), the groups in ascending order and disjoint; every shared length in
+// [0, L]; a sequence outside every group shares nothing; and the rows of one
+// group's members name the same blocks below the shorter of their two shared
+// lengths (checked against the group's member with the longest shared
+// length, which implies it for every pair).  Lengths are taken as the kernels
+// take them: clamped, whole 16-token tiles.
+__global__ __launch_bounds__(kCheckThreads) void check_prefix_kernel(
+    const int32_t *__restrict__ lens, const int32_t *__restrict__ tables,
+    const int32_t *__restrict__ groups, int num_groups, const int32_t *__restrict__ shared_lens,
+    int S, int mb, int lgB, int max_ctx, int max_members) {
+  bool bad = false;
+  for (int i = threadIdx.x; i < num_groups; i += kCheckThreads) {
+    const int first = groups[2 * i], count = groups[2 * i + 1];
+    bad |= first < 0 || count < 1 || count > max_members || first >= S || count > S - first;
+    if (i > 0) bad |= first < groups[2 * i - 2] + groups[2 * i - 1];
+  }
+  // each sequence: its group by binary search over the (ascending) firsts
+  for (int s = threadIdx.x; s < S; s += kCheckThreads) {
+    const int L = min(max(lens[s], 0), max_ctx);
+    const int raw = shared_lens[s];
+    bad |= raw < 0 || raw > L;
+    const int sh = min(max(raw, 0), L) & ~15;
+    int lo = 0, hi = num_groups - 1, gi = -1;
+    while (lo <= hi) {
+      const int mid = (lo + hi) / 2;
+      if (groups[2 * mid] <= s) {
+        gi = mid;
+        lo = mid + 1;
+      } else {
+        hi = mid - 1;
+      }
+    }
+    const bool member = gi >= 0 && s < groups[2 * gi] + groups[2 * gi + 1];
+    if (!member) {
+      bad |= sh > 0;
+      continue;
+    }
+    const int f = groups[2 * gi];
+    if (f < 0 || f >= S) continue;  // flagged above
+    const int count = max(0, min(min(groups[2 * gi + 1], S - f), max_members));
+    int top = f, top_sh = -1;
+    for (int m = f; m < f + count; ++m) {
+      const int Lm = min(max(lens[m], 0), max_ctx);
+      const int shm = min(max(shared_lens[m], 0), Lm) & ~15;
+      if (shm > top_sh) {
+        top_sh = shm;
+        top = m;
+      }
+    }
+    const int nblk = (sh + (1 << lgB) - 1) >> lgB;
+    for (int j = 0; j < nblk && j < mb; ++j)
+      bad |= tables[(int64_t)s * mb + j] != tables[(int64_t)top * mb + j];
+  }
+  publish(bad);
+}
+
 // The verdict of the check just enqueued on `stream`.
 int32_t read_verdict(hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
@@ -130,6 +187,16 @@ int32_t check_queries(const int32_t *lens, const int32_t *query_start, int32_t n
                       int32_t num_tokens, int32_t max_query_len, hipStream_t stream) {
   hipLaunchKernelGGL(check_queries_kernel, dim3(1), dim3(kCheckThreads), 0, stream, lens,
                      query_start, num_seqs, num_tokens, max_query_len);
+  return read_verdict(stream);
+}
+
+int32_t check_prefix_groups(const int32_t *lens, const int32_t *tables, const int32_t *groups,
+                            int32_t num_groups, const int32_t *shared_lens, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t log2_block_size,
+                            int32_t max_context_len, int32_t max_members, hipStream_t stream) {
+  hipLaunchKernelGGL(check_prefix_kernel, dim3(1), dim3(kCheckThreads), 0, stream, lens, tables,
+                     groups, num_groups, shared_lens, num_seqs, max_blocks_per_seq,
+                     log2_block_size, max_context_len, max_members);
   return read_verdict(stream);
 }
 

@@ -448,30 +448,53 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
   }
 }
 
-// Merge of the partition partials of one (sequence, query head): weights
-// l_p * 2^(m_p - max m), summed in ascending partition order.
+// Merge of the partition partials of one (sequence, query head) per wave
+// (four rows per workgroup, D / 64 elements per lane): weights
+// l_p * 2^(m_p - max m), summed in ascending position order.  A row has
+// `slots` partial slots: partitions 0 .. P-1, and with shared prefixes
+// (shared_lens non-null) a last slot holding the prefix, positions
+// [0, shared length), which comes first; partitions that lie wholly inside
+// the shared length were not computed and are skipped.  The shared length is
+// taken as the decode kernel takes it (clamped to the context, whole 16-token
+// tiles).
+constexpr int kMergeRows = 4;
 template <int D>
-__global__ __launch_bounds__(D) void paged_decode_merge_kernel(
+__global__ __launch_bounds__(64 * kMergeRows) void paged_decode_merge_kernel(
     const int32_t *__restrict__ context_lens, const float *__restrict__ ws_o,
-    const float *__restrict__ ws_ml, float *__restrict__ out, int hq, int cap, int ps, int P) {
-  const int row = blockIdx.x;  // s * hq + h
+    const float *__restrict__ ws_ml, float *__restrict__ out, int rows, int hq, int cap, int ps,
+    int P, const int32_t *__restrict__ shared_lens, int slots) {
+  constexpr int EPL = D / 64;  // elements per lane
+  const int row = blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
   const int s = row / hq;
   int L = context_lens[s];
   L = max(0, min(L, cap));  // the same clamp as the decode kernel
   const int n = min((L + ps - 1) / ps, P);
-  if (n <= 1) return;
-  const float *ml = ws_ml + (int64_t)row * P * 2;
-  const float *o = ws_o + (int64_t)row * P * D;
-  float M = ml[0];
-  for (int j = 1; j < n; ++j) M = fmaxf(M, ml[2 * j]);
-  const int d = threadIdx.x;
-  float num = 0.f, den = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float w = ml[2 * j + 1] * __builtin_amdgcn_exp2f(ml[2 * j] - M);
-    num = fmaf(w, o[(int64_t)j * D + d], num);
+  const int sh = shared_lens ? min(max(shared_lens[s], 0), L) & ~15 : 0;
+  if (n <= 1 && sh == 0) return;  // written by the decode kernel directly
+  const int first = sh > 0 ? sh / ps : 0;  // first partition with private positions
+  const float *ml = ws_ml + (int64_t)row * slots * 2;
+  const float *o = ws_o + (int64_t)row * slots * D + lane * EPL;
+  const int pre = slots - 1;  // the prefix slot (used when sh > 0)
+  float M = sh > 0 ? ml[2 * pre] : -__builtin_huge_valf();
+  for (int j = first; j < n; ++j) M = fmaxf(M, ml[2 * j]);
+  float num[EPL], den = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) num[e] = 0.f;
+  auto add = [&](int j) {
+    const float mj = ml[2 * j];
+    const float w = mj == -__builtin_huge_valf() ? 0.f
+                                                 : ml[2 * j + 1] * __builtin_amdgcn_exp2f(mj - M);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, o[(int64_t)j * D + e], num[e]);
     den += w;
-  }
-  out[(int64_t)row * D + d] = num / den;
+  };
+  if (sh > 0) add(pre);
+  for (int j = first; j < n; ++j) add(j);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    out[(int64_t)row * D + lane * EPL + e] = den > 0.f ? num[e] / den : 0.f;
 }
 
 template <typename T, int D, int G, bool SMALLB>
@@ -527,16 +550,20 @@ bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group) {
 hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream) {
   const uint32_t rows = (uint32_t)((int64_t)a.num_seqs * a.num_q_heads);
   const int cap = a.max_blocks_per_seq << a.log2_block_size;
+  const bool pfx = a.num_groups > 0;
+  const int32_t *sh = pfx ? a.shared_lens : nullptr;
+  const int slots = a.num_partitions + (pfx ? 1 : 0);
+  const uint32_t grid = (rows + kMergeRows - 1) / kMergeRows;
   switch (a.head_dim) {
     case 64:
-      hipLaunchKernelGGL((paged_decode_merge_kernel<64>), dim3(rows), dim3(64), 0, stream,
-                         a.context_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, cap,
-                         a.partition_size, a.num_partitions);
+      hipLaunchKernelGGL((paged_decode_merge_kernel<64>), dim3(grid), dim3(64 * kMergeRows), 0,
+                         stream, a.context_lens, a.ws_o, a.ws_ml, a.out, (int)rows,
+                         a.num_q_heads, cap, a.partition_size, a.num_partitions, sh, slots);
       break;
     case 128:
-      hipLaunchKernelGGL((paged_decode_merge_kernel<128>), dim3(rows), dim3(128), 0, stream,
-                         a.context_lens, a.ws_o, a.ws_ml, a.out, a.num_q_heads, cap,
-                         a.partition_size, a.num_partitions);
+      hipLaunchKernelGGL((paged_decode_merge_kernel<128>), dim3(grid), dim3(64 * kMergeRows), 0,
+                         stream, a.context_lens, a.ws_o, a.ws_ml, a.out, (int)rows,
+                         a.num_q_heads, cap, a.partition_size, a.num_partitions, sh, slots);
       break;
     default: return hipErrorNotSupported;
   }
@@ -544,14 +571,18 @@ hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const bool pfx = a.num_groups > 0;
   if (a.order) {
-    const hipError_t e =
-        launch_schedule(a.context_lens, a.order, a.num_seqs, a.num_partitions, a.partition_size,
-                        a.max_blocks_per_seq << a.log2_block_size, stream);
+    const hipError_t e = launch_schedule(
+        a.context_lens, a.order, a.num_seqs, a.num_partitions, a.partition_size,
+        a.max_blocks_per_seq << a.log2_block_size, stream, pfx ? a.groups : nullptr,
+        pfx ? a.shared_lens : nullptr, pfx ? a.num_groups : 0, G);
     if (e != hipSuccess) return e;
   }
   if (a.kv_dtype == 2 || a.kv_dtype == 3 ||  // 8-bit pools: matrix-core kernel only
-      decode_mfma_supported(a.dtype, a.head_dim, a.num_q_heads / a.num_kv_heads))
+      pfx ||                                  // so are shared-prefix items
+      decode_mfma_supported(a.dtype, a.head_dim, G))
     return launch_decode_mfma(a, stream);
   if (a.dtype == 0) return launch_d<float>(a, stream);
   if (a.dtype == 1) return launch_d<uint16_t>(a, stream);

@@ -421,7 +421,22 @@ struct MfmaDecode {
 // last nq positions and row R attends positions up to L - nq + R / gh (the
 // causal mask of multi_query.hip).  Each wave carries NC column sets, which
 // share every K/V load, the V staging and the V^T operand reads.
-template <int G, bool SMALLB, int Q8, bool MQ, int NC = 1>
+//
+// Shared-prefix mode (PFX, decode only): besides the (sequence, partition)
+// items, the launch has items for prefix groups -- a group is a run of
+// `count` consecutive sequences from `first` whose table rows name the same
+// blocks below their shared lengths shared_lens[s].  Item (group, column set
+// c, KV head) reads the group's shared tiles once for 16 (member, query head)
+// pairs: column n is R = 16 c + n (member R / G, head R % G; at most 64 / G
+// members, so at most four sets), walked like a sequence item (tiles
+// round-robin over the four waves) through the table row of the set's
+// member with the longest shared length; column R attends positions below
+// its member's shared length.  A sequence's own items then cover only
+// [shared length, L), and every member's prefix partial and private
+// partials meet in the merge kernel.  Shared lengths are used rounded down
+// to whole 16-token tiles, so a private walk still starts on a tile
+// boundary.
+template <int G, bool SMALLB, int Q8, bool MQ, int NC = 1, bool PFX = false>
 __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_kernel(
     const uint16_t *__restrict__ q,
     const typename MfmaDecode<G, SMALLB, Q8>::KV *__restrict__ kc,
@@ -430,7 +445,8 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
     float v_scale, int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P,
     const int32_t *__restrict__ query_start, int num_tokens, int gh, int max_q, int csets,
-    const int32_t *__restrict__ order) {
+    const int32_t *__restrict__ order, const int32_t *__restrict__ groups,
+    const int32_t *__restrict__ shared_lens, int slots) {
   using K = MfmaDecode<G, SMALLB, Q8>;
   using TileT = typename K::TileT;
   constexpr bool FP8 = K::FP8;
@@ -449,40 +465,91 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     if (id >= num_seqs * hkv * P) return;
   }
   // work item: KV head fastest, then (sequence, partition) from the
-  // longest-first list or the fixed order (as in decode.hip)
+  // longest-first list or the fixed order (as in decode.hip); with PFX, the
+  // prefix-group items follow the num_seqs * P sequence items
   const int kvh = id % hkv;
   const int item = order ? order[id / hkv] : id / hkv;
   if (item < 0) return;  // listed as empty (past the sequence's end)
-  const int s = item % num_seqs;
-  const int p = (P - 1) - item / num_seqs;
   const int hq = hkv * (MQ ? gh : G);
-
-  int L = context_lens[s];
-  L = max(0, min(L, mb << lgB));
-  int qs = 0, nq = 0, ncols[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) ncols[c] = G;
-  if constexpr (MQ) {
-    qs = max(0, min(query_start[s], num_tokens));
-    nq = max(0, min(min(query_start[s + 1] - qs, L), min(max_q, num_tokens - qs)));
-#pragma unroll
-    for (int c = 0; c < NC; ++c) ncols[c] = min(nq * gh - G * (NC * cgroup + c), G);
-    if (ncols[0] <= 0) return;
-  }
-  const int nparts = min((L + ps - 1) / ps, P);
-  if (p >= max(nparts, 1)) return;
-  const int t0 = p * ps;
-  const int t1 = min(L, t0 + ps);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int32_t *tbl = block_tables + (int64_t)s * mb;
+
+  // the walk: tiles cstart(j) = t0 + (wave + 4 j) * 16 of [t0, t1) through
+  // table row tbl
+  bool pitem = false;
+  int s = 0, p = 0, L = 0, nparts = 1, t0 = 0, t1 = 0, sh = 0;
+  int qs = 0, nq = 0, ncols[NC];
+  const int32_t *tbl;
+  // prefix item: its column set, this lane's column (member, head) and its
+  // sequence
+  int pset = 0, pfirst = 0, pmember = 0, pseq = 0;
+  bool pcol = false;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) ncols[c] = G;
+  if constexpr (PFX) pitem = item >= num_seqs * P;
+  if (pitem) {
+    // (PFX only: NC == 1, no multi-query)
+    const int pi = item - num_seqs * P;
+    const int gi = pi >> 2;
+    pset = pi & 3;
+    pfirst = min(max(groups[2 * gi], 0), num_seqs - 1);
+    const int count = min(max(groups[2 * gi + 1], 0), min(num_seqs - pfirst, 64 / G));
+    const int R = 16 * pset + n;
+    pmember = R / G;
+    pcol = pmember < count;
+    pseq = pfirst + min(pmember, max(count - 1, 0));
+    ncols[0] = min(max(count * G - 16 * pset, 0), 16);
+    int shm = 0;
+    if (pcol) {
+      const int Lm = max(0, min(context_lens[pseq], mb << lgB));
+      shm = min(max(shared_lens[pseq], 0), Lm) & ~(kTile - 1);
+    }
+    sh = shm;
+    // the walk covers the longest shared length among the set's columns
+    // (every wave has the same columns; lanes of one column hold the same
+    // value), through the table row of the member that has it: members'
+    // rows name the same blocks below their shared lengths, so that row
+    // serves every column
+    int wmax = shm;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) wmax = max(wmax, __shfl_xor(wmax, off));
+    t1 = __builtin_amdgcn_readfirstlane(wmax);
+    if (t1 <= 0) return;  // the same in every wave: the workgroup leaves whole
+    const uint64_t longest = __builtin_amdgcn_ballot_w64(pcol && shm == wmax);
+    const int walk_seq = __builtin_amdgcn_readlane(pseq, (int)__builtin_ctzll(longest));
+    tbl = block_tables + (int64_t)walk_seq * mb;
+  } else {
+    s = item % num_seqs;
+    p = (P - 1) - item / num_seqs;
+    L = context_lens[s];
+    L = max(0, min(L, mb << lgB));
+    if constexpr (MQ) {
+      qs = max(0, min(query_start[s], num_tokens));
+      nq = max(0, min(min(query_start[s + 1] - qs, L), min(max_q, num_tokens - qs)));
+#pragma unroll
+      for (int c = 0; c < NC; ++c) ncols[c] = min(nq * gh - G * (NC * cgroup + c), G);
+      if (ncols[0] <= 0) return;
+    }
+    nparts = min((L + ps - 1) / ps, P);
+    if (p >= max(nparts, 1)) return;
+    t0 = p * ps;
+    t1 = min(L, t0 + ps);
+    if constexpr (PFX) {
+      // positions below the shared length come from the group's prefix item
+      sh = min(max(shared_lens[s], 0), L) & ~(kTile - 1);
+      if (p < sh / ps) return;  // the whole partition is shared: no partial
+      t0 = max(t0, sh);
+    }
+    tbl = block_tables + (int64_t)s * mb;
+  }
 
   // B operand of q.K for each column set: column n is query head n % G of
   // this KV head (decode), or row 16 c + n of the chunk (multi-query; columns
-  // past the chunk are zero and fully masked)
+  // past the chunk are zero and fully masked), or (member, head) of the
+  // group (prefix item)
   bf16x8 qb[NC][4];
   int cpos[NC];
 #pragma unroll
@@ -501,11 +568,14 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
               bf16x8, *reinterpret_cast<const u32x4 *>(qrow + k_step_elem<FP8>(g, k)));
       }
     } else {
-      const uint16_t *qrow = q + ((int64_t)s * hq + kvh * G + n % G) * kD;
+      const int qseq = pitem ? pseq : s;
+      const int qhead = pitem ? (16 * pset + n) % G : n % G;
+      const uint16_t *qrow = q + ((int64_t)qseq * hq + kvh * G + qhead) * kD;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         qb[c][k] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4 *>(qrow + k_step_elem<FP8>(g, k)));
+      if (pitem) cpos[c] = pcol ? sh - 1 : -1;
     }
   }
 
@@ -523,8 +593,9 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   }
   int slot = 0;
   // the wave's LDS slice: V rows of the pair in the loop, then its results
+  constexpr int kCols = PFX ? 16 : G;  // result columns a wave may hold
   constexpr int kSlice =
-      K::kSliceBytes > G * kD * 4 ? K::kSliceBytes : G * kD * 4;
+      K::kSliceBytes > kCols * kD * 4 ? K::kSliceBytes : kCols * kD * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves][kSlice];
   typename K::KV *slice = reinterpret_cast<typename K::KV *>(smem[wave]);
 
@@ -537,7 +608,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   // full tiles round-robin over the waves (this wave's j-th tile is tile
   // wave + 4j), two-stage register pipeline, the last one or two peeled; the
   // final partial tile goes to the wave it falls to, with masked loads
-  const int nfull = (t1 - t0) / kTile;
+  const int nfull = max(t1 - t0, 0) / kTile;
   const int nw = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
   auto cstart = [&](int j) { return t0 + (wave + kWaves * j) * kTile; };
 
@@ -549,7 +620,8 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   // again soon, so its rows are read normally; every other block's V rows
   // (and K rows, in bfloat16 pools) are streamed with non-temporal loads.
   // (The hint only steers caching; entries past a neighbour's length may
-  // match by chance, which is harmless.)
+  // match by chance, which is harmless.)  A prefix item's tiles are read by
+  // the group's other column sets too and always use ordinary loads.
   int ent_cur = 0, ent_next = 0;
   uint64_t nt_cur = 0, nt_next = 0;
   auto chunk_entries = [&](int c, uint64_t &ntmask) {
@@ -559,9 +631,11 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     if (!SMALLB && cs < t1) {
       const int jb = cs >> lgB;
       e = tbl[jb];
-      const bool prev_same = s > 0 && tbl[jb - mb] == e;
-      const bool next_same = s + 1 < num_seqs && tbl[jb + mb] == e;
-      stream = !prev_same && !next_same;
+      if (!pitem) {
+        const bool prev_same = s > 0 && tbl[jb - mb] == e;
+        const bool next_same = s + 1 < num_seqs && tbl[jb + mb] == e;
+        stream = !prev_same && !next_same;
+      }
     }
     ntmask = __builtin_amdgcn_ballot_w64(stream);
     return e;
@@ -571,7 +645,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   // the j-th tile's block id; stream_v receives its hint
   auto entry = [&](int j, bool &stream_v) {
     if constexpr (SMALLB) {
-      stream_v = true;
+      stream_v = !pitem;
       return 0;
     }
     if (j > 0 && (j & 63) == 0) {
@@ -672,13 +746,16 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   // This wave's results per column, one column set at a time: the maximum m
   // is already the column's; the sum combines the four lane groups; the
   // accumulators (lane (g, n): column n, elements 16 b + 4 g + i) go to the
-  // wave's LDS slice, which its own loop no longer uses.  Columns past G
-  // repeat earlier ones (decode).
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  float *wacc = reinterpret_cast<float *>(smem[wave]);  // [G][kD]
-  // a sequence with one partition goes straight to out (its merge skips it)
-  const bool final_out = nparts <= 1;
+  // wave's LDS slice, which its own loop no longer uses.  A sequence item's
+  // columns past G repeat earlier ones (decode); a prefix item's 16 columns
+  // are all its own.
+  __shared__ float sm_m[kWaves][kCols];
+  __shared__ float sm_l[kWaves][kCols];
+  float *wacc = reinterpret_cast<float *>(smem[wave]);  // [kCols][kD]
+  const int wcols = pitem ? 16 : G;  // distinct columns of this item
+  // a sequence with one partition and no shared prefix goes straight to out
+  // (its merge skips it)
+  const bool final_out = !pitem && nparts <= 1 && sh == 0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     if (ncols[c] <= 0) break;  // the group's later sets are empty too
@@ -686,7 +763,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     float lcol = lsum[c];
     lcol += __shfl_xor(lcol, 16);
     lcol += __shfl_xor(lcol, 32);
-    if (n < G) {
+    if (n < wcols) {
 #pragma unroll
       for (int b = 0; b < 8; ++b)
         *reinterpret_cast<f32x4 *>(wacc + n * kD + 16 * b + 4 * g) = acc[c][b];
@@ -696,7 +773,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < G * kD; i += kThreads) {
+    for (int i = threadIdx.x; i < wcols * kD; i += kThreads) {
       const int h = i / kD;
       const int d = i % kD;
       float M = sm_m[0][h];
@@ -711,20 +788,31 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
         o = fmaf(reinterpret_cast<const float *>(smem[w])[h * kD + d], f, o);
       }
       int64_t row;
+      int slot_of = p;
       if constexpr (MQ) {
         if (h >= ncols[c]) continue;
         const int R = G * (NC * cgroup + c) + h;
         row = (int64_t)(qs + R / gh) * hq + kvh * gh + R % gh;
       } else {
-        row = (int64_t)s * hq + kvh * G + h;
+        if (pitem) {
+          // (member, head) of the group; its prefix partial is the row's
+          // last slot
+          if (h >= ncols[0]) continue;
+          const int R = 16 * pset + h;
+          row = (int64_t)(pfirst + R / G) * hq + kvh * G + R % G;
+          slot_of = slots - 1;
+        } else {
+          row = (int64_t)s * hq + kvh * G + h;
+        }
       }
       if (final_out) {
         out[row * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
       } else {
-        ws_o[(row * P + p) * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
+        const int64_t at = row * slots + slot_of;
+        ws_o[at * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
         if (d == 0) {
-          ws_ml[(row * P + p) * 2 + 0] = M;
-          ws_ml[(row * P + p) * 2 + 1] = ls;
+          ws_ml[at * 2 + 0] = M;
+          ws_ml[at * 2 + 1] = ls;
         }
       }
     }
@@ -735,19 +823,25 @@ template <int G, bool SMALLB, int Q8>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
   using KV = typename MfmaDecode<G, SMALLB, Q8>::KV;
   constexpr bool FP8 = Q8 != 0;  // scaled 8-bit codes
-  const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
+  const bool pfx = a.num_groups > 0;
+  // with groups, four column-set items per group follow the sequence items
+  const int64_t grid =
+      ((int64_t)a.num_seqs * a.num_partitions + (pfx ? 4 * (int64_t)a.num_groups : 0)) *
+      a.num_kv_heads;
   if (grid <= 0) return hipSuccess;
   // the K scale multiplies every score, so it joins the softmax scale
   const float sl2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
-  hipLaunchKernelGGL((paged_decode_mfma_kernel<G, SMALLB, Q8, false>), dim3((uint32_t)grid),
-                     dim3(kThreads), 0, stream, static_cast<const uint16_t *>(a.q),
-                     static_cast<const KV *>(a.k_cache), static_cast<const KV *>(a.v_cache),
-                     a.block_tables, a.context_lens, a.out, a.ws_o, a.ws_ml, sl2,
-                     FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads, a.log2_block_size,
-                     a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions,
-                     nullptr, 0, 0, 0, 1, a.order);
+  auto kernel = pfx ? paged_decode_mfma_kernel<G, SMALLB, Q8, false, 1, true>
+                    : paged_decode_mfma_kernel<G, SMALLB, Q8, false, 1, false>;
+  hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t *>(a.q), static_cast<const KV *>(a.k_cache),
+                     static_cast<const KV *>(a.v_cache), a.block_tables, a.context_lens, a.out,
+                     a.ws_o, a.ws_ml, sl2, FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads,
+                     a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.partition_size,
+                     a.num_partitions, nullptr, 0, 0, 0, 1, a.order, a.groups, a.shared_lens,
+                     a.num_partitions + (pfx ? 1 : 0));
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_partitions <= 1) return e;
+  if (e != hipSuccess || (a.num_partitions <= 1 && !pfx)) return e;
   return launch_partition_merge(a, stream);
 }
 
@@ -778,7 +872,7 @@ hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
                      a.ws_o, a.ws_ml, sl2, FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads,
                      a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.partition_size,
                      a.num_partitions, a.query_start, a.num_tokens, gh, a.max_query_len, csets,
-                     a.order);
+                     a.order, nullptr, nullptr, a.num_partitions);
   return hipGetLastError();
 }
 
@@ -811,6 +905,10 @@ bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
   // faster there (Llama-7B-shaped layer, G = 1: 382 vs 387 us); 8-bit pools
   // run only here, for every G
   return dtype == 1 && head_dim == kD && (group == 4 || group == 8);
+}
+
+bool decode_prefix_supported(int32_t head_dim, int32_t group) {
+  return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 bool decode_q8_supported(int32_t head_dim, int32_t group) {

@@ -27,8 +27,16 @@ struct DecodeArgs {
                            // -1 = dtype
   float k_scale = 1.f;     // 8-bit pools: stored code c means value(c) * scale
   float v_scale = 1.f;
-  int32_t *order = nullptr;  // [S * P] dispatch order of the (sequence, partition) items,
-                             // written by launch_decode_schedule; nullptr = fixed order
+  int32_t *order = nullptr;  // [S * P (+ num_groups)] dispatch order of the (sequence,
+                             // partition) items and the prefix items, written by
+                             // launch_schedule; nullptr = fixed order
+  // shared prefixes (matrix-core kernel only): num_groups > 0 adds four items
+  // (16-column sets) per group and KV head that read the group's shared tiles
+  // once; the partials then have num_partitions + 1 slots per row, the last
+  // one the prefix's
+  const int32_t *groups = nullptr;       // [num_groups][2] (first sequence, members)
+  const int32_t *shared_lens = nullptr;  // [num_seqs] positions read through the group
+  int32_t num_groups = 0;
 };
 
 // Launches with more workgroups than this run their longest items first (a
@@ -41,7 +49,9 @@ bool schedule_wanted(int64_t workgroups, int64_t num_seqs, int64_t P);
 // per partition, cap = the most tokens a sequence may have.  launch_decode
 // and launch_multi_query call it when their args carry an order buffer.
 hipError_t launch_schedule(const int32_t *context_lens, int32_t *order, int num_seqs, int P,
-                           int ps, int cap, hipStream_t stream);
+                           int ps, int cap, hipStream_t stream,
+                           const int32_t *groups = nullptr, const int32_t *shared_lens = nullptr,
+                           int num_groups = 0, int group = 1);
 
 // Enqueues decode (and the partition merge when P > 1).  Returns hipSuccess or
 // the launch error; hipErrorNotSupported when no kernel is compiled for the
@@ -53,6 +63,9 @@ bool decode_supported(int32_t dtype, int32_t head_dim, int32_t group);
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
 // 8-bit (FP8 / INT8) pools with bfloat16 queries: head_dim 128, G in {1, 2, 4, 8}.
 bool decode_q8_supported(int32_t head_dim, int32_t group);
+// Shared-prefix items (bfloat16 or 8-bit pools, bfloat16 q): head_dim 128,
+// G in {1, 2, 4, 8}; at most 64 / G members per group.
+bool decode_prefix_supported(int32_t head_dim, int32_t group);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 
 // Merge of the per-partition partials into `out` (P > 1 only).
@@ -126,6 +139,10 @@ int32_t check_tables(const int32_t *lens, const int32_t *tables, int32_t num_seq
                      int32_t max_context_len, hipStream_t stream);
 int32_t check_queries(const int32_t *lens, const int32_t *query_start, int32_t num_seqs,
                       int32_t num_tokens, int32_t max_query_len, hipStream_t stream);
+int32_t check_prefix_groups(const int32_t *lens, const int32_t *tables, const int32_t *groups,
+                            int32_t num_groups, const int32_t *shared_lens, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t log2_block_size,
+                            int32_t max_context_len, int32_t max_members, hipStream_t stream);
 int32_t check_slots(const int32_t *slots, int32_t num_tokens, int64_t num_slots,
                     hipStream_t stream);
 int32_t check_pairs(const int32_t *pairs, int32_t num_pairs, int32_t num_blocks,

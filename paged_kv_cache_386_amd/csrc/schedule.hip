@@ -12,8 +12,12 @@
 //
 // Item c (c < num_seqs * P) is sequence c % num_seqs and partition
 // P - 1 - c / num_seqs -- the fixed order's numbering; an item past its
-// sequence's last partition is listed as ~c, so that its workgroups exit
-// without reading the context length.  Items are bucketed by
+// sequence's last partition (or, with shared prefixes, wholly inside its
+// shared length) is listed as ~c, so that its workgroups exit without
+// reading the context length.  With shared prefixes, items num_seqs * P +
+// 4 i + c are column set c of prefix group i, sized by the longest shared
+// length among the members with columns in that set (empty when there are
+// none).  Items are bucketed by
 // token count (512 size classes of 2^shift tokens, longest class first; an
 // item past the sequence's last partition, which does no work, sorts last)
 // with a counting sort in LDS that keeps, within a class, the fixed order
@@ -48,7 +52,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 //     a wave.
 __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
     const int32_t *__restrict__ context_lens, int32_t *__restrict__ order, int num_seqs, int P,
-    int ps, int cap, int shift) {
+    int ps, int cap, int shift, const int32_t *__restrict__ groups,
+    const int32_t *__restrict__ shared_lens, int num_groups, int G) {
   // class-major, so one thread reads a class's 16 wave counts as 4 vectors
   __shared__ __attribute__((aligned(16))) int start[kSizeClasses + 1][kSchedWaves];
   __shared__ int wave_total[kSchedWaves];
@@ -56,18 +61,44 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n = num_seqs * P;
+  const int nseq_items = num_seqs * P;
+  const int n = nseq_items + 4 * num_groups;
   const int chunk = ((n + kSchedWaves - 1) / kSchedWaves + 63) / 64 * 64;
   const int begin = min(n, wave * chunk), end = min(n, begin + chunk);
 
+  // a sequence's shared length as the decode kernel takes it
+  auto shared = [&](int s, int L) {
+    return shared_lens ? min(max(shared_lens[s], 0), L) & ~15 : 0;
+  };
   // the same clamps and partition bounds as the decode kernels
   auto size_class = [&](int c) -> int {
-    const int s = c % num_seqs;
-    const int p = (P - 1) - c / num_seqs;
-    const int L = max(0, min(context_lens[s], cap));
-    const int nparts = min((L + ps - 1) / ps, P);
-    if (p >= max(nparts, 1)) return kSizeClasses;
-    const int tokens = min(L, p * ps + ps) - p * ps;
+    int tokens;
+    if (c >= nseq_items) {
+      // a prefix item (group gi, column set c & 3): it walks the longest
+      // shared length among the members with columns in its set
+      const int gi = (c - nseq_items) >> 2;
+      const int cset = (c - nseq_items) & 3;
+      const int first = min(max(groups[2 * gi], 0), num_seqs - 1);
+      const int count = min(max(groups[2 * gi + 1], 0), min(num_seqs - first, 64 / G));
+      const int m1 = min(count, (16 * cset + 15) / G + 1);
+      int longest = 0;
+      for (int m = 16 * cset / G; m < m1; ++m) {
+        const int L = max(0, min(context_lens[first + m], cap));
+        longest = max(longest, shared(first + m, L));
+      }
+      if (longest == 0) return kSizeClasses;
+      tokens = longest;
+    } else {
+      const int s = c % num_seqs;
+      const int p = (P - 1) - c / num_seqs;
+      const int L = max(0, min(context_lens[s], cap));
+      const int nparts = min((L + ps - 1) / ps, P);
+      if (p >= max(nparts, 1)) return kSizeClasses;
+      const int sh = shared(s, L);
+      if (p < sh / ps) return kSizeClasses;  // wholly inside the shared prefix
+      // (zero tokens still runs: it writes the empty partial the merge reads)
+      tokens = max(0, min(L, p * ps + ps) - max(p * ps, sh));
+    }
     return (kSizeClasses - 1) - min(tokens >> shift, kSizeClasses - 1);
   };
 
@@ -131,13 +162,15 @@ bool schedule_wanted(int64_t workgroups, int64_t num_seqs, int64_t P) {
 }
 
 hipError_t launch_schedule(const int32_t *context_lens, int32_t *order, int num_seqs, int P,
-                           int ps, int cap, hipStream_t stream) {
+                           int ps, int cap, hipStream_t stream, const int32_t *groups,
+                           const int32_t *shared_lens, int num_groups, int group) {
   // one partition spans every clamped context: size the classes by the cap
   if (P <= 1) ps = cap;
   int shift = 0;
   while ((ps >> shift) >= kSizeClasses) ++shift;
   hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream,
-                     context_lens, order, num_seqs, P, ps, cap, shift);
+                     context_lens, order, num_seqs, P, ps, cap, shift, groups, shared_lens,
+                     num_groups, group);
   return hipGetLastError();
 }
 

@@ -64,10 +64,18 @@ int main(void) {
   pa_engine_destroy(e);
 
   /* size queries and argument checks of the device calls (nothing launched) */
-  CHECK(paged_attention_num_partitions(256, 8, 8192, 0) == 4);
+  CHECK(paged_attention_num_partitions(256, 8, 8192, 0) == 2);
   CHECK(paged_attention_workspace_size(256, 32, 8, 128, 8192, 0) ==
-        (size_t)256 * 32 * 4 * 130 * 4 + (size_t)256 * 4 * 4); /* partials + dispatch list */
-  CHECK(paged_attention_multi_query_partitions(256, 32, 8, 5, 8192, 0) == 4);
+        (size_t)256 * 32 * 2 * 130 * 4 + (size_t)256 * 2 * 4); /* partials + dispatch list */
+  CHECK(paged_attention_multi_query_partitions(256, 32, 8, 5, 8192, 0) == 2);
+  /* shared prefixes: one more partial slot per row, four list entries per group */
+  CHECK(paged_attention_prefix_workspace_size(256, 32, 8, 128, 8192, 0, 16, PA_BF16) ==
+        (size_t)256 * 32 * 3 * 130 * 4 + (size_t)(256 * 2 + 4 * 16) * 4);
+  CHECK(paged_attention_prefix_workspace_size(256, 32, 8, 128, 8192, 0, 16, PA_F32) ==
+        paged_attention_workspace_size(256, 32, 8, 128, 8192, 0));
+  CHECK(paged_attention_decode_prefix(NULL, NULL, NULL, NULL, NULL, NULL, 3, NULL, 0.1f, 1.f,
+                                      1.f, NULL, 2, 8, 2, 128, 16, 8, 4, 64, PA_BF16, 0, NULL, 0,
+                                      NULL) == PA_ERR_SHAPE); /* more groups than sequences */
   CHECK(paged_attention_decode(NULL, NULL, NULL, NULL, NULL, 0.1f, NULL, 1, 4, 2, 96, 16, 8, 4,
                                64, PA_BF16, 0, NULL, 0, NULL) == PA_ERR_UNSUPPORTED);
   CHECK(kv_cache_write_fp8(NULL, NULL, NULL, 1, NULL, NULL, 8, 16, 2, 128, PA_BF16, 0.f, 1.f,

@@ -1,0 +1,296 @@
+"""Decode with shared prefixes read once per group
+(paged_attention_decode_prefix) through the C ABI against the oracle (needs
+an MI355X).
+
+The groups only change which reads are shared, so the oracle is plain paged
+decode on the same tables.  Covered: the GQA prefix-sharing batch and the
+continuous-batching fork step at full size in the benchmark's launch
+configuration (every output element); prefix and fork workloads at every G,
+several block and partition sizes, over bfloat16, FP8 and INT8 pools;
+hand-made groups and shared lengths at the edges (a member sharing nothing,
+a whole context shared, shared lengths off the 16-token grid or ending on a
+partition edge, a short first member, waves with no columns); dominant tiles
+at the prefix walk's block-id rollovers; bitwise determinism and invariance
+under relabelling physical blocks; an fp32 pool (groups ignored: bit for bit
+plain decode); and index checking of bad groups.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8, int8
+from oracle import oracle as O
+from workloads import (make_case, make_fork_case, make_fp8_case, make_int8_case,
+                       make_prefix_case, make_private_case)
+from workloads.generate import bf16_bits_from_f32, permute_pool, settle_step
+
+from gpu_helpers import REGRESS, TOL, DeviceCase, check_indices, max_err, oracle_step, say, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_386_amd as pa
+    pa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def host_groups(case, min_shared=16):
+    import paged_kv_cache_386_amd as pa
+    return pa.prefix_groups(case.block_tables, case.context_lens, case.block_size,
+                            case.num_q_heads, case.num_kv_heads, min_shared)
+
+
+def run_prefix(case, groups, shared, ps=0, pool=None, kind=None, scales=(1.0, 1.0), tables=None):
+    """paged_attention_decode_prefix on the case's tables (after its step)."""
+    import paged_kv_cache_386_amd as pa
+    check_indices(case)
+    if pool is None:
+        kc, vc = to_torch(case.k_cache, case.dtype), to_torch(case.v_cache, case.dtype)
+    else:
+        kc, vc = (torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in pool)
+    tb = case.block_tables if tables is None else tables
+    out = torch.full(case.q.shape, 7.0, dtype=torch.float32, device="cuda")
+    g = torch.from_numpy(np.ascontiguousarray(groups, np.int32).reshape(-1, 2)).cuda()
+    sh = torch.from_numpy(np.ascontiguousarray(shared, np.int32)).cuda()
+    pa.paged_attention_decode_prefix(
+        to_torch(case.q, "bf16" if pool is not None else case.dtype), kc, vc,
+        torch.from_numpy(np.ascontiguousarray(tb)).cuda(),
+        torch.from_numpy(case.context_lens).cuda(), g, sh, float(case.scale), out,
+        max_context_len=case.max_context_len, k_scale=scales[0], v_scale=scales[1],
+        partition_size=ps)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_decode(case):
+    return O.paged_attention_decode(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                    case.context_lens, case.scale, case.block_size, case.dtype)
+
+
+def compare(case, groups, shared, name, ps=0):
+    say(f"{name}: S={case.num_seqs} G={case.num_q_heads // case.num_kv_heads} "
+        f"B={case.block_size} ps={ps} groups={len(groups)} shared={int(np.sum(shared))}")
+    got = run_prefix(case, groups, shared, ps)
+    err = max_err(got, oracle_decode(case))
+    say(f"{name}: max abs err {err:.3e}")
+    assert err <= TOL[case.dtype] and err <= REGRESS[case.dtype], f"{name}: {err}"
+    return got
+
+
+# ---------------------------------------------------------------- full size
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_named_workload_full_size(cfg):
+    """Every output of the prefix-sharing batch (16 groups of 16 sequences)
+    and of the fork step (groups of 4 siblings), with the groups the host
+    finds, in the benchmark's launch configuration."""
+    c = settle_step(make_case(cfg))
+    g, sh = host_groups(c)
+    say(f"cfg{cfg} prefix: {len(g)} groups, {int(sh.sum())} shared of "
+        f"{int(c.context_lens.sum())} tokens")
+    assert len(g) >= 16
+    compare(c, g, sh, f"cfg{cfg}-prefix-full")
+
+
+# ---------------------------------------------------------------- small workloads
+
+@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("B", [4, 16, 64])
+def test_prefix_workloads(G, Hkv, B):
+    rng = np.random.default_rng(10 * G + B)
+    lens = np.clip(np.rint(rng.lognormal(np.log(300), 1.0, 48)), 1, 2500).astype(int)
+    c = settle_step(make_prefix_case(f"pfx-G{G}-B{B}", lens, 16, 256, G * Hkv, Hkv, 128, B,
+                                     "bf16", 10 * G + B))
+    g, sh = host_groups(c)
+    assert len(g) > 0
+    for ps in (0, -1, 64, 512):
+        compare(c, g, sh, f"pfx-G{G}-B{B}", ps)
+
+
+@pytest.mark.parametrize("G,Hkv", [(4, 2), (8, 1), (1, 4)])
+def test_fork_workloads(G, Hkv):
+    rng = np.random.default_rng(G)
+    lens = rng.integers(16, 1500, size=40)
+    c = settle_step(make_fork_case(f"fork-G{G}", lens, 8, 4, G * Hkv, Hkv, 128, 16, "bf16", G))
+    g, sh = host_groups(c)
+    assert len(g) >= 8
+    for ps in (0, 128):
+        compare(c, g, sh, f"fork-G{G}", ps)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "int8"])
+@pytest.mark.parametrize("G,Hkv", [(4, 2), (1, 4), (8, 1)])
+def test_8bit_pools(kind, G, Hkv):
+    rng = np.random.default_rng(G + 3)
+    lens = np.clip(np.rint(rng.lognormal(np.log(400), 1.0, 32)), 1, 3000).astype(int)
+    base = settle_step(make_prefix_case(f"pfx8-{kind}-G{G}", lens, 16, 512, G * Hkv, Hkv, 128,
+                                        16, "bf16", G + 3))
+    c8 = (make_fp8_case if kind == "fp8" else make_int8_case)(base, G + 3)
+    g, sh = host_groups(base)
+    ref_fn = fp8.paged_attention_decode_fp8 if kind == "fp8" else int8.paged_attention_decode_int8
+    ref = ref_fn(base.q, c8.k8, c8.v8, base.block_tables, base.context_lens, base.scale,
+                 base.block_size, "bf16", c8.k_scale, c8.v_scale)
+    for ps in (0, -1, 256):
+        say(f"{kind} prefix G={G} ps={ps}: {len(g)} groups")
+        got = run_prefix(base, g, sh, ps, pool=(c8.k8, c8.v8), kind=kind,
+                         scales=(float(c8.k_scale), float(c8.v_scale)))
+        err = max_err(got, ref)
+        say(f"{kind} prefix G={G} ps={ps}: max abs err {err:.3e}")
+        assert err <= TOL["bf16"], err
+
+
+def test_full_size_fp8_prefix_workload():
+    base = settle_step(make_case(2))
+    c8 = make_fp8_case(base, 2)
+    g, sh = host_groups(base)
+    say("fp8 cfg2 prefix, full size")
+    got = run_prefix(base, g, sh, 0, pool=(c8.k8, c8.v8), kind="fp8",
+                     scales=(float(c8.k_scale), float(c8.v_scale)))
+    ref = fp8.paged_attention_decode_fp8(base.q, c8.k8, c8.v8, base.block_tables,
+                                         base.context_lens, base.scale, base.block_size, "bf16",
+                                         c8.k_scale, c8.v_scale)
+    err = max_err(got, ref)
+    say(f"fp8 cfg2 prefix full size: all {got.size} outputs, max abs err {err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
+# ---------------------------------------------------------------- edges
+
+def shared_block_case(lens, G, Hkv, B, seed, shared_blocks):
+    """Private-case pool whose sequences' first shared_blocks[s] table entries
+    are replaced by those of sequence 0 (so they read sequence 0's blocks
+    there)."""
+    c = make_private_case(f"edge-{seed}", lens, G * Hkv, Hkv, 128, B, "bf16", seed)
+    tb = c.block_tables.copy()
+    for s, k in enumerate(shared_blocks):
+        tb[s, :k] = tb[0, :k]
+    c.block_tables = tb
+    return c
+
+
+@pytest.mark.parametrize("G,Hkv", [(4, 2), (8, 1), (2, 2)])
+def test_hand_made_groups(G, Hkv):
+    B = 16
+    lens = [700, 700, 33, 512, 640, 100, 257, 900, 64, 700]
+    # table entries taken from sequence 0 (never past its 688 full-block
+    # tokens for sequences that run past them)
+    blocks = [44, 44, 3, 32, 40, 7, 17, 43, 4, 44]
+    c = shared_block_case(lens, G, Hkv, B, 50 + G, blocks)
+    # one group over all ten (at most 64 / G members: split if needed);
+    # shared lengths: a member sharing nothing, one sharing its whole context
+    # (512, on a 512-token partition edge), lengths off the tile grid (33,
+    # 250 -> 240), the first member's whole context
+    sh = np.array([700, 690, 33, 512, 600, 0, 250, 688, 64, 17], np.int32)
+    maxm = 64 // G
+    groups = [[f, min(maxm, 10 - f)] for f in range(0, 10, maxm)]
+    # group starts other than sequence 0 need their own members to agree:
+    # the tables above agree with sequence 0 below every shared length
+    for ps in (0, -1, 32, 512):
+        compare(c, groups, sh, f"hand-G{G}", ps)
+
+
+def test_waves_without_columns_and_single_member_groups():
+    """Two members at G = 4 fill 8 of a prefix item's 64 columns (waves 1-3
+    have none); a group of one member reads its own prefix."""
+    c = shared_block_case([300, 300, 200, 50], 4, 2, 16, 61, [18, 18, 12, 3])
+    sh = np.array([290, 288, 192, 48], np.int32)
+    compare(c, [[0, 2], [2, 1], [3, 1]], sh, "sparse-groups", 0)
+    compare(c, [[0, 2], [2, 1], [3, 1]], sh, "sparse-groups", 64)
+
+
+def test_f32_pool_ignores_groups():
+    import paged_kv_cache_386_amd as pa
+    c = shared_block_case([300, 300, 200], 4, 2, 16, 62, [18, 18, 12])
+    c.q = (c.q.astype(np.uint32) << 16).view(np.float32)
+    c.k_cache = (c.k_cache.astype(np.uint32) << 16).view(np.float32)
+    c.v_cache = (c.v_cache.astype(np.uint32) << 16).view(np.float32)
+    c.dtype = "f32"
+    sh = np.array([288, 288, 192], np.int32)
+    got = run_prefix(c, [[0, 3]], sh, 64)
+    dc = DeviceCase(c)
+    want = dc.run_decode(64).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert pa.prefix_workspace_size(3, 8, 2, 128, 300, 64, 1, pa.PA_F32) == \
+        pa.workspace_size(3, 8, 2, 128, 300, 64)
+
+
+def test_determinism_and_permutation_invariance():
+    rng = np.random.default_rng(70)
+    lens = np.clip(np.rint(rng.lognormal(np.log(300), 1.0, 32)), 1, 2000).astype(int)
+    c = settle_step(make_prefix_case("pfx-perm", lens, 16, 256, 32, 8, 128, 16, "bf16", 70))
+    g, sh = host_groups(c)
+    say(f"prefix determinism: {len(g)} groups")
+    a = run_prefix(c, g, sh, 64)
+    b = run_prefix(c, g, sh, 64)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    k2, v2, t2, _, _, _ = permute_pool(c, 7)
+    c.k_cache, c.v_cache, c.block_tables = k2, v2, t2
+    say("prefix determinism: relabelled pool")
+    p = run_prefix(c, g, sh, 64)
+    assert np.array_equal(a.view(np.uint32), p.view(np.uint32))
+
+
+# ---------------------------------------------------------------- long shared prefixes
+
+def test_dominant_tiles_in_long_shared_prefix():
+    """A group of four sequences sharing 8992 tokens (562 tiles), all with one
+    query u: spike tiles (keys scoring 40 above the rest) at the prefix walk's
+    block-id rollovers (each wave of a prefix item walks every tile, so tiles
+    63/64/127/128), at its last shared tile, and one in each member's private
+    part.  Each member's output must be the mean V of its spike tiles."""
+    B, L, S, G, Hkv = 16, 12000, 4, 4, 1
+    c = shared_block_case([L] * S, G, Hkv, B, 80, [9000 // B] * S)
+    u_bits = bf16_bits_from_f32(np.random.default_rng(81).standard_normal(128,
+                                                                         dtype=np.float32))
+    c.q = np.broadcast_to(u_bits, (S, G * Hkv, 128)).copy()
+    u = (u_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    kst = bf16_bits_from_f32((40.0 / (float(c.scale) * float(u @ u)) * u).astype(np.float32))
+    sh = np.full(S, 9000 // B * B, np.int32)
+    k = c.k_cache.copy()
+    want = np.zeros((S, 128))
+    for s in range(S):
+        tiles = [63, 64, 127, 128, 9000 // 16 - 1, 600 + 37 * s]
+        pos = np.concatenate([np.arange(16 * t, 16 * t + 16) for t in tiles])
+        blk, off = c.block_tables[s, pos // B], pos % B
+        k[blk, 0, off] = kst
+        vv = (c.v_cache[blk, 0, off].astype(np.uint32) << 16).view(np.float32)
+        want[s] = vv.astype(np.float64).mean(axis=0)
+    c.k_cache = k
+    for ps in (0, -1):
+        say(f"prefix spikes ps={ps}")
+        got = run_prefix(c, [[0, S]], sh, ps)
+        err = float(np.abs(got - want[:, None, :]).max())
+        say(f"prefix spikes ps={ps}: max abs err {err:.3e}")
+        assert err <= 1e-4, err
+
+
+# ---------------------------------------------------------------- index checking
+
+def test_index_check_rejects_bad_groups():
+    import paged_kv_cache_386_amd as pa
+    c = shared_block_case([300, 300, 200, 120], 4, 2, 16, 90, [18, 18, 12, 0])
+    good_sh = np.array([288, 288, 192, 0], np.int32)
+    base = run_prefix(c, [[0, 3]], good_sh, 64)
+    pa.set_index_check(True)
+    try:
+        same = run_prefix(c, [[0, 3]], good_sh, 64)
+        assert np.array_equal(base.view(np.uint32), same.view(np.uint32))
+        bad_cases = [
+            ([[0, 3]], np.array([288, 288, 192, 16], np.int32)),   # non-member shares
+            ([[0, 3]], np.array([288, 288, 201 + 100, 0], np.int32)),  # beyond L
+            ([[0, 4]], np.array([288, 288, 192, 64], np.int32)),   # member rows disagree
+            ([[2, 2], [0, 3]], good_sh),                            # not ascending
+            ([[0, 17]], good_sh),                                   # too many members
+        ]
+        for groups, sh in bad_cases:
+            say(f"index check: groups {groups} shared {sh.tolist()}")
+            with pytest.raises(pa.PagedAttnError) as e:
+                run_prefix(c, groups, sh, 64)
+            assert e.value.status == pa.PA_ERR_INDEX
+    finally:
+        pa.set_index_check(False)

@@ -48,7 +48,7 @@ def _cases():
 def test_noalloc_matches_allocating_decode():
     import paged_kv_cache_386_amd as pa
     big, small = _cases()
-    runs = [(big, 0), (small, 512), (big, 0)]
+    runs = [(big, 2048), (small, 512), (big, 2048)]
     for case, ps in runs:
         need = pa.workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                  case.head_dim, case.max_context_len, ps)
