@@ -649,6 +649,9 @@ def main() -> int:
                     help="the workload over an FP8 (E4M3) pool: quantising write and FP8 decode")
     ap.add_argument("--kv-int8", action="store_true",
                     help="the workload over an INT8 pool: quantising write and INT8 decode")
+    ap.add_argument("--device-sort", action="store_true",
+                    help="sort the work on the device in every call instead of passing the "
+                         "dispatch list planned on the host (paged_attention_decode_plan)")
     ap.add_argument("--no-prefix", action="store_true",
                     help="plain paged_attention_decode even where sequences share prefixes "
                          "(default: paged_attention_decode_prefix with the groups "
@@ -756,12 +759,22 @@ def main() -> int:
     if not args.no_prefix:
         groups_np, shared_np = pa.prefix_groups(case.block_tables, case.context_lens,
                                                 case.block_size, Hq, Hkv, 16)
-    use_prefix = len(groups_np) > 0
     kv_code = pa.PA_BF16 if c8 is None else (pa.PA_FP8_E4M3 if args.kv_fp8 else pa.PA_INT8)
     if case.dtype == "f32":
         kv_code = pa.PA_F32
+    # the dispatch list, planned on the host from the lengths it knows (as
+    # the tables and groups are); --device-sort sorts in every call instead
+    dispatch_np = None
+    if not args.device_sort:
+        dispatch_np = pa.decode_plan(case.context_lens, groups_np, shared_np, num_q_heads=Hq,
+                                     num_kv_heads=Hkv, head_dim=D, block_size=case.block_size,
+                                     max_blocks_per_seq=case.max_blocks_per_seq,
+                                     max_context_len=max_ctx, kv_dtype=kv_code,
+                                     partition_size=args.partition_size)
+    use_prefix = len(groups_np) > 0 or dispatch_np is not None
+    dispatch_d = None if dispatch_np is None else torch.from_numpy(dispatch_np).to(dev)
     if use_prefix:
-        groups_d = torch.from_numpy(groups_np).to(dev)
+        groups_d = torch.from_numpy(groups_np.reshape(-1, 2)).to(dev)
         shared_d = torch.from_numpy(shared_np).to(dev)
         ws_bytes = pa.prefix_workspace_size(S, Hq, Hkv, D, max_ctx, args.partition_size,
                                             len(groups_np), kv_code)
@@ -785,7 +798,8 @@ def main() -> int:
                 q, kc, vc, tables, lens, groups_d, shared_d, float(case.scale), out,
                 max_context_len=max_ctx, k_scale=1.0 if c8 is None else float(c8.k_scale),
                 v_scale=1.0 if c8 is None else float(c8.v_scale),
-                partition_size=args.partition_size, workspace=ws, stream=stream)
+                partition_size=args.partition_size, workspace=ws, dispatch=dispatch_d,
+                stream=stream)
         elif c8 is None:
             pa.paged_attention_decode(q, kc, vc, tables, lens, float(case.scale), out,
                                       max_context_len=max_ctx,
@@ -862,9 +876,11 @@ def main() -> int:
             "partition_size": ps if P > 1 else None, "num_partitions": P,
             "prefix_groups": int(len(groups_np)),
             "shared_tokens": int(shared_np.sum()),
+            "dispatch": "device sort" if dispatch_np is None else "planned on the host",
             "step": ("copy_blocks + kv_cache_write + " if has_step else "") +
-                    ("paged_attention_decode_prefix (shared prefixes read once per group; "
-                     "+ merge)" if use_prefix else "paged_attention_decode (+ split-K merge)"),
+                    ("paged_attention_decode_prefix (shared prefixes read once per group, "
+                     "dispatch list planned on the host; + merge)" if use_prefix else
+                     "paged_attention_decode (+ split-K merge)"),
         },
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "decode_us": round(dec_us, 2),
@@ -873,9 +889,10 @@ def main() -> int:
                           for k, q in (("p10", 10), ("p50", 50), ("p90", 90))},
         "roofline": {
             "bound": "hbm",
-            "kernel": ("paged_attention_decode_prefix (dispatch sort, decode kernel with the "
-                       "prefix items, merge; one call)" if use_prefix else
-                       "paged_attention_decode (decode kernel + partition merge, one call)"),
+            "kernel": ("paged_attention_decode_prefix (decode kernel with the prefix items, "
+                       "merge; one call)" if use_prefix else
+                       "paged_attention_decode (dispatch sort, decode kernel, partition merge; "
+                       "one call)"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

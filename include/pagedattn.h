@@ -172,6 +172,14 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
  *                  group must name the same blocks below the shorter of
  *                  their two shared lengths.  Lengths are used rounded down
  *                  to whole 16-token tiles.
+ *   dispatch       device int32 list of the launch's work items in the order
+ *                  to run them, as paged_attention_decode_plan writes it for
+ *                  the same arguments (planned on the host, where the lengths
+ *                  are known, instead of sorted on the device), or NULL to
+ *                  sort on the device as paged_attention_decode does.  The
+ *                  order changes timing only; the list must hold every item
+ *                  of the launch exactly once (entries that are not an item
+ *                  of it are skipped and their outputs go unwritten)
  *   kv_dtype       the pool's element type: PA_F32 or PA_BF16 (q the same),
  *                  PA_FP8_E4M3 or PA_INT8 (q bfloat16; k_scale and v_scale as
  *                  in paged_attention_decode_fp8; ignored otherwise)
@@ -193,13 +201,38 @@ int32_t paged_attention_decode(const void *q, const void *k_cache, const void *v
 int32_t paged_attention_decode_prefix(const void *q, const void *k_cache, const void *v_cache,
                                       const int32_t *block_tables, const int32_t *context_lens,
                                       const int32_t *prefix_groups, int32_t num_groups,
-                                      const int32_t *shared_lens, float scale, float k_scale,
-                                      float v_scale, float *out, int32_t num_seqs,
-                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t block_size, int32_t num_blocks,
+                                      const int32_t *shared_lens, const int32_t *dispatch,
+                                      float scale, float k_scale, float v_scale, float *out,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
                                       int32_t kv_dtype, int32_t partition_size, void *workspace,
                                       size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_decode_plan -- the dispatch list of
+ * paged_attention_decode_prefix for these arguments, computed on the host:
+ * every work item of the launch (the (sequence, partition) items, then four
+ * 16-column items per prefix group when the prefix path runs), longest first
+ * by tokens to attend, equal sizes in item order, items with no work last.
+ * A launch starts workgroups in list order, so the long items no longer
+ * finish last (the longest-processing-time rule of list scheduling).
+ *
+ *   context_lens, prefix_groups, shared_lens   host copies of the device
+ *                  arrays the call will get (groups and shared lengths may
+ *                  be NULL when num_groups is 0)
+ *   dispatch       host int32 out, capacity entries
+ * Every other argument is paged_attention_decode_prefix's.  Returns the
+ * number of entries written (num_seqs * P + 4 * groups on the prefix path),
+ * or PA_ERR_NULL, PA_ERR_SHAPE (including capacity too small), PA_ERR_DTYPE.
+ */
+int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *prefix_groups,
+                                    int32_t num_groups, const int32_t *shared_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    int32_t kv_dtype, int32_t partition_size, int32_t *dispatch,
+                                    int32_t capacity);
 
 /* Workspace bytes of paged_attention_decode_prefix: with the prefix path,
  * 4 * num_seqs * num_q_heads * (P + 1) * (head_dim + 2) for the partials plus
@@ -525,7 +558,10 @@ int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cac
  *     every chunk at most its context length and max_query_len;
  *   kv_cache_write (_fp8, _int8) checks every slot < num_blocks*block_size
  *     (negative slots are padding);
- *   copy_blocks checks both ids of every pair in [0, num_blocks).
+ *   copy_blocks checks both ids of every pair in [0, num_blocks);
+ *   paged_attention_decode_prefix also checks the groups and shared lengths
+ *     (the rules stated there) and that a given dispatch list holds every
+ *     item exactly once (lists of at most 65536 items).
  * A check runs one small kernel on the call's stream, synchronises that
  * stream and reads back one device word the library owns (one per device;
  * calls that overlap on one device race on it); on a bad index the call

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     PA_INT8,
     PagedAttnError,
     copy_blocks,
+    decode_plan,
     index_check,
     kv_cache_write,
     kv_cache_write_fp8,

@@ -34,10 +34,12 @@ SIGNATURES = {
     "paged_attention_decode": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
                                       _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                       _VP, ctypes.c_size_t, _VP]),
-    "paged_attention_decode_prefix": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP,
+    "paged_attention_decode_prefix": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP,
                                              ctypes.c_float, ctypes.c_float, ctypes.c_float, _VP,
                                              _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                              _I32, _I32, _VP, ctypes.c_size_t, _VP]),
+    "paged_attention_decode_plan": (_I32, [_VP, _VP, _I32, _VP, _I32, _I32, _I32, _I32, _I32,
+                                           _I32, _I32, _I32, _I32, _VP, _I32]),
     "paged_attention_prefix_workspace_size": (ctypes.c_size_t, [_I32] * 8),
     "pa_prefix_groups": (_I32, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
     "paged_attention_decode_noalloc": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP,
@@ -268,16 +270,43 @@ def prefix_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, he
         num_groups, kv_dtype))
 
 
+def decode_plan(context_lens, groups, shared_lens, *, num_q_heads: int, num_kv_heads: int,
+                head_dim: int, block_size: int, max_blocks_per_seq: int, max_context_len: int,
+                kv_dtype: int, partition_size: int = 0):
+    """The dispatch list of paged_attention_decode_prefix planned on the host
+    (paged_attention_decode_plan): numpy int32.  ``context_lens``,
+    ``groups`` ([n, 2] or None) and ``shared_lens`` are host arrays."""
+    import numpy as np
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = int(lens.shape[0])
+    ng = 0 if groups is None else int(len(groups))
+    g = np.ascontiguousarray(groups if ng else np.zeros((1, 2)), dtype=np.int32)
+    sh = np.ascontiguousarray(shared_lens if ng else np.zeros(max(S, 1)), dtype=np.int32)
+    P = num_partitions(S, num_kv_heads, max_context_len, partition_size)
+    if P < 0:
+        raise PagedAttnError("paged_attention_num_partitions", P)
+    cap = max(S * P + 4 * ng, 1)
+    out = np.zeros(cap, np.int32)
+    n = lib().paged_attention_decode_plan(
+        lens.ctypes.data, g.ctypes.data if ng else 0, ng, sh.ctypes.data if ng else 0, S,
+        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        int(max_context_len), int(kv_dtype), int(partition_size), out.ctypes.data, cap)
+    if n < 0:
+        raise PagedAttnError("paged_attention_decode_plan", n)
+    return out[:n].copy()
+
+
 def paged_attention_decode_prefix(q, k_cache, v_cache, block_tables, context_lens, groups,
                                   shared_lens, scale: float, out, *, max_context_len: int,
                                   k_scale: float = 1.0, v_scale: float = 1.0,
-                                  partition_size: int = 0, workspace=None,
+                                  partition_size: int = 0, workspace=None, dispatch=None,
                                   stream=None) -> None:
     """Decode with shared prefixes read once per group (see
     include/pagedattn.h).  ``groups``: device int32 [n, 2] (first sequence,
     members); ``shared_lens``: device int32 [S].  The pool may be float32,
     bfloat16, or 8-bit codes (uint8 = FP8 E4M3, int8 = INT8, with bfloat16 q
-    and the two scales)."""
+    and the two scales).  ``dispatch``: an optional device int32 list from
+    ``decode_plan`` (else the device sorts the work)."""
     import torch
     S, Hq, D = q.shape
     NB, Hkv, B, D2 = k_cache.shape
@@ -297,7 +326,8 @@ def paged_attention_decode_prefix(q, k_cache, v_cache, block_tables, context_len
         raise ValueError("groups and shared_lens must be contiguous")
     st = lib().paged_attention_decode_prefix(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-        _ptr(groups) if ng else 0, ng, _ptr(shared_lens) if ng else 0, float(scale),
+        _ptr(groups) if ng else 0, ng, _ptr(shared_lens) if ng else 0, _ptr(dispatch),
+        float(scale),
         float(k_scale), float(v_scale), _ptr(out), S, Hq, Hkv, D, B, NB, MB,
         int(max_context_len), kv, int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream))

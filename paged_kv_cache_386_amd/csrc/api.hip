@@ -5,7 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <new>
+#include <vector>
 
 #include "internal.h"
 #include "pagedattn.h"
@@ -242,7 +244,7 @@ int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
                     int32_t kv_dtype, float k_scale, float v_scale, int32_t partition_size,
                     void *workspace, size_t workspace_bytes, void *stream,
                     const int32_t *groups = nullptr, int32_t num_groups = 0,
-                    const int32_t *shared_lens = nullptr) {
+                    const int32_t *shared_lens = nullptr, const int32_t *dispatch = nullptr) {
   if (!known_dtype(dtype)) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
@@ -313,9 +315,14 @@ int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
     // one partition covers any context the kernel will accept after clamping
     a.partition_size = (int32_t)((int64_t)max_blocks_per_seq * block_size);
   }
-  // with room for it, the longest-first list; else the fixed order
-  if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order)
+  // a list the caller planned; else, with room for it, the longest-first
+  // list sorted on the device; else the fixed order
+  if (dispatch) {
+    a.order = const_cast<int32_t *>(dispatch);
+    a.order_ready = true;
+  } else if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order) {
     a.order = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + w.partials);
+  }
   if (pa::index_check_on()) {
     int32_t st = pa::check_tables(context_lens, block_tables, num_seqs, max_blocks_per_seq,
                                   a.log2_block_size, num_blocks, max_context_len,
@@ -325,6 +332,9 @@ int32_t decode_impl(const void *q, const void *k_cache, const void *v_cache,
                                    num_seqs, max_blocks_per_seq, a.log2_block_size,
                                    max_context_len, 64 / (num_q_heads / num_kv_heads),
                                    static_cast<hipStream_t>(stream));
+    if (st == PA_OK && dispatch)
+      st = pa::check_dispatch(dispatch, (int32_t)((int64_t)num_seqs * P + 4 * (int64_t)num_groups),
+                              static_cast<hipStream_t>(stream));
     if (st != PA_OK) return st;
   }
   const hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(stream));
@@ -404,10 +414,10 @@ size_t paged_attention_prefix_workspace_size(int32_t num_seqs, int32_t num_q_hea
 int32_t paged_attention_decode_prefix(const void *q, const void *k_cache, const void *v_cache,
                                       const int32_t *block_tables, const int32_t *context_lens,
                                       const int32_t *prefix_groups, int32_t num_groups,
-                                      const int32_t *shared_lens, float scale, float k_scale,
-                                      float v_scale, float *out, int32_t num_seqs,
-                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t block_size, int32_t num_blocks,
+                                      const int32_t *shared_lens, const int32_t *dispatch,
+                                      float scale, float k_scale, float v_scale, float *out,
+                                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
                                       int32_t kv_dtype, int32_t partition_size, void *workspace,
                                       size_t workspace_bytes, void *stream) {
@@ -421,7 +431,80 @@ int32_t paged_attention_decode_prefix(const void *q, const void *k_cache, const 
                      is_q8(kv_dtype) ? k_scale : 1.f, is_q8(kv_dtype) ? v_scale : 1.f,
                      partition_size, workspace, workspace_bytes, stream,
                      pfx ? prefix_groups : nullptr, pfx ? num_groups : 0,
-                     pfx ? shared_lens : nullptr);
+                     pfx ? shared_lens : nullptr, dispatch);
+}
+
+int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *prefix_groups,
+                                    int32_t num_groups, const int32_t *shared_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                                    int32_t kv_dtype, int32_t partition_size, int32_t *dispatch,
+                                    int32_t capacity) {
+  if (!known_pool_dtype(kv_dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 || num_groups < 0 ||
+      num_groups > num_seqs || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return 0;
+  const bool pfx = prefix_path(kv_dtype, head_dim, num_q_heads, num_kv_heads, num_groups);
+  const int32_t ng = pfx ? num_groups : 0;
+  if (!context_lens || !dispatch || (ng > 0 && (!prefix_groups || !shared_lens)))
+    return PA_ERR_NULL;
+  int32_t ps = 0;
+  const int32_t P = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps);
+  if (P < 0) return P;
+  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+  if (P <= 1) ps = (int32_t)cap;  // as decode: one partition spans any clamped context
+  const int64_t n = (int64_t)num_seqs * P + 4 * (int64_t)ng;
+  if (n >= (int64_t(1) << 31) || capacity < n) return PA_ERR_SHAPE;
+  const int32_t G = num_q_heads / num_kv_heads;
+  // the decode kernels' clamps and item bounds: tokens of item c, -1 when it
+  // does no work
+  auto L_of = [&](int32_t s) {
+    return (int32_t)std::min<int64_t>(std::max(context_lens[s], 0), cap);
+  };
+  auto shared_of = [&](int32_t s, int32_t L) {
+    return ng > 0 ? (std::min(std::max(shared_lens[s], 0), L) & ~15) : 0;
+  };
+  std::vector<std::pair<int64_t, int32_t>> items((size_t)n);
+  for (int64_t c = 0; c < n; ++c) {
+    int64_t tokens;
+    if (c < (int64_t)num_seqs * P) {
+      const int32_t s = (int32_t)(c % num_seqs);
+      const int32_t p = (P - 1) - (int32_t)(c / num_seqs);
+      const int32_t L = L_of(s);
+      const int32_t nparts = std::min((int32_t)(((int64_t)L + ps - 1) / ps), P);
+      const int32_t sh = shared_of(s, L);
+      if (p >= std::max(nparts, 1) || (sh > 0 && p < sh / ps)) {
+        tokens = -1;
+      } else {
+        tokens = std::max<int64_t>(
+            0, std::min<int64_t>(L, (int64_t)p * ps + ps) - std::max<int64_t>((int64_t)p * ps, sh));
+      }
+    } else {
+      const int64_t gi = (c - (int64_t)num_seqs * P) >> 2;
+      const int32_t cset = (int32_t)((c - (int64_t)num_seqs * P) & 3);
+      const int32_t first = std::min(std::max(prefix_groups[2 * gi], 0), num_seqs - 1);
+      const int32_t count =
+          std::min(std::max(prefix_groups[2 * gi + 1], 0), std::min(num_seqs - first, 64 / G));
+      tokens = -1;
+      for (int32_t m = 16 * cset / G; m < std::min(count, (16 * cset + 15) / G + 1); ++m) {
+        const int32_t sh = shared_of(first + m, L_of(first + m));
+        if (sh > 0) tokens = std::max<int64_t>(tokens, sh);
+      }
+    }
+    items[(size_t)c] = {tokens, (int32_t)c};
+  }
+  // longest first; equal sizes keep item order (members of a prefix group and
+  // the column sets of one group stay side by side); items with no work last
+  std::stable_sort(items.begin(), items.end(),
+                   [](const std::pair<int64_t, int32_t> &x,
+                      const std::pair<int64_t, int32_t> &y) { return x.first > y.first; });
+  for (int64_t i = 0; i < n; ++i) dispatch[i] = items[(size_t)i].second;
+  return (int32_t)n;
 }
 
 }  // extern "C"

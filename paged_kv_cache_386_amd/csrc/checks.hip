@@ -148,6 +148,29 @@ __global__ __launch_bounds__(kCheckThreads) void check_prefix_kernel(
   publish(bad);
 }
 
+// A dispatch list the caller planned: a permutation of the items 0 .. n-1
+// (each exactly once; n at most 65536 items, the bitmap in LDS).
+constexpr int kMaxListItems = 65536;
+__global__ __launch_bounds__(kCheckThreads) void check_dispatch_kernel(
+    const int32_t *__restrict__ dispatch, int n) {
+  __shared__ uint32_t seen[kMaxListItems / 32];
+  for (int i = threadIdx.x; i < kMaxListItems / 32; i += kCheckThreads) seen[i] = 0u;
+  __syncthreads();
+  bool bad = n > kMaxListItems;
+  if (!bad) {
+    for (int i = threadIdx.x; i < n; i += kCheckThreads) {
+      const int c = dispatch[i];
+      if (c < 0 || c >= n) {
+        bad = true;
+      } else {
+        const uint32_t bit = 1u << (c & 31);
+        bad |= (atomicOr(&seen[c >> 5], bit) & bit) != 0u;
+      }
+    }
+  }
+  publish(bad);
+}
+
 // The verdict of the check just enqueued on `stream`.
 int32_t read_verdict(hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
@@ -197,6 +220,12 @@ int32_t check_prefix_groups(const int32_t *lens, const int32_t *tables, const in
   hipLaunchKernelGGL(check_prefix_kernel, dim3(1), dim3(kCheckThreads), 0, stream, lens, tables,
                      groups, num_groups, shared_lens, num_seqs, max_blocks_per_seq,
                      log2_block_size, max_context_len, max_members);
+  return read_verdict(stream);
+}
+
+int32_t check_dispatch(const int32_t *dispatch, int32_t num_items, hipStream_t stream) {
+  hipLaunchKernelGGL(check_dispatch_kernel, dim3(1), dim3(kCheckThreads), 0, stream, dispatch,
+                     num_items);
   return read_verdict(stream);
 }
 

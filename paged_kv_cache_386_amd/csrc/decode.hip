@@ -298,7 +298,8 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
   // num_kv_heads is a multiple of 8.
   const int kvh = blockIdx.x % hkv;
   const int item = order ? order[blockIdx.x / hkv] : (int)(blockIdx.x / hkv);
-  if (item < 0) return;  // listed as empty (past the sequence's end)
+  // listed as empty (past the sequence's end), or not an item of this launch
+  if (item < 0 || item >= num_seqs * P) return;
   const int s = item % num_seqs;
   const int p = (P - 1) - item / num_seqs;
   const int hq = hkv * G;
@@ -573,7 +574,7 @@ hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const bool pfx = a.num_groups > 0;
-  if (a.order) {
+  if (a.order && !a.order_ready) {
     const hipError_t e = launch_schedule(
         a.context_lens, a.order, a.num_seqs, a.num_partitions, a.partition_size,
         a.max_blocks_per_seq << a.log2_block_size, stream, pfx ? a.groups : nullptr,

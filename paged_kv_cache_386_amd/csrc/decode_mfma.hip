@@ -469,7 +469,10 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   // prefix-group items follow the num_seqs * P sequence items
   const int kvh = id % hkv;
   const int item = order ? order[id / hkv] : id / hkv;
-  if (item < 0) return;  // listed as empty (past the sequence's end)
+  // listed as empty (past the sequence's end), or not an item of this launch
+  // (a list the caller planned is trusted only this far)
+  const int nitems = MQ ? num_seqs * P : (int)(gridDim.x / hkv);
+  if (item < 0 || item >= nitems) return;
   const int hq = hkv * (MQ ? gh : G);
 
   const int lane = threadIdx.x & 63;

@@ -27,9 +27,10 @@ struct DecodeArgs {
                            // -1 = dtype
   float k_scale = 1.f;     // 8-bit pools: stored code c means value(c) * scale
   float v_scale = 1.f;
-  int32_t *order = nullptr;  // [S * P (+ num_groups)] dispatch order of the (sequence,
+  int32_t *order = nullptr;  // [S * P (+ 4 * num_groups)] dispatch order of the (sequence,
                              // partition) items and the prefix items, written by
                              // launch_schedule; nullptr = fixed order
+  bool order_ready = false;  // order was planned by the caller: no sort kernel
   // shared prefixes (matrix-core kernel only): num_groups > 0 adds four items
   // (16-column sets) per group and KV head that read the group's shared tiles
   // once; the partials then have num_partitions + 1 slots per row, the last
@@ -143,6 +144,7 @@ int32_t check_prefix_groups(const int32_t *lens, const int32_t *tables, const in
                             int32_t num_groups, const int32_t *shared_lens, int32_t num_seqs,
                             int32_t max_blocks_per_seq, int32_t log2_block_size,
                             int32_t max_context_len, int32_t max_members, hipStream_t stream);
+int32_t check_dispatch(const int32_t *dispatch, int32_t num_items, hipStream_t stream);
 int32_t check_slots(const int32_t *slots, int32_t num_tokens, int64_t num_slots,
                     hipStream_t stream);
 int32_t check_pairs(const int32_t *pairs, int32_t num_pairs, int32_t num_blocks,

@@ -73,7 +73,7 @@ int main(void) {
         (size_t)256 * 32 * 3 * 130 * 4 + (size_t)(256 * 2 + 4 * 16) * 4);
   CHECK(paged_attention_prefix_workspace_size(256, 32, 8, 128, 8192, 0, 16, PA_F32) ==
         paged_attention_workspace_size(256, 32, 8, 128, 8192, 0));
-  CHECK(paged_attention_decode_prefix(NULL, NULL, NULL, NULL, NULL, NULL, 3, NULL, 0.1f, 1.f,
+  CHECK(paged_attention_decode_prefix(NULL, NULL, NULL, NULL, NULL, NULL, 3, NULL, NULL, 0.1f, 1.f,
                                       1.f, NULL, 2, 8, 2, 128, 16, 8, 4, 64, PA_BF16, 0, NULL, 0,
                                       NULL) == PA_ERR_SHAPE); /* more groups than sequences */
   CHECK(paged_attention_decode(NULL, NULL, NULL, NULL, NULL, 0.1f, NULL, 1, 4, 2, 96, 16, 8, 4,

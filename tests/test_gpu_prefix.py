@@ -11,8 +11,9 @@ hand-made groups and shared lengths at the edges (a member sharing nothing,
 a whole context shared, shared lengths off the 16-token grid or ending on a
 partition edge, a short first member, waves with no columns); dominant tiles
 at the prefix walk's block-id rollovers; bitwise determinism and invariance
-under relabelling physical blocks; an fp32 pool (groups ignored: bit for bit
-plain decode); and index checking of bad groups.
+under relabelling physical blocks; a dispatch list planned on the host (bit
+for bit the device-sorted result); an fp32 pool (groups ignored: bit for bit
+plain decode); and index checking of bad groups and lists.
 """
 import numpy as np
 import pytest
@@ -45,7 +46,19 @@ def host_groups(case, min_shared=16):
                             case.num_q_heads, case.num_kv_heads, min_shared)
 
 
-def run_prefix(case, groups, shared, ps=0, pool=None, kind=None, scales=(1.0, 1.0), tables=None):
+def plan(case, groups, shared, ps=0, kv_dtype=None):
+    import paged_kv_cache_386_amd as pa
+    return pa.decode_plan(case.context_lens, groups, shared, num_q_heads=case.num_q_heads,
+                          num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                          block_size=case.block_size,
+                          max_blocks_per_seq=case.max_blocks_per_seq,
+                          max_context_len=case.max_context_len,
+                          kv_dtype=pa.PA_BF16 if kv_dtype is None else kv_dtype,
+                          partition_size=ps)
+
+
+def run_prefix(case, groups, shared, ps=0, pool=None, kind=None, scales=(1.0, 1.0), tables=None,
+               dispatch=None):
     """paged_attention_decode_prefix on the case's tables (after its step)."""
     import paged_kv_cache_386_amd as pa
     check_indices(case)
@@ -62,7 +75,8 @@ def run_prefix(case, groups, shared, ps=0, pool=None, kind=None, scales=(1.0, 1.
         torch.from_numpy(np.ascontiguousarray(tb)).cuda(),
         torch.from_numpy(case.context_lens).cuda(), g, sh, float(case.scale), out,
         max_context_len=case.max_context_len, k_scale=scales[0], v_scale=scales[1],
-        partition_size=ps)
+        partition_size=ps,
+        dispatch=None if dispatch is None else torch.from_numpy(dispatch).cuda())
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -95,6 +109,20 @@ def test_named_workload_full_size(cfg):
         f"{int(c.context_lens.sum())} tokens")
     assert len(g) >= 16
     compare(c, g, sh, f"cfg{cfg}-prefix-full")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_planned_dispatch_matches_device_sort(cfg):
+    """A dispatch list planned on the host gives the same bits as the
+    device's sort (the order changes timing only), with and without groups."""
+    c = settle_step(make_case(cfg))
+    g, sh = host_groups(c)
+    for groups, shared in ((g, sh), (np.zeros((0, 2), np.int32), np.zeros_like(sh))):
+        lst = plan(c, groups, shared)
+        say(f"cfg{cfg} planned dispatch: {len(lst)} items, {len(groups)} groups")
+        a = run_prefix(c, groups, shared, 0)
+        b = run_prefix(c, groups, shared, 0, dispatch=lst)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 # ---------------------------------------------------------------- small workloads
@@ -291,6 +319,15 @@ def test_index_check_rejects_bad_groups():
             say(f"index check: groups {groups} shared {sh.tolist()}")
             with pytest.raises(pa.PagedAttnError) as e:
                 run_prefix(c, groups, sh, 64)
+            assert e.value.status == pa.PA_ERR_INDEX
+        # a planned list must hold every item once
+        lst = plan(c, [[0, 3]], good_sh, 64)
+        same = run_prefix(c, [[0, 3]], good_sh, 64, dispatch=lst)
+        assert np.array_equal(base.view(np.uint32), same.view(np.uint32))
+        for bad in (np.concatenate([lst[:-1], lst[:1]]), np.concatenate([lst[:-1], [len(lst)]])):
+            say(f"index check: dispatch list {bad.tolist()}")
+            with pytest.raises(pa.PagedAttnError) as e:
+                run_prefix(c, [[0, 3]], good_sh, 64, dispatch=bad.astype(np.int32))
             assert e.value.status == pa.PA_ERR_INDEX
     finally:
         pa.set_index_check(False)
