@@ -503,16 +503,9 @@ def multi_query_bench(args) -> int:
     b = c.base
     q = to_dev(c.q, dev)
     c8 = None
-    if args.kv_int8:
-        print("--kv-int8 is not available with --multi-query", file=sys.stderr)
-        return 2
-    if args.kv_fp8:
-        if args.multi_query != "spec-verify":
-            print("--kv-fp8 with --multi-query: spec-verify only (FP8 multi-query runs at most "
-                  "64 rows per KV head)", file=sys.stderr)
-            return 2
-        from workloads.generate import make_fp8_case
-        c8 = make_fp8_case(b, 71)
+    if args.kv_fp8 or args.kv_int8:
+        from workloads.generate import make_fp8_case, make_int8_case
+        c8 = make_fp8_case(b, 71) if args.kv_fp8 else make_int8_case(b, 71)
         kc = torch.from_numpy(c8.k8).to(dev)
         vc = torch.from_numpy(c8.v8).to(dev)
     else:
@@ -531,7 +524,9 @@ def multi_query_bench(args) -> int:
 
     def call():
         if c8 is not None:
-            pa.paged_attention_multi_query_fp8(
+            mq8 = (pa.paged_attention_multi_query_fp8 if args.kv_fp8 else
+                   pa.paged_attention_multi_query_int8)
+            mq8(
                 q, kc, vc, tables, lens, qs, float(b.scale), float(c8.k_scale),
                 float(c8.v_scale), out, max_query_len=c.max_query_len, max_context_len=max_ctx,
                 partition_size=args.partition_size, workspace=ws, stream=stream)
@@ -586,12 +581,15 @@ def multi_query_bench(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if c8 is None else "fp8-e4m3 (bf16 q)",
+        "dtype": "bf16" if c8 is None else
+                 ("fp8-e4m3 (bf16 q)" if args.kv_fp8 else "int8 (bf16 q)"),
         "data": "synthetic (seeded N(0,1) q/K/V; lengths as described)" + (
-            "" if c8 is None else f"; K/V as random E4M3 codes, k_scale {float(c8.k_scale)}, "
-                                  f"v_scale {float(c8.v_scale)}"),
+            "" if c8 is None else
+            f"; K/V as random {'E4M3' if args.kv_fp8 else 'INT8'} codes, k_scale "
+            f"{float(c8.k_scale)}, v_scale {float(c8.v_scale)}"),
         "config": {"workload": f"{args.multi_query}: {MULTI_QUERY_NAMES[args.multi_query]}"
-                               + (" over an FP8 pool" if c8 is not None else ""),
+                               + ("" if c8 is None else
+                                  " over an FP8 pool" if args.kv_fp8 else " over an INT8 pool"),
                    "num_seqs": b.num_seqs, "num_tokens": c.num_tokens,
                    "max_query_len": c.max_query_len, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": b.block_size,

@@ -427,9 +427,12 @@ size_t paged_attention_multi_query_workspace_size(int32_t num_seqs, int32_t num_
  * products ([P1] sections 5.3 and 5.4: FP8 KV cache, speculative decoding).
  * Arguments as in paged_attention_multi_query, with q in bfloat16 and
  * k_cache, v_cache one code per byte; k_scale, v_scale finite and > 0.
- * Supported: head_dim 128 and at most 64 (token, head) rows per KV head
- * (max_query_len * G <= 64: verification-sized chunks, on the decode
- * kernel's walk); longer chunks give PA_ERR_UNSUPPORTED.
+ * Chunks of at most 64 (token, head) rows per KV head at head_dim 128
+ * (verification-sized) run on the decode kernel's walk; longer chunks
+ * (chunked prefill) and head_dim 64 on the row-tile kernel, which loads the
+ * codes and widens them exactly to bfloat16 as it stages each tile in LDS.
+ * Supported: head_dim 64 or 128; any G; block_size a power of two in
+ * [1, 1024].
  * Errors: as paged_attention_multi_query.
  */
 int32_t paged_attention_multi_query_fp8(const void *q, const void *k_cache, const void *v_cache,

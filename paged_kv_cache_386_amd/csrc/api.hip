@@ -585,11 +585,9 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
   if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
   if (!pa::multi_query_supported(dtype, head_dim)) return PA_ERR_UNSUPPORTED;
   if (is_q8(kv_dtype)) {
-    // the decode walk only: bf16 queries, head_dim 128, at most 64 (token,
-    // head) rows per KV head
-    if (dtype != PA_BF16 || head_dim != 128 ||
-        (int64_t)max_query_len * (num_q_heads / num_kv_heads) > pa::kMqFewRows)
-      return PA_ERR_UNSUPPORTED;
+    // bf16 queries; both kernels (the decode walk for at most 64 (token,
+    // head) rows per KV head at head_dim 128, the row-tile kernel otherwise)
+    if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
     if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_SHAPE;
   }
   const int64_t G = num_q_heads / num_kv_heads;

@@ -42,6 +42,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -86,28 +87,69 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-template <int D>
+// Four signed 8-bit codes (one dword) to fp32 (exact).
+__device__ __forceinline__ void i8x4_to_f32(uint32_t w, float (&f)[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) f[b] = (float)((int32_t)(w << (24 - 8 * b)) >> 24);
+}
+
+// Eight 8-bit codes to eight bfloat16 values, exactly (an E4M3 value has at
+// most 4 significant bits, an INT8 code at most 7): FP8 through gfx950's
+// scaled conversion at scale 1 (two codes of a 16-bit half per instruction,
+// the low byte into the low half; OCP E4M3), INT8 widened to fp32, whose
+// high halves are the bfloat16 values, paired with one byte permute.
+template <int Q8>
+__device__ __forceinline__ u32x4 widen8(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if constexpr (Q8 == 1) {
+      r[2 * h] = __builtin_bit_cast(uint32_t,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, false));
+      r[2 * h + 1] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], 1.f, true));
+    } else {
+      float f[4];
+      i8x4_to_f32(w[h], f);
+      r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+      r[2 * h + 1] =
+          __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
+    }
+  }
+  return r;
+}
+
+// Q8: the pool's element kind -- 0 bfloat16, 1 FP8 (E4M3), 2 INT8.  An 8-bit
+// tile is loaded as codes (8 bytes per chunk) and widened exactly to
+// bfloat16 when it is stored to LDS, so the products are those of the
+// bfloat16 pool.
+template <int D, int Q8>
 struct TileRegs {
   // K and V: chunk c = threadIdx + 256 j of the tile (token c / (D/8),
   // elements 8 (c % (D/8)) .. +7)
   static constexpr int kKChunks = kTk * D / 8 / kThreads;  // 4 (D=128) or 2 (D=64)
-  u32x4 k[kKChunks];
-  u32x4 v[kKChunks];
+  using Chunk = typename std::conditional<Q8 == 0, u32x4, u32x2>::type;
+  Chunk k[kKChunks];
+  Chunk v[kKChunks];
 };
 
-template <int D, int RS>
+template <int D, int RS, int Q8>
 __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, const int32_t *__restrict__ block_tables,
+    const uint16_t *__restrict__ q, const void *__restrict__ kc_raw,
+    const void *__restrict__ vc_raw, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
-    int num_tokens, int hkv, int G, int lgB, int nb, int mb, int max_q, int row_tiles, int units,
-    int ps, int P, const int32_t *__restrict__ order) {
+    float v_scale, int num_tokens, int hkv, int G, int lgB, int nb, int mb, int max_q,
+    int row_tiles, int units, int ps, int P, const int32_t *__restrict__ order) {
+  using KV = typename std::conditional<Q8 == 0, uint16_t, uint8_t>::type;
+  const KV *__restrict__ kc = static_cast<const KV *>(kc_raw);
+  const KV *__restrict__ vc = static_cast<const KV *>(vc_raw);
   constexpr int kRows = 64 * RS;  // query rows per workgroup
   constexpr int kKs = kTk == 64 ? D + 8 : D;  // K tile row stride (elements), padded
   constexpr int kSteps = D / 32;              // k-steps of q.K
   constexpr int kDb = D / 16;                 // 16-element blocks of the output
-  using Regs = TileRegs<D>;
+  using Regs = TileRegs<D, Q8>;
+  using Chunk = typename Regs::Chunk;
 
   // XCD-aware order.  A unit r is a KV head (r % hkv) of a (sequence,
   // partition) item (r / hkv: from the longest-first list when there is one,
@@ -224,20 +266,29 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
                (int64_t)(((k0 + tt0 + kTokStep * j) & bm1) * D + 8 * dc);
 #pragma unroll
     for (int j = 0; j < Regs::kKChunks; ++j)
-      T.k[j] = *reinterpret_cast<const u32x4 *>(kc + off[j]);
+      T.k[j] = *reinterpret_cast<const Chunk *>(kc + off[j]);
 #pragma unroll
     for (int j = 0; j < Regs::kKChunks; ++j) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(vc + off[j]);
-      T.v[j] = k0 + tt0 + kTokStep * j <= pos_last ? v : u32x4{0, 0, 0, 0};
+      const Chunk v = *reinterpret_cast<const Chunk *>(vc + off[j]);
+      T.v[j] = k0 + tt0 + kTokStep * j <= pos_last ? v : Chunk{};
     }
   };
-  // registers -> LDS buffer `buf`, both row-major
+  // registers -> LDS buffer `buf`, both row-major (8-bit codes widened to
+  // bfloat16 here, once the loads have landed)
   auto store_tile = [&](const Regs &T, int buf) {
 #pragma unroll
     for (int j = 0; j < Regs::kKChunks; ++j) {
       const int c = threadIdx.x + kThreads * j;
-      *reinterpret_cast<u32x4 *>(&sk_buf[buf][(c / (D / 8)) * kKs + 8 * (c % (D / 8))]) = T.k[j];
-      *reinterpret_cast<u32x4 *>(&sv_buf[buf][(c / (D / 8)) * kVs + 8 * (c % (D / 8))]) = T.v[j];
+      u32x4 kw, vw;
+      if constexpr (Q8 == 0) {
+        kw = T.k[j];
+        vw = T.v[j];
+      } else {
+        kw = widen8<Q8>(T.k[j]);
+        vw = widen8<Q8>(T.v[j]);
+      }
+      *reinterpret_cast<u32x4 *>(&sk_buf[buf][(c / (D / 8)) * kKs + 8 * (c % (D / 8))]) = kw;
+      *reinterpret_cast<u32x4 *>(&sv_buf[buf][(c / (D / 8)) * kVs + 8 * (c % (D / 8))]) = vw;
     }
   };
 
@@ -409,7 +460,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     l += __shfl_xor(l, 32);
     const int R = row0 + (wave * RS + r) * 16 + c16;
     if (R < row_end) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+      // (8-bit pools: the V scale multiplies the normalised output)
+      const float inv = l > 0.f ? v_scale / l : 0.f;
       const int64_t orow = (int64_t)(qs + R / G) * hq + kvh * G + R % G;
       float *o = split ? ws_o + (orow * P + part) * D : out + orow * D;
 #pragma unroll
@@ -479,7 +531,7 @@ hipError_t launch_merge(const MultiQueryArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int RS>
+template <int D, int RS, int Q8>
 hipError_t launch_typed(const MultiQueryArgs &a, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t rows = (int64_t)a.max_query_len * G;
@@ -487,24 +539,34 @@ hipError_t launch_typed(const MultiQueryArgs &a, hipStream_t stream) {
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
   if (units <= 0 || row_tiles <= 0) return hipSuccess;
   const int64_t grid = (units + kXcds - 1) / kXcds * kXcds * row_tiles;
-  hipLaunchKernelGGL((paged_multi_query_kernel<D, RS>), dim3((uint32_t)grid), dim3(kThreads), 0,
-                     stream, static_cast<const uint16_t *>(a.q),
-                     static_cast<const uint16_t *>(a.k_cache),
-                     static_cast<const uint16_t *>(a.v_cache), a.block_tables, a.context_lens,
-                     a.query_start, a.out, a.ws_o, a.ws_ml, a.scale * kLog2e, a.num_tokens,
-                     a.num_kv_heads, G, a.log2_block_size, a.num_blocks, a.max_blocks_per_seq,
-                     a.max_query_len, row_tiles, (int)units, a.partition_size, a.num_partitions,
-                     a.order);
+  // 8-bit pools: the K scale multiplies every score, so it joins the softmax
+  // scale; the V scale multiplies the output
+  const float sl2 = a.scale * (Q8 ? a.k_scale : 1.f) * kLog2e;
+  hipLaunchKernelGGL((paged_multi_query_kernel<D, RS, Q8>), dim3((uint32_t)grid), dim3(kThreads),
+                     0, stream, static_cast<const uint16_t *>(a.q), a.k_cache, a.v_cache,
+                     a.block_tables, a.context_lens, a.query_start, a.out, a.ws_o, a.ws_ml, sl2,
+                     Q8 ? a.v_scale : 1.f, a.num_tokens, a.num_kv_heads, G, a.log2_block_size,
+                     a.num_blocks, a.max_blocks_per_seq, a.max_query_len, row_tiles, (int)units,
+                     a.partition_size, a.num_partitions, a.order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions <= 1) return e;
   return launch_merge(a, stream);
 }
 
-template <int D>
+template <int D, int Q8>
 hipError_t launch_d(const MultiQueryArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.max_query_len * (a.num_q_heads / a.num_kv_heads);
-  if (rows > 64) return launch_typed<D, 2>(a, stream);
-  return launch_typed<D, 1>(a, stream);
+  if (rows > 64) return launch_typed<D, 2, Q8>(a, stream);
+  return launch_typed<D, 1, Q8>(a, stream);
+}
+
+template <int D>
+hipError_t launch_kind(const MultiQueryArgs &a, hipStream_t stream) {
+  switch (a.kv_dtype) {
+    case 2: return launch_d<D, 1>(a, stream);  // FP8 E4M3
+    case 3: return launch_d<D, 2>(a, stream);  // INT8
+    default: return launch_d<D, 0>(a, stream);
+  }
 }
 
 }  // namespace
@@ -524,9 +586,6 @@ int64_t multi_query_workgroups(int64_t num_seqs, int64_t num_q_heads, int64_t nu
 }
 
 hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream) {
-  // 8-bit pools run only on the decode walk (at most 64 rows per KV head)
-  if ((a.kv_dtype == 2 || a.kv_dtype == 3) && !multi_query_few_rows_supported(a))
-    return hipErrorNotSupported;
   if (a.order) {
     const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
                                            INT32_MAX);
@@ -541,8 +600,8 @@ hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream) {
     return launch_merge(a, stream);
   }
   switch (a.head_dim) {
-    case 64: return launch_d<64>(a, stream);
-    case 128: return launch_d<128>(a, stream);
+    case 64: return launch_kind<64>(a, stream);
+    case 128: return launch_kind<128>(a, stream);
     default: return hipErrorNotSupported;
   }
 }

@@ -63,9 +63,14 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 def test_bench_option_guards():
-    """Option combinations the benchmark refuses before touching a GPU, and
-    the 8-bit decode modes reaching their own path (no multi-query guard)."""
+    """The 8-bit options reach their own entry points in both modes: the
+    multi-query mode picks the FP8 or INT8 multi-query call, the decode mode
+    the FP8 or INT8 decode (no multi-query guard in the decode path)."""
     src = open(os.path.join(ROOT, "bench.py")).read()
     body = src[src.index("def multi_query_bench"):src.index("def main")]
-    assert "--kv-int8 is not available with --multi-query" in body
-    assert src.count("--kv-int8 is not available with --multi-query") == 1
+    assert "pa.paged_attention_multi_query_fp8 if args.kv_fp8 else" in body
+    assert "pa.paged_attention_multi_query_int8" in body
+    main = src[src.index("def main"):]
+    assert "pa.paged_attention_decode_fp8 if args.kv_fp8 else pa.paged_attention_decode_int8" \
+        in main
+    assert "is not available with --multi-query" not in src

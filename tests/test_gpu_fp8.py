@@ -233,16 +233,52 @@ def test_multi_query_matches_oracle(G, Hkv, q_lens, B, ps):
     assert err <= TOL["bf16"], f"G={G} B={B} ps={ps}: {err}"
 
 
-def test_multi_query_longer_chunks_are_unsupported():
-    import paged_kv_cache_386_amd as pa
+@pytest.mark.parametrize("G,Hkv,q_lens", [(4, 2, [512, 65, 0, 300]), (8, 1, [200, 9, 513, 64]),
+                                          (1, 4, [512, 130, 1, 77])])
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("B,ps", [(16, 0), (4, -1), (16, 128)])
+def test_multi_query_long_chunks(G, Hkv, q_lens, D, B, ps):
+    """Chunks of more than 64 rows per KV head (chunked prefill) over an FP8
+    pool, on the row-tile kernel: every output element."""
     from workloads import make_multi_query_case
-    base = make_private_case("f8mq-long", [100, 200], 8, 2, 128, 16, "bf16", 70)
-    c8 = make_fp8_case(base, 70)
-    mq = make_multi_query_case(base, [17, 5], 70)   # 17 tokens x 4 heads = 68 rows
-    say("fp8 multi-query: chunk over 64 rows per KV head")
-    with pytest.raises(pa.PagedAttnError) as e:
-        _run_mq_fp8(c8, mq)
-    assert e.value.status == -4  # PA_ERR_UNSUPPORTED
+    lens = [max(q, L) for q, L in zip(q_lens, [700, 1500, 513, 64])]
+    base = make_private_case(f"f8cp-{G}-{D}", lens, G * Hkv, Hkv, D, B, "bf16", 90 + G + D)
+    c8 = make_fp8_case(base, 90 + G)
+    mq = make_multi_query_case(base, q_lens, 91 + G)
+    say(f"fp8 chunked prefill G={G} D={D} B={B} ps={ps} q_lens={q_lens}")
+    got = _run_mq_fp8(c8, mq, ps)
+    ref = fp8.paged_attention_multi_query_fp8(mq.q, c8.k8, c8.v8, base.block_tables,
+                                              base.context_lens, mq.query_start, base.scale,
+                                              base.block_size, "bf16", c8.k_scale, c8.v_scale)
+    err = max_err(got, ref)
+    say(f"fp8 chunked prefill G={G} D={D} ps={ps}: max abs err {err:.3e}")
+    assert err <= TOL["bf16"], f"G={G} D={D} B={B} ps={ps}: {err}"
+
+
+def test_multi_query_chunked_prefill_workload():
+    """The chunked-prefill workload (16 sequences, contexts U[1024, 8192], a
+    512-token chunk each) over an FP8 pool at full size in the benchmark's
+    launch configuration; every output of four sequences against the oracle
+    (the whole pool, tables and launch as run)."""
+    from workloads import make_multi_query_workload
+    from workloads.generate import subset_sequences, make_multi_query_case as mqc
+    c = make_multi_query_workload("chunked-prefill")
+    b = c.base
+    c8 = make_fp8_case(b, 72)
+    say(f"fp8 chunked prefill full size: S={b.num_seqs} T={c.num_tokens}")
+    got = _run_mq_fp8(c8, c)
+    assert np.isfinite(got).all()
+    keep = [0, 5, 10, 15]
+    sub = subset_sequences(b, keep)
+    rows = np.concatenate([np.arange(c.query_start[s], c.query_start[s + 1]) for s in keep])
+    sq = mqc(sub, np.diff(c.query_start)[keep], 72)
+    sq.q = c.q[rows]
+    ref = fp8.paged_attention_multi_query_fp8(sq.q, c8.k8, c8.v8, sub.block_tables,
+                                              sub.context_lens, sq.query_start, b.scale,
+                                              b.block_size, "bf16", c8.k_scale, c8.v_scale)
+    err = max_err(got[rows], ref)
+    say(f"fp8 chunked prefill full size: {len(rows)} rows, max abs err {err:.3e}")
+    assert err <= TOL["bf16"], f"max abs err {err}"
 
 
 def test_multi_query_full_size_verification():
