@@ -375,14 +375,19 @@ def serving_bench(args) -> int:
     def randn(*shape):
         return torch.randn(*shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
-    kc = torch.zeros((NB, Hkv, B, D), dtype=torch.bfloat16, device=dev)
+    # the pool: bfloat16, or 8-bit codes (one byte per element, one scale per
+    # cache) written by the engine's quantising writes from bfloat16 rows
+    pool_dtype = torch.uint8 if args.kv_fp8 else torch.int8 if args.kv_int8 else torch.bfloat16
+    k_scale, v_scale = (0.25, 0.5) if args.kv_fp8 else (0.02, 0.03) if args.kv_int8 else (1., 1.)
+    kc = torch.zeros((NB, Hkv, B, D), dtype=pool_dtype, device=dev)
     vc = torch.zeros_like(kc)
     q, kn, vn = randn(mb, Hq, D), randn(mb, Hkv, D), randn(mb, Hkv, D)
     pk, pv = randn(R, Hkv, D), randn(R, Hkv, D)
     out = torch.empty((mb, Hq, D), dtype=torch.float32, device=dev)
     scale = float(np.float32(1.0 / np.sqrt(D)))
     eng = pa.Engine(kc, vc, num_q_heads=Hq, max_batch=mb, max_context_len=c["max_context_len"],
-                    max_prompt_rows=R)
+                    max_prompt_rows=R, k_scale=k_scale, v_scale=v_scale,
+                    host_plan=not args.no_host_plan)
     rng = np.random.default_rng(c["seed"])
     for r in range(c["requests"]):
         samples = c["samples"] if r % c["fork_every"] == c["fork_every"] - 1 else 1
@@ -424,8 +429,14 @@ def serving_bench(args) -> int:
     gpu_ms = np.array([a.elapsed_time(b) for a, b in ev])
     tokens = sum(x.batch for x in infos)
     ctx = sum(x.context_tokens for x in infos)
-    kv_token_bytes = 2 * Hkv * D * 2
+    uniq = sum(x.unique_tokens for x in infos)
+    kv_token_bytes = 2 * Hkv * D * kc.element_size()
+    # unique bytes (each shared prefix slot once, as the decode benchmark
+    # counts them) per second of GPU step time; attended beside it
+    unique_gbps = uniq * kv_token_bytes / (gpu_ms.sum() * 1e-3) / 1e9
     attended_gbps = ctx * kv_token_bytes / (gpu_ms.sum() * 1e-3) / 1e9
+    host_us = np.array([x.host_us for x in infos])
+    wait_us = np.array([x.wait_us for x in infos])
     rec = {
         "metric": SERVING_METRIC,
         "value": round(tokens / wall, 1),
@@ -437,33 +448,48 @@ def serving_bench(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if pool_dtype == torch.bfloat16 else
+                 ("fp8-e4m3 pool (bf16 q and rows)" if args.kv_fp8 else
+                  "int8 pool (bf16 q and rows)"),
         "data": "synthetic (fixed N(0,1) token rows; seeded request lengths and samples)",
         "config": {
             "workload": ("serving: engine over 8192 queued requests, prompts U[16,1536], "
                          "outputs U[16,512], every 8th with 4 samples, <=512 seqs/step, "
-                         "32q/8kv, d128, B16, 40960-block pool"),
+                         "32q/8kv, d128, B16, 40960-block pool"
+                         + (", FP8 pool" if args.kv_fp8 else ", INT8 pool" if args.kv_int8
+                            else "")),
             **{k: v for k, v in c.items() if k not in ("seed",)},
+            "host_plan": not args.no_host_plan,
         },
         "step_latency_ms": {
             "gpu_mean": round(float(gpu_ms.mean()), 4),
             "gpu_p50": round(float(np.percentile(gpu_ms, 50)), 4),
             "gpu_p99": round(float(np.percentile(gpu_ms, 99)), 4),
-            "host_enqueue_mean": round(float(host.mean() * 1e3), 4),
+            # the host's time in pa_engine_step, and of it the wait for a
+            # staging buffer the device still reads (the host runs ahead)
+            "host_call_mean": round(float(host.mean() * 1e3), 4),
+            "host_wait_mean": round(float(wait_us.mean() / 1e3), 4),
+            "host_work_mean": round(float((host_us - wait_us).mean() / 1e3), 4),
             "wall_mean": round(wall / K * 1e3, 4),
         },
         "batch_mean": round(tokens / K, 1),
         "context_tokens_per_step": round(ctx / K, 1),
+        "unique_tokens_per_step": round(uniq / K, 1),
         "attended_kv_tokens_per_s": round(ctx / wall, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": "one engine step (index copy, prompt writes, copies, token writes, decode)",
-            "achieved": round(attended_gbps, 1),
+            "achieved": round(unique_gbps, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
-            "frac": round(attended_gbps / PEAK_HBM_GBPS, 4),
+            "frac": round(unique_gbps / PEAK_HBM_GBPS, 4),
             "traffic": None,
-            "algorithmic_bytes_per_step": int(ctx * kv_token_bytes / K),
+            "frac_definition": ("unique KV bytes per step (attended tokens with each shared "
+                                "prefix slot once, 2 * kv_heads * head_dim * element bytes "
+                                "each) / mean GPU step time / 8 TB/s"),
+            "algorithmic_bytes_per_step": int(uniq * kv_token_bytes / K),
+            "attended_bytes_per_step": int(ctx * kv_token_bytes / K),
+            "effective_gbps": round(attended_gbps, 1),
         },
         "admitted": sum(x.admitted for x in infos),
         "finished": sum(x.finished for x in infos),
@@ -647,6 +673,9 @@ def main() -> int:
                     help="the workload over an FP8 (E4M3) pool: quantising write and FP8 decode")
     ap.add_argument("--kv-int8", action="store_true",
                     help="the workload over an INT8 pool: quantising write and INT8 decode")
+    ap.add_argument("--no-host-plan", action="store_true",
+                    help="--serving: plain decode with the device sort instead of the "
+                         "engine's host-planned prefix groups and dispatch list")
     ap.add_argument("--device-sort", action="store_true",
                     help="sort the work on the device in every call instead of passing the "
                          "dispatch list planned on the host (paged_attention_decode_plan)")

@@ -42,16 +42,26 @@
  *     admitted request's first sample is a new sequence holding its prompt,
  *     the others are forks of it; they get their first slots after the
  *     running sequences (batch rows nr .. n-1);
- *  3. one host-to-device copy of the step's index arrays, then on `stream`:
+ *  3. with host_plan (pa_engine_config), the decode call is planned on the
+ *     host from the step's tables and lengths: the shared-prefix groups
+ *     (pa_prefix_groups: forked samples share their prompt's blocks) and the
+ *     longest-first dispatch list (paged_attention_decode_plan);
+ *  4. one host-to-device copy of the step's index arrays, then on `stream`:
  *     kv_cache_write of the admitted prompts, copy_blocks of the
- *     copy-on-write pairs, kv_cache_write of the new tokens and
- *     paged_attention_decode over the whole batch;
- *  4. every sequence that has now produced its max_new_tokens tokens is freed.
+ *     copy-on-write pairs, kv_cache_write of the new tokens (the quantising
+ *     writes for an 8-bit pool) and decode over the whole batch
+ *     (paged_attention_decode_prefix with the step's groups and list when
+ *     host_plan is set, else paged_attention_decode; the FP8 / INT8 forms
+ *     for an 8-bit pool);
+ *  5. every sequence that has now produced its max_new_tokens tokens is freed.
  *
  * The token data are the caller's: a step reads the prompt rows of the
  * admitted sequences from prompt_k/prompt_v (packed in admission order), and
  * row i of q, k_new and v_new for batch row i; decode writes out row i.  The
- * step's info (below) says which sequence each row belongs to.
+ * step's info (below) says which sequence each row belongs to.  Token rows
+ * and q are in the pool's dtype, or bfloat16 for an 8-bit pool (FP8 E4M3 or
+ * INT8, one scale per cache: [P3] architecture figure, FP8/INT8 in the
+ * kernel layer), whose writes quantise them.
  *
  * Sequence ids: sample s of request r is (r << 8) | s.  A preempted sample
  * keeps its id when it is re-admitted.
@@ -98,6 +108,10 @@ typedef struct pa_engine_config {
                                  a preempted sequence is re-admitted whole) */
   int32_t partition_size;     /* decode partition policy, as in pagedattn.h */
   int32_t device;             /* 1 = run on the current HIP device, 0 = plan only */
+  float k_scale, v_scale;     /* 8-bit pools (dtype PA_FP8_E4M3 or PA_INT8): a stored
+                                 code c means value(c) * scale; finite and > 0 */
+  int32_t host_plan;          /* 1 = find shared prefixes and plan the dispatch list on
+                                 the host every step (step 3); 0 = plain decode */
 } pa_engine_config;
 
 /* Per-step report.  The arrays are the engine's host memory, valid until the
@@ -123,10 +137,24 @@ typedef struct pa_step_info {
   const int64_t *preempted_seq_ids; /* [preempted] */
   const int64_t *finished_seq_ids;  /* [finished] */
   int32_t max_blocks_per_seq;       /* row length of block_tables */
+  int32_t num_groups;               /* shared-prefix groups of the step (host_plan) */
+  const int32_t *prefix_groups;     /* [num_groups][2] (first batch row, members) */
+  const int32_t *shared_lens;       /* [batch] positions read through the group */
+  int32_t dispatch_len;             /* entries of the dispatch list (host_plan) */
+  const int32_t *dispatch;          /* [dispatch_len] */
+  int64_t unique_tokens;            /* attended tokens with each shared prefix slot once
+                                       (context_tokens less, per group, the members' shared
+                                       lengths beyond the longest; the groups are found
+                                       even without host_plan) */
+  float host_us;                    /* host time of the call, microseconds */
+  float wait_us;                    /* of it, waiting for a staging buffer to free up
+                                       (the device still reading it two steps back) */
 } pa_step_info;
 
 /* Creates an engine over the caller's pool (device pointers laid out as in
  * pagedattn.h; ignored when cfg->device is 0).  *out receives the engine.
+ * dtype PA_FP8_E4M3 or PA_INT8 needs head_dim 128 (the 8-bit decode) and
+ * valid scales; other dtypes ignore the scales.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_OOM
  * (host or device allocation failed), PA_ERR_LAUNCH. */
 int32_t pa_engine_create(const pa_engine_config *cfg, void *k_cache, void *v_cache,
@@ -148,11 +176,11 @@ int32_t pa_engine_submit(pa_engine *e, int64_t request_id, int32_t prompt_len,
                          int32_t max_new_tokens, int32_t num_samples);
 
 /* One step (see above).  Device pointers (ignored when planning only):
- *   q          [max_batch][num_q_heads][head_dim], dtype
+ *   q          [max_batch][num_q_heads][head_dim], dtype (bfloat16 for an 8-bit pool)
  *   k_new,
- *   v_new      [max_batch][num_kv_heads][head_dim], dtype
+ *   v_new      [max_batch][num_kv_heads][head_dim], the same
  *   prompt_k,
- *   prompt_v   [max_prompt_rows][num_kv_heads][head_dim], dtype
+ *   prompt_v   [max_prompt_rows][num_kv_heads][head_dim], the same
  *   out        float32 [max_batch][num_q_heads][head_dim]
  * An empty step (nothing running or admitted) enqueues nothing.  A step
  * that preempts admits nothing.

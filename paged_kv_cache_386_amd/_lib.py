@@ -649,7 +649,8 @@ class BlockManager:
 class EngineConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_blocks", "block_size", "num_q_heads", "num_kv_heads", "head_dim", "dtype",
-        "max_batch", "max_context_len", "max_prompt_rows", "partition_size", "device")]
+        "max_batch", "max_context_len", "max_prompt_rows", "partition_size", "device")] + [
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("host_plan", ctypes.c_int32)]
 
 
 class _StepInfo(ctypes.Structure):
@@ -665,6 +666,10 @@ class _StepInfo(ctypes.Structure):
         ("block_tables", _P32), ("copy_pairs", _P32), ("admitted_seq_ids", _P64),
         ("admitted_rows", _P32), ("prompt_slots", _P32), ("preempted_seq_ids", _P64),
         ("finished_seq_ids", _P64), ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_groups", ctypes.c_int32), ("prefix_groups", _P32), ("shared_lens", _P32),
+        ("dispatch_len", ctypes.c_int32), ("dispatch", _P32),
+        ("unique_tokens", ctypes.c_int64),
+        ("host_us", ctypes.c_float), ("wait_us", ctypes.c_float),
     ]
 
 
@@ -674,8 +679,11 @@ class StepInfo:
 
     def __init__(self, raw: _StepInfo, arrays: bool = True):
         for k in ("batch", "admitted", "prompt_rows", "preempted", "finished", "num_copies",
-                  "max_context_len", "free_blocks", "context_tokens"):
+                  "max_context_len", "free_blocks", "context_tokens", "num_groups",
+                  "dispatch_len", "unique_tokens"):
             setattr(self, k, int(getattr(raw, k)))
+        self.host_us = float(raw.host_us)
+        self.wait_us = float(raw.wait_us)
         if not arrays:
             return
         import numpy as np
@@ -699,6 +707,10 @@ class StepInfo:
         self.prompt_slots = arr(raw.prompt_slots, raw.prompt_rows, np.int32)
         self.preempted_seq_ids = arr(raw.preempted_seq_ids, raw.preempted, np.int64)
         self.finished_seq_ids = arr(raw.finished_seq_ids, raw.finished, np.int64)
+        self.prefix_groups = arr(raw.prefix_groups, 2 * raw.num_groups, np.int32,
+                                 (raw.num_groups, 2))
+        self.shared_lens = arr(raw.shared_lens, n, np.int32)
+        self.dispatch = arr(raw.dispatch, raw.dispatch_len, np.int32)
 
 
 class Engine:
@@ -712,7 +724,8 @@ class Engine:
     def __init__(self, k_cache=None, v_cache=None, *, num_q_heads: int, max_batch: int,
                  max_context_len: int, max_prompt_rows: int = 0, partition_size: int = 0,
                  num_blocks: int = 0, block_size: int = 0, num_kv_heads: int = 0,
-                 head_dim: int = 0, dtype: int = PA_BF16):
+                 head_dim: int = 0, dtype: int = PA_BF16, k_scale: float = 1.0,
+                 v_scale: float = 1.0, host_plan: bool = True):
         device = k_cache is not None
         if device:
             num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
@@ -723,7 +736,8 @@ class Engine:
         self.cfg = EngineConfig(num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
                                 dtype, max_batch, max_context_len,
                                 max_prompt_rows or max_context_len, partition_size,
-                                1 if device else 0)
+                                1 if device else 0, float(k_scale), float(v_scale),
+                                1 if host_plan else 0)
         self._pool = (k_cache, v_cache)
         h = ctypes.c_void_p()
         _check("pa_engine_create", lib().pa_engine_create(

@@ -469,7 +469,10 @@ int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *
   auto shared_of = [&](int32_t s, int32_t L) {
     return ng > 0 ? (std::min(std::max(shared_lens[s], 0), L) & ~15) : 0;
   };
-  std::vector<std::pair<int64_t, int32_t>> items((size_t)n);
+  // sort keys: (tokens + 1) in the high word, complemented so that larger
+  // counts come first, the item number in the low word (equal counts keep
+  // item order; no work, tokens = -1, sorts last)
+  std::vector<uint64_t> keys((size_t)n);
   for (int64_t c = 0; c < n; ++c) {
     int64_t tokens;
     if (c < (int64_t)num_seqs * P) {
@@ -496,14 +499,12 @@ int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *
         if (sh > 0) tokens = std::max<int64_t>(tokens, sh);
       }
     }
-    items[(size_t)c] = {tokens, (int32_t)c};
+    keys[(size_t)c] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)(tokens + 1)) << 32) | (uint32_t)c;
   }
   // longest first; equal sizes keep item order (members of a prefix group and
   // the column sets of one group stay side by side); items with no work last
-  std::stable_sort(items.begin(), items.end(),
-                   [](const std::pair<int64_t, int32_t> &x,
-                      const std::pair<int64_t, int32_t> &y) { return x.first > y.first; });
-  for (int64_t i = 0; i < n; ++i) dispatch[i] = items[(size_t)i].second;
+  std::sort(keys.begin(), keys.end());
+  for (int64_t i = 0; i < n; ++i) dispatch[i] = (int32_t)(keys[(size_t)i] & 0xFFFFFFFFu);
   return (int32_t)n;
 }
 

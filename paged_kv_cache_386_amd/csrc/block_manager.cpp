@@ -26,8 +26,15 @@ struct pa_block_manager {
   struct Seq {
     std::vector<int32_t> table;
     int32_t len = 0;
+    uint64_t mark = 0;  // the last prepare_decode call that listed it
   };
   std::unordered_map<int64_t, Seq> seqs;
+  // prepare_decode's scratch, kept across calls: a call counter that marks
+  // the sequences and simulated reference counts it has seen (a block's
+  // simulated count is valid while its stamp equals the counter)
+  uint64_t calls = 0;
+  std::vector<uint64_t> sim_stamp;
+  std::vector<int32_t> sim_refs;
 
   int32_t take() {
     const int32_t b = free_list.back();
@@ -87,6 +94,8 @@ pa_block_manager *pa_bm_create(int32_t num_blocks, int32_t block_size) {
     bm->free_list.resize(num_blocks);
     for (int32_t i = 0; i < num_blocks; ++i) bm->free_list[i] = i;
     bm->refs.assign(num_blocks, 0);
+    bm->sim_stamp.assign(num_blocks, 0);
+    bm->sim_refs.assign(num_blocks, 0);
   } catch (...) {
     delete bm;
     return nullptr;
@@ -198,25 +207,29 @@ int32_t pa_bm_prepare_decode(pa_block_manager *bm, const int64_t *seq_ids, int32
   if (!seq_ids || !slot_mapping || !copy_pairs || !num_pairs || !block_tables || !context_lens)
     return PA_ERR_NULL;
   try {
-    // plan: look every id up once, refuse repeats, and count the blocks the
-    // appends take in this order, with reference counts simulated on a copy
+    // plan: look every id up once, refuse repeats (marked by this call's
+    // number), and count the blocks the appends take in this order, with
+    // reference counts simulated on stamped scratch
     std::vector<pa_block_manager::Seq *> seqs(n);
-    std::unordered_set<int64_t> seen;
-    std::unordered_map<int32_t, int32_t> sim_refs;
+    const uint64_t call = ++bm->calls;
     int64_t need = 0;
+    auto ref = [&](int32_t b) {
+      return bm->sim_stamp[b] == call ? bm->sim_refs[b] : bm->refs[b];
+    };
     for (int32_t i = 0; i < n; ++i) {
       auto it = bm->seqs.find(seq_ids[i]);
       if (it == bm->seqs.end()) return PA_ERR_NO_SEQ;
-      if (!seen.insert(seq_ids[i]).second) return PA_ERR_SEQ_EXISTS;
       pa_block_manager::Seq &s = it->second;
+      if (s.mark == call) return PA_ERR_SEQ_EXISTS;
+      s.mark = call;
       seqs[i] = &s;
       if (bm->blocks_for((int64_t)s.len + 1) > max_blocks) return PA_ERR_SHAPE;
-      auto ref = [&](int32_t b) {
-        auto f = sim_refs.find(b);
-        return f == sim_refs.end() ? bm->refs[b] : f->second;
-      };
       const int32_t c = bm->append_cost(s, ref);
-      if (c && s.len % bm->block_size != 0) sim_refs[s.table.back()] = ref(s.table.back()) - 1;
+      if (c && s.len % bm->block_size != 0) {
+        const int32_t b = s.table.back();
+        bm->sim_refs[b] = ref(b) - 1;
+        bm->sim_stamp[b] = call;
+      }
       need += c;
     }
     if (need > (int64_t)bm->free_list.size()) return PA_ERR_OOM;
@@ -235,7 +248,8 @@ int32_t pa_bm_prepare_decode(pa_block_manager *bm, const int64_t *seq_ids, int32
       const pa_block_manager::Seq &s = *seqs[i];
       int32_t *row = block_tables + (int64_t)i * max_blocks;
       const int32_t nb = (int32_t)s.table.size();
-      for (int32_t j = 0; j < max_blocks; ++j) row[j] = j < nb ? s.table[j] : pad_block;
+      std::copy(s.table.begin(), s.table.end(), row);
+      std::fill(row + nb, row + max_blocks, pad_block);
       context_lens[i] = s.len;
     }
   } catch (...) {

@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <deque>
 #include <new>
 #include <unordered_map>
@@ -66,8 +67,12 @@ struct pa_engine {
   std::unordered_map<int64_t, int32_t> live_requests;  // request -> samples not finished
   int64_t next_group = 0;
 
-  // index arrays, int32: [slots maxb][lens maxb][pairs 2 maxb][prompt slots R][tables maxb*MB]
-  size_t off_lens = 0, off_pairs = 0, off_prompt = 0, off_tables = 0, words = 0;
+  // index arrays, int32: [slots maxb][lens maxb][pairs 2 maxb][groups 2 maxb]
+  // [shared lengths maxb][dispatch list cap][prompt slots R][tables maxb*MB]
+  size_t off_lens = 0, off_pairs = 0, off_groups = 0, off_shared = 0, off_dispatch = 0;
+  size_t off_prompt = 0, off_tables = 0, words = 0;
+  int32_t dispatch_cap = 0;
+  bool q8 = false;  // an 8-bit pool (FP8 E4M3 or INT8)
   int32_t *staging[2] = {nullptr, nullptr};  // pinned host (device mode) or heap
   // double buffering: step t uses staging[t % 2] and dev_index[t % 2]; the
   // index copy runs on the engine's own copy stream, so that it overlaps the
@@ -152,16 +157,24 @@ int32_t pa_engine_create(const pa_engine_config *cfg, void *k_cache, void *v_cac
   if (!cfg || !out) return PA_ERR_NULL;
   *out = nullptr;
   const pa_engine_config c = *cfg;
-  if (c.dtype != PA_F32 && c.dtype != PA_BF16) return PA_ERR_DTYPE;
+  const bool q8 = c.dtype == PA_FP8_E4M3 || c.dtype == PA_INT8;
+  if (c.dtype != PA_F32 && c.dtype != PA_BF16 && !q8) return PA_ERR_DTYPE;
   if (c.num_blocks <= 0 || c.block_size <= 0 || c.block_size > 1024 ||
       (c.block_size & (c.block_size - 1)) || c.num_q_heads <= 0 || c.num_kv_heads <= 0 ||
       c.num_q_heads % c.num_kv_heads || c.max_batch <= 0 || c.max_batch > 65536 ||
       c.max_context_len <= 0 || c.max_prompt_rows < c.max_context_len ||
       (int64_t)c.num_blocks * c.block_size >= (int64_t(1) << 31) ||
-      (c.device != 0 && c.device != 1))
+      (c.device != 0 && c.device != 1) || (c.host_plan != 0 && c.host_plan != 1))
     return PA_ERR_SHAPE;
-  if (!pa::decode_supported(c.dtype, c.head_dim, c.num_q_heads / c.num_kv_heads))
+  if (q8) {
+    if (!pa::decode_q8_supported(c.head_dim, c.num_q_heads / c.num_kv_heads))
+      return PA_ERR_UNSUPPORTED;
+    if (!(c.k_scale > 0.f && c.k_scale < __builtin_huge_valf()) ||
+        !(c.v_scale > 0.f && c.v_scale < __builtin_huge_valf()))
+      return PA_ERR_SHAPE;
+  } else if (!pa::decode_supported(c.dtype, c.head_dim, c.num_q_heads / c.num_kv_heads)) {
     return PA_ERR_UNSUPPORTED;
+  }
   if (paged_attention_num_partitions(1, c.num_kv_heads, c.max_context_len, c.partition_size) < 0)
     return PA_ERR_SHAPE;
   if (c.device && (!k_cache || !v_cache)) return PA_ERR_NULL;
@@ -169,6 +182,7 @@ int32_t pa_engine_create(const pa_engine_config *cfg, void *k_cache, void *v_cac
   pa_engine *e = new (std::nothrow) pa_engine();
   if (!e) return PA_ERR_OOM;
   e->cfg = c;
+  e->q8 = q8;
   e->k_cache = k_cache;
   e->v_cache = v_cache;
   e->max_blocks = cdiv(c.max_context_len, c.block_size);
@@ -179,9 +193,26 @@ int32_t pa_engine_create(const pa_engine_config *cfg, void *k_cache, void *v_cac
     return PA_ERR_OOM;
   }
   const size_t mb = (size_t)c.max_batch;
+  // the longest dispatch list of any step: batch * partitions (largest for
+  // the longest context) plus four entries per prefix group
+  int64_t cap = 0;
+  if (c.host_plan)
+    for (int32_t n = 1; n <= c.max_batch; ++n)
+      cap = std::max<int64_t>(
+          cap, (int64_t)n * paged_attention_num_partitions(n, c.num_kv_heads, c.max_context_len,
+                                                           c.partition_size) +
+                   4 * (int64_t)n);
+  if (cap >= (int64_t(1) << 31)) {
+    release(e);
+    return PA_ERR_SHAPE;
+  }
+  e->dispatch_cap = (int32_t)cap;
   e->off_lens = mb;
   e->off_pairs = 2 * mb;
-  e->off_prompt = 4 * mb;
+  e->off_groups = 4 * mb;
+  e->off_shared = 6 * mb;
+  e->off_dispatch = 7 * mb;
+  e->off_prompt = e->off_dispatch + (size_t)cap;
   e->off_tables = e->off_prompt + (size_t)c.max_prompt_rows;
   e->words = e->off_tables + mb * (size_t)e->max_blocks;
   const size_t bytes = e->words * sizeof(int32_t);
@@ -238,9 +269,12 @@ int32_t pa_engine_create(const pa_engine_config *cfg, void *k_cache, void *v_cac
     // allowed bounds every step
     size_t ws = 0;
     for (int32_t s = 1; s <= c.max_batch; ++s)
-      ws = std::max(ws, paged_attention_workspace_size(s, c.num_q_heads, c.num_kv_heads,
-                                                       c.head_dim, c.max_context_len,
-                                                       c.partition_size));
+      ws = std::max(ws, c.host_plan ? paged_attention_prefix_workspace_size(
+                                          s, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                          c.max_context_len, c.partition_size, s, c.dtype)
+                                    : paged_attention_workspace_size(
+                                          s, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                          c.max_context_len, c.partition_size));
     if (ws) {
       if (hipMalloc(&e->workspace, ws) != hipSuccess) {
         e->workspace = nullptr;
@@ -295,6 +329,8 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
                        const void *prompt_k, const void *prompt_v, float scale, float *out,
                        void *stream, pa_step_info *info) {
   if (!e || !info) return PA_ERR_NULL;
+  using clock = std::chrono::steady_clock;
+  const auto t_start = clock::now();
   const pa_engine_config &c = e->cfg;
   if (c.device && (!q || !k_new || !v_new || !prompt_k || !prompt_v || !out)) return PA_ERR_NULL;
   hipStream_t st = (hipStream_t)stream;
@@ -302,13 +338,18 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
 
   // the staging buffer of this step was last copied from two steps ago
   const int buf = e->parity;
+  double wait_us = 0.0;
   if (e->pending[buf]) {
+    const auto t0 = clock::now();
     if (hipEventSynchronize(e->copied[buf]) != hipSuccess) return PA_ERR_LAUNCH;
+    wait_us = std::chrono::duration<double, std::micro>(clock::now() - t0).count();
     e->pending[buf] = false;
   }
   int32_t *hs = e->staging[buf];
   int32_t *slots = hs, *lens = hs + e->off_lens, *pairs = hs + e->off_pairs;
   int32_t *prompt_slots = hs + e->off_prompt, *tables = hs + e->off_tables;
+  int32_t *groups = hs + e->off_groups, *shared = hs + e->off_shared;
+  int32_t *dispatch = hs + e->off_dispatch;
 
   e->batch_ids.clear();
   e->admitted_ids.clear();
@@ -388,8 +429,35 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
       ctx_tokens += lens[i];
     }
 
+    // 3. the decode call planned on the host: shared-prefix groups (forked
+    //    samples hold their prompt's blocks) and the longest-first list
+    int32_t ng = 0, nd = 0;
+    int64_t unique_tokens = ctx_tokens;
+    if (n > 0) {
+      ng = pa_prefix_groups(tables, lens, n, MB, B, 64 / (c.num_q_heads / c.num_kv_heads), 16,
+                            groups, shared);
+      if (ng < 0) return ng;
+      // a group's members read the shared slots [0, longest shared length) once
+      for (int32_t g = 0; g < ng; ++g) {
+        int64_t sum = 0, longest = 0;
+        for (int32_t m = groups[2 * g]; m < groups[2 * g] + groups[2 * g + 1]; ++m) {
+          sum += shared[m];
+          longest = std::max<int64_t>(longest, shared[m]);
+        }
+        unique_tokens -= sum - longest;
+      }
+      if (!c.host_plan) ng = 0;  // counted only
+    }
+    if (c.host_plan && n > 0) {
+      nd = paged_attention_decode_plan(lens, groups, ng, shared, n, c.num_q_heads,
+                                       c.num_kv_heads, c.head_dim, B, MB, max_ctx, c.dtype,
+                                       c.partition_size, dispatch, e->dispatch_cap);
+      if (nd < 0) return nd;
+    }
+
     // 4. the device work: one copy of the index arrays, then prompt writes,
     //    copy-on-write copies, new-token writes and decode, in stream order
+    //    (an 8-bit pool: quantising writes of bfloat16 rows, 8-bit decode)
     if (c.device && n > 0) {
       const size_t words = e->off_tables + (size_t)n * MB;
       int32_t *dix = e->dev_index[buf];
@@ -406,10 +474,23 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
       const int32_t *d_pairs = dix + e->off_pairs;
       const int32_t *d_prompt = dix + e->off_prompt;
       const int32_t *d_tables = dix + e->off_tables;
+      const int32_t *d_groups = dix + e->off_groups, *d_shared = dix + e->off_shared;
+      const int32_t *d_dispatch = dix + e->off_dispatch;
+      auto write = [&](const void *k, const void *v, const int32_t *sl, int32_t rows) {
+        if (c.dtype == PA_FP8_E4M3)
+          return kv_cache_write_fp8(k, v, sl, rows, e->k_cache, e->v_cache, c.num_blocks, B,
+                                    c.num_kv_heads, c.head_dim, PA_BF16, c.k_scale, c.v_scale,
+                                    stream);
+        if (c.dtype == PA_INT8)
+          return kv_cache_write_int8(k, v, sl, rows, e->k_cache, e->v_cache, c.num_blocks, B,
+                                     c.num_kv_heads, c.head_dim, PA_BF16, c.k_scale, c.v_scale,
+                                     stream);
+        return kv_cache_write(k, v, sl, rows, e->k_cache, e->v_cache, c.num_blocks, B,
+                              c.num_kv_heads, c.head_dim, c.dtype, stream);
+      };
       int32_t rc;
       if (rows_used) {
-        rc = kv_cache_write(prompt_k, prompt_v, d_prompt, rows_used, e->k_cache, e->v_cache,
-                            c.num_blocks, B, c.num_kv_heads, c.head_dim, c.dtype, stream);
+        rc = write(prompt_k, prompt_v, d_prompt, rows_used);
         if (rc != PA_OK) return rc;
       }
       if (np) {
@@ -417,13 +498,26 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
                          c.head_dim, c.dtype, pairs, stream);
         if (rc != PA_OK) return rc;
       }
-      rc = kv_cache_write(k_new, v_new, d_slots, n, e->k_cache, e->v_cache, c.num_blocks, B,
-                          c.num_kv_heads, c.head_dim, c.dtype, stream);
+      rc = write(k_new, v_new, d_slots, n);
       if (rc != PA_OK) return rc;
-      rc = paged_attention_decode(q, e->k_cache, e->v_cache, d_tables, d_lens, scale, out, n,
-                                  c.num_q_heads, c.num_kv_heads, c.head_dim, B, c.num_blocks,
-                                  MB, max_ctx, c.dtype, c.partition_size, e->workspace,
-                                  e->workspace_bytes, stream);
+      if (c.host_plan) {
+        rc = paged_attention_decode_prefix(
+            q, e->k_cache, e->v_cache, d_tables, d_lens, ng ? d_groups : nullptr, ng,
+            ng ? d_shared : nullptr, d_dispatch, scale, c.k_scale, c.v_scale, out, n,
+            c.num_q_heads, c.num_kv_heads, c.head_dim, B, c.num_blocks, MB, max_ctx, c.dtype,
+            c.partition_size, e->workspace, e->workspace_bytes, stream);
+      } else if (e->q8) {
+        auto dec = c.dtype == PA_FP8_E4M3 ? paged_attention_decode_fp8
+                                          : paged_attention_decode_int8;
+        rc = dec(q, e->k_cache, e->v_cache, d_tables, d_lens, scale, c.k_scale, c.v_scale, out,
+                 n, c.num_q_heads, c.num_kv_heads, c.head_dim, B, c.num_blocks, MB, max_ctx,
+                 c.partition_size, e->workspace, e->workspace_bytes, stream);
+      } else {
+        rc = paged_attention_decode(q, e->k_cache, e->v_cache, d_tables, d_lens, scale, out, n,
+                                    c.num_q_heads, c.num_kv_heads, c.head_dim, B, c.num_blocks,
+                                    MB, max_ctx, c.dtype, c.partition_size, e->workspace,
+                                    e->workspace_bytes, stream);
+      }
       if (rc != PA_OK) return rc;
       if (hipEventRecord(e->consumed[buf], st) != hipSuccess) return PA_ERR_LAUNCH;
       e->used[buf] = true;
@@ -466,6 +560,15 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
     info->preempted_seq_ids = e->preempted_ids.data();
     info->finished_seq_ids = e->finished_ids.data();
     info->max_blocks_per_seq = MB;
+    info->num_groups = ng;
+    info->unique_tokens = unique_tokens;
+    info->prefix_groups = groups;
+    info->shared_lens = shared;
+    info->dispatch_len = nd;
+    info->dispatch = dispatch;
+    info->wait_us = (float)wait_us;
+    info->host_us =
+        (float)std::chrono::duration<double, std::micro>(clock::now() - t_start).count();
   } catch (...) {
     return PA_ERR_OOM;
   }

@@ -45,6 +45,7 @@ int main(void) {
   cfg.num_blocks = 64; cfg.block_size = 16; cfg.num_q_heads = 8; cfg.num_kv_heads = 2;
   cfg.head_dim = 128; cfg.dtype = PA_BF16; cfg.max_batch = 8; cfg.max_context_len = 256;
   cfg.max_prompt_rows = 256; cfg.partition_size = 0; cfg.device = 0;
+  cfg.k_scale = 1.f; cfg.v_scale = 1.f; cfg.host_plan = 1;
   pa_engine *e = NULL;
   CHECK(pa_engine_create(&cfg, NULL, NULL, &e) == PA_OK && e != NULL);
   CHECK(pa_engine_submit(e, 5, 20, 3, 2) == PA_OK);

@@ -171,7 +171,7 @@ def test_engine_create_rejects_bad_configs():
     lib = _lib.lib()
     base = dict(num_blocks=64, block_size=16, num_q_heads=8, num_kv_heads=2, head_dim=128,
                 dtype=1, max_batch=8, max_context_len=256, max_prompt_rows=256,
-                partition_size=0, device=0)
+                partition_size=0, device=0, k_scale=1.0, v_scale=1.0, host_plan=1)
 
     def create(**kw):
         cfg = dict(base, **kw)
@@ -192,6 +192,14 @@ def test_engine_create_rejects_bad_configs():
     assert create(num_q_heads=32, num_kv_heads=2) == -4   # group of 16
     assert create(partition_size=24) == -2
     assert create(device=1) == -1                 # no pool given
+    assert create(host_plan=2) == -2
+    assert create(host_plan=0) == 0
+    # 8-bit pools: head_dim 128 and valid scales
+    assert create(dtype=pa.PA_FP8_E4M3, k_scale=0.25, v_scale=0.5) == 0
+    assert create(dtype=pa.PA_INT8, k_scale=0.02, v_scale=0.03) == 0
+    assert create(dtype=pa.PA_FP8_E4M3, k_scale=0.0) == -2
+    assert create(dtype=pa.PA_INT8, v_scale=float("inf")) == -2
+    assert create(dtype=pa.PA_FP8_E4M3, head_dim=64, k_scale=0.25, v_scale=0.5) == -4
     assert lib.pa_engine_create(None, None, None, None) == -1
 
 

@@ -3,7 +3,9 @@ calls of pagedattn.h (needs an MI355X): the block manager's slots, copy pairs,
 block tables and lengths drive copy_blocks, kv_cache_write and
 paged_attention_decode for many steps, with forks, finishes, admissions and
 preemption; the pool must hold each sequence's recorded tokens bit for bit and
-decode must match the oracle's dense attention over them."""
+decode must match the oracle's dense attention over them.  The same for the
+native engine, with and without its host planning (shared-prefix groups and
+dispatch list), and over FP8 / INT8 pools."""
 import numpy as np
 import pytest
 import torch
@@ -82,22 +84,46 @@ def test_serving_loop_preempts_when_the_pool_is_full():
     assert loop.preempted > 0
 
 
+@pytest.mark.parametrize("host_plan", [True, False])
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,B,NB,ps", [
     ("bf16", 32, 8, 128, 16, 800, 0),   # matrix-core decode, automatic partitions
     ("bf16", 16, 2, 128, 16, 800, 64),  # groups of 8, forced 64-token partitions
     ("f32", 8, 2, 64, 16, 800, 0),      # vector decode
     ("bf16", 32, 8, 128, 16, 90, 0),    # small pool: preemption and recompute
 ])
-def test_engine_steps_match_oracle(dtype, Hq, Hkv, D, B, NB, ps):
+def test_engine_steps_match_oracle(dtype, Hq, Hkv, D, B, NB, ps, host_plan):
     """The native engine (scheduler, block manager, one index copy and four
     device calls per step) over a stream of requests with parallel samples:
     after every step the pool holds each batch row's tokens bit for bit and
-    decode matches dense attention over them."""
+    decode matches dense attention over them; with host_plan, the step's
+    decode reads the forked samples' shared prompt blocks once per group in
+    the order planned on the host."""
     from serving_loop import EngineHarness, drive_engine
-    say(f"engine {dtype} Hq={Hq} Hkv={Hkv} D={D} B={B} NB={NB} ps={ps}")
+    say(f"engine {dtype} Hq={Hq} Hkv={Hkv} D={D} B={B} NB={NB} ps={ps} plan={host_plan}")
     h = EngineHarness("device", dtype, Hq, Hkv, D, B, NB, max_batch=48, max_ctx=400,
-                      seed=NB + D, partition_size=ps)
+                      seed=NB + D, partition_size=ps, host_plan=host_plan)
     drive_engine(h, num_requests=36, seed=NB + D, max_prompt=300, max_new=40)
+    assert h.copies > 0
+    if NB < 100:
+        assert h.preempted > 0
+    if host_plan and dtype == "bf16":
+        assert h.groups_seen > 0
+    h.eng.close()
+
+
+@pytest.mark.parametrize("kv8", ["fp8", "int8"])
+@pytest.mark.parametrize("Hq,Hkv,NB,ps", [(32, 8, 800, 0), (8, 8, 800, 64), (32, 8, 90, 0)])
+def test_engine_8bit_pools(kv8, Hq, Hkv, NB, ps):
+    """The engine over an FP8 / INT8 pool: bfloat16 token rows quantised by
+    its writes; after every step the pool holds the oracle's codes of each
+    row's tokens and decode matches dense attention over their dequantised
+    values (forks sharing prompt blocks, copy-on-write, preemption in the
+    small pool)."""
+    from serving_loop import EngineHarness, drive_engine
+    say(f"engine {kv8} Hq={Hq} Hkv={Hkv} NB={NB} ps={ps}")
+    h = EngineHarness("device", "bf16", Hq, Hkv, 128, 16, NB, max_batch=48, max_ctx=400,
+                      seed=NB + Hq, partition_size=ps, kv8=kv8)
+    drive_engine(h, num_requests=36, seed=NB + Hq, max_prompt=300, max_new=40)
     assert h.copies > 0
     if NB < 100:
         assert h.preempted > 0
