@@ -33,6 +33,10 @@
 //    matrix cores give fp32-grade weights.
 //  * The causal mask is applied to scores (token t > the row's position
 //    gets -inf) only in tiles that reach past the workgroup's first row.
+//  * Software pipeline: K runs one tile ahead of V, so each wave issues the
+//    q.K products of tile t + 1 while its vector unit forms tile t's
+//    probabilities, and the tiles arrive by gfx950's direct global -> LDS
+//    loads (no staging registers), a full iteration ahead of their use.
 //
 // Workgroups are mapped to the 8 XCDs so that all row tiles of one
 // (sequence, KV head), which read the same K/V, run on one XCD and share its
@@ -123,16 +127,6 @@ __device__ __forceinline__ u32x4 widen8(u32x2 w) {
 // tile is loaded as codes (8 bytes per chunk) and widened exactly to
 // bfloat16 when it is stored to LDS, so the products are those of the
 // bfloat16 pool.
-template <int D, int Q8>
-struct TileRegs {
-  // K and V: chunk c = threadIdx + 256 j of the tile (token c / (D/8),
-  // elements 8 (c % (D/8)) .. +7)
-  static constexpr int kKChunks = kTk * D / 8 / kThreads;  // 4 (D=128) or 2 (D=64)
-  using Chunk = typename std::conditional<Q8 == 0, u32x4, u32x2>::type;
-  Chunk k[kKChunks];
-  Chunk v[kKChunks];
-};
-
 template <int D, int RS, int Q8>
 __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     const uint16_t *__restrict__ q, const void *__restrict__ kc_raw,
@@ -145,11 +139,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   const KV *__restrict__ kc = static_cast<const KV *>(kc_raw);
   const KV *__restrict__ vc = static_cast<const KV *>(vc_raw);
   constexpr int kRows = 64 * RS;  // query rows per workgroup
-  constexpr int kKs = kTk == 64 ? D + 8 : D;  // K tile row stride (elements), padded
   constexpr int kSteps = D / 32;              // k-steps of q.K
   constexpr int kDb = D / 16;                 // 16-element blocks of the output
-  using Regs = TileRegs<D, Q8>;
-  using Chunk = typename Regs::Chunk;
 
   // XCD-aware order.  A unit r is a KV head (r % hkv) of a (sequence,
   // partition) item (r / hkv: from the longest-first list when there is one,
@@ -202,7 +193,6 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   // operand of q.K; sl2 becomes |sl2| once q carries the scale's sign
   int pos[RS];
   bf16x8 qb[RS][kSteps];
-  int wave_last = -1;
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
     const int R = row0 + (wave * RS + r) * 16 + c16;
@@ -220,77 +210,145 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
         qb[r][k] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4 *>(qrow + 32 * k) ^ u32x4{flip, flip, flip, flip});
     }
-    // the wave's last attended position (rows are ascending in position)
-    const int Rw = min(row0 + (wave * RS + r) * 16 + 15, row_end - 1);
-    if (row0 + (wave * RS + r) * 16 < row_end) wave_last = max(wave_last, L - n + Rw / G);
   }
   sl2 = fmaxf(__builtin_fabsf(sl2), 1.17549435e-38f);
   // kSlack in raw score units, kept finite so that the first tile with a
   // finite maximum always sets m (-inf + slack stays -inf)
   const float slack = fminf(kSlack / sl2, 3.40282347e38f);
 
-  // both tiles row-major; V rows are padded differently from K rows so that
-  // the transposing reads of V (4 rows x 32 bytes per 16 lanes) and the
-  // 16-row reads of K are both free of bank conflicts.  Two buffers of each:
-  // the next tile is stored into one while the waves compute on the other.
-  constexpr int kVs = D + 16;
-  __shared__ __attribute__((aligned(16))) uint16_t sk_buf[2][kTk * kKs];
-  __shared__ __attribute__((aligned(16))) uint16_t sv_buf[2][kTk * kVs];
-  // physical block of each token of the next tiles, two slots: the table is
-  // read one tile ahead of the K/V rows it locates, so that the two reads
-  // never wait on each other
-  __shared__ uint32_t sbid[2][kTk];
+  // K and V tiles in LDS as unpadded rows of 2 D bytes whose 16-byte chunks
+  // are permuted per row (chunk c of row t stored at c ^ swz(t)), so that
+  // the 16-row reads of K and the transposing reads of V (4 rows x 32 bytes
+  // per 16 lanes) meet every bank once.  A tile is filled in 1 KB groups:
+  // group j of wave w is bytes [1024 (4 j + w), +1024), lane l writing its
+  // 16 bytes at 16 l -- the layout of gfx950's direct global -> LDS loads,
+  // which bfloat16 pools use (8-bit codes arrive the same way and are widened
+  // in LDS, see below).  K runs one tile ahead of V (the scores of tile t + 1 are
+  // computed while tile t's probabilities are formed); in iteration t the
+  // waves read K(t + 1) and V(t) while K(t + 2) and V(t + 1) arrive in the
+  // other two buffers.
+  constexpr int kCpr = D / 8;            // 16-byte chunks per row
+  constexpr int kRpb = 16 / kCpr;        // rows per 256 bytes (all 64 banks)
+  constexpr int kRpg = 512 / D;          // rows per 1 KB group
+  constexpr int kGroups = D / 32;        // 1 KB groups per wave and tile
+  // (four separate arrays, each named statically in the loop below: the
+  // compiler then knows that reading one buffer never waits for the direct
+  // loads into another)
+  __shared__ __attribute__((aligned(1024))) uint16_t sk0[kTk * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sk1[kTk * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv0[kTk * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sv1[kTk * D];
+  // physical block of each token of three consecutive tiles (tile j in slot
+  // j % 3): the table is read ahead of the K/V rows it locates, so that the
+  // two reads never wait on each other
+  __shared__ uint32_t sbid[3][kTk];
+  auto swz_k = [](int t) { return (t / kRpb) & (kCpr - 1); };
+  auto swz_v = [](int t) { return 2 * ((t / kRpb) & (kCpr / 2 - 1)); };
 
   auto table_entry = [&](int k0) -> uint32_t {  // token k0 + threadIdx.x (< 64 threads)
     const int tok = k0 + (int)threadIdx.x;
     return tok <= pos_last ? min((uint32_t)tbl[tok >> lgB], (uint32_t)(nb - 1)) : 0u;
   };
 
-  // global -> registers for the tile at k0.  Thread t takes head_dim chunk
-  // t % (D/8) of tokens t / (D/8) + kTokStep j; a token's K and V rows share
-  // one offset, and the block ids come from LDS in one batch.  Tokens past
-  // pos_last have table entry 0, so every address is a row of the pool;
-  // their V rows are zeroed (p = 0 there, and 0 * NaN would not vanish),
-  // their K rows only meet masked scores.
-  constexpr int kTokStep = kThreads / (D / 8);
-  auto load_tile = [&](Regs &T, int k0, const uint32_t *ids) {
-    const int dc = (int)threadIdx.x % (D / 8);
-    const int tt0 = (int)threadIdx.x / (D / 8);
-    uint32_t id[Regs::kKChunks];
+  // This lane's share of a tile: in group j, row kRpg (4 j + wave) + lane /
+  // kCpr, stored chunk lane % kCpr, which holds the row's chunk
+  // (lane % kCpr) ^ swz(row).  Tokens past pos_last have table entry 0, so
+  // every address is a row of the pool.
+  const int grow = lane / kCpr;
+  auto src_off = [&](int k0, const uint32_t *ids, int j, bool is_v) -> int64_t {
+    const int t = kRpg * (kWaves * j + wave) + grow;
+    const int c = (lane % kCpr) ^ (is_v ? swz_v(t) : swz_k(t));
+    return (int64_t)ids[t] * block_elems + head_off + (int64_t)(((k0 + t) & bm1) * D + 8 * c);
+  };
+  auto lds_group = [&](uint16_t *buf, int j) { return buf + 512 * (kWaves * j + wave); };
+  // bfloat16: the loads write LDS themselves
+  auto dma_rows = [&](const KV *pool, uint16_t *buf, int k0, const uint32_t *ids, bool is_v) {
 #pragma unroll
-    for (int j = 0; j < Regs::kKChunks; ++j) id[j] = ids[tt0 + kTokStep * j];
-    int64_t off[Regs::kKChunks];
+    for (int j = 0; j < kGroups; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void *)(pool + src_off(k0, ids, j, is_v)),
+          (__attribute__((address_space(3))) void *)lds_group(buf, j), 16, 0, 0);
+  };
+  // through registers: a bfloat16 V tile holding tokens past pos_last, whose
+  // rows there are zeroed (p = 0 there, and 0 * NaN would not vanish; K rows
+  // there only meet masked scores)
+  auto fetch_v_tail = [&](uint16_t *buf, int k0, const uint32_t *ids) {
+    u32x4 R[kGroups];
 #pragma unroll
-    for (int j = 0; j < Regs::kKChunks; ++j)
-      off[j] = (int64_t)id[j] * block_elems + head_off +
-               (int64_t)(((k0 + tt0 + kTokStep * j) & bm1) * D + 8 * dc);
+    for (int j = 0; j < kGroups; ++j) {
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(vc + src_off(k0, ids, j, true));
+      R[j] = k0 + kRpg * (kWaves * j + wave) + grow <= pos_last ? x : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
-    for (int j = 0; j < Regs::kKChunks; ++j)
-      T.k[j] = *reinterpret_cast<const Chunk *>(kc + off[j]);
+    for (int j = 0; j < kGroups; ++j)
+      *reinterpret_cast<u32x4 *>(lds_group(buf, j) + 8 * lane) = R[j];
+  };
+
+  // 8-bit pools.  A tile's codes are loaded directly in 1 KB groups too:
+  // group g = 4 j + wave holds rows kQRows g .. +kQRows-1 (16 codes per
+  // lane) and lands in the first half of the 2 KB those rows take as
+  // bfloat16.  The wave that loaded a group widens it there: it reads the
+  // codes, then writes the rows over the same 2 KB, which no other wave
+  // touches, so the rewrite needs no barrier of its own (LDS serves a
+  // wave's instructions in order, and the writes wait on the read's data).
+  constexpr int kQGroups = D / 64;  // code groups per wave and tile
+  constexpr int kQRows = 1024 / D;  // rows per code group
+  constexpr int kQcpr = D / 16;     // 16-code chunks per row
+  auto dma_codes = [&](const KV *pool, uint16_t *buf, int k0, const uint32_t *ids) {
 #pragma unroll
-    for (int j = 0; j < Regs::kKChunks; ++j) {
-      const Chunk v = *reinterpret_cast<const Chunk *>(vc + off[j]);
-      T.v[j] = k0 + tt0 + kTokStep * j <= pos_last ? v : Chunk{};
+    for (int j = 0; j < kQGroups; ++j) {
+      const int g = kWaves * j + wave;
+      const int t = kQRows * g + lane / kQcpr;
+      const int64_t off = (int64_t)ids[t] * block_elems + head_off +
+                          (int64_t)(((k0 + t) & bm1) * D + 16 * (lane % kQcpr));
+      __builtin_amdgcn_global_load_lds(
+          (const void *)(pool + off), (__attribute__((address_space(3))) void *)(buf + 1024 * g),
+          16, 0, 0);
     }
   };
-  // registers -> LDS buffer `buf`, both row-major (8-bit codes widened to
-  // bfloat16 here, once the loads have landed)
-  auto store_tile = [&](const Regs &T, int buf) {
+  auto expand_codes = [&](uint16_t *buf, int k0, bool is_v) {
 #pragma unroll
-    for (int j = 0; j < Regs::kKChunks; ++j) {
-      const int c = threadIdx.x + kThreads * j;
-      u32x4 kw, vw;
-      if constexpr (Q8 == 0) {
-        kw = T.k[j];
-        vw = T.v[j];
-      } else {
-        kw = widen8<Q8>(T.k[j]);
-        vw = widen8<Q8>(T.v[j]);
-      }
-      *reinterpret_cast<u32x4 *>(&sk_buf[buf][(c / (D / 8)) * kKs + 8 * (c % (D / 8))]) = kw;
-      *reinterpret_cast<u32x4 *>(&sv_buf[buf][(c / (D / 8)) * kVs + 8 * (c % (D / 8))]) = vw;
+    for (int j = 0; j < kQGroups; ++j) {
+      const int g = kWaves * j + wave;
+      const int t = kQRows * g + lane / kQcpr;
+      const u32x4 codes = *reinterpret_cast<const u32x4 *>(buf + 1024 * g + 8 * lane);
+      u32x4 lo = widen8<Q8>(u32x2{codes[0], codes[1]});
+      u32x4 hi = widen8<Q8>(u32x2{codes[2], codes[3]});
+      if (is_v && k0 + t > pos_last) lo = hi = u32x4{0, 0, 0, 0};
+      const int c = 2 * (lane % kQcpr);
+      const int sw = is_v ? swz_v(t) : swz_k(t);
+      *reinterpret_cast<u32x4 *>(buf + t * D + 8 * (c ^ sw)) = lo;
+      *reinterpret_cast<u32x4 *>(buf + t * D + 8 * ((c + 1) ^ sw)) = hi;
     }
   };
+
+  // S^T of one tile into sc: k-step outermost, so that the 4 * RS
+  // accumulator chains interleave and no product waits on the one before it.
+  // Row 16 tb + c16 keeps swz_k(c16) for every tb.
+  const int sk_lane = c16 * D;
+  const int swk = swz_k(c16);
+  auto scores = [&](f32x4 (&sc)[RS][4], const uint16_t *sk) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) sc[r][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k) {
+      const uint16_t *kp = sk + sk_lane + 8 * ((4 * k + g4) ^ swk);
+      bf16x8 a[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        a[tb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(kp + 16 * tb * D));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int r = 0; r < RS; ++r)
+          sc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], qb[r][k], sc[r][tb], 0, 0, 0);
+    }
+  };
+  // V rows 32 kk + 16 h + 4 g4 + c16 / 4 keep swz_v(4 g4 + c16 / 4)
+  const int sv_lane = (4 * g4 + c16 / 4) * D + 4 * (c16 & 1);
+  const int swv = swz_v(4 * g4 + c16 / 4);
 
   f32x4 acc[RS][kDb];
 #pragma unroll
@@ -304,150 +362,182 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     lsum[r] = 0.f;
   }
 
-  // Pipeline, one barrier per tile.  In iteration it the waves compute on
-  // tile it (buffer it & 1) while the loads of tile it + 1 are in flight;
-  // then each wave stores tile it + 1 into the other buffer (last read by
-  // tile it - 1, before the previous barrier), writes the block ids of tile
-  // it + 2 into the id slot tile it used (read when tile it's loads were
-  // issued, before the previous barrier), and after the barrier issues the
-  // loads of tile it + 2.
-  Regs T;
+  // bfloat16 V tile at k0 into buf: directly, or through registers when it
+  // runs past pos_last (at most the last tile)
+  auto fetch_v = [&](uint16_t *buf, int k0, const uint32_t *ids) {
+    if (k0 + kTk - 1 <= pos_last)
+      dma_rows(vc, buf, k0, ids, true);
+    else
+      fetch_v_tail(buf, k0, ids);
+  };
+
+  // Prologue: block ids of tiles 0..2, K and V of tile 0, K of tile 1, and
+  // the scores of tile 0.
   uint32_t id_next = 0;
-  if (threadIdx.x < kTk) sbid[0][threadIdx.x] = table_entry(k_begin);
+  if (threadIdx.x < kTk) {
+    sbid[0][threadIdx.x] = table_entry(k_begin);
+    sbid[1][threadIdx.x] = ntiles > 1 ? table_entry(k_begin + kTk) : 0u;
+  }
   __syncthreads();
-  load_tile(T, k_begin, sbid[0]);
-  if (threadIdx.x < kTk && ntiles > 1) id_next = table_entry(k_begin + kTk);
-  store_tile(T, 0);
-  if (threadIdx.x < kTk) sbid[1][threadIdx.x] = id_next;
+  if constexpr (Q8 == 0) {
+    dma_rows(kc, sk0, k_begin, sbid[0], false);
+    if (ntiles > 1) dma_rows(kc, sk1, k_begin + kTk, sbid[1], false);
+    fetch_v(sv0, k_begin, sbid[0]);
+  } else {
+    dma_codes(kc, sk0, k_begin, sbid[0]);
+    if (ntiles > 1) dma_codes(kc, sk1, k_begin + kTk, sbid[1]);
+    dma_codes(vc, sv0, k_begin, sbid[0]);
+    expand_codes(sk0, k_begin, false);
+    if (ntiles > 1) expand_codes(sk1, k_begin + kTk, false);
+    expand_codes(sv0, k_begin, true);
+  }
+  if (threadIdx.x < kTk) sbid[2][threadIdx.x] = ntiles > 2 ? table_entry(k_begin + 2 * kTk) : 0u;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads are in LDS
   __syncthreads();
-  if (ntiles > 1) load_tile(T, k_begin + kTk, sbid[1]);
-  if (threadIdx.x < kTk && ntiles > 2) id_next = table_entry(k_begin + 2 * kTk);
-  for (int it = 0; it < ntiles; ++it) {
+  if (threadIdx.x < kTk && ntiles > 3) id_next = table_entry(k_begin + 3 * kTk);
+  f32x4 sc[RS][4];
+  scores(sc, sk0);
+  __syncthreads();  // every wave is done with K(0) before K(2) replaces it
+
+  // Iteration it (of parity P, a compile-time constant in each half of the
+  // unrolled loop): reads K(it + 1) from sk[1 - P] and V(it) from sv[P].
+  int slot = 0;  // it % 3
+  auto iteration = [&](auto parity, int it) {
+    constexpr int P = decltype(parity)::value;
+    uint16_t *const sk_this = P ? sk1 : sk0;  // K(it), then K(it + 2)
+    uint16_t *const sk_next = P ? sk0 : sk1;  // K(it + 1)
+    uint16_t *const sv_this = P ? sv1 : sv0;  // V(it)
+    uint16_t *const sv_next = P ? sv0 : sv1;  // V(it - 1), then V(it + 1)
     const int k0 = k_begin + it * kTk;
-    if (k0 <= wave_last) {  // else all of this wave's rows end earlier
-      const uint16_t *sk = sk_buf[it & 1];
-      const uint16_t *sv = sv_buf[it & 1];
-      const bool masked = k0 + kTk - 1 > pos_first;
+    const int slot1 = slot == 2 ? 0 : slot + 1;
+    const int slot2 = slot1 == 2 ? 0 : slot1 + 1;
+    // K(it + 2) into the buffer K(it) left (last read in iteration it - 1),
+    // V(it + 1) into the one V(it - 1) left: they land during this
+    // iteration (8-bit codes are widened at its end).
+    if constexpr (Q8 == 0) {
+      if (it + 2 < ntiles) dma_rows(kc, sk_this, k0 + 2 * kTk, sbid[slot2], false);
+      if (it + 1 < ntiles) fetch_v(sv_next, k0 + kTk, sbid[slot1]);
+    } else {
+      if (it + 2 < ntiles) dma_codes(kc, sk_this, k0 + 2 * kTk, sbid[slot2]);
+      if (it + 1 < ntiles) dma_codes(vc, sv_next, k0 + kTk, sbid[slot1]);
+    }
 
-      // S^T for each 16-token block tb and row set r.  Each product phase
-      // runs at raised wave priority, so that a wave with products to
-      // issue goes ahead of one in its softmax and the matrix cores of the
-      // SIMD stay fed.
-      __builtin_amdgcn_s_setprio(1);
-      f32x4 sc[RS][4];
+    // Online softmax of tile it.  The running maximum m is kept on the raw
+    // scores (sl2 > 0: q carries a negative scale's sign, and a zero scale
+    // is raised to the least normal float, which gives every unmasked p = 1
+    // as zero does), and p = 2^((x - m) sl2): exactly 1 at the maximum.
+    // Masked positions (only in tiles that reach past the workgroup's first
+    // row) become -inf, so p = 0.
+    const bool masked = k0 + kTk - 1 > pos_first;
+    float mu[RS];
 #pragma unroll
-      for (int r = 0; r < RS; ++r)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) sc[r][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-        for (int k = 0; k < kSteps; ++k) {
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8,
-              *reinterpret_cast<const u32x4 *>(&sk[(16 * tb + c16) * kKs + 32 * k + 8 * g4]));
-#pragma unroll
-          for (int r = 0; r < RS; ++r)
-            sc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[r][k], sc[r][tb], 0, 0, 0);
-        }
-      }
-
-      __builtin_amdgcn_s_setprio(0);
-
-      // online softmax per row set; then the hi/lo probability operands.
-      // The running maximum m is kept on the raw scores (sl2 > 0: q carries
-      // a negative scale's sign, and a zero scale is raised to the least
-      // normal float, which gives every unmasked p = 1 as zero does), and
-      // p = 2^((x - m) sl2): exactly 1 at the maximum.  Masked positions
-      // (only in tiles that reach past the workgroup's first row) become
-      // -inf, so p = 0.
-      bf16x8 phi[RS][2], plo[RS][2];
-#pragma unroll
-      for (int r = 0; r < RS; ++r) {
-        if (masked) {
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (k0 + 16 * tb + 4 * g4 + i > pos[r]) sc[r][tb][i] = neg_inf();
-        }
-        float cm = neg_inf();
+    for (int r = 0; r < RS; ++r) {
+      if (masked) {
+        // token k0 + 16 tb + 4 g4 + i lies past the row's position
+        const int lim = pos[r] - k0 - 4 * g4;
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[r][tb][i]);
-        cm = group_max4(cm);
-        // wave-uniform branch (lanes that need no rescale scale by exactly
-        // 1), so the accumulators are updated in place
-        const bool up = cm > m[r] + slack;  // false while both are -inf
-        if (__builtin_amdgcn_ballot_w64(up)) {
-          const float alpha =
-              up ? __builtin_amdgcn_exp2f((m[r] - cm) * sl2) : 1.f;  // 0 when m was -inf
-          lsum[r] *= alpha;
-#pragma unroll
-          for (int b = 0; b < kDb; ++b) acc[r][b] *= alpha;
-          m[r] = up ? cm : m[r];
-        }
-        const float mu = (m[r] == neg_inf()) ? 0.f : m[r];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          uint32_t hw[4], lw[4];
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            float pr[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int jj = j + u;
-              const int tb = 2 * kk + (jj >> 2);
-              pr[u] = __builtin_amdgcn_exp2f((sc[r][tb][jj & 3] - mu) * sl2);
-            }
-            lsum[r] += pr[0] + pr[1];
-            const uint32_t h = bf16x2_bits(pr[0], pr[1]);
-            hw[j >> 1] = h;
-            lw[j >> 1] = bf16x2_bits(pr[0] - __uint_as_float(h << 16),
-                                     pr[1] - __uint_as_float(h & 0xFFFF0000u));
-          }
-          phi[r][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-          plo[r][kk] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
-        }
+          for (int i = 0; i < 4; ++i)
+            if (16 * tb + i > lim) sc[r][tb][i] = neg_inf();
       }
+      float cm = neg_inf();
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[r][tb][i]);
+      cm = group_max4(cm);
+      // wave-uniform branch (lanes that need no rescale scale by exactly
+      // 1), so the accumulators are updated in place
+      const bool up = cm > m[r] + slack;  // false while both are -inf
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float alpha =
+            up ? __builtin_amdgcn_exp2f((m[r] - cm) * sl2) : 1.f;  // 0 when m was -inf
+        lsum[r] *= alpha;
+#pragma unroll
+        for (int b = 0; b < kDb; ++b) acc[r][b] *= alpha;
+        m[r] = up ? cm : m[r];
+      }
+      mu[r] = (m[r] == neg_inf()) ? 0.f : m[r];
+    }
 
-      // O^T += V^T P^T
-      __builtin_amdgcn_s_setprio(1);
+    // The scores of tile it + 1 on the matrix cores while the vector unit
+    // turns tile it's scores into the hi/lo probability operands (on the
+    // last tile the products read a stale buffer and are discarded).
+    __builtin_amdgcn_s_setprio(1);
+    f32x4 sn[RS][4];
+    scores(sn, sk_next);
+    bf16x8 phi[RS][2], plo[RS][2];
 #pragma unroll
-      for (int b = 0; b < kDb; ++b) {
+    for (int r = 0; r < RS; ++r) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          // gfx950's transposing LDS read: within each 16-lane group, lane c
-          // points at 4 elements of row (base + c / 4) and receives, from the
-          // rows base .. base + 3, the element in its own column -- here
-          // element 16 b + c16 of tokens 32 kk + 4 g4 + 0..3 (and + 16)
-          const uint16_t *vr = &sv[(32 * kk + 4 * g4 + c16 / 4) * kVs + 16 * b + 4 * (c16 % 4)];
-          const u32x2 lo = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vr)));
-          const u32x2 hi = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vr + 16 * kVs)));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t hw[4], lw[4];
 #pragma unroll
-          for (int r = 0; r < RS; ++r) {
-            acc[r][b] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[r][kk], acc[r][b], 0, 0, 0);
-            acc[r][b] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[r][kk], acc[r][b], 0, 0, 0);
+        for (int j = 0; j < 8; j += 2) {
+          float pr[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int jj = j + u;
+            const int tb = 2 * kk + (jj >> 2);
+            pr[u] = __builtin_amdgcn_exp2f((sc[r][tb][jj & 3] - mu[r]) * sl2);
           }
+          lsum[r] += pr[0] + pr[1];
+          const uint32_t h = bf16x2_bits(pr[0], pr[1]);
+          hw[j >> 1] = h;
+          lw[j >> 1] = bf16x2_bits(pr[0] - __uint_as_float(h << 16),
+                                   pr[1] - __uint_as_float(h & 0xFFFF0000u));
+        }
+        phi[r][kk] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+        plo[r][kk] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+      }
+    }
+
+    // O^T += V^T P^T.  gfx950's transposing LDS read: within each 16-lane
+    // group, lane c points at 4 elements of row (base + c / 4) and receives,
+    // from the rows base .. base + 3, the element in its own column -- here
+    // element 16 b + c16 of tokens 32 kk + 4 g4 + 0..3 (and + 16).
+    const uint16_t *sv = sv_this + sv_lane;
+#pragma unroll
+    for (int b = 0; b < kDb; ++b) {
+      const uint16_t *vb = sv + 8 * ((2 * b + ((c16 & 3) >> 1)) ^ swv);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + 32 * kk * D)));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2,
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vb + (32 * kk + 16) * D)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int r = 0; r < RS; ++r) {
+          acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[r][kk], acc[r][b], 0, 0, 0);
+          acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[r][kk], acc[r][b], 0, 0, 0);
         }
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (it + 1 < ntiles) {
-      store_tile(T, (it + 1) & 1);
-      if (threadIdx.x < kTk && it + 2 < ntiles) sbid[it & 1][threadIdx.x] = id_next;
-      __syncthreads();
-      if (it + 2 < ntiles) load_tile(T, k0 + 2 * kTk, sbid[it & 1]);  // during the products
-      if (threadIdx.x < kTk && it + 3 < ntiles) id_next = table_entry(k0 + 3 * kTk);
-    }
-  }
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) sc[r][tb] = sn[r][tb];
 
+    if constexpr (Q8 != 0) {
+      if (it + 2 < ntiles) expand_codes(sk_this, k0 + 2 * kTk, false);
+      if (it + 1 < ntiles) expand_codes(sv_next, k0 + kTk, true);
+    }
+    // the ids of tile it + 3 into the slot of tile it (last read when V(it)
+    // was fetched)
+    if (threadIdx.x < kTk && it + 3 < ntiles) sbid[slot][threadIdx.x] = id_next;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads are in LDS
+    __syncthreads();
+    if (threadIdx.x < kTk && it + 4 < ntiles) id_next = table_entry(k0 + 4 * kTk);
+    slot = slot1;
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    iteration(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntiles) iteration(std::integral_constant<int, 1>{}, it + 1);
+  }
   // normalise and write: lane (g4, c16) holds row c16 of each row set,
   // elements 16 b + 4 g4 .. +3.  A sequence whose context fits in one
   // partition goes straight to out (the merge skips it); the others leave
