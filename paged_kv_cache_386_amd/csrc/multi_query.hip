@@ -64,6 +64,7 @@ constexpr float kSlack = 8.f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -238,10 +239,12 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t sk1[kTk * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sv0[kTk * D];
   __shared__ __attribute__((aligned(1024))) uint16_t sv1[kTk * D];
-  // physical block of each token of three consecutive tiles (tile j in slot
-  // j % 3): the table is read ahead of the K/V rows it locates, so that the
-  // two reads never wait on each other
-  __shared__ uint32_t sbid[3][kTk];
+  // Byte addresses of each token's K and V rows (this KV head) for three
+  // consecutive tiles (tile j in slot j % 3), written by the 64 threads that
+  // read the block table, one tile ahead of the loads that use them: the
+  // table read and the row reads never wait on each other, and a lane's
+  // load address is one add.
+  __shared__ __attribute__((aligned(16))) uint64_t sadr[3][kTk][2];
   auto swz_k = [](int t) { return (t / kRpb) & (kCpr - 1); };
   auto swz_v = [](int t) { return 2 * ((t / kRpb) & (kCpr / 2 - 1)); };
 
@@ -250,34 +253,45 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     return tok <= pos_last ? min((uint32_t)tbl[tok >> lgB], (uint32_t)(nb - 1)) : 0u;
   };
 
-  // This lane's share of a tile: in group j, row kRpg (4 j + wave) + lane /
-  // kCpr, stored chunk lane % kCpr, which holds the row's chunk
-  // (lane % kCpr) ^ swz(row).  Tokens past pos_last have table entry 0, so
-  // every address is a row of the pool.
+  constexpr int kEs = Q8 ? 1 : 2;  // bytes per element
+  const uint64_t kbase = (uint64_t)kc + (uint64_t)head_off * kEs;
+  const uint64_t vbase = (uint64_t)vc + (uint64_t)head_off * kEs;
+  const uint64_t block_bytes = (uint64_t)block_elems * kEs;
+  auto put_addrs = [&](int slot, int k0, uint32_t id) {  // threads < 64
+    const int tok = k0 + (int)threadIdx.x;
+    const uint64_t off = (uint64_t)id * block_bytes + (uint64_t)((tok & bm1) * D * kEs);
+    *reinterpret_cast<u64x2 *>(&sadr[slot][threadIdx.x][0]) = u64x2{kbase + off, vbase + off};
+  };
+
+  // This lane's share of a tile: in group j, row t0 + kRpg kWaves j, stored
+  // chunk lane % kCpr, which holds the row's chunk (lane % kCpr) ^ swz(row)
+  // -- the same chunk in every group.  Tokens past pos_last have table entry
+  // 0, so every address is a row of the pool.
   const int grow = lane / kCpr;
-  auto src_off = [&](int k0, const uint32_t *ids, int j, bool is_v) -> int64_t {
-    const int t = kRpg * (kWaves * j + wave) + grow;
-    const int c = (lane % kCpr) ^ (is_v ? swz_v(t) : swz_k(t));
-    return (int64_t)ids[t] * block_elems + head_off + (int64_t)(((k0 + t) & bm1) * D + 8 * c);
+  const int t0 = kRpg * wave + grow;
+  const uint32_t ck = 16 * ((lane % kCpr) ^ swz_k(t0));  // byte offset in the row
+  const uint32_t cv = 16 * ((lane % kCpr) ^ swz_v(t0));
+  auto row_addr = [&](int slot, int j, bool is_v) -> uint64_t {
+    return sadr[slot][t0 + kRpg * kWaves * j][is_v] + (is_v ? cv : ck);
   };
   auto lds_group = [&](uint16_t *buf, int j) { return buf + 512 * (kWaves * j + wave); };
   // bfloat16: the loads write LDS themselves
-  auto dma_rows = [&](const KV *pool, uint16_t *buf, int k0, const uint32_t *ids, bool is_v) {
+  auto dma_rows = [&](uint16_t *buf, int slot, bool is_v) {
 #pragma unroll
     for (int j = 0; j < kGroups; ++j)
       __builtin_amdgcn_global_load_lds(
-          (const void *)(pool + src_off(k0, ids, j, is_v)),
+          (const void *)row_addr(slot, j, is_v),
           (__attribute__((address_space(3))) void *)lds_group(buf, j), 16, 0, 0);
   };
   // through registers: a bfloat16 V tile holding tokens past pos_last, whose
   // rows there are zeroed (p = 0 there, and 0 * NaN would not vanish; K rows
   // there only meet masked scores)
-  auto fetch_v_tail = [&](uint16_t *buf, int k0, const uint32_t *ids) {
+  auto fetch_v_tail = [&](uint16_t *buf, int k0, int slot) {
     u32x4 R[kGroups];
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
-      const u32x4 x = *reinterpret_cast<const u32x4 *>(vc + src_off(k0, ids, j, true));
-      R[j] = k0 + kRpg * (kWaves * j + wave) + grow <= pos_last ? x : u32x4{0, 0, 0, 0};
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(row_addr(slot, j, true));
+      R[j] = k0 + t0 + kRpg * kWaves * j <= pos_last ? x : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < kGroups; ++j)
@@ -294,19 +308,22 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   constexpr int kQGroups = D / 64;  // code groups per wave and tile
   constexpr int kQRows = 1024 / D;  // rows per code group
   constexpr int kQcpr = D / 16;     // 16-code chunks per row
-  auto dma_codes = [&](const KV *pool, uint16_t *buf, int k0, const uint32_t *ids) {
+  auto dma_codes = [&](uint16_t *buf, int slot, bool is_v) {
 #pragma unroll
     for (int j = 0; j < kQGroups; ++j) {
       const int g = kWaves * j + wave;
       const int t = kQRows * g + lane / kQcpr;
-      const int64_t off = (int64_t)ids[t] * block_elems + head_off +
-                          (int64_t)(((k0 + t) & bm1) * D + 16 * (lane % kQcpr));
       __builtin_amdgcn_global_load_lds(
-          (const void *)(pool + off), (__attribute__((address_space(3))) void *)(buf + 1024 * g),
-          16, 0, 0);
+          (const void *)(sadr[slot][t][is_v] + 16 * (lane % kQcpr)),
+          (__attribute__((address_space(3))) void *)(buf + 1024 * g), 16, 0, 0);
     }
   };
   auto expand_codes = [&](uint16_t *buf, int k0, bool is_v) {
+    // this wave's direct loads of the codes must have landed.  Placed by
+    // hand: the compiler's own wait is missing on the path where the K
+    // tile's expansion before this one is skipped, and codes that land after
+    // the rewrite would leave raw bytes among the bfloat16 rows.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
     for (int j = 0; j < kQGroups; ++j) {
       const int g = kWaves * j + wave;
@@ -364,34 +381,35 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
 
   // bfloat16 V tile at k0 into buf: directly, or through registers when it
   // runs past pos_last (at most the last tile)
-  auto fetch_v = [&](uint16_t *buf, int k0, const uint32_t *ids) {
+  auto fetch_v = [&](uint16_t *buf, int k0, int slot) {
     if (k0 + kTk - 1 <= pos_last)
-      dma_rows(vc, buf, k0, ids, true);
+      dma_rows(buf, slot, true);
     else
-      fetch_v_tail(buf, k0, ids);
+      fetch_v_tail(buf, k0, slot);
   };
 
   // Prologue: block ids of tiles 0..2, K and V of tile 0, K of tile 1, and
   // the scores of tile 0.
   uint32_t id_next = 0;
   if (threadIdx.x < kTk) {
-    sbid[0][threadIdx.x] = table_entry(k_begin);
-    sbid[1][threadIdx.x] = ntiles > 1 ? table_entry(k_begin + kTk) : 0u;
+    put_addrs(0, k_begin, table_entry(k_begin));
+    put_addrs(1, k_begin + kTk, ntiles > 1 ? table_entry(k_begin + kTk) : 0u);
   }
   __syncthreads();
   if constexpr (Q8 == 0) {
-    dma_rows(kc, sk0, k_begin, sbid[0], false);
-    if (ntiles > 1) dma_rows(kc, sk1, k_begin + kTk, sbid[1], false);
-    fetch_v(sv0, k_begin, sbid[0]);
+    dma_rows(sk0, 0, false);
+    if (ntiles > 1) dma_rows(sk1, 1, false);
+    fetch_v(sv0, k_begin, 0);
   } else {
-    dma_codes(kc, sk0, k_begin, sbid[0]);
-    if (ntiles > 1) dma_codes(kc, sk1, k_begin + kTk, sbid[1]);
-    dma_codes(vc, sv0, k_begin, sbid[0]);
+    dma_codes(sk0, 0, false);
+    if (ntiles > 1) dma_codes(sk1, 1, false);
+    dma_codes(sv0, 0, true);
     expand_codes(sk0, k_begin, false);
     if (ntiles > 1) expand_codes(sk1, k_begin + kTk, false);
     expand_codes(sv0, k_begin, true);
   }
-  if (threadIdx.x < kTk) sbid[2][threadIdx.x] = ntiles > 2 ? table_entry(k_begin + 2 * kTk) : 0u;
+  if (threadIdx.x < kTk)
+    put_addrs(2, k_begin + 2 * kTk, ntiles > 2 ? table_entry(k_begin + 2 * kTk) : 0u);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads are in LDS
   __syncthreads();
   if (threadIdx.x < kTk && ntiles > 3) id_next = table_entry(k_begin + 3 * kTk);
@@ -415,11 +433,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     // V(it + 1) into the one V(it - 1) left: they land during this
     // iteration (8-bit codes are widened at its end).
     if constexpr (Q8 == 0) {
-      if (it + 2 < ntiles) dma_rows(kc, sk_this, k0 + 2 * kTk, sbid[slot2], false);
-      if (it + 1 < ntiles) fetch_v(sv_next, k0 + kTk, sbid[slot1]);
+      if (it + 2 < ntiles) dma_rows(sk_this, slot2, false);
+      if (it + 1 < ntiles) fetch_v(sv_next, k0 + kTk, slot1);
     } else {
-      if (it + 2 < ntiles) dma_codes(kc, sk_this, k0 + 2 * kTk, sbid[slot2]);
-      if (it + 1 < ntiles) dma_codes(vc, sv_next, k0 + kTk, sbid[slot1]);
+      if (it + 2 < ntiles) dma_codes(sk_this, slot2, false);
+      if (it + 1 < ntiles) dma_codes(sv_next, slot1, true);
     }
 
     // Online softmax of tile it.  The running maximum m is kept on the raw
@@ -528,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     }
     // the ids of tile it + 3 into the slot of tile it (last read when V(it)
     // was fetched)
-    if (threadIdx.x < kTk && it + 3 < ntiles) sbid[slot][threadIdx.x] = id_next;
+    if (threadIdx.x < kTk && it + 3 < ntiles) put_addrs(slot, k0 + 3 * kTk, id_next);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads are in LDS
     __syncthreads();
     if (threadIdx.x < kTk && it + 4 < ntiles) id_next = table_entry(k0 + 4 * kTk);
