@@ -905,8 +905,11 @@ def main() -> int:
             "shared_tokens": int(shared_np.sum()),
             "dispatch": "device sort" if dispatch_np is None else "planned on the host",
             "step": ("copy_blocks + kv_cache_write + " if has_step else "") +
-                    ("paged_attention_decode_prefix (shared prefixes read once per group, "
-                     "dispatch list planned on the host; + merge)" if use_prefix else
+                    ("paged_attention_decode_prefix (" +
+                     ("shared prefixes read once per group, " if len(groups_np) else
+                      "no shared prefixes found, ") +
+                     ("dispatch list planned on the host; " if dispatch_np is not None else
+                      "dispatch sorted on the device; ") + "+ merge)" if use_prefix else
                      "paged_attention_decode (+ split-K merge)"),
         },
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
