@@ -4,9 +4,10 @@ verification) through the C ABI against the oracle (needs an MI355X).
 Every output element at sizes the oracle finishes in seconds (chunks from 0
 tokens to whole prompts, tiles of 64 tokens with ragged tails, every block
 size, G from 1 to 8, both row-tile widths), and every output element of the
-two full-size workloads.  Also bitwise determinism, invariance under relabelling
-physical blocks, rows outside every chunk left untouched, and NaN-poisoned
-unused slots never reaching the output."""
+two full-size workloads, within the 2e-3 tolerance and the 1e-4 regression
+bound.  Also bitwise determinism, invariance under relabelling physical
+blocks, rows outside every chunk left untouched, and NaN-poisoned unused slots
+never reaching the output."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +16,7 @@ from oracle import oracle as O
 from workloads import make_multi_query_case, make_multi_query_workload, make_private_case
 from workloads.generate import permute_pool, subset_sequences, make_multi_query_case as mqc
 
-from gpu_helpers import TOL, max_err, say, to_torch
+from gpu_helpers import REGRESS, TOL, max_err, say, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -73,7 +74,7 @@ def compare(c, name, ps=0):
     got = run_gpu(c, ps=ps)
     ref = oracle(c)
     err = max_err(got, ref)
-    assert err <= TOL["bf16"], f"{name}: max abs err {err}"
+    assert err <= TOL["bf16"] and err <= REGRESS["bf16"], f"{name}: max abs err {err}"
     return got, ref
 
 
@@ -154,7 +155,7 @@ def test_full_size_workloads(name):
     assert np.isfinite(got).all()
     err = max_err(got, oracle(c))
     say(f"{name} full size: all {got.size} outputs, max abs err {err:.3e}")
-    assert err <= TOL["bf16"], f"{name}: max abs err {err}"
+    assert err <= TOL["bf16"] and err <= REGRESS["bf16"], f"{name}: max abs err {err}"
 
 
 @pytest.mark.parametrize("G,Hkv,maxq", [(4, 8, 4), (8, 4, 2), (1, 8, 16), (2, 4, 8),
