@@ -223,11 +223,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   // per 16 lanes) meet every bank once.  A tile is filled in 1 KB groups:
   // group j of wave w is bytes [1024 (4 j + w), +1024), lane l writing its
   // 16 bytes at 16 l -- the layout of gfx950's direct global -> LDS loads,
-  // which bfloat16 pools use (8-bit codes arrive the same way and are widened
-  // in LDS, see below).  K runs one tile ahead of V (the scores of tile t + 1 are
-  // computed while tile t's probabilities are formed); in iteration t the
-  // waves read K(t + 1) and V(t) while K(t + 2) and V(t + 1) arrive in the
-  // other two buffers.
+  // which bfloat16 pools use (8-bit codes arrive the same way and are
+  // widened in LDS, see below).  K runs one tile ahead of V (the scores of
+  // tile t + 1 are computed while tile t's probabilities are formed); in
+  // iteration t the waves read K(t + 1) and V(t) while K(t + 2) and V(t + 1)
+  // arrive in the other two buffers.
   constexpr int kCpr = D / 8;            // 16-byte chunks per row
   constexpr int kRpb = 16 / kCpr;        // rows per 256 bytes (all 64 banks)
   constexpr int kRpg = 512 / D;          // rows per 1 KB group
@@ -290,7 +290,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     u32x4 R[kGroups];
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
-      const u32x4 x = *reinterpret_cast<const u32x4 *>(row_addr(slot, j, true));
+      const u32x4 x =
+          *reinterpret_cast<const __attribute__((address_space(1))) u32x4 *>(row_addr(slot, j, true));
       R[j] = k0 + t0 + kRpg * kWaves * j <= pos_last ? x : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
