@@ -584,19 +584,25 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   }
 }
 
-// Merge of the partition partials of one (query token, head) row, D threads:
-// workgroup (s, i, h) takes head h of token i of sequence s's chunk, and,
-// when the sequence was split, combines the partitions the token's position
-// reaches (log-sum-exp weights, ascending partition order).  Rows of
-// sequences that fit in one partition were written to out directly.
+// Merge of the partition partials of the (query token, head) rows, one wave
+// per row, kMqMergeRows rows per workgroup: row (s, i, h) is head h of token
+// i of sequence s's chunk, and, when the sequence was split, combines the
+// partitions the token's position reaches (log-sum-exp weights, ascending
+// partition order).  Rows of sequences that fit in one partition were
+// written to out directly.
+constexpr int kMqMergeRows = 4;
 template <int D>
-__global__ __launch_bounds__(D) void paged_multi_query_merge_kernel(
+__global__ __launch_bounds__(64 * kMqMergeRows) void paged_multi_query_merge_kernel(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
-    int num_tokens, int hq, int cap, int max_q, int ps, int P) {
-  const int h = blockIdx.x % hq;
-  const int i = (blockIdx.x / hq) % max_q;
-  const int s = blockIdx.x / (hq * max_q);
+    int num_tokens, int hq, int cap, int max_q, int ps, int P, int64_t rows) {
+  constexpr int EPL = D / 64;  // elements per lane
+  const int64_t rr =
+      (int64_t)blockIdx.x * kMqMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (rr >= rows) return;
+  const int h = (int)(rr % hq);
+  const int i = (int)((rr / hq) % max_q);
+  const int s = (int)(rr / ((int64_t)hq * max_q));
   int L = context_lens[s];
   L = max(0, min(L, cap));
   if (min((L + ps - 1) / ps, P) <= 1) return;  // written to out directly
@@ -608,35 +614,40 @@ __global__ __launch_bounds__(D) void paged_multi_query_merge_kernel(
   const int np = min(pos / ps + 1, P);
   const int64_t row = (int64_t)(qs + i) * hq + h;
   const float *ml = ws_ml + row * P * 2;
-  const float *o = ws_o + row * P * D;
+  const float *o = ws_o + row * P * D + (threadIdx.x & 63) * EPL;
   float M = ml[0];
   for (int j = 1; j < np; ++j) M = fmaxf(M, ml[2 * j]);
-  const int d = threadIdx.x;
-  float num = 0.f, den = 0.f;
+  float num[EPL], den = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) num[e] = 0.f;
   for (int j = 0; j < np; ++j) {
     const float w = ml[2 * j] == neg_inf() ? 0.f
                                            : ml[2 * j + 1] * __builtin_amdgcn_exp2f(ml[2 * j] - M);
-    num = fmaf(w, o[(int64_t)j * D + d], num);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, o[(int64_t)j * D + e], num[e]);
     den += w;
   }
-  out[row * D + d] = den > 0.f ? num / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    out[row * D + (threadIdx.x & 63) * EPL + e] = den > 0.f ? num[e] / den : 0.f;
 }
 
 hipError_t launch_merge(const MultiQueryArgs &a, hipStream_t stream) {
-  const int64_t wgs = (int64_t)a.num_seqs * a.max_query_len * a.num_q_heads;
-  if (wgs <= 0) return hipSuccess;
+  const int64_t rows = (int64_t)a.num_seqs * a.max_query_len * a.num_q_heads;
+  if (rows <= 0) return hipSuccess;
   const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
                                          INT32_MAX);
+  const uint32_t grid = (uint32_t)((rows + kMqMergeRows - 1) / kMqMergeRows);
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((paged_multi_query_merge_kernel<64>), dim3((uint32_t)wgs), dim3(64), 0,
-                       stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out,
+    hipLaunchKernelGGL((paged_multi_query_merge_kernel<64>), dim3(grid), dim3(64 * kMqMergeRows),
+                       0, stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out,
                        a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
-                       a.num_partitions);
+                       a.num_partitions, rows);
   else
-    hipLaunchKernelGGL((paged_multi_query_merge_kernel<128>), dim3((uint32_t)wgs), dim3(128), 0,
-                       stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out,
+    hipLaunchKernelGGL((paged_multi_query_merge_kernel<128>), dim3(grid), dim3(64 * kMqMergeRows),
+                       0, stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out,
                        a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
-                       a.num_partitions);
+                       a.num_partitions, rows);
   return hipGetLastError();
 }
 
