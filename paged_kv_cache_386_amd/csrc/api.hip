@@ -461,6 +461,7 @@ int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *
   const int64_t n = (int64_t)num_seqs * P + 4 * (int64_t)ng;
   if (n >= (int64_t(1) << 31) || capacity < n) return PA_ERR_SHAPE;
   const int32_t G = num_q_heads / num_kv_heads;
+  const bool short_rule = ng > 0 && pa::short_members(kv_dtype);
   // the decode kernels' clamps and item bounds: tokens of item c, -1 when it
   // does no work
   auto L_of = [&](int32_t s) {
@@ -481,7 +482,9 @@ int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *
       const int32_t L = L_of(s);
       const int32_t nparts = std::min((int32_t)(((int64_t)L + ps - 1) / ps), P);
       const int32_t sh = shared_of(s, L);
-      if (p >= std::max(nparts, 1) || (sh > 0 && p < sh / ps)) {
+      // (a short member's prefix item reads its private tile too)
+      if (p >= std::max(nparts, 1) || (sh > 0 && p < sh / ps) ||
+          (short_rule && pa::prefix_short(L, sh))) {
         tokens = -1;
       } else {
         tokens = std::max<int64_t>(
@@ -494,10 +497,14 @@ int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *
       const int32_t count =
           std::min(std::max(prefix_groups[2 * gi + 1], 0), std::min(num_seqs - first, 64 / G));
       tokens = -1;
+      bool extra = false;  // a short member's private tile
       for (int32_t m = 16 * cset / G; m < std::min(count, (16 * cset + 15) / G + 1); ++m) {
-        const int32_t sh = shared_of(first + m, L_of(first + m));
+        const int32_t L = L_of(first + m);
+        const int32_t sh = shared_of(first + m, L);
         if (sh > 0) tokens = std::max<int64_t>(tokens, sh);
+        extra = extra || (short_rule && pa::prefix_short(L, sh) && L > sh);
       }
+      if (tokens > 0 && extra) tokens += 16;
     }
     keys[(size_t)c] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)(tokens + 1)) << 32) | (uint32_t)c;
   }

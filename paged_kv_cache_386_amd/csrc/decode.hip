@@ -463,7 +463,7 @@ template <int D>
 __global__ __launch_bounds__(64 * kMergeRows) void paged_decode_merge_kernel(
     const int32_t *__restrict__ context_lens, const float *__restrict__ ws_o,
     const float *__restrict__ ws_ml, float *__restrict__ out, int rows, int hq, int cap, int ps,
-    int P, const int32_t *__restrict__ shared_lens, int slots) {
+    int P, const int32_t *__restrict__ shared_lens, int slots, int short_rule) {
   constexpr int EPL = D / 64;  // elements per lane
   const int row = blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= rows) return;
@@ -473,7 +473,9 @@ __global__ __launch_bounds__(64 * kMergeRows) void paged_decode_merge_kernel(
   L = max(0, min(L, cap));  // the same clamp as the decode kernel
   const int n = min((L + ps - 1) / ps, P);
   const int sh = shared_lens ? min(max(shared_lens[s], 0), L) & ~15 : 0;
-  if (n <= 1 && sh == 0) return;  // written by the decode kernel directly
+  // written by the decode kernel directly: one partition and no shared
+  // prefix, or a short member of a prefix group (its prefix item wrote it)
+  if ((n <= 1 && sh == 0) || (short_rule && prefix_short(L, sh))) return;
   const int first = sh > 0 ? sh / ps : 0;  // first partition with private positions
   const float *ml = ws_ml + (int64_t)row * slots * 2;
   const float *o = ws_o + (int64_t)row * slots * D + lane * EPL;
@@ -559,12 +561,14 @@ hipError_t launch_partition_merge(const DecodeArgs &a, hipStream_t stream) {
     case 64:
       hipLaunchKernelGGL((paged_decode_merge_kernel<64>), dim3(grid), dim3(64 * kMergeRows), 0,
                          stream, a.context_lens, a.ws_o, a.ws_ml, a.out, (int)rows,
-                         a.num_q_heads, cap, a.partition_size, a.num_partitions, sh, slots);
+                         a.num_q_heads, cap, a.partition_size, a.num_partitions, sh, slots,
+                         (int)short_members(a.kv_dtype));
       break;
     case 128:
       hipLaunchKernelGGL((paged_decode_merge_kernel<128>), dim3(grid), dim3(64 * kMergeRows), 0,
                          stream, a.context_lens, a.ws_o, a.ws_ml, a.out, (int)rows,
-                         a.num_q_heads, cap, a.partition_size, a.num_partitions, sh, slots);
+                         a.num_q_heads, cap, a.partition_size, a.num_partitions, sh, slots,
+                         (int)short_members(a.kv_dtype));
       break;
     default: return hipErrorNotSupported;
   }
@@ -578,7 +582,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     const hipError_t e = launch_schedule(
         a.context_lens, a.order, a.num_seqs, a.num_partitions, a.partition_size,
         a.max_blocks_per_seq << a.log2_block_size, stream, pfx ? a.groups : nullptr,
-        pfx ? a.shared_lens : nullptr, pfx ? a.num_groups : 0, G);
+        pfx ? a.shared_lens : nullptr, pfx ? a.num_groups : 0, G,
+        pfx && short_members(a.kv_dtype));
     if (e != hipSuccess) return e;
   }
   if (a.kv_dtype == 2 || a.kv_dtype == 3 ||  // 8-bit pools: matrix-core kernel only

@@ -543,6 +543,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     if constexpr (PFX) {
       // positions below the shared length come from the group's prefix item
       sh = min(max(shared_lens[s], 0), L) & ~(kTile - 1);
+      if (Q8 != 0 && prefix_short(L, sh)) return;  // the prefix item reads it all
       if (p < sh / ps) return;  // the whole partition is shared: no partial
       t0 = max(t0, sh);
     }
@@ -744,6 +745,36 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     }
   }
 
+  if constexpr (PFX && Q8 != 0) {
+    // A prefix item also reads the private tile [sh, L) of each short member
+    // of its set (one tile each, the set's members dealt round-robin to the
+    // waves), with every other member's columns masked, so that those
+    // members' rows are complete here.
+    if (pitem) {
+      const int gi = (item - num_seqs * P) >> 2;
+      const int count = min(max(groups[2 * gi + 1], 0), min(num_seqs - pfirst, 64 / G));
+      const int mset = 16 / G;  // members per column set
+      for (int mm = wave; mm < mset; mm += kWaves) {
+        const int mem = (16 * pset) / G + mm;
+        if (mem >= count) break;
+        const int seq = pfirst + mem;
+        const int Lm = max(0, min(context_lens[seq], mb << lgB));
+        const int shm = min(max(shared_lens[seq], 0), Lm) & ~(kTile - 1);
+        if (!prefix_short(Lm, shm) || Lm == shm) continue;
+        const int32_t *tbm = block_tables + (int64_t)seq * mb;
+        const int ent = SMALLB ? 0 : tbm[shm >> lgB];
+        int cpos_m[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) cpos_m[c] = (pcol && pmember == mem) ? Lm - 1 : -1;
+        TileT A;
+        K::template load<true>(A, kc, vc, tbm, ent, true, shm, Lm, lgB, nb, g, n, row_elems,
+                               head_off, block_elems);
+        K::template compute<true, NC>(A, qb, acc, m, lsum, p0, slot, slice, shm, Lm, g, n, sl2,
+                                       cpos_m);
+      }
+    }
+  }
+
   K::template flush<NC>(p0, slot, slice, acc, g, n);
 
   // This wave's results per column, one column set at a time: the maximum m
@@ -792,6 +823,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
       }
       int64_t row;
       int slot_of = p;
+      bool to_out = final_out;
       if constexpr (MQ) {
         if (h >= ncols[c]) continue;
         const int R = G * (NC * cgroup + c) + h;
@@ -802,13 +834,18 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
           // last slot
           if (h >= ncols[0]) continue;
           const int R = 16 * pset + h;
-          row = (int64_t)(pfirst + R / G) * hq + kvh * G + R % G;
+          const int seq = pfirst + R / G;
+          row = (int64_t)seq * hq + kvh * G + R % G;
           slot_of = slots - 1;
+          // a short member's row is complete: straight to out
+          const int Lm = max(0, min(context_lens[seq], mb << lgB));
+          to_out = Q8 != 0 &&
+                   prefix_short(Lm, min(max(shared_lens[seq], 0), Lm) & ~(kTile - 1));
         } else {
           row = (int64_t)s * hq + kvh * G + h;
         }
       }
-      if (final_out) {
+      if (to_out) {
         out[row * kD + d] = ls > 0.f ? v_scale * (o / ls) : 0.f;
       } else {
         const int64_t at = row * slots + slot_of;

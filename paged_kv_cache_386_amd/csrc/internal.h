@@ -40,6 +40,17 @@ struct DecodeArgs {
   int32_t num_groups = 0;
 };
 
+// Over 8-bit pools, a member of a prefix group whose private positions
+// [sh, L) fit in one 16-token tile ("short"): the group's prefix item reads
+// that tile too and writes the member's rows to out, so the member has no
+// sequence items and no merge (measured on the GQA prefix batch: FP8
+// 90.7 -> 87.1 us per call; over bf16 pools the longer prefix items cost
+// more than they save, 167.5 -> 168.5 us, so bf16 keeps separate items).
+// sh is the shared length as the kernels take it (clamped to [0, L],
+// rounded down to 16 tokens).
+__host__ __device__ inline bool prefix_short(int L, int sh) { return sh > 0 && L - sh <= 16; }
+__host__ __device__ inline bool short_members(int kv_dtype) { return kv_dtype == 2 || kv_dtype == 3; }
+
 // Launches with more workgroups than this run their longest items first (a
 // smaller grid is resident at once, so its order does not matter).
 constexpr int64_t kScheduleMinWorkgroups = 1024;
@@ -52,7 +63,7 @@ bool schedule_wanted(int64_t workgroups, int64_t num_seqs, int64_t P);
 hipError_t launch_schedule(const int32_t *context_lens, int32_t *order, int num_seqs, int P,
                            int ps, int cap, hipStream_t stream,
                            const int32_t *groups = nullptr, const int32_t *shared_lens = nullptr,
-                           int num_groups = 0, int group = 1);
+                           int num_groups = 0, int group = 1, bool short_rule = false);
 
 // Enqueues decode (and the partition merge when P > 1).  Returns hipSuccess or
 // the launch error; hipErrorNotSupported when no kernel is compiled for the

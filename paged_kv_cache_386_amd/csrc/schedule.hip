@@ -53,7 +53,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
     const int32_t *__restrict__ context_lens, int32_t *__restrict__ order, int num_seqs, int P,
     int ps, int cap, int shift, const int32_t *__restrict__ groups,
-    const int32_t *__restrict__ shared_lens, int num_groups, int G) {
+    const int32_t *__restrict__ shared_lens, int num_groups, int G, int short_rule) {
   // class-major, so one thread reads a class's 16 wave counts as 4 vectors
   __shared__ __attribute__((aligned(16))) int start[kSizeClasses + 1][kSchedWaves];
   __shared__ int wave_total[kSchedWaves];
@@ -82,12 +82,15 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
       const int count = min(max(groups[2 * gi + 1], 0), min(num_seqs - first, 64 / G));
       const int m1 = min(count, (16 * cset + 15) / G + 1);
       int longest = 0;
+      bool extra = false;  // a short member's private tile
       for (int m = 16 * cset / G; m < m1; ++m) {
         const int L = max(0, min(context_lens[first + m], cap));
-        longest = max(longest, shared(first + m, L));
+        const int sh = shared(first + m, L);
+        longest = max(longest, sh);
+        extra = extra || (short_rule && prefix_short(L, sh) && L > sh);
       }
       if (longest == 0) return kSizeClasses;
-      tokens = longest;
+      tokens = longest + (extra ? 16 : 0);
     } else {
       const int s = c % num_seqs;
       const int p = (P - 1) - c / num_seqs;
@@ -95,6 +98,8 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
       const int nparts = min((L + ps - 1) / ps, P);
       if (p >= max(nparts, 1)) return kSizeClasses;
       const int sh = shared(s, L);
+      // a short member's prefix item reads its private tile too
+      if (short_rule && prefix_short(L, sh)) return kSizeClasses;
       if (p < sh / ps) return kSizeClasses;  // wholly inside the shared prefix
       // (zero tokens still runs: it writes the empty partial the merge reads)
       tokens = max(0, min(L, p * ps + ps) - max(p * ps, sh));
@@ -163,14 +168,15 @@ bool schedule_wanted(int64_t workgroups, int64_t num_seqs, int64_t P) {
 
 hipError_t launch_schedule(const int32_t *context_lens, int32_t *order, int num_seqs, int P,
                            int ps, int cap, hipStream_t stream, const int32_t *groups,
-                           const int32_t *shared_lens, int num_groups, int group) {
+                           const int32_t *shared_lens, int num_groups, int group,
+                           bool short_rule) {
   // one partition spans every clamped context: size the classes by the cap
   if (P <= 1) ps = cap;
   int shift = 0;
   while ((ps >> shift) >= kSizeClasses) ++shift;
   hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream,
                      context_lens, order, num_seqs, P, ps, cap, shift, groups, shared_lens,
-                     num_groups, group);
+                     num_groups, group, (int)short_rule);
   return hipGetLastError();
 }
 

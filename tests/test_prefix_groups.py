@@ -118,11 +118,14 @@ def test_small_prefix_cases(B):
 
 # ---------------------------------------------------------------- host plan
 
-def plan_items(case, g, sh, P, ps, G):
+def plan_items(case, g, sh, P, ps, G, short_rule):
     """Tokens each work item attends (None: no work), restated from the
     decode call's contract: sequence items attend their partition's
-    positions past the shared length; a prefix item (group, column set)
-    the longest shared length of the members with columns in its set."""
+    positions past the shared length; a prefix item (group, column set) the
+    longest shared length of the members with columns in its set.  Over
+    8-bit pools (short_rule) a short member, one whose private positions fit
+    in one 16-token tile, has no sequence items, and its prefix item attends
+    one more tile when that member has a private position."""
     S, B = case.num_seqs, case.block_size
     cap = case.max_blocks_per_seq * B
     L = np.minimum(np.maximum(case.context_lens.astype(np.int64), 0), cap)
@@ -133,7 +136,8 @@ def plan_items(case, g, sh, P, ps, G):
     for c in range(S * P):
         s, p = c % S, (P - 1) - c // S
         nparts = min(-(-int(L[s]) // ps), P)
-        if p >= max(nparts, 1) or (sh_eff[s] > 0 and p < sh_eff[s] // ps):
+        short = short_rule and sh_eff[s] > 0 and L[s] - sh_eff[s] <= 16
+        if p >= max(nparts, 1) or (sh_eff[s] > 0 and p < sh_eff[s] // ps) or short:
             tok.append(None)
         else:
             tok.append(max(0, min(int(L[s]), p * ps + ps) - max(p * ps, int(sh_eff[s]))))
@@ -141,26 +145,32 @@ def plan_items(case, g, sh, P, ps, G):
         for cset in range(4):
             ms = [m for m in range(count) if 16 * cset <= m * G + G - 1 and m * G < 16 * cset + 16]
             best = max([int(sh_eff[first + m]) for m in ms if sh_eff[first + m] > 0], default=None)
-            tok.append(best)
+            extra = short_rule and any(0 < sh_eff[first + m] < L[first + m] <= sh_eff[first + m] + 16
+                                       for m in ms)
+            tok.append(None if best is None else best + (16 if extra else 0))
     return tok
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 @pytest.mark.parametrize("cfg", [2, 4])
-def test_plan_is_longest_first_permutation(cfg):
+def test_plan_is_longest_first_permutation(cfg, kv):
     import paged_kv_cache_386_amd as pa
     c = make_case(cfg)
     Hq, Hkv, D, B = c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size
     g, sh = groups_of(c.block_tables, c.context_lens, B, G=Hq // Hkv, Hkv=Hkv)
+    dt = {"bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3, "int8": pa.PA_INT8}[kv]
+    short = [(int(L) - int(s) <= 16 and s > 0) for L, s in zip(c.context_lens, sh)]
+    assert any(short) and not all(short)  # both kinds of member occur
     for ps in (0, 512, -1):
         P = pa.num_partitions(c.num_seqs, Hkv, c.max_context_len, ps)
         psz = pa.partition_tokens(c.num_seqs, Hkv, c.max_context_len, ps)
         lst = pa.decode_plan(c.context_lens, g, sh, num_q_heads=Hq, num_kv_heads=Hkv,
                              head_dim=D, block_size=B, max_blocks_per_seq=c.max_blocks_per_seq,
-                             max_context_len=c.max_context_len, kv_dtype=pa.PA_BF16,
+                             max_context_len=c.max_context_len, kv_dtype=dt,
                              partition_size=ps)
         n = c.num_seqs * P + 4 * len(g)
         assert sorted(lst.tolist()) == list(range(n))
-        tok = plan_items(c, g, sh, P, psz, Hq // Hkv)
+        tok = plan_items(c, g, sh, P, psz, Hq // Hkv, short_rule=kv != "bf16")
         seq = [tok[i] for i in lst.tolist()]
         work = [t for t in seq if t is not None]
         assert work == sorted(work, reverse=True)
