@@ -501,7 +501,9 @@ int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping
  *                  are skipped; two tokens must not share a slot)
  *   k_cache,
  *   v_cache        device FP8 pool (layout above), modified in place
- * head_dim must be a multiple of 16; scales finite and > 0.
+ * head_dim must be a multiple of 16; scales finite and > 0; k and v aligned
+ * to four elements (16 bytes for PA_F32, 8 for PA_BF16; PA_ERR_SHAPE
+ * otherwise).
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_LAUNCH; PA_ERR_INDEX
  * with index checking on.
  */

@@ -529,9 +529,12 @@ int32_t write_q8(const void *k, const void *v, const int32_t *slot_mapping, int3
   if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
   if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
   if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_SHAPE;
-  if ((int64_t)num_kv_heads * head_dim / 16 > (int64_t)128 * 65535) return PA_ERR_SHAPE;
+  if ((int64_t)num_kv_heads * head_dim / 4 > (int64_t)128 * 65535) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  // the rows are read four elements per load
+  const uintptr_t quad = 4 * (uintptr_t)(src_dtype == PA_F32 ? 4 : 2);
+  if (((uintptr_t)k | (uintptr_t)v) % quad != 0) return PA_ERR_SHAPE;
   if (pa::index_check_on()) {
     const int32_t st = pa::check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * block_size,
                                        static_cast<hipStream_t>(stream));

@@ -35,7 +35,8 @@ constexpr int kCopyVecsPerThread = 4;
 
 // grid.x = token, grid.y = stripe of the token's rows (hkv heads of head_vecs
 // 16-byte vectors each, contiguous in the source).  Vector j belongs to head
-// j / head_vecs and lands in that head's slab of the slot's block.
+// j / head_vecs and lands in that head's slab of the slot's block.  The row is
+// loaded before the slot is read, so the two loads overlap.
 __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(
     const u32x4 *__restrict__ k, const u32x4 *__restrict__ v,
     const int32_t *__restrict__ slot_mapping, u32x4 *__restrict__ kc, u32x4 *__restrict__ vc,
@@ -44,6 +45,8 @@ __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(
   const int row_vecs = hkv * head_vecs;
   const int j = blockIdx.y * kWriteThreads + threadIdx.x;
   if (j >= row_vecs) return;
+  const u32x4 kx = k[i * row_vecs + j];
+  const u32x4 vx = v[i * row_vecs + j];
   const int32_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_slots) return;
   const int h = j / head_vecs;
@@ -51,8 +54,6 @@ __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_kernel(
   const int64_t blk = slot >> lgB;
   const int off = slot & ((1 << lgB) - 1);
   const int64_t dst = (((blk * hkv + h) << lgB) + off) * head_vecs + jj;
-  const u32x4 kx = k[i * row_vecs + j];
-  const u32x4 vx = v[i * row_vecs + j];
   kc[dst] = kx;
   vc[dst] = vx;
 }
@@ -104,41 +105,50 @@ __device__ __forceinline__ float widen<uint16_t>(uint16_t x) {
   return __uint_as_float((uint32_t)x << 16);
 }
 
-// grid.x = token, grid.y = stripe of the token's 16-element groups (hkv heads
-// of head_vecs groups each).  Group j of head h = j / head_vecs is divided by
-// the cache's scale, encoded, and stored as one 16-byte vector in that head's
-// slab of the slot's block.
+template <typename T>
+struct Quad;  // four source elements, one vector load
+template <>
+struct Quad<float> {
+  typedef float type __attribute__((ext_vector_type(4)));
+};
+template <>
+struct Quad<uint16_t> {
+  typedef uint16_t type __attribute__((ext_vector_type(4)));
+};
+
+// grid.x = token, grid.y = stripe of the token's 4-element words (hkv heads
+// of head_words words each).  Word j of head h = j / head_words: its four
+// elements are each divided by the cache's scale and encoded, and the four
+// codes are stored as one 32-bit word in that head's slab of the slot's
+// block.  Four elements per lane keep each lane's divide-and-encode chain
+// short; the row is loaded before the slot is read.
 template <typename T, int Q8>
 __global__ __launch_bounds__(kWriteThreads) void kv_cache_write_q8_kernel(
-    const T *__restrict__ k, const T *__restrict__ v, const int32_t *__restrict__ slot_mapping,
-    u32x4 *__restrict__ kc, u32x4 *__restrict__ vc, float k_scale, float v_scale,
-    int64_t num_slots, int lgB, int hkv, int head_vecs) {
+    const typename Quad<T>::type *__restrict__ k, const typename Quad<T>::type *__restrict__ v,
+    const int32_t *__restrict__ slot_mapping, uint32_t *__restrict__ kc,
+    uint32_t *__restrict__ vc, float k_scale, float v_scale, int64_t num_slots, int lgB, int hkv,
+    int head_words) {
   const int64_t i = blockIdx.x;
-  const int row_vecs = hkv * head_vecs;
+  const int row_words = hkv * head_words;
   const int j = blockIdx.y * kWriteThreads + threadIdx.x;
-  if (j >= row_vecs) return;
+  if (j >= row_words) return;
+  const typename Quad<T>::type kx = k[i * row_words + j];
+  const typename Quad<T>::type vx = v[i * row_words + j];
   const int32_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_slots) return;
-  const int h = j / head_vecs;
-  const int jj = j - h * head_vecs;
+  const int h = j / head_words;
+  const int jj = j - h * head_words;
   const int64_t blk = slot >> lgB;
   const int off = slot & ((1 << lgB) - 1);
-  const int64_t dst = (((blk * hkv + h) << lgB) + off) * head_vecs + jj;
-  const int64_t src = (i * row_vecs + j) * 16;  // elements
-  u32x4 ko, vo;
+  const int64_t dst = (((blk * hkv + h) << lgB) + off) * head_words + jj;
+  uint32_t kw = 0, vw = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t kw = 0, vw = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      kw |= encode8<Q8>(widen<T>(k[src + 4 * w + b]) / k_scale) << (8 * b);
-      vw |= encode8<Q8>(widen<T>(v[src + 4 * w + b]) / v_scale) << (8 * b);
-    }
-    ko[w] = kw;
-    vo[w] = vw;
+  for (int b = 0; b < 4; ++b) {
+    kw |= encode8<Q8>(widen<T>(kx[b]) / k_scale) << (8 * b);
+    vw |= encode8<Q8>(widen<T>(vx[b]) / v_scale) << (8 * b);
   }
-  kc[dst] = ko;
-  vc[dst] = vo;
+  kc[dst] = kw;
+  vc[dst] = vw;
 }
 
 // grid.x = pair, grid.y = stripe of kCopyThreads*kCopyVecsPerThread vectors of
@@ -189,15 +199,16 @@ namespace {
 template <typename T, int Q8>
 void launch_q8(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
                void *k_cache, void *v_cache, int64_t num_slots, int32_t log2_block_size,
-               int32_t num_kv_heads, int head_vecs, float k_scale, float v_scale,
+               int32_t num_kv_heads, int head_words, float k_scale, float v_scale,
                hipStream_t stream) {
-  const int64_t row_vecs = (int64_t)head_vecs * num_kv_heads;
-  const int64_t stripes = (row_vecs + kWriteThreads - 1) / kWriteThreads;
+  typedef typename Quad<T>::type Q;
+  const int64_t row_words = (int64_t)head_words * num_kv_heads;
+  const int64_t stripes = (row_words + kWriteThreads - 1) / kWriteThreads;
   hipLaunchKernelGGL((kv_cache_write_q8_kernel<T, Q8>),
                      dim3((uint32_t)num_tokens, (uint32_t)stripes), dim3(kWriteThreads), 0,
-                     stream, static_cast<const T *>(k), static_cast<const T *>(v), slot_mapping,
-                     static_cast<u32x4 *>(k_cache), static_cast<u32x4 *>(v_cache), k_scale,
-                     v_scale, num_slots, (int)log2_block_size, (int)num_kv_heads, head_vecs);
+                     stream, static_cast<const Q *>(k), static_cast<const Q *>(v), slot_mapping,
+                     static_cast<uint32_t *>(k_cache), static_cast<uint32_t *>(v_cache), k_scale,
+                     v_scale, num_slots, (int)log2_block_size, (int)num_kv_heads, head_words);
 }
 
 }  // namespace
@@ -209,7 +220,7 @@ hipError_t launch_kv_cache_write_q8(const void *k, const void *v, const int32_t 
                                     int32_t kv_dtype, float k_scale, float v_scale,
                                     hipStream_t stream) {
   if (num_tokens <= 0) return hipSuccess;
-  const int hv = head_dim / 16;
+  const int hv = head_dim / 4;  // 4-element words per head row
   if (src_dtype == 0) {
     if (kv_dtype == 2)
       launch_q8<float, 1>(k, v, slot_mapping, num_tokens, k_cache, v_cache, num_slots,

@@ -148,6 +148,13 @@ def test_cache_ops_reject_bad_arguments_on_host():
     assert lib.kv_cache_write(0, 0, 0, 0, 0, 0, 10, 16, 2, 128, 1, 0) == 0  # nothing to do
     assert lib.copy_blocks(1, 2, 1, 0, 10, 16, 2, 128, 1, None, 0) == -1
     assert lib.copy_blocks(1, 2, 1, 1, 10, 15, 2, 128, 1, None, 0) == -2
+    # 8-bit writes read source rows four elements per load: k and v must be
+    # aligned to 8 bytes (bf16 rows) or 16 bytes (fp32 rows)
+    for fn in (lib.kv_cache_write_fp8, lib.kv_cache_write_int8):
+        assert fn(0x1008, 0x2000, 1, 4, 1, 1, 10, 16, 2, 128, 0, 1.0, 1.0, 0) == -2  # f32
+        assert fn(0x1000, 0x2004, 1, 4, 1, 1, 10, 16, 2, 128, 1, 1.0, 1.0, 0) == -2  # bf16
+        assert fn(0, 0x2000, 1, 4, 1, 1, 10, 16, 2, 128, 1, 1.0, 1.0, 0) == -1
+        assert fn(0x1000, 0x2000, 1, 4, 1, 1, 10, 16, 2, 128, 1, 0.0, 1.0, 0) == -2  # scale
 
 
 def test_copy_alias_check_on_host():
