@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark: one paged-decode serving step on one MI355X.
 
-A step is the whole hot path over one batch: the copy-on-write block copies,
-the write of every sequence's new token into the pool, and paged decode
-attention (with its split-K merge).  The default workload is the GQA
+A step is the whole hot path over one batch: the copy-on-write block copies
+and the write of every sequence's new token into the pool (one
+kv_cache_append launch; --two-launch-edits: copy_blocks then kv_cache_write),
+and paged decode attention (with its split-K merge).  The default workload is the GQA
 prefix-sharing batch: 256 sequences, lognormal context lengths (median 1024,
 cap 8192), 32 query / 8 KV heads, head_dim 128, 16-token blocks, bf16, each
 group of 16 sequences sharing the physical blocks of a 1024-token prefix.
@@ -676,6 +677,9 @@ def main() -> int:
     ap.add_argument("--no-host-plan", action="store_true",
                     help="--serving: plain decode with the device sort instead of the "
                          "engine's host-planned prefix groups and dispatch list")
+    ap.add_argument("--two-launch-edits", action="store_true",
+                    help="the step's cache edits as copy_blocks then kv_cache_write (or "
+                         "kv_cache_write_fp8 / _int8) instead of one kv_cache_append launch")
     ap.add_argument("--device-sort", action="store_true",
                     help="sort the work on the device in every call instead of passing the "
                          "dispatch list planned on the host (paged_attention_decode_plan)")
@@ -811,6 +815,11 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def edits():
+        if not args.two_launch_edits:
+            pa.kv_cache_append(pairs, k_new, v_new, slots, kc, vc,
+                               k_scale=1.0 if c8 is None else float(c8.k_scale),
+                               v_scale=1.0 if c8 is None else float(c8.v_scale), stream=stream)
+            return
         pa.copy_blocks(pairs, kc, vc, stream=stream)
         if c8 is None:
             pa.kv_cache_write(k_new, v_new, slots, kc, vc, stream=stream)
@@ -904,7 +913,9 @@ def main() -> int:
             "prefix_groups": int(len(groups_np)),
             "shared_tokens": int(shared_np.sum()),
             "dispatch": "device sort" if dispatch_np is None else "planned on the host",
-            "step": ("copy_blocks + kv_cache_write + " if has_step else "") +
+            "step": (("copy_blocks + kv_cache_write + " if args.two_launch_edits else
+                      "kv_cache_append (copies + new-token writes, one launch) + ")
+                     if has_step else "") +
                     ("paged_attention_decode_prefix (" +
                      ("shared prefixes read once per group, " if len(groups_np) else
                       "no shared prefixes found, ") +

@@ -550,6 +550,42 @@ int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cac
                     const int32_t *host_pairs, void *stream);
 
 /*
+ * kv_cache_append -- a step's cache edits in one launch: copy_blocks of the
+ * pairs, then the write of the new tokens (kv_cache_write, or
+ * kv_cache_write_fp8 / _int8 for a quantising write), with exactly the
+ * pools those two calls in that order leave ([P3] section "关键设计二：
+ * Copy-on-Write": a forked sequence's shared last block is copied before it
+ * appends; [P1] sections 3.1 and 3.3: the new token's K/V goes into its
+ * slot).  Both run concurrently: a copy skips the positions that new tokens
+ * write in its source or destination block, and the workgroup of a token
+ * that writes into a copy's source block copies that position's old rows
+ * first (unless a token also writes that position of the destination).
+ *
+ *   src_dst_pairs  device int32 [num_pairs][2] (may be NULL when num_pairs is 0)
+ *   k, v           device, [num_tokens][num_kv_heads][head_dim], src_dtype
+ *   slot_mapping   device int32 [num_tokens]
+ *   k_cache,
+ *   v_cache        device pool of kv_dtype (layout above), modified in place
+ *   src_dtype      kv_dtype (rows stored bit for bit), or PA_F32 / PA_BF16
+ *                  with an 8-bit kv_dtype (quantised with k_scale, v_scale as
+ *                  in kv_cache_write_fp8 / _int8; the scales are ignored
+ *                  otherwise)
+ *   host_pairs     optional host copy of the pairs for the overlap check
+ * The preconditions are those of the two calls: every dst distinct and never
+ * a src (PA_ERR_ALIAS when host_pairs is given), no two tokens on one slot;
+ * pairs and slots outside the pool are skipped.  k and v aligned to 16 bytes
+ * (stored rows) or to four elements (quantised rows), else PA_ERR_SHAPE.
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_ALIAS,
+ * PA_ERR_LAUNCH; PA_ERR_INDEX with index checking on.
+ */
+int32_t kv_cache_append(const int32_t *src_dst_pairs, int32_t num_pairs, const void *k,
+                        const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+                        void *k_cache, void *v_cache, int32_t num_blocks, int32_t block_size,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
+                        int32_t kv_dtype, float k_scale, float v_scale,
+                        const int32_t *host_pairs, void *stream);
+
+/*
  * Index checking -- a debug mode, off by default.  It is on when the
  * environment variable PAGEDATTN_CHECK is "1" at the library's first call
  * that consults it, or after pagedattn_set_index_check(1) (0 turns it off).
@@ -564,6 +600,7 @@ int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cac
  *   kv_cache_write (_fp8, _int8) checks every slot < num_blocks*block_size
  *     (negative slots are padding);
  *   copy_blocks checks both ids of every pair in [0, num_blocks);
+ *   kv_cache_append makes both of those checks;
  *   paged_attention_decode_prefix also checks the groups and shared lengths
  *     (the rules stated there) and that a given dispatch list holds every
  *     item exactly once (lists of at most 65536 items).

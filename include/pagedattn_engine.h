@@ -47,9 +47,9 @@
  *     (pa_prefix_groups: forked samples share their prompt's blocks) and the
  *     longest-first dispatch list (paged_attention_decode_plan);
  *  4. one host-to-device copy of the step's index arrays, then on `stream`:
- *     kv_cache_write of the admitted prompts, copy_blocks of the
- *     copy-on-write pairs, kv_cache_write of the new tokens (the quantising
- *     writes for an 8-bit pool) and decode over the whole batch
+ *     kv_cache_write of the admitted prompts, one kv_cache_append of the
+ *     copy-on-write pairs and the new tokens (the quantising writes for an
+ *     8-bit pool) and decode over the whole batch
  *     (paged_attention_decode_prefix with the step's groups and list when
  *     host_plan is set, else paged_attention_decode; the FP8 / INT8 forms
  *     for an 8-bit pool);

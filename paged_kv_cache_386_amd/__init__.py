@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     copy_blocks,
     decode_plan,
     index_check,
+    kv_cache_append,
     kv_cache_write,
     kv_cache_write_fp8,
     kv_cache_write_int8,

@@ -76,6 +76,8 @@ SIGNATURES = {
     "paged_attention_partition_tokens": (_I32, [_I32] * 4),
     "kv_cache_write": (_I32, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
     "copy_blocks": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP]),
+    "kv_cache_append": (_I32, [_VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32,
+                               _I32, _I32, ctypes.c_float, ctypes.c_float, _VP, _VP]),
     "pagedattn_status_string": (ctypes.c_char_p, [_I32]),
     "pagedattn_set_index_check": (None, [_I32]),
     "pagedattn_index_check": (_I32, []),
@@ -545,6 +547,37 @@ def copy_blocks(src_dst_pairs, k_cache, v_cache, *, host_pairs=None, stream=None
                            _dtype_code(k_cache), hp, _stream(stream))
     del keep
     _check("copy_blocks", st)
+
+
+def kv_cache_append(src_dst_pairs, k, v, slot_mapping, k_cache, v_cache, *, k_scale: float = 1.0,
+                    v_scale: float = 1.0, host_pairs=None, stream=None) -> None:
+    """copy_blocks(src_dst_pairs) followed by the write of k[i], v[i] at slot
+    slot_mapping[i], in one launch.  With k and v of the pool's dtype the rows
+    are stored as they are (kv_cache_write); with float32 or bfloat16 rows and
+    an 8-bit pool they are quantised with k_scale and v_scale
+    (kv_cache_write_fp8 / _int8).  ``host_pairs`` turns on the host-side
+    overlap check of copy_blocks."""
+    NB, Hkv, B, D = k_cache.shape
+    P = src_dst_pairs.shape[0] if src_dst_pairs is not None and src_dst_pairs.dim() == 2 else 0
+    T = k.shape[0] if k is not None else 0
+    for t in (k, v, slot_mapping, k_cache, v_cache, src_dst_pairs):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    hp = None
+    keep = None
+    if host_pairs is not None:
+        import numpy as np
+        keep = np.ascontiguousarray(np.asarray(host_pairs), dtype=np.int32)
+        hp = keep.ctypes.data_as(ctypes.c_void_p)
+    kv = _dtype_code(k_cache)
+    src = _dtype_code(k) if k is not None else kv
+    st = lib().kv_cache_append(_ptr(src_dst_pairs) if P else None, P,
+                               _ptr(k) if T else None, _ptr(v) if T else None,
+                               _ptr(slot_mapping) if T else None, T, _ptr(k_cache),
+                               _ptr(v_cache), NB, B, Hkv, D, src, kv, float(k_scale),
+                               float(v_scale), hp, _stream(stream))
+    del keep
+    _check("kv_cache_append", st)
 
 
 # ---------------------------------------------------------------- block manager

@@ -670,6 +670,38 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
 
 }  // namespace
 
+namespace {
+
+// The copy_blocks precondition on host copies of the pairs: every dst
+// distinct and never a src, so the pairs commute and may run concurrently.
+// Ids outside the pool (and src == dst) are skipped by the kernels and
+// ignored here.  PA_OK, PA_ERR_ALIAS, or PA_ERR_SHAPE when the host is out
+// of memory.
+int32_t pairs_alias_status(const int32_t *host_pairs, int32_t num_pairs, int32_t num_blocks) {
+  bool *is_dst = new (std::nothrow) bool[(size_t)num_blocks]();
+  bool *is_src = new (std::nothrow) bool[(size_t)num_blocks]();
+  int32_t status = PA_OK;
+  if (!is_dst || !is_src) {
+    status = PA_ERR_SHAPE;
+  } else {
+    for (int32_t i = 0; i < num_pairs && status == PA_OK; ++i) {
+      const int32_t s = host_pairs[2 * i], d = host_pairs[2 * i + 1];
+      if (s >= 0 && s < num_blocks && d >= 0 && d < num_blocks && s != d) {
+        if (is_dst[d]) status = PA_ERR_ALIAS;
+        is_dst[d] = true;
+        is_src[s] = true;
+      }
+    }
+    for (int32_t b = 0; b < num_blocks && status == PA_OK; ++b)
+      if (is_dst[b] && is_src[b]) status = PA_ERR_ALIAS;
+  }
+  delete[] is_dst;
+  delete[] is_src;
+  return status;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t paged_attention_multi_query(const void *q, const void *k_cache, const void *v_cache,
@@ -760,28 +792,7 @@ int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cac
   if (num_pairs == 0) return PA_OK;
   if (!src_dst_pairs || !k_cache || !v_cache) return PA_ERR_NULL;
   if (host_pairs) {
-    // every dst distinct and never a src: then the pairs commute and may run
-    // concurrently.  Ids outside the pool are skipped by the kernel and
-    // ignored here.
-    bool *is_dst = new (std::nothrow) bool[(size_t)num_blocks]();
-    bool *is_src = new (std::nothrow) bool[(size_t)num_blocks]();
-    int32_t status = PA_OK;
-    if (!is_dst || !is_src) {
-      status = PA_ERR_SHAPE;
-    } else {
-      for (int32_t i = 0; i < num_pairs && status == PA_OK; ++i) {
-        const int32_t s = host_pairs[2 * i], d = host_pairs[2 * i + 1];
-        if (s >= 0 && s < num_blocks && d >= 0 && d < num_blocks && s != d) {
-          if (is_dst[d]) status = PA_ERR_ALIAS;
-          is_dst[d] = true;
-          is_src[s] = true;
-        }
-      }
-      for (int32_t b = 0; b < num_blocks && status == PA_OK; ++b)
-        if (is_dst[b] && is_src[b]) status = PA_ERR_ALIAS;
-    }
-    delete[] is_dst;
-    delete[] is_src;
+    const int32_t status = pairs_alias_status(host_pairs, num_pairs, num_blocks);
     if (status != PA_OK) return status;
   }
   if (pa::index_check_on()) {
@@ -793,6 +804,63 @@ int32_t copy_blocks(const int32_t *src_dst_pairs, int32_t num_pairs, void *k_cac
   const hipError_t e = pa::launch_copy_blocks(src_dst_pairs, num_pairs, k_cache, v_cache,
                                               num_blocks, block_bytes,
                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int32_t kv_cache_append(const int32_t *src_dst_pairs, int32_t num_pairs, const void *k,
+                        const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+                        void *k_cache, void *v_cache, int32_t num_blocks, int32_t block_size,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
+                        int32_t kv_dtype, float k_scale, float v_scale,
+                        const int32_t *host_pairs, void *stream) {
+  if (!known_pool_dtype(kv_dtype) || !known_pool_dtype(src_dtype)) return PA_ERR_DTYPE;
+  const bool quantise = kv_dtype != src_dtype;
+  // a quantising write takes fp32 or bfloat16 rows into an 8-bit pool
+  if (quantise && ((kv_dtype != PA_FP8_E4M3 && kv_dtype != PA_INT8) ||
+                   (src_dtype != PA_F32 && src_dtype != PA_BF16)))
+    return PA_ERR_DTYPE;
+  if (num_pairs < 0 || num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 ||
+      !head_row_ok(head_dim, kv_dtype))
+    return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
+  if ((int64_t)num_blocks * block_size >= (int64_t(1) << 31)) return PA_ERR_SHAPE;
+  if (quantise && !valid_scale(k_scale)) return PA_ERR_SHAPE;
+  if (quantise && !valid_scale(v_scale)) return PA_ERR_SHAPE;
+  const int64_t head_row_bytes = (int64_t)head_dim * elem_bytes(kv_dtype);
+  const int64_t block_bytes = head_row_bytes * num_kv_heads * block_size;
+  const int64_t per = 256 * 4 * 16;  // bytes a copy workgroup moves
+  if ((int64_t)num_pairs * 2 * ((block_bytes + per - 1) / per) + num_tokens >=
+      (int64_t(1) << 31))
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0 && num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || (num_pairs > 0 && !src_dst_pairs) ||
+      (num_tokens > 0 && (!k || !v || !slot_mapping)))
+    return PA_ERR_NULL;
+  // source rows are read 16 bytes (stored bytes) or four elements
+  // (quantised) per load
+  const uintptr_t align = quantise ? 4 * (uintptr_t)elem_bytes(src_dtype) : 16;
+  if (num_tokens > 0 && ((uintptr_t)k | (uintptr_t)v) % align != 0) return PA_ERR_SHAPE;
+  if (host_pairs && num_pairs > 0) {
+    const int32_t status = pairs_alias_status(host_pairs, num_pairs, num_blocks);
+    if (status != PA_OK) return status;
+  }
+  if (pa::index_check_on()) {
+    if (num_pairs > 0) {
+      const int32_t st = pa::check_pairs(src_dst_pairs, num_pairs, num_blocks,
+                                         static_cast<hipStream_t>(stream));
+      if (st != PA_OK) return st;
+    }
+    if (num_tokens > 0) {
+      const int32_t st = pa::check_slots(slot_mapping, num_tokens,
+                                         (int64_t)num_blocks * block_size,
+                                         static_cast<hipStream_t>(stream));
+      if (st != PA_OK) return st;
+    }
+  }
+  const hipError_t e = pa::launch_kv_cache_append(
+      src_dst_pairs, num_pairs, k, v, slot_mapping, num_tokens, k_cache, v_cache, num_blocks,
+      log2_exact(block_size), num_kv_heads, head_row_bytes, src_dtype, kv_dtype, k_scale,
+      v_scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -14,7 +14,9 @@
 //  * copy_blocks: whole physical blocks copied onto others, the copy-on-write
 //    step taken before a forked sequence appends to a shared block
 //    ("关键设计二：Copy-on-Write" section of the devpress.csdn.net/amd vLLM
-//    walkthrough).
+//    walkthrough);
+//  * kv_cache_append: a step's copies and its new tokens' writes in one
+//    launch, with the result of copy_blocks followed by the write.
 //
 // Both move raw bits with 16-byte vector loads and stores (NaN payloads and
 // signed zeros survive), and both skip indices outside the pool so a bad index
@@ -176,6 +178,160 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   }
 }
 
+// Both halves of a step's cache edits in one grid: workgroups [0, copy_wgs)
+// copy stripes of the pairs' blocks (grid role of copy_blocks_kernel: pair,
+// stripe, K or V), the rest write one new token each (its whole K and V
+// rows).  The outcome is that of every copy followed by every write:
+//  * a position of a copy's destination that a token writes is left to the
+//    token (the copy skips it);
+//  * a position of a copy's source that a token writes is copied by that
+//    token's workgroup, which reads the old row before it writes the new one
+//    (the copy skips it too), unless a token also writes that position of
+//    the destination;
+//  * every other position is copied by the copy workgroups and written by
+//    no token.
+// The skipped positions are found by scanning the slots (copy workgroups)
+// and the pairs (token workgroups); pairs with an id outside the pool or
+// src == dst are skipped here as in copy_blocks.  KIND 0 stores the source
+// rows' bytes (16-byte vectors), KIND 1 / 2 quantise T rows to FP8 / INT8
+// codes (four elements per 32-bit word, as kv_cache_write_q8_kernel).
+constexpr int kAppendThreads = 256;
+constexpr int kAppendVecsPerThread = 4;
+constexpr int kMaxSkipWords = 32;  // a skip bit per position of a block (B <= 1024)
+
+template <int KIND, typename T>
+__global__ __launch_bounds__(kAppendThreads) void kv_cache_append_kernel(
+    const int32_t *__restrict__ pairs, int num_pairs, int copy_wgs, int cstripes,
+    const void *__restrict__ k, const void *__restrict__ v,
+    const int32_t *__restrict__ slot_mapping, int num_tokens, u32x4 *__restrict__ kc,
+    u32x4 *__restrict__ vc, int32_t num_blocks, int lgB, int hkv, int hv, float k_scale,
+    float v_scale) {
+  const int tid = threadIdx.x;
+  const int B = 1 << lgB;
+  const int64_t num_slots = (int64_t)num_blocks << lgB;
+  const int bid = blockIdx.x;
+  if (bid < copy_wgs) {
+    __shared__ uint32_t skip[kMaxSkipWords];
+    const int i = bid / (2 * cstripes);
+    const int rem = bid - i * 2 * cstripes;
+    const int z = rem / cstripes, y = rem - z * cstripes;
+    const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+    if (tid < kMaxSkipWords) skip[tid] = 0u;
+    __syncthreads();
+    for (int t = tid; t < num_tokens; t += kAppendThreads) {
+      const int32_t slot = slot_mapping[t];
+      if (slot < 0 || slot >= num_slots) continue;
+      const int32_t b = slot >> lgB;
+      if (b == src || b == dst) {
+        const int q = slot & (B - 1);
+        atomicOr(&skip[q >> 5], 1u << (q & 31));
+      }
+    }
+    __syncthreads();
+    // the block: hkv << lgB rows of hv vectors, position q = row % B
+    const int64_t block_vecs = ((int64_t)hkv << lgB) * hv;
+    u32x4 *cache = z == 0 ? kc : vc;
+    const u32x4 *sp = cache + (int64_t)src * block_vecs;
+    u32x4 *dp = cache + (int64_t)dst * block_vecs;
+    const int64_t base = (int64_t)y * kAppendThreads * kAppendVecsPerThread + tid;
+    u32x4 tmp[kAppendVecsPerThread];
+    bool keep[kAppendVecsPerThread];
+#pragma unroll
+    for (int u = 0; u < kAppendVecsPerThread; ++u) {
+      const int64_t j = base + (int64_t)u * kAppendThreads;
+      keep[u] = false;
+      if (j < block_vecs) {
+        const int q = (int)((j / hv) & (B - 1));
+        keep[u] = !((skip[q >> 5] >> (q & 31)) & 1u);
+      }
+      if (keep[u]) tmp[u] = sp[j];
+    }
+#pragma unroll
+    for (int u = 0; u < kAppendVecsPerThread; ++u)
+      if (keep[u]) dp[base + (int64_t)u * kAppendThreads] = tmp[u];
+    return;
+  }
+
+  const int t = bid - copy_wgs;
+  const int32_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int32_t blk = slot >> lgB;
+  const int q = slot & (B - 1);
+  const int lane = tid & 63;
+  const int row_vecs = hkv * hv;  // 16-byte vectors of one position's rows
+  // a position's row of head h in block b, in 16-byte vectors
+  auto row_at = [&](int64_t b, int h) { return (((b * hkv + h) << lgB) + q) * hv; };
+
+  // 1. pairs whose source is this token's block: copy the old rows of
+  // position q to their destination first (each wave scans every pair, so
+  // the waves meet the same matches in the same order)
+  bool copied = false;
+  for (int p0 = 0; p0 < num_pairs; p0 += 64) {
+    const int p = p0 + lane;
+    int32_t src = -1, dst = -1;
+    if (p < num_pairs) {
+      src = pairs[2 * p];
+      dst = pairs[2 * p + 1];
+    }
+    const bool match = p < num_pairs && src == blk && dst >= 0 && dst < num_blocks && dst != src;
+    uint64_t m = __builtin_amdgcn_ballot_w64(match);
+    while (m) {
+      const int l = (int)__builtin_ctzll(m);
+      m &= m - 1;
+      const int32_t d = __builtin_amdgcn_readlane(dst, l);
+      // a token that writes position q of the destination wins over the copy
+      const int64_t dslot = ((int64_t)d << lgB) + q;
+      bool taken = false;
+      for (int t0 = 0; t0 < num_tokens && !taken; t0 += 64) {
+        const int tt = t0 + lane;
+        taken = __builtin_amdgcn_ballot_w64(tt < num_tokens && slot_mapping[tt] == dslot) != 0;
+      }
+      if (taken) continue;
+      copied = true;
+      for (int j = tid; j < row_vecs; j += kAppendThreads) {
+        const int h = j / hv, jj = j - h * hv;
+        kc[row_at(d, h) + jj] = kc[row_at(blk, h) + jj];
+        vc[row_at(d, h) + jj] = vc[row_at(blk, h) + jj];
+      }
+    }
+  }
+  // every old row is read before any thread overwrites it
+  if (copied) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+
+  // 2. the token's rows
+  if constexpr (KIND == 0) {
+    const u32x4 *ks = static_cast<const u32x4 *>(k) + (int64_t)t * row_vecs;
+    const u32x4 *vs = static_cast<const u32x4 *>(v) + (int64_t)t * row_vecs;
+    for (int j = tid; j < row_vecs; j += kAppendThreads) {
+      const int h = j / hv, jj = j - h * hv;
+      const u32x4 kx = ks[j], vx = vs[j];
+      kc[row_at(blk, h) + jj] = kx;
+      vc[row_at(blk, h) + jj] = vx;
+    }
+  } else {
+    typedef typename Quad<T>::type Q;
+    const int hw = 4 * hv;  // 32-bit code words per head row
+    const Q *ks = static_cast<const Q *>(k) + (int64_t)t * hkv * hw;
+    const Q *vs = static_cast<const Q *>(v) + (int64_t)t * hkv * hw;
+    uint32_t *kw32 = reinterpret_cast<uint32_t *>(kc);
+    uint32_t *vw32 = reinterpret_cast<uint32_t *>(vc);
+    for (int j = tid; j < hkv * hw; j += kAppendThreads) {
+      const int h = j / hw, jj = j - h * hw;
+      const Q kx = ks[j], vx = vs[j];
+      uint32_t kw = 0, vw = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        kw |= encode8<KIND>(widen<T>(kx[b]) / k_scale) << (8 * b);
+        vw |= encode8<KIND>(widen<T>(vx[b]) / v_scale) << (8 * b);
+      }
+      kw32[4 * row_at(blk, h) + jj] = kw;
+      vw32[4 * row_at(blk, h) + jj] = vw;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,
@@ -249,6 +405,39 @@ hipError_t launch_copy_blocks(const int32_t *pairs, int32_t num_pairs, void *k_c
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)num_pairs, (uint32_t)stripes, 2),
                      dim3(kCopyThreads), 0, stream, pairs, static_cast<u32x4 *>(k_cache),
                      static_cast<u32x4 *>(v_cache), num_blocks, block_vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_cache_append(const int32_t *pairs, int32_t num_pairs, const void *k,
+                                  const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+                                  void *k_cache, void *v_cache, int32_t num_blocks,
+                                  int32_t log2_block_size, int32_t num_kv_heads,
+                                  int64_t head_row_bytes, int32_t src_dtype, int32_t kv_dtype,
+                                  float k_scale, float v_scale, hipStream_t stream) {
+  const int hv = (int)(head_row_bytes / 16);
+  const int64_t block_vecs = ((int64_t)num_kv_heads << log2_block_size) * hv;
+  const int64_t per = (int64_t)kAppendThreads * kAppendVecsPerThread;
+  const int cstripes = (int)((block_vecs + per - 1) / per);
+  const int copy_wgs = num_pairs * 2 * cstripes;
+  const int64_t grid = (int64_t)copy_wgs + num_tokens;
+  if (grid <= 0) return hipSuccess;
+  u32x4 *kc = static_cast<u32x4 *>(k_cache), *vc = static_cast<u32x4 *>(v_cache);
+#define PA_APPEND(KIND, T)                                                                    \
+  hipLaunchKernelGGL((kv_cache_append_kernel<KIND, T>), dim3((uint32_t)grid),                 \
+                     dim3(kAppendThreads), 0, stream, pairs, num_pairs, copy_wgs, cstripes, k, \
+                     v, slot_mapping, num_tokens, kc, vc, num_blocks, (int)log2_block_size,    \
+                     (int)num_kv_heads, hv, k_scale, v_scale)
+  if (kv_dtype == src_dtype)
+    PA_APPEND(0, uint16_t);
+  else if (kv_dtype == 2 && src_dtype == 0)
+    PA_APPEND(1, float);
+  else if (kv_dtype == 2)
+    PA_APPEND(1, uint16_t);
+  else if (src_dtype == 0)
+    PA_APPEND(2, float);
+  else
+    PA_APPEND(2, uint16_t);
+#undef PA_APPEND
   return hipGetLastError();
 }
 

@@ -493,12 +493,12 @@ int32_t pa_engine_step(pa_engine *e, const void *q, const void *k_new, const voi
         rc = write(prompt_k, prompt_v, d_prompt, rows_used);
         if (rc != PA_OK) return rc;
       }
-      if (np) {
-        rc = copy_blocks(d_pairs, np, e->k_cache, e->v_cache, c.num_blocks, B, c.num_kv_heads,
-                         c.head_dim, c.dtype, pairs, stream);
-        if (rc != PA_OK) return rc;
-      }
-      rc = write(k_new, v_new, d_slots, n);
+      // the step's copies and its new tokens in one launch (after the prompt
+      // rows, which a copy may read)
+      rc = kv_cache_append(np ? d_pairs : nullptr, np, k_new, v_new, d_slots, n, e->k_cache,
+                           e->v_cache, c.num_blocks, B, c.num_kv_heads, c.head_dim,
+                           e->q8 ? PA_BF16 : c.dtype, c.dtype, c.k_scale, c.v_scale,
+                           np ? pairs : nullptr, stream);
       if (rc != PA_OK) return rc;
       if (c.host_plan) {
         rc = paged_attention_decode_prefix(

@@ -165,4 +165,13 @@ hipError_t launch_copy_blocks(const int32_t *pairs, int32_t num_pairs, void *k_c
                               void *v_cache, int32_t num_blocks, int64_t block_bytes,
                               hipStream_t stream);
 
+// copy_blocks then the write, in one launch (cache_ops.hip): stored bytes
+// when kv_dtype == src_dtype, else a quantising write into an 8-bit pool.
+hipError_t launch_kv_cache_append(const int32_t *pairs, int32_t num_pairs, const void *k,
+                                  const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+                                  void *k_cache, void *v_cache, int32_t num_blocks,
+                                  int32_t log2_block_size, int32_t num_kv_heads,
+                                  int64_t head_row_bytes, int32_t src_dtype, int32_t kv_dtype,
+                                  float k_scale, float v_scale, hipStream_t stream);
+
 }  // namespace pa

@@ -155,6 +155,26 @@ def test_cache_ops_reject_bad_arguments_on_host():
         assert fn(0x1000, 0x2004, 1, 4, 1, 1, 10, 16, 2, 128, 1, 1.0, 1.0, 0) == -2  # bf16
         assert fn(0, 0x2000, 1, 4, 1, 1, 10, 16, 2, 128, 1, 1.0, 1.0, 0) == -1
         assert fn(0x1000, 0x2000, 1, 4, 1, 1, 10, 16, 2, 128, 1, 0.0, 1.0, 0) == -2  # scale
+    # kv_cache_append: pairs, k, v, slots, T, pools, NB, B, Hkv, D, src, kv, scales, host, stream
+    app = lib.kv_cache_append
+    assert app(0, 0, 0, 0, 0, 0, 1, 1, 10, 16, 2, 128, 1, 1, 1.0, 1.0, None, 0) == 0  # no work
+    assert app(0, 0, 0, 0, 0, 0, 1, 1, 10, 16, 2, 128, 3, 2, 1.0, 1.0, None, 0) == -3  # int8->fp8
+    assert app(0, 0, 0, 0, 0, 0, 1, 1, 10, 16, 2, 128, 0, 1, 1.0, 1.0, None, 0) == -3  # f32->bf16
+    assert app(0, 0, 0, 0, 0, 0, 1, 1, 10, 15, 2, 128, 1, 1, 1.0, 1.0, None, 0) == -2  # B
+    assert app(0, 0, 0, 0, 0, 0, 1, 1, 10, 16, 2, 100, 1, 1, 1.0, 1.0, None, 0) == -2  # D
+    assert app(0, 0, 0, 0, 0, 0, 1, 1, 10, 16, 2, 128, 1, 2, 0.0, 1.0, None, 0) == -2  # scale
+    assert app(0, 1, 0, 0, 0, 0, 1, 1, 10, 16, 2, 128, 1, 1, 1.0, 1.0, None, 0) == -1  # pairs
+    assert app(0, 0, 0x1000, 0x2000, 0, 3, 1, 1, 10, 16, 2, 128, 1, 1, 1.0, 1.0, None, 0) == -1
+    assert app(0, 0, 0x1008, 0x2000, 4, 3, 1, 1, 10, 16, 2, 128, 1, 1, 1.0, 1.0, None,
+               0) == -2  # stored rows: 16-byte aligned
+    assert app(0, 0, 0x1004, 0x2000, 4, 3, 1, 1, 10, 16, 2, 128, 1, 2, 1.0, 1.0, None,
+               0) == -2  # bf16 rows quantised: 8-byte aligned
+    hp = np.array([[1, 2], [3, 2]], np.int32)  # two copies onto block 2
+    assert app(8, 2, 0, 0, 0, 0, 1, 1, 10, 16, 2, 128, 1, 1, 1.0, 1.0, hp.ctypes.data,
+               0) == -6
+    hp = np.array([[1, 2], [2, 3]], np.int32)  # block 2 both a dst and a src
+    assert app(8, 2, 0, 0, 0, 0, 1, 1, 10, 16, 2, 128, 1, 1, 1.0, 1.0, hp.ctypes.data,
+               0) == -6
 
 
 def test_copy_alias_check_on_host():
