@@ -12,9 +12,11 @@ Inputs are seeded synthetic data resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is the step's unique HBM bytes (each distinct
 KV slot read once -- the least HBM must deliver -- plus q, out, tables,
-partials and the edits) per second of step time.  `roofline` prices the decode
-call (the dispatch sort of large launches, the decode kernel and the partition
-merge, timed with HIP events on the stream they run on) against the MI355X HBM
+partials and the edits) per second of step time (the timed steps run with no
+event between their launches).  `roofline` prices the decode call (the
+dispatch sort of large launches, the decode kernel and the partition merge;
+the mean of as many calls back to back, timed with HIP events on the stream
+they run on) against the MI355X HBM
 peak with the same unique algorithmic bytes: `frac` is the one "% of peak"
 figure of the line.  Beside it: `effective_gbps`, the same call priced with
 attended bytes (K and V once per sequence and KV head through its block
@@ -853,8 +855,9 @@ def main() -> int:
         decode()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # 1. the timed steps: nothing but the step's own launches between the two
+    # events (an event recorded between two kernels holds the queue for
+    # about 5 us on these GPUs, so per-call events would lengthen the step)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -863,15 +866,34 @@ def main() -> int:
     for i in range(args.steps):
         if has_step:
             edits()
-        ev[i][0].record(stream)
         decode()
-        ev[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(end) / args.steps
+    # 2. the decode call's mean duration: the same number of calls back to
+    # back between two events on the launch stream
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for i in range(args.steps):
+        decode()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dec_us = d0.elapsed_time(d1) * 1e3 / args.steps
+    # 3. the spread of single calls, each between its own pair of events
+    # (which adds the events' own time to every sample)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        if has_step:
+            edits()
+        ev[i][0].record(stream)
+        decode()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    dec_us = float(dec_ms.mean() * 1e3)
 
     dec_unique = decode_bytes(case, P, ps, unique=True)
     dec_attended = decode_bytes(case, P, ps, unique=False)
@@ -924,8 +946,11 @@ def main() -> int:
                      "paged_attention_decode (+ split-K merge)"),
         },
         "attended_kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        # mean decode-call time: `steps` calls back to back between two HIP
+        # events on the launch stream
         "decode_us": round(dec_us, 2),
-        # per-call spread of the same HIP-event timings
+        # spread of single calls, each between its own pair of events (their
+        # own time included, a few us per call)
         "decode_us_pct": {k: round(float(np.percentile(dec_ms, q)) * 1e3, 2)
                           for k, q in (("p10", 10), ("p50", 50), ("p90", 90))},
         "roofline": {
@@ -941,8 +966,8 @@ def main() -> int:
             "traffic": traffic,
             "frac_definition": ("unique algorithmic bytes per decode call (each distinct KV "
                                 "slot once, plus q, out, used table entries, lengths, split "
-                                "partials and the dispatch list) / mean decode-call time / "
-                                "8 TB/s"),
+                                "partials and the dispatch list) / mean decode-call time "
+                                "(calls back to back between two HIP events) / 8 TB/s"),
             "algorithmic_bytes_per_call": dec_unique,
             "attended_bytes_per_call": dec_attended,
             # a shared block counted once per sequence that reads it: above
