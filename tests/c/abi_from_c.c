@@ -81,6 +81,12 @@ int main(void) {
                                64, PA_BF16, 0, NULL, 0, NULL) == PA_ERR_UNSUPPORTED);
   CHECK(kv_cache_write_fp8(NULL, NULL, NULL, 1, NULL, NULL, 8, 16, 2, 128, PA_BF16, 0.f, 1.f,
                            NULL) == PA_ERR_SHAPE); /* a zero scale */
+  CHECK(kv_cache_append(NULL, 0, NULL, NULL, NULL, 0, NULL, NULL, 8, 16, 2, 128, PA_BF16, PA_BF16,
+                        1.f, 1.f, NULL, NULL) == PA_OK); /* nothing to do */
+  CHECK(kv_cache_append(NULL, 2, NULL, NULL, NULL, 0, NULL, NULL, 8, 16, 2, 128, PA_BF16, PA_BF16,
+                        1.f, 1.f, NULL, NULL) == PA_ERR_NULL);
+  CHECK(kv_cache_append(NULL, 0, NULL, NULL, NULL, 1, NULL, NULL, 8, 16, 2, 128, PA_INT8,
+                        PA_FP8_E4M3, 1.f, 1.f, NULL, NULL) == PA_ERR_DTYPE);
   CHECK(strncmp(pagedattn_version(), "libpagedattn", 12) == 0);
   /* the index-checking switch (a debug mode; no call here reaches a check) */
   pagedattn_set_index_check(1);

@@ -175,3 +175,32 @@ def test_write_and_copy_check_their_indices():
     assert torch.equal(dc.k_cache[1].view(torch.int16), before[0].view(torch.int16))
     assert np.array_equal(dc.k_cache[3].view(torch.int16).cpu().numpy(),
                           before[2].view(torch.int16).cpu().numpy())
+
+
+def test_append_checks_pairs_and_slots():
+    """kv_cache_append makes both checks: a bad pair or a bad slot returns
+    PA_ERR_INDEX with nothing launched; valid indices run."""
+    import paged_kv_cache_386_amd as pa
+    c, dc = _case()
+    NB, B = c.num_blocks, c.block_size
+    T = 3
+    k = torch.ones((T, c.num_kv_heads, c.head_dim), dtype=torch.bfloat16, device="cuda")
+    before = dc.k_cache.clone()
+    say("index check: kv_cache_append")
+    ok_slots = torch.tensor([-1, 1 * B + 2, 4 * B], dtype=torch.int32, device="cuda")
+    bad_slots = torch.tensor([-1, NB * B, 4 * B], dtype=torch.int32, device="cuda")
+    ok_pairs = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+    bad_pairs = torch.tensor([[0, 1], [NB, 2]], dtype=torch.int32, device="cuda")
+    _expect_index_error(lambda: pa.kv_cache_append(bad_pairs, k, k, ok_slots, dc.k_cache,
+                                                   dc.v_cache))
+    _expect_index_error(lambda: pa.kv_cache_append(ok_pairs, k, k, bad_slots, dc.k_cache,
+                                                   dc.v_cache))
+    torch.cuda.synchronize()
+    assert torch.equal(dc.k_cache.view(torch.int16), before.view(torch.int16))
+    pa.kv_cache_append(ok_pairs, k, k, ok_slots, dc.k_cache, dc.v_cache)
+    torch.cuda.synchronize()
+    # block 1 is block 0 except position 2, which holds the new token's ones
+    got = dc.k_cache[1].view(torch.int16).cpu().numpy()
+    want = before[0].view(torch.int16).cpu().numpy().copy()
+    want[:, 2] = np.int16(0x3F80)  # bfloat16 1.0
+    assert np.array_equal(got, want)
