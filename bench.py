@@ -530,6 +530,10 @@ def multi_query_bench(args) -> int:
     pa.lib()
     c = make_multi_query_workload(args.multi_query, poison=False)
     b = c.base
+    if args.multi_query == "spec-verify" and args.verify_tokens != 5:
+        from workloads import make_multi_query_case
+        c = make_multi_query_case(b, np.minimum(b.context_lens, args.verify_tokens), 7,
+                                  c.name, c.description)
     q = to_dev(c.q, dev)
     c8 = None
     if args.kv_fp8 or args.kv_int8:
@@ -547,12 +551,44 @@ def multi_query_bench(args) -> int:
     max_ctx = int(b.context_lens.max())
     P = pa.multi_query_partitions(b.num_seqs, b.num_q_heads, b.num_kv_heads, c.max_query_len,
                                   max_ctx, args.partition_size)
-    ws = torch.empty(max(pa.multi_query_workspace_size(
-        b.num_seqs, c.num_tokens, b.num_q_heads, b.num_kv_heads, b.head_dim, c.max_query_len,
-        max_ctx, args.partition_size), 1), dtype=torch.uint8, device=dev)
+    # shared prefixes (speculative verification: the groups' prompts): found
+    # by the host in the tables it built, at most 16 members per group
+    groups_np = np.zeros((0, 2), np.int32)
+    shared_np = np.zeros(b.num_seqs, np.int32)
+    if not args.no_prefix and args.multi_query == "spec-verify":
+        groups_np, shared_np = pa.prefix_groups(b.block_tables, b.context_lens, b.block_size,
+                                                b.num_q_heads, b.num_kv_heads, 16)
+        keep = []
+        for f, m in groups_np.tolist():
+            keep += [[s, min(16, f + m - s)] for s in range(f, f + m, 16)]
+        groups_np = np.array(keep, np.int32).reshape(-1, 2)
+    use_prefix = len(groups_np) > 0
+    # the library takes prefix items over bf16 pools with at most 8 (token,
+    # head) rows per sequence and KV head; otherwise the call is the plain one
+    prefix_items = (use_prefix and c8 is None and
+                    c.max_query_len * (b.num_q_heads // b.num_kv_heads) <= 8)
+    kv_code = (pa.PA_BF16 if c8 is None else pa.PA_FP8_E4M3 if args.kv_fp8 else pa.PA_INT8)
+    if use_prefix:
+        groups_d = torch.from_numpy(groups_np).to(dev)
+        shared_d = torch.from_numpy(shared_np).to(dev)
+        ws_bytes = pa.multi_query_prefix_workspace_size(
+            b.num_seqs, c.num_tokens, b.num_q_heads, b.num_kv_heads, b.head_dim,
+            c.max_query_len, max_ctx, args.partition_size, len(groups_np), kv_code)
+    else:
+        ws_bytes = pa.multi_query_workspace_size(
+            b.num_seqs, c.num_tokens, b.num_q_heads, b.num_kv_heads, b.head_dim,
+            c.max_query_len, max_ctx, args.partition_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def call():
-        if c8 is not None:
+        if use_prefix:
+            pa.paged_attention_multi_query_prefix(
+                q, kc, vc, tables, lens, qs, groups_d, shared_d, float(b.scale), out,
+                max_query_len=c.max_query_len, max_context_len=max_ctx,
+                k_scale=1.0 if c8 is None else float(c8.k_scale),
+                v_scale=1.0 if c8 is None else float(c8.v_scale),
+                partition_size=args.partition_size, workspace=ws, stream=stream)
+        elif c8 is not None:
             mq8 = (pa.paged_attention_multi_query_fp8 if args.kv_fp8 else
                    pa.paged_attention_multi_query_int8)
             mq8(
@@ -616,13 +652,24 @@ def multi_query_bench(args) -> int:
             "" if c8 is None else
             f"; K/V as random {'E4M3' if args.kv_fp8 else 'INT8'} codes, k_scale "
             f"{float(c8.k_scale)}, v_scale {float(c8.v_scale)}"),
-        "config": {"workload": f"{args.multi_query}: {MULTI_QUERY_NAMES[args.multi_query]}"
+        "config": {"workload": f"{args.multi_query}: " + MULTI_QUERY_NAMES[args.multi_query].replace(
+                       "5 tokens", f"{args.verify_tokens} tokens")
                                + ("" if c8 is None else
                                   " over an FP8 pool" if args.kv_fp8 else " over an INT8 pool"),
                    "num_seqs": b.num_seqs, "num_tokens": c.num_tokens,
                    "max_query_len": c.max_query_len, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": b.block_size,
-                   "total_context_tokens": int(b.context_lens.sum()), "num_partitions": P},
+                   "total_context_tokens": int(b.context_lens.sum()), "num_partitions": P,
+                   "prefix_groups": int(len(groups_np)),
+                   "call": ("paged_attention_multi_query_prefix (shared prefixes read once "
+                            "per group; + merge)" if prefix_items else
+                            "paged_attention_multi_query_prefix (the plain call, groups "
+                            "ignored: prefix items take bf16 pools with at most 8 rows per "
+                            "sequence and KV head)"
+                            if use_prefix else
+                            "paged_attention_multi_query" + ("" if c8 is None else
+                                                             "_fp8" if args.kv_fp8 else
+                                                             "_int8"))},
         "attended_pairs_per_s": round(attended * Hq / (us * 1e-6), 1),
         "query_tokens_per_s": round(c.num_tokens / (us * 1e-6), 1),
         "kernel_us": round(us, 2),
@@ -685,10 +732,13 @@ def main() -> int:
     ap.add_argument("--device-sort", action="store_true",
                     help="sort the work on the device in every call instead of passing the "
                          "dispatch list planned on the host (paged_attention_decode_plan)")
+    ap.add_argument("--verify-tokens", type=int, default=5,
+                    help="--multi-query spec-verify: tokens to verify per sequence")
     ap.add_argument("--no-prefix", action="store_true",
-                    help="plain paged_attention_decode even where sequences share prefixes "
-                         "(default: paged_attention_decode_prefix with the groups "
-                         "pa_prefix_groups finds in the host tables)")
+                    help="plain paged_attention_decode (or, with --multi-query spec-verify, "
+                         "paged_attention_multi_query) even where sequences share prefixes "
+                         "(default: the _prefix call with the groups pa_prefix_groups finds "
+                         "in the host tables)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()

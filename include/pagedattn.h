@@ -464,6 +464,64 @@ int32_t paged_attention_multi_query_int8(const void *q, const void *k_cache, con
                                          size_t workspace_bytes, void *stream);
 
 /*
+ * paged_attention_multi_query_prefix -- paged_attention_multi_query (or its
+ * FP8 / INT8 form, by kv_dtype) for a batch whose sequences share prefixes,
+ * reading each shared block once per group instead of once per sequence
+ * ([P1] section 5.2 prefix caching, section 5.4 speculative decoding: the
+ * draft tokens of sequences that share a prompt are verified against the
+ * same prefix blocks; [P3] "关键设计二：Copy-on-Write").  The result is that
+ * of the plain call on the same tables: the groups only change which reads
+ * are shared.
+ *
+ *   prefix_groups,
+ *   num_groups,
+ *   shared_lens    as in paged_attention_decode_prefix, with at most 16
+ *                  members per group (pa_prefix_groups with max_members 16)
+ *   kv_dtype       PA_BF16, PA_FP8_E4M3 or PA_INT8 (q bfloat16; k_scale and
+ *                  v_scale as in paged_attention_multi_query_fp8, ignored for
+ *                  PA_BF16); prefix items over bf16 pools only (over 8-bit
+ *                  pools the shared walk measured slower: the call is the
+ *                  plain FP8 / INT8 one)
+ *   workspace      at least paged_attention_multi_query_prefix_workspace_size
+ *                  (...) bytes
+ * Every other argument is paged_attention_multi_query's.  The prefix path
+ * serves bf16 pools with at most 8 (token, head) rows per sequence and KV
+ * head (max_query_len * G <= 8) at head_dim 128: items per (group, KV head)
+ * attend the group's shared positions for 16 of the members' (token, head)
+ * rows each, every row up to its own position and below its member's shared
+ * length, and each sequence's own items attend only the rest of its context;
+ * the merge then combines every row's prefix and private partials in
+ * ascending position order.  With more rows per member an item covers too
+ * few members for the shared walk to pay (each item walks the whole prefix):
+ * there, as with num_groups 0, the call is the plain one and the groups are
+ * ignored.
+ * Supported and errors: as paged_attention_multi_query (and its FP8 / INT8
+ * forms); PA_ERR_SHAPE for num_groups outside [0, num_seqs], PA_ERR_NULL for
+ * missing groups or shared lengths.  Groups and shared lengths that break the
+ * rules give unspecified numbers, every access staying in bounds; with index
+ * checking on they give PA_ERR_INDEX.
+ */
+int32_t paged_attention_multi_query_prefix(
+    const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start, const int32_t *prefix_groups,
+    int32_t num_groups, const int32_t *shared_lens, float scale, float k_scale, float v_scale,
+    float *out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_query_len, int32_t max_context_len, int32_t kv_dtype, int32_t partition_size,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes paged_attention_multi_query_prefix needs: with the prefix
+ * path, 4 * num_tokens * num_q_heads * (P + 1) * (head_dim + 2) for the
+ * partials (the last slot of each row the prefix's), plus the dispatch list
+ * (4 bytes per item: the num_seqs * P sequence items and the groups' items)
+ * for launches of more than 1024 workgroups; otherwise
+ * paged_attention_multi_query_workspace_size. */
+size_t paged_attention_multi_query_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t max_query_len, int32_t max_context_len, int32_t partition_size,
+    int32_t num_groups, int32_t kv_dtype);
+
+/*
  * kv_cache_write -- store each new token's K and V rows in the pool.
  *
  * For i in [0, num_tokens) with slot = slot_mapping[i] >= 0: copies
@@ -603,7 +661,9 @@ int32_t kv_cache_append(const int32_t *src_dst_pairs, int32_t num_pairs, const v
  *   kv_cache_append makes both of those checks;
  *   paged_attention_decode_prefix also checks the groups and shared lengths
  *     (the rules stated there) and that a given dispatch list holds every
- *     item exactly once (lists of at most 65536 items).
+ *     item exactly once (lists of at most 65536 items);
+ *   paged_attention_multi_query_prefix makes the multi-query checks and
+ *     checks the groups and shared lengths (at most 16 members).
  * A check runs one small kernel on the call's stream, synchronises that
  * stream and reads back one device word the library owns (one per device;
  * calls that overlap on one device race on it); on a bad index the call

@@ -59,6 +59,11 @@ SIGNATURES = {
                                                 _I32, _VP, ctypes.c_size_t, _VP]),
     "paged_attention_multi_query_partitions": (_I32, [_I32] * 6),
     "paged_attention_multi_query_workspace_size": (ctypes.c_size_t, [_I32] * 8),
+    "paged_attention_multi_query_prefix": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP,
+                                                  ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                                  _VP] + [_I32] * 12 + [_VP, ctypes.c_size_t,
+                                                                       _VP]),
+    "paged_attention_multi_query_prefix_workspace_size": (ctypes.c_size_t, [_I32] * 10),
     "paged_attention_decode_fp8": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float,
                                           ctypes.c_float, ctypes.c_float, _VP, _I32, _I32, _I32,
                                           _I32, _I32, _I32, _I32, _I32, _I32, _VP,
@@ -414,6 +419,54 @@ def paged_attention_multi_query_int8(q, k_cache, v_cache, block_tables, context_
     _multi_query_q8("paged_attention_multi_query_int8", torch.int8, q, k_cache, v_cache,
                     block_tables, context_lens, query_start, scale, k_scale, v_scale, out,
                     max_query_len, max_context_len, partition_size, workspace, stream)
+
+
+def multi_query_prefix_workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int,
+                                      num_kv_heads: int, head_dim: int, max_query_len: int,
+                                      max_context_len: int, partition_size: int,
+                                      num_groups: int, kv_dtype: int) -> int:
+    return int(lib().paged_attention_multi_query_prefix_workspace_size(
+        num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len,
+        max_context_len, partition_size, num_groups, kv_dtype))
+
+
+def paged_attention_multi_query_prefix(q, k_cache, v_cache, block_tables, context_lens,
+                                       query_start, groups, shared_lens, scale: float, out, *,
+                                       max_query_len: int, max_context_len: int,
+                                       k_scale: float = 1.0, v_scale: float = 1.0,
+                                       partition_size: int = 0, workspace=None,
+                                       stream=None) -> None:
+    """paged_attention_multi_query for a batch whose sequences share prefix
+    blocks (include/pagedattn.h): ``groups`` int32 [n, 2] (first sequence,
+    members) and ``shared_lens`` int32 [S] on the device, as pa_prefix_groups
+    gives them.  The pool's dtype picks bf16, FP8 or INT8; q is bfloat16."""
+    import torch
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q/k_cache/v_cache shapes disagree")
+    S = context_lens.shape[0]
+    if query_start.shape[0] != S + 1:
+        raise ValueError("query_start must have num_seqs + 1 entries")
+    MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    ng = int(groups.shape[0]) if groups is not None and groups.dim() == 2 else 0
+    for t in (q, k_cache, v_cache, block_tables, context_lens, query_start, out, groups,
+              shared_lens):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    kv = _dtype_code(k_cache)
+    need = multi_query_prefix_workspace_size(S, T, Hq, Hkv, D, max_query_len, max_context_len,
+                                             partition_size, ng, kv)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().paged_attention_multi_query_prefix(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start), _ptr(groups) if ng else None, ng,
+        _ptr(shared_lens) if ng else None, float(scale), float(k_scale), float(v_scale),
+        _ptr(out), S, T, Hq, Hkv, D, B, NB, MB, int(max_query_len), int(max_context_len), kv,
+        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("paged_attention_multi_query_prefix", st)
 
 
 def _multi_query_q8(fn, pool_dtype, q, k_cache, v_cache, block_tables, context_lens,

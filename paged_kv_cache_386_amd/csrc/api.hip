@@ -142,16 +142,41 @@ DecodeWorkspace decode_workspace(int64_t num_seqs, int64_t num_q_heads, int64_t 
 struct MultiQueryWorkspace {
   size_t partials, order;
 };
+// With num_groups > 0 (shared prefixes, decode walk only) every row has P + 1
+// partial slots (the last one the prefix's) and the list also holds the
+// groups' prefix items.
 MultiQueryWorkspace multi_query_workspace(int64_t num_seqs, int64_t num_tokens,
                                           int64_t num_q_heads, int64_t num_kv_heads,
-                                          int64_t head_dim, int64_t max_query_len, int64_t P) {
+                                          int64_t head_dim, int64_t max_query_len, int64_t P,
+                                          int64_t num_groups = 0) {
   MultiQueryWorkspace w;
-  w.partials =
-      P > 1 ? (size_t)(num_tokens * num_q_heads * P * (head_dim + 2)) * sizeof(float) : 0;
+  const int64_t slots = P + (num_groups > 0 ? 1 : 0);
+  w.partials = slots > 1
+                   ? (size_t)(num_tokens * num_q_heads * slots * (head_dim + 2)) * sizeof(float)
+                   : 0;
+  const int64_t ipg =
+      num_groups > 0 ? pa::mq_prefix_items_per_group(max_query_len, num_q_heads / num_kv_heads)
+                     : 0;
+  const int64_t items = num_seqs * P + ipg * num_groups;
   const int64_t wgs = pa::multi_query_workgroups(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                 max_query_len, P);
-  w.order = pa::schedule_wanted(wgs, num_seqs, P) ? (size_t)(num_seqs * P) * sizeof(int32_t) : 0;
+                                                 max_query_len, P) +
+                      ipg * num_groups * num_kv_heads;
+  w.order = pa::schedule_wanted(wgs, items, 1) ? (size_t)items * sizeof(int32_t) : 0;
   return w;
+}
+
+// Whether a multi-query call with shared prefixes takes the prefix path
+// (the decode walk over a bf16 pool, head_dim 128, at most kMqPrefixRows
+// (token, head) rows per sequence and KV head; else it is the plain
+// multi-query call).  Over 8-bit pools the prefix items measured slower
+// even at 2 tokens per sequence (FP8 100.9 -> 106.1 us, INT8 112.1 -> 116.0
+// on the speculative-verification structure): half the bytes per position
+// leave less for the shared walk to save.
+bool mq_prefix_path(int32_t kv_dtype, int32_t head_dim, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t max_query_len, int32_t num_groups) {
+  return num_groups > 0 && kv_dtype == PA_BF16 && head_dim == 128 && num_kv_heads > 0 &&
+         num_q_heads % num_kv_heads == 0 && max_query_len > 0 &&
+         (int64_t)max_query_len * (num_q_heads / num_kv_heads) <= pa::kMqPrefixRows;
 }
 
 }  // namespace
@@ -582,8 +607,10 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
                          int32_t max_blocks_per_seq, int32_t max_query_len,
                          int32_t max_context_len, int32_t dtype, int32_t kv_dtype, float k_scale,
                          float v_scale, int32_t partition_size, void *workspace,
-                         size_t workspace_bytes, void *stream) {
+                         size_t workspace_bytes, void *stream, const int32_t *groups = nullptr,
+                         int32_t num_groups = 0, const int32_t *shared_lens = nullptr) {
   if (!known_dtype(dtype)) return PA_ERR_DTYPE;
+  if (num_groups < 0 || num_groups > std::max(num_seqs, 0)) return PA_ERR_SHAPE;
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0 ||
       max_context_len < 0)
@@ -617,13 +644,16 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
     return PA_ERR_NULL;
+  if (num_groups > 0 && (!groups || !shared_lens)) return PA_ERR_NULL;
   float *ws_o = nullptr, *ws_ml = nullptr;
-  const MultiQueryWorkspace w = multi_query_workspace(num_seqs, num_tokens, num_q_heads,
-                                                      num_kv_heads, head_dim, max_query_len, P);
-  if (P > 1) {
+  const MultiQueryWorkspace w =
+      multi_query_workspace(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                            max_query_len, P, num_groups);
+  const int64_t slots = P + (num_groups > 0 ? 1 : 0);
+  if (slots > 1) {
     if (!workspace || workspace_bytes < w.partials) return PA_ERR_WORKSPACE;
     ws_o = static_cast<float *>(workspace);
-    ws_ml = ws_o + (size_t)num_tokens * num_q_heads * P * head_dim;
+    ws_ml = ws_o + (size_t)num_tokens * num_q_heads * slots * head_dim;
   }
   pa::MultiQueryArgs a;
   a.q = q;
@@ -651,6 +681,9 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
   a.num_partitions = P;
   a.ws_o = ws_o;
   a.ws_ml = ws_ml;
+  a.groups = groups;
+  a.shared_lens = shared_lens;
+  a.num_groups = num_groups;
   // with room for it, the longest-first list; else the fixed order
   if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order)
     a.order = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + w.partials);
@@ -661,6 +694,10 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
     if (st == PA_OK)
       st = pa::check_queries(context_lens, query_start, num_seqs, num_tokens, max_query_len,
                              st_stream);
+    if (st == PA_OK && num_groups > 0)
+      st = pa::check_prefix_groups(context_lens, block_tables, groups, num_groups, shared_lens,
+                                   num_seqs, max_blocks_per_seq, a.log2_block_size,
+                                   max_context_len, pa::kMqPrefixMembers, st_stream);
     if (st != PA_OK) return st;
   }
   const hipError_t e = pa::launch_multi_query(a, static_cast<hipStream_t>(stream));
@@ -752,6 +789,45 @@ int32_t paged_attention_multi_query_int8(const void *q, const void *k_cache, con
                           block_size, num_blocks, max_blocks_per_seq, max_query_len,
                           max_context_len, PA_BF16, PA_INT8, k_scale, v_scale,
                           partition_size, workspace, workspace_bytes, stream);
+}
+
+int32_t paged_attention_multi_query_prefix(
+    const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+    const int32_t *context_lens, const int32_t *query_start, const int32_t *prefix_groups,
+    int32_t num_groups, const int32_t *shared_lens, float scale, float k_scale, float v_scale,
+    float *out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    int32_t max_query_len, int32_t max_context_len, int32_t kv_dtype, int32_t partition_size,
+    void *workspace, size_t workspace_bytes, void *stream) {
+  if (!known_pool_dtype(kv_dtype)) return PA_ERR_DTYPE;
+  if (num_groups < 0) return PA_ERR_SHAPE;
+  const bool pfx = mq_prefix_path(kv_dtype, head_dim, num_q_heads, num_kv_heads, max_query_len,
+                                  num_groups);
+  const bool q8 = is_q8(kv_dtype);
+  return multi_query_impl(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                          out, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_blocks_per_seq, max_query_len,
+                          max_context_len, q8 ? PA_BF16 : kv_dtype, kv_dtype,
+                          q8 ? k_scale : 1.f, q8 ? v_scale : 1.f, partition_size, workspace,
+                          workspace_bytes, stream, pfx ? prefix_groups : nullptr,
+                          pfx ? num_groups : 0, pfx ? shared_lens : nullptr);
+}
+
+size_t paged_attention_multi_query_prefix_workspace_size(
+    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t max_query_len, int32_t max_context_len, int32_t partition_size,
+    int32_t num_groups, int32_t kv_dtype) {
+  if (!mq_prefix_path(kv_dtype, head_dim, num_q_heads, num_kv_heads, max_query_len, num_groups))
+    return paged_attention_multi_query_workspace_size(num_seqs, num_tokens, num_q_heads,
+                                                      num_kv_heads, head_dim, max_query_len,
+                                                      max_context_len, partition_size);
+  if (num_tokens < 0 || num_seqs < 0 || num_groups > num_seqs) return 0;
+  const int32_t P = paged_attention_multi_query_partitions(
+      num_seqs, num_q_heads, num_kv_heads, max_query_len, max_context_len, partition_size);
+  if (P < 1) return 0;
+  const MultiQueryWorkspace w = multi_query_workspace(
+      num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, max_query_len, P, num_groups);
+  return w.partials + w.order;
 }
 
 int32_t kv_cache_write(const void *k, const void *v, const int32_t *slot_mapping,

@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     float v_scale, int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P,
     const int32_t *__restrict__ query_start, int num_tokens, int gh, int max_q, int csets,
     const int32_t *__restrict__ order, const int32_t *__restrict__ groups,
-    const int32_t *__restrict__ shared_lens, int slots) {
+    const int32_t *__restrict__ shared_lens, int slots, int ipg, int ngroups) {
   using K = MfmaDecode<G, SMALLB, Q8>;
   using TileT = typename K::TileT;
   constexpr bool FP8 = K::FP8;
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     const int t = id / 8;
     cgroup = t % cgroups;
     id = (t / cgroups) * 8 + id % 8;
-    if (id >= num_seqs * hkv * P) return;
+    if (id >= (num_seqs * P + (PFX ? ipg * ngroups : 0)) * hkv) return;
   }
   // work item: KV head fastest, then (sequence, partition) from the
   // longest-first list or the fixed order (as in decode.hip); with PFX, the
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   const int item = order ? order[id / hkv] : id / hkv;
   // listed as empty (past the sequence's end), or not an item of this launch
   // (a list the caller planned is trusted only this far)
-  const int nitems = MQ ? num_seqs * P : (int)(gridDim.x / hkv);
+  const int nitems = MQ ? num_seqs * P + (PFX ? ipg * ngroups : 0) : (int)(gridDim.x / hkv);
   if (item < 0 || item >= nitems) return;
   const int hq = hkv * (MQ ? gh : G);
 
@@ -490,11 +490,76 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
   // sequence
   int pset = 0, pfirst = 0, pmember = 0, pseq = 0;
   bool pcol = false;
+  // a multi-query prefix item: each column's output row (token * hq + head)
+  // and the last position it attends, or -1
+  int mrow[NC], mcpos[NC];
+  __shared__ int sm_prow[(MQ && PFX) ? NC : 1][16];
 #pragma unroll
   for (int c = 0; c < NC; ++c) ncols[c] = G;
   if constexpr (PFX) pitem = item >= num_seqs * P;
-  if (pitem) {
-    // (PFX only: NC == 1, no multi-query)
+  if (MQ && pitem) {
+    // Item gi * ipg + ci of group gi covers the group's rows 16 (NC ci + c)
+    // + n: the members' (token, head) rows in member order, token-major
+    // within a member.  A column attends the prefix positions below its
+    // member's shared length, up to its own token's position.
+    if (cgroup > 0) return;  // the item's sets are all in column group 0
+    const int pi = item - num_seqs * P;
+    const int gi = pi / ipg, ci = pi - gi * ipg;
+    pfirst = min(max(groups[2 * gi], 0), num_seqs - 1);
+    const int count = min(max(groups[2 * gi + 1], 0), min(num_seqs - pfirst, kMqPrefixMembers));
+    int colsh[NC], colseq[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      mrow[c] = -1;
+      mcpos[c] = -1;
+      colsh[c] = 0;
+      colseq[c] = pfirst;
+    }
+    int off = 0;
+    for (int mm = 0; mm < count; ++mm) {
+      const int sm = pfirst + mm;
+      const int Lm = max(0, min(context_lens[sm], mb << lgB));
+      const int qsm = max(0, min(query_start[sm], num_tokens));
+      const int nqm =
+          max(0, min(min(query_start[sm + 1] - qsm, Lm), min(max_q, num_tokens - qsm)));
+      const int shm = min(max(shared_lens[sm], 0), Lm) & ~(kTile - 1);
+      const int rows_m = nqm * gh;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int R = 16 * (NC * ci + c) + n;
+        if (R >= off && R < off + rows_m) {
+          const int r = R - off;
+          mrow[c] = (qsm + r / gh) * hq + kvh * gh + r % gh;
+          mcpos[c] = min(shm - 1, Lm - nqm + r / gh);
+          colsh[c] = shm;
+          colseq[c] = sm;
+        }
+      }
+      off += rows_m;
+    }
+    int shx = 0, seqx = pfirst;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      ncols[c] = min(max(off - 16 * (NC * ci + c), 0), 16);
+      if (mrow[c] >= 0 && colsh[c] > shx) {
+        shx = colsh[c];
+        seqx = colseq[c];
+      }
+    }
+    if (wave == 0 && g == 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sm_prow[c][n] = mrow[c];
+    }
+    int wmax = shx;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) wmax = max(wmax, __shfl_xor(wmax, o));
+    t1 = __builtin_amdgcn_readfirstlane(wmax);
+    if (t1 <= 0) return;  // the same in every wave: the workgroup leaves whole
+    const uint64_t longest = __builtin_amdgcn_ballot_w64(shx == wmax);
+    const int walk_seq = __builtin_amdgcn_readlane(seqx, (int)__builtin_ctzll(longest));
+    tbl = block_tables + (int64_t)walk_seq * mb;
+  } else if (pitem) {
+    // (decode: NC == 1)
     const int pi = item - num_seqs * P;
     const int gi = pi >> 2;
     pset = pi & 3;
@@ -543,7 +608,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     if constexpr (PFX) {
       // positions below the shared length come from the group's prefix item
       sh = min(max(shared_lens[s], 0), L) & ~(kTile - 1);
-      if (Q8 != 0 && prefix_short(L, sh)) return;  // the prefix item reads it all
+      if (Q8 != 0 && !MQ && prefix_short(L, sh)) return;  // the prefix item reads it all
       if (p < sh / ps) return;  // the whole partition is shared: no partial
       t0 = max(t0, sh);
     }
@@ -561,11 +626,12 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     cpos[c] = INT_MAX;
     if constexpr (MQ) {
       const int R = G * (NC * cgroup + c) + n;  // this column's row of the chunk
-      cpos[c] = n < ncols[c] ? L - nq + R / gh : -1;
+      cpos[c] = pitem ? mcpos[c] : n < ncols[c] ? L - nq + R / gh : -1;
+      const int64_t qr = pitem ? mrow[c] : n < ncols[c] ? (int64_t)(qs + R / gh) * hq + kvh * gh + R % gh : -1;
 #pragma unroll
       for (int k = 0; k < 4; ++k) qb[c][k] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-      if (n < ncols[c]) {
-        const uint16_t *qrow = q + ((int64_t)(qs + R / gh) * hq + kvh * gh + R % gh) * kD;
+      if (qr >= 0) {
+        const uint16_t *qrow = q + qr * kD;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           qb[c][k] = __builtin_bit_cast(
@@ -745,7 +811,7 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
     }
   }
 
-  if constexpr (PFX && Q8 != 0) {
+  if constexpr (PFX && Q8 != 0 && !MQ) {
     // A prefix item also reads the private tile [sh, L) of each short member
     // of its set (one tile each, the set's members dealt round-robin to the
     // waves), with every other member's columns masked, so that those
@@ -826,8 +892,15 @@ __global__ __launch_bounds__(kThreads, NC == 1 ? 3 : 2) void paged_decode_mfma_k
       bool to_out = final_out;
       if constexpr (MQ) {
         if (h >= ncols[c]) continue;
-        const int R = G * (NC * cgroup + c) + h;
-        row = (int64_t)(qs + R / gh) * hq + kvh * gh + R % gh;
+        if (pitem) {
+          // the row's prefix partial is its last slot
+          row = sm_prow[c][h];
+          if (row < 0) continue;
+          slot_of = slots - 1;
+        } else {
+          const int R = G * (NC * cgroup + c) + h;
+          row = (int64_t)(qs + R / gh) * hq + kvh * gh + R % gh;
+        }
       } else {
         if (pitem) {
           // (member, head) of the group; its prefix partial is the row's
@@ -879,7 +952,7 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
                      a.ws_o, a.ws_ml, sl2, FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads,
                      a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.partition_size,
                      a.num_partitions, nullptr, 0, 0, 0, 1, a.order, a.groups, a.shared_lens,
-                     a.num_partitions + (pfx ? 1 : 0));
+                     a.num_partitions + (pfx ? 1 : 0), 4, a.num_groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (a.num_partitions <= 1 && !pfx)) return e;
   return launch_partition_merge(a, stream);
@@ -895,15 +968,25 @@ template <bool SMALLB, int Q8>
 hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
   using KV = typename MfmaDecode<16, SMALLB, Q8>::KV;
   constexpr bool FP8 = Q8 != 0;
-  const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
-  if (items <= 0) return hipSuccess;
   const int gh = a.num_q_heads / a.num_kv_heads;
+  const bool pfx = a.num_groups > 0;
+  // with groups, ipg prefix items per group follow the sequence items
+  const int ipg = pfx ? (int)mq_prefix_items_per_group(a.max_query_len, gh) : 0;
+  const int64_t items =
+      ((int64_t)a.num_seqs * a.num_partitions + (int64_t)ipg * a.num_groups) * a.num_kv_heads;
+  if (items <= 0) return hipSuccess;
   const int csets = (int)(((int64_t)a.max_query_len * gh + 15) / 16);
   // two column sets per wave from 17 rows up (one pass over K/V for 32
   // columns), one otherwise
   const int64_t grid = (items + 7) / 8 * 8 * multi_query_few_rows_groups(csets);
-  auto kernel = csets >= 2 ? paged_decode_mfma_kernel<16, SMALLB, Q8, true, 2>
-                           : paged_decode_mfma_kernel<16, SMALLB, Q8, true, 1>;
+  // (prefix items come over bf16 pools with at most 8 rows per KV head: one
+  // column set)
+  if (pfx && (csets > 1 || Q8 != 0)) return hipErrorNotSupported;
+  auto kernel = csets >= 2 ? paged_decode_mfma_kernel<16, SMALLB, Q8, true, 2, false>
+                           : paged_decode_mfma_kernel<16, SMALLB, Q8, true, 1, false>;
+  if constexpr (Q8 == 0) {
+    if (pfx) kernel = paged_decode_mfma_kernel<16, SMALLB, 0, true, 1, true>;
+  }
   // as in decode: the K scale joins the softmax scale, the V scale the output
   const float sl2 = a.scale * (FP8 ? a.k_scale : 1.f) * kLog2e;
   hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
@@ -912,7 +995,8 @@ hipError_t launch_mq(const MultiQueryArgs &a, hipStream_t stream) {
                      a.ws_o, a.ws_ml, sl2, FP8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads,
                      a.log2_block_size, a.num_blocks, a.max_blocks_per_seq, a.partition_size,
                      a.num_partitions, a.query_start, a.num_tokens, gh, a.max_query_len, csets,
-                     a.order, nullptr, nullptr, a.num_partitions);
+                     a.order, pfx ? a.groups : nullptr, pfx ? a.shared_lens : nullptr,
+                     a.num_partitions + (pfx ? 1 : 0), ipg, pfx ? a.num_groups : 0);
   return hipGetLastError();
 }
 

@@ -60,10 +60,14 @@ bool schedule_wanted(int64_t workgroups, int64_t num_seqs, int64_t P);
 // sequence's last partition last and as ~c (negative); ps = tokens
 // per partition, cap = the most tokens a sequence may have.  launch_decode
 // and launch_multi_query call it when their args carry an order buffer.
+// With groups: ipg items per group follow the sequence items; a decode
+// prefix item (group = G) is sized by the members with columns in its set,
+// a multi-query one (group = 0) by every member.
 hipError_t launch_schedule(const int32_t *context_lens, int32_t *order, int num_seqs, int P,
                            int ps, int cap, hipStream_t stream,
                            const int32_t *groups = nullptr, const int32_t *shared_lens = nullptr,
-                           int num_groups = 0, int group = 1, bool short_rule = false);
+                           int num_groups = 0, int group = 1, bool short_rule = false,
+                           int ipg = 4);
 
 // Enqueues decode (and the partition merge when P > 1).  Returns hipSuccess or
 // the launch error; hipErrorNotSupported when no kernel is compiled for the
@@ -103,7 +107,28 @@ struct MultiQueryArgs {
   int32_t kv_dtype = -1;     // 2 = FP8 E4M3, 3 = INT8 pool (decode walk only); -1 = dtype
   float k_scale = 1.f;       // 8-bit pools: stored code c means value(c) * scale
   float v_scale = 1.f;
+  // shared prefixes (decode walk only): groups [num_groups][2] (first
+  // sequence, members), shared_lens [num_seqs]; the partials then hold one
+  // more slot per row (P + 1, the prefix partial last)
+  const int32_t *groups = nullptr;
+  const int32_t *shared_lens = nullptr;
+  int32_t num_groups = 0;
 };
+
+// Most members of a shared-prefix group in a multi-query call.
+constexpr int kMqPrefixMembers = 16;
+// A multi-query call takes prefix items only with at most this many (token,
+// head) rows per sequence and KV head, so that one 16-column item covers at
+// least two members (measured on the speculative-verification structure,
+// G = 4: 1 and 2 tokens per sequence gain 17% and 7%, 3 break even, 5 lose
+// 10%: each item walks the whole prefix, and L2 already serves most of the
+// members' repeated reads).
+constexpr int64_t kMqPrefixRows = 8;
+// Prefix items per group of such a call: each covers 16 (member, token,
+// head) rows.
+inline int64_t mq_prefix_items_per_group(int64_t max_query_len, int64_t gh) {
+  return (kMqPrefixMembers * max_query_len * gh + 15) / 16;
+}
 
 // Workgroups of a multi-query launch (either kernel), for the schedule
 // decision and the workspace size.

@@ -586,16 +586,19 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
 
 // Merge of the partition partials of the (query token, head) rows, one wave
 // per row, kMqMergeRows rows per workgroup: row (s, i, h) is head h of token
-// i of sequence s's chunk, and, when the sequence was split, combines the
-// partitions the token's position reaches (log-sum-exp weights, ascending
-// partition order).  Rows of sequences that fit in one partition were
-// written to out directly.
+// i of sequence s's chunk, and, when the sequence was split or has a shared
+// prefix, combines its prefix partial (the row's last slot) and the
+// partitions with private positions that the token's position reaches
+// (log-sum-exp weights, prefix first, then ascending partition order).  Rows
+// of sequences that fit in one partition and share no prefix were written
+// to out directly.
 constexpr int kMqMergeRows = 4;
 template <int D>
 __global__ __launch_bounds__(64 * kMqMergeRows) void paged_multi_query_merge_kernel(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
-    int num_tokens, int hq, int cap, int max_q, int ps, int P, int64_t rows) {
+    int num_tokens, int hq, int cap, int max_q, int ps, int P, int64_t rows,
+    const int32_t *__restrict__ shared_lens, int slots) {
   constexpr int EPL = D / 64;  // elements per lane
   const int64_t rr =
       (int64_t)blockIdx.x * kMqMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -605,7 +608,9 @@ __global__ __launch_bounds__(64 * kMqMergeRows) void paged_multi_query_merge_ker
   const int s = (int)(rr / ((int64_t)hq * max_q));
   int L = context_lens[s];
   L = max(0, min(L, cap));
-  if (min((L + ps - 1) / ps, P) <= 1) return;  // written to out directly
+  const int sh = shared_lens ? min(max(shared_lens[s], 0), L) & ~15 : 0;
+  if (min((L + ps - 1) / ps, P) <= 1 && sh == 0) return;  // written to out directly
+  const int first = sh / ps;  // the first partition with private positions
   const int qs = max(0, min(query_start[s], num_tokens));
   int n = query_start[s + 1] - qs;
   n = max(0, min(min(n, L), min(max_q, num_tokens - qs)));
@@ -613,20 +618,23 @@ __global__ __launch_bounds__(64 * kMqMergeRows) void paged_multi_query_merge_ker
   const int pos = L - n + i;
   const int np = min(pos / ps + 1, P);
   const int64_t row = (int64_t)(qs + i) * hq + h;
-  const float *ml = ws_ml + row * P * 2;
-  const float *o = ws_o + row * P * D + (threadIdx.x & 63) * EPL;
-  float M = ml[0];
-  for (int j = 1; j < np; ++j) M = fmaxf(M, ml[2 * j]);
+  const float *ml = ws_ml + row * slots * 2;
+  const float *o = ws_o + row * slots * D + (threadIdx.x & 63) * EPL;
+  const int pre = slots - 1;  // the prefix slot (used when sh > 0)
+  float M = sh > 0 ? ml[2 * pre] : neg_inf();
+  for (int j = first; j < np; ++j) M = fmaxf(M, ml[2 * j]);
   float num[EPL], den = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.f;
-  for (int j = 0; j < np; ++j) {
+  auto add = [&](int j) {
     const float w = ml[2 * j] == neg_inf() ? 0.f
                                            : ml[2 * j + 1] * __builtin_amdgcn_exp2f(ml[2 * j] - M);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, o[(int64_t)j * D + e], num[e]);
     den += w;
-  }
+  };
+  if (sh > 0) add(pre);
+  for (int j = first; j < np; ++j) add(j);
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
     out[row * D + (threadIdx.x & 63) * EPL + e] = den > 0.f ? num[e] / den : 0.f;
@@ -635,6 +643,8 @@ __global__ __launch_bounds__(64 * kMqMergeRows) void paged_multi_query_merge_ker
 hipError_t launch_merge(const MultiQueryArgs &a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_seqs * a.max_query_len * a.num_q_heads;
   if (rows <= 0) return hipSuccess;
+  const bool pfx = a.num_groups > 0;
+  const int slots = a.num_partitions + (pfx ? 1 : 0);
   const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
                                          INT32_MAX);
   const uint32_t grid = (uint32_t)((rows + kMqMergeRows - 1) / kMqMergeRows);
@@ -642,12 +652,12 @@ hipError_t launch_merge(const MultiQueryArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((paged_multi_query_merge_kernel<64>), dim3(grid), dim3(64 * kMqMergeRows),
                        0, stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out,
                        a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
-                       a.num_partitions, rows);
+                       a.num_partitions, rows, pfx ? a.shared_lens : nullptr, slots);
   else
     hipLaunchKernelGGL((paged_multi_query_merge_kernel<128>), dim3(grid), dim3(64 * kMqMergeRows),
                        0, stream, a.context_lens, a.query_start, a.ws_o, a.ws_ml, a.out,
                        a.num_tokens, a.num_q_heads, cap, a.max_query_len, a.partition_size,
-                       a.num_partitions, rows);
+                       a.num_partitions, rows, pfx ? a.shared_lens : nullptr, slots);
   return hipGetLastError();
 }
 
@@ -709,14 +719,19 @@ hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream) {
   if (a.order) {
     const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
                                            INT32_MAX);
-    const hipError_t e = launch_schedule(a.context_lens, a.order, a.num_seqs,
-                                         a.num_partitions, a.partition_size, cap, stream);
+    const bool pfx = a.num_groups > 0;
+    const hipError_t e = launch_schedule(
+        a.context_lens, a.order, a.num_seqs, a.num_partitions, a.partition_size, cap, stream,
+        pfx ? a.groups : nullptr, pfx ? a.shared_lens : nullptr, pfx ? a.num_groups : 0, 0,
+        false,
+        pfx ? (int)mq_prefix_items_per_group(a.max_query_len, a.num_q_heads / a.num_kv_heads)
+            : 4);
     if (e != hipSuccess) return e;
   }
   if (multi_query_few_rows_supported(a)) {
     // a few rows per KV head: the decode walk, one wave per 16-token tile
     hipError_t e = launch_multi_query_few_rows(a, stream);
-    if (e != hipSuccess || a.num_partitions <= 1) return e;
+    if (e != hipSuccess || (a.num_partitions <= 1 && a.num_groups == 0)) return e;
     return launch_merge(a, stream);
   }
   switch (a.head_dim) {

@@ -15,9 +15,10 @@
 // sequence's last partition (or, with shared prefixes, wholly inside its
 // shared length) is listed as ~c, so that its workgroups exit without
 // reading the context length.  With shared prefixes, items num_seqs * P +
-// 4 i + c are column set c of prefix group i, sized by the longest shared
-// length among the members with columns in that set (empty when there are
-// none).  Items are bucketed by
+// ipg i + c are item c of prefix group i: in decode (ipg = 4) column set c,
+// sized by the longest shared length among the members with columns in that
+// set (empty when there are none); in a multi-query call, sized by the
+// longest shared length of the group.  Items are bucketed by
 // token count (512 size classes of 2^shift tokens, longest class first; an
 // item past the sequence's last partition, which does no work, sorts last)
 // with a counting sort in LDS that keeps, within a class, the fixed order
@@ -53,7 +54,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
     const int32_t *__restrict__ context_lens, int32_t *__restrict__ order, int num_seqs, int P,
     int ps, int cap, int shift, const int32_t *__restrict__ groups,
-    const int32_t *__restrict__ shared_lens, int num_groups, int G, int short_rule) {
+    const int32_t *__restrict__ shared_lens, int num_groups, int G, int short_rule, int ipg) {
   // class-major, so one thread reads a class's 16 wave counts as 4 vectors
   __shared__ __attribute__((aligned(16))) int start[kSizeClasses + 1][kSchedWaves];
   __shared__ int wave_total[kSchedWaves];
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int nseq_items = num_seqs * P;
-  const int n = nseq_items + 4 * num_groups;
+  const int n = nseq_items + ipg * num_groups;
   const int chunk = ((n + kSchedWaves - 1) / kSchedWaves + 63) / 64 * 64;
   const int begin = min(n, wave * chunk), end = min(n, begin + chunk);
 
@@ -74,16 +75,19 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(
   auto size_class = [&](int c) -> int {
     int tokens;
     if (c >= nseq_items) {
-      // a prefix item (group gi, column set c & 3): it walks the longest
-      // shared length among the members with columns in its set
-      const int gi = (c - nseq_items) >> 2;
-      const int cset = (c - nseq_items) & 3;
+      // a prefix item (group gi, column set cset): it walks the longest
+      // shared length among the members with columns in its set (decode),
+      // or among all the members (multi-query, G == 0)
+      const int gi = (c - nseq_items) / ipg;
+      const int cset = (c - nseq_items) - gi * ipg;
       const int first = min(max(groups[2 * gi], 0), num_seqs - 1);
-      const int count = min(max(groups[2 * gi + 1], 0), min(num_seqs - first, 64 / G));
-      const int m1 = min(count, (16 * cset + 15) / G + 1);
+      const int count =
+          min(max(groups[2 * gi + 1], 0), min(num_seqs - first, G ? 64 / G : kMqPrefixMembers));
+      const int m0 = G ? 16 * cset / G : 0;
+      const int m1 = G ? min(count, (16 * cset + 15) / G + 1) : count;
       int longest = 0;
       bool extra = false;  // a short member's private tile
-      for (int m = 16 * cset / G; m < m1; ++m) {
+      for (int m = m0; m < m1; ++m) {
         const int L = max(0, min(context_lens[first + m], cap));
         const int sh = shared(first + m, L);
         longest = max(longest, sh);
@@ -169,14 +173,14 @@ bool schedule_wanted(int64_t workgroups, int64_t num_seqs, int64_t P) {
 hipError_t launch_schedule(const int32_t *context_lens, int32_t *order, int num_seqs, int P,
                            int ps, int cap, hipStream_t stream, const int32_t *groups,
                            const int32_t *shared_lens, int num_groups, int group,
-                           bool short_rule) {
+                           bool short_rule, int ipg) {
   // one partition spans every clamped context: size the classes by the cap
   if (P <= 1) ps = cap;
   int shift = 0;
   while ((ps >> shift) >= kSizeClasses) ++shift;
   hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream,
                      context_lens, order, num_seqs, P, ps, cap, shift, groups, shared_lens,
-                     num_groups, group, (int)short_rule);
+                     num_groups, group, (int)short_rule, ipg);
   return hipGetLastError();
 }
 
