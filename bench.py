@@ -768,7 +768,8 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the paged-decode "
-              "path has no cross-GPU exchange in this build", file=sys.stderr)
+              "library has no cross-GPU exchange (each GPU would run its own share of the "
+              "sequences and KV heads)", file=sys.stderr)
         return 2
     rank = int(os.environ.get("RANK", "0"))
 
