@@ -21,9 +21,10 @@
  *       drops one reference to the old one).
  *
  * Readings where the pages are loose: blocks are reference counted, and a
- * block returns to the free list when its count reaches zero (the listing
- * frees the old block outright while its comment says "decrement the
- * reference count"); the slot of position t is table[t / B] * B + t % B; a
+ * block returns to the free list when its count reaches zero (the page's
+ * code frees the old block outright, although its own comment speaks of
+ * lowering a reference count); the slot of position t is table[t / B] * B +
+ * t % B; a
  * new block is needed exactly when the new position is a multiple of B.
  *
  * The manager is host memory only and not thread safe: calls on one manager
