@@ -4,8 +4,9 @@ followed by its write (stored rows, or FP8 / INT8 quantisation), on the
 orderings that the one-launch form has to resolve -- a token writing a
 copy's destination, a token writing a copy's source (with and without a
 token on the same position of the destination), several copies of one
-source, random mixes, skipped pairs and slots -- at block sizes 1, 16 and
-512, and on the full-size GQA prefix and fork steps."""
+source, random mixes, skipped pairs and slots -- at block sizes 1, 16, 512
+and 1024 (a copy's skip mask then spans all its 32 words), and on the
+full-size GQA prefix and fork steps."""
 import zlib
 
 import numpy as np
@@ -147,7 +148,7 @@ def test_append_matches_copy_then_write(src, kv, kind):
     _run(pairs, k, v, slots, kc, vc, B, src, kv, host_pairs=kind != "skipped")
 
 
-@pytest.mark.parametrize("B", [1, 16, 512])
+@pytest.mark.parametrize("B", [1, 16, 512, 1024])
 @pytest.mark.parametrize("src,kv", [("bf16", "bf16"), ("bf16", "fp8")])
 def test_append_block_sizes(B, src, kv):
     rng = np.random.default_rng(B)
