@@ -459,6 +459,10 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
 // taken as the decode kernel takes it (clamped to the context, whole 16-token
 // tiles).
 constexpr int kMergeRows = 4;
+// Partials of a row the merge loads in one batch (max, sum and rows): the
+// prefix's and two partitions cover the GQA prefix batch (merge 5.95 -> 5.28
+// us per call).
+constexpr int kMergeAhead = 3;
 template <int D>
 __global__ __launch_bounds__(64 * kMergeRows) void paged_decode_merge_kernel(
     const int32_t *__restrict__ context_lens, const float *__restrict__ ws_o,
@@ -480,21 +484,49 @@ __global__ __launch_bounds__(64 * kMergeRows) void paged_decode_merge_kernel(
   const float *ml = ws_ml + (int64_t)row * slots * 2;
   const float *o = ws_o + (int64_t)row * slots * D + lane * EPL;
   const int pre = slots - 1;  // the prefix slot (used when sh > 0)
-  float M = sh > 0 ? ml[2 * pre] : -__builtin_huge_valf();
-  for (int j = first; j < n; ++j) M = fmaxf(M, ml[2 * j]);
+  // the partials in merge order: the prefix's, then the private partitions
+  // ascending; the first kMergeAhead are loaded (max, sum and rows) in one
+  // batch, so their rows do not wait on the maximum
+  const int cnt = (sh > 0 ? 1 : 0) + max(n - first, 0);
+  auto slot_at = [&](int k) { return sh > 0 ? (k == 0 ? pre : first + k - 1) : first + k; };
+  float am[kMergeAhead], al[kMergeAhead], ao[kMergeAhead][EPL];
+#pragma unroll
+  for (int k = 0; k < kMergeAhead; ++k) {
+    am[k] = -__builtin_huge_valf();
+    al[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ao[k][e] = 0.f;
+    if (k < cnt) {
+      const int j = slot_at(k);
+      am[k] = ml[2 * j];
+      al[k] = ml[2 * j + 1];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ao[k][e] = o[(int64_t)j * D + e];
+    }
+  }
+  float M = -__builtin_huge_valf();
+#pragma unroll
+  for (int k = 0; k < kMergeAhead; ++k) M = fmaxf(M, am[k]);
+  for (int k = kMergeAhead; k < cnt; ++k) M = fmaxf(M, ml[2 * slot_at(k)]);
   float num[EPL], den = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.f;
-  auto add = [&](int j) {
-    const float mj = ml[2 * j];
-    const float w = mj == -__builtin_huge_valf() ? 0.f
-                                                 : ml[2 * j + 1] * __builtin_amdgcn_exp2f(mj - M);
+  auto add = [&](float mj, float lj, const float *oj) {
+    const float w = mj == -__builtin_huge_valf() ? 0.f : lj * __builtin_amdgcn_exp2f(mj - M);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, o[(int64_t)j * D + e], num[e]);
+    for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, oj[e], num[e]);
     den += w;
   };
-  if (sh > 0) add(pre);
-  for (int j = first; j < n; ++j) add(j);
+#pragma unroll
+  for (int k = 0; k < kMergeAhead; ++k)
+    if (k < cnt) add(am[k], al[k], ao[k]);
+  for (int k = kMergeAhead; k < cnt; ++k) {
+    const int j = slot_at(k);
+    float oj[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) oj[e] = o[(int64_t)j * D + e];
+    add(ml[2 * j], ml[2 * j + 1], oj);
+  }
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
     out[(int64_t)row * D + lane * EPL + e] = den > 0.f ? num[e] / den : 0.f;

@@ -593,6 +593,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
 // of sequences that fit in one partition and share no prefix were written
 // to out directly.
 constexpr int kMqMergeRows = 4;
+// partials of a row loaded in one batch (as in the decode merge)
+constexpr int kMqMergeAhead = 3;
 template <int D>
 __global__ __launch_bounds__(64 * kMqMergeRows) void paged_multi_query_merge_kernel(
     const int32_t *__restrict__ context_lens, const int32_t *__restrict__ query_start,
@@ -621,20 +623,49 @@ __global__ __launch_bounds__(64 * kMqMergeRows) void paged_multi_query_merge_ker
   const float *ml = ws_ml + row * slots * 2;
   const float *o = ws_o + row * slots * D + (threadIdx.x & 63) * EPL;
   const int pre = slots - 1;  // the prefix slot (used when sh > 0)
-  float M = sh > 0 ? ml[2 * pre] : neg_inf();
-  for (int j = first; j < np; ++j) M = fmaxf(M, ml[2 * j]);
+  // the partials in merge order (the prefix's, then the private partitions
+  // ascending); the first kMqMergeAhead are loaded (max, sum and rows) in
+  // one batch, so their rows do not wait on the maximum
+  const int cnt = (sh > 0 ? 1 : 0) + max(np - first, 0);
+  auto slot_at = [&](int k) { return sh > 0 ? (k == 0 ? pre : first + k - 1) : first + k; };
+  float am[kMqMergeAhead], al[kMqMergeAhead], ao[kMqMergeAhead][EPL];
+#pragma unroll
+  for (int k = 0; k < kMqMergeAhead; ++k) {
+    am[k] = neg_inf();
+    al[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ao[k][e] = 0.f;
+    if (k < cnt) {
+      const int j = slot_at(k);
+      am[k] = ml[2 * j];
+      al[k] = ml[2 * j + 1];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ao[k][e] = o[(int64_t)j * D + e];
+    }
+  }
+  float M = neg_inf();
+#pragma unroll
+  for (int k = 0; k < kMqMergeAhead; ++k) M = fmaxf(M, am[k]);
+  for (int k = kMqMergeAhead; k < cnt; ++k) M = fmaxf(M, ml[2 * slot_at(k)]);
   float num[EPL], den = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.f;
-  auto add = [&](int j) {
-    const float w = ml[2 * j] == neg_inf() ? 0.f
-                                           : ml[2 * j + 1] * __builtin_amdgcn_exp2f(ml[2 * j] - M);
+  auto add = [&](float mj, float lj, const float *oj) {
+    const float w = mj == neg_inf() ? 0.f : lj * __builtin_amdgcn_exp2f(mj - M);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, o[(int64_t)j * D + e], num[e]);
+    for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, oj[e], num[e]);
     den += w;
   };
-  if (sh > 0) add(pre);
-  for (int j = first; j < np; ++j) add(j);
+#pragma unroll
+  for (int k = 0; k < kMqMergeAhead; ++k)
+    if (k < cnt) add(am[k], al[k], ao[k]);
+  for (int k = kMqMergeAhead; k < cnt; ++k) {
+    const int j = slot_at(k);
+    float oj[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) oj[e] = o[(int64_t)j * D + e];
+    add(ml[2 * j], ml[2 * j + 1], oj);
+  }
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
     out[row * D + (threadIdx.x & 63) * EPL + e] = den > 0.f ? num[e] / den : 0.f;
