@@ -645,6 +645,12 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
     return PA_ERR_NULL;
   if (num_groups > 0 && (!groups || !shared_lens)) return PA_ERR_NULL;
+  // the launch's items (the prefix items after the sequence items), times
+  // the KV heads, index the grid in 32 bits
+  if (num_groups > 0 &&
+      ((int64_t)num_seqs * P + pa::mq_prefix_items_per_group(max_query_len, G) * num_groups) *
+                  num_kv_heads + 8 >= (int64_t(1) << 31))
+    return PA_ERR_SHAPE;
   float *ws_o = nullptr, *ws_ml = nullptr;
   const MultiQueryWorkspace w =
       multi_query_workspace(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
