@@ -6,7 +6,8 @@ The order may change timing only: every item must run exactly once, so the
 outputs with the list must equal, bit for bit, those of the fixed order (a
 workspace with room for the partials but not the list), and both must match
 the oracle.  The output buffer is filled with NaN before each run, so an item
-that never ran shows up.
+that never ran shows up.  With shared prefixes the list also holds the
+groups' prefix items, sized by the longest shared length they walk.
 """
 import numpy as np
 import pytest
@@ -201,5 +202,92 @@ def test_list_is_longest_first_permutation(S, Hkv, ps, top):
     nparts = np.minimum((L + tokens_per_part - 1) // tokens_per_part, P)
     tok = np.minimum(L, (p + 1) * tokens_per_part) - p * tokens_per_part
     key = np.where(p < np.maximum(nparts, 1), tok >> shift, -1)
+    assert (np.diff(key) <= 0).all(), "not longest first"
+    assert np.array_equal(listed < 0, key < 0), "empty items are the negative entries"
+
+
+@pytest.mark.parametrize("ps", [512, 0])
+def test_multi_query_prefix_list(ps):
+    """A multi-query call with shared prefixes (2 tokens per sequence, G = 4:
+    prefix items): its list holds the sequence items and the groups' prefix
+    items once each, longest first -- a prefix item sized by its group's
+    longest shared length, a sequence item by its private positions in its
+    partition -- with empty items negative; and the outputs with the list
+    equal, bit for bit, those of the fixed order."""
+    import paged_kv_cache_386_amd as pa
+    from workloads import make_multi_query_case, make_prefix_case
+    from workloads.generate import settle_step
+    S, G, Hkv, D, max_q = 160, 4, 8, 128, 2
+    rng = np.random.default_rng(61)
+    lens = rng.integers(3, 3000, size=S)
+    lens[:4] = [1024, 1030, 700, 2]
+    base = settle_step(make_prefix_case("schedule-mqp", lens, 16, 1024, G * Hkv, Hkv, D, 16,
+                                        "bf16", 61))
+    q_lens = np.minimum(base.context_lens, max_q)
+    q_lens[5] = 0
+    c = make_multi_query_case(base, q_lens, 61)
+    g, sh = pa.prefix_groups(base.block_tables, base.context_lens, base.block_size,
+                             G * Hkv, Hkv, 16)
+    assert len(g) > 0 and (g[:, 1] <= 16).all()
+    T, Hq = c.num_tokens, G * Hkv
+    max_ctx = int(base.context_lens.max())
+    P = pa.multi_query_partitions(S, Hq, Hkv, max_q, max_ctx, ps)
+    ipg = -(-16 * max_q * G // 16)
+    n_items = S * P + ipg * len(g)
+    full = pa.multi_query_prefix_workspace_size(S, T, Hq, Hkv, D, max_q, max_ctx, ps, len(g),
+                                                pa.PA_BF16)
+    partial = T * Hq * (P + 1) * (D + 2) * 4
+    assert full == partial + 4 * n_items, "the case must be large enough for the list"
+    say(f"schedule mq prefix: S={S} P={P} groups={len(g)} items={n_items}")
+    args = [to_torch(c.q, "bf16"), to_torch(base.k_cache, "bf16"), to_torch(base.v_cache, "bf16"),
+            torch.from_numpy(base.block_tables).cuda(), torch.from_numpy(base.context_lens).cuda(),
+            torch.from_numpy(c.query_start).cuda(), torch.from_numpy(g).cuda(),
+            torch.from_numpy(sh).cuda(), float(base.scale)]
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device="cuda")
+    outs, listed = [], None
+    for nbytes in (full, partial):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        out.fill_(float("nan"))
+        pa.paged_attention_multi_query_prefix(*args, out, max_query_len=max_q,
+                                              max_context_len=max_ctx, partition_size=ps,
+                                              workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        if nbytes == full:
+            listed = ws[partial:].cpu().numpy().view(np.int32).copy()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    ref = O.paged_attention_multi_query(c.q, base.k_cache, base.v_cache, base.block_tables,
+                                        base.context_lens, c.query_start, base.scale,
+                                        base.block_size, base.dtype)
+    assert max_err(outs[0], ref) <= TOL["bf16"]
+    # the list: a permutation, longest first by the restated sizes
+    order = np.where(listed < 0, ~listed, listed)
+    assert np.array_equal(np.sort(order), np.arange(n_items))
+    cap = base.block_tables.shape[1] * base.block_size
+    pst = pa.partition_tokens(S, Hkv, max_ctx, ps) if P > 1 else cap
+    if P > 1:
+        pst = -(-pst // 64) * 64 if ps == 0 else ps
+    shift = 0
+    while (pst >> shift) >= 512:
+        shift += 1
+    L = np.minimum(np.maximum(base.context_lens.astype(np.int64), 0), cap)
+    she = np.minimum(np.maximum(sh.astype(np.int64), 0), L) & ~15
+    key = []
+    for it in order.tolist():
+        if it < S * P:
+            s, p = it % S, (P - 1) - it // S
+            nparts = min(-(-int(L[s]) // pst), P)
+            if p >= max(nparts, 1) or p < she[s] // pst:
+                key.append(-1)
+                continue
+            tok = max(0, min(int(L[s]), p * pst + pst) - max(p * pst, int(she[s])))
+        else:
+            f, m = g[(it - S * P) // ipg].tolist()
+            tok = int(she[f:f + min(m, 16)].max())
+            if tok == 0:
+                key.append(-1)
+                continue
+        key.append(min(tok >> shift, 511))
+    key = np.array(key)
     assert (np.diff(key) <= 0).all(), "not longest first"
     assert np.array_equal(listed < 0, key < 0), "empty items are the negative entries"
