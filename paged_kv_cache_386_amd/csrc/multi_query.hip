@@ -340,16 +340,16 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     }
   };
 
-  // S^T of one tile into sc: k-step outermost, so that the 4 * RS
+  // S^T of one tile into sc, less the running maximum: the first product of
+  // each chain starts from seed[r] = (-m, -m, -m, -m) of the lane's row (0
+  // while m is -inf), so the scores come out relative to m and the softmax
+  // needs no subtraction per score.  k-step outermost, so that the 4 * RS
   // accumulator chains interleave and no product waits on the one before it.
   // Row 16 tb + c16 keeps swz_k(c16) for every tb.
   const int sk_lane = c16 * D;
   const int swk = swz_k(c16);
+  f32x4 seed[RS];
   auto scores = [&](f32x4 (&sc)[RS][4], const uint16_t *sk) {
-#pragma unroll
-    for (int r = 0; r < RS; ++r)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) sc[r][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kSteps; ++k) {
       const uint16_t *kp = sk + sk_lane + 8 * ((4 * k + g4) ^ swk);
@@ -361,7 +361,8 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int r = 0; r < RS; ++r)
-          sc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], qb[r][k], sc[r][tb], 0, 0, 0);
+          sc[r][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tb], qb[r][k],
+                                                              k ? sc[r][tb] : seed[r], 0, 0, 0);
     }
   };
   // V rows 32 kk + 16 h + 4 g4 + c16 / 4 keep swz_v(4 g4 + c16 / 4)
@@ -378,6 +379,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   for (int r = 0; r < RS; ++r) {
     m[r] = neg_inf();
     lsum[r] = 0.f;
+    seed[r] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // bfloat16 V tile at k0 into buf: directly, or through registers when it
@@ -444,11 +446,13 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
     // Online softmax of tile it.  The running maximum m is kept on the raw
     // scores (sl2 > 0: q carries a negative scale's sign, and a zero scale
     // is raised to the least normal float, which gives every unmasked p = 1
-    // as zero does), and p = 2^((x - m) sl2): exactly 1 at the maximum.
-    // Masked positions (only in tiles that reach past the workgroup's first
-    // row) become -inf, so p = 0.
+    // as zero does).  The tile's scores arrive as x - m (x while m is -inf,
+    // from the seed they were issued with), and p = 2^((x - m) sl2).  When
+    // the tile's maximum passes m + slack, m moves to it and the scores shift
+    // by the same amount, so p is exactly 1 at the new maximum.  Masked
+    // positions (only in tiles that reach past the workgroup's first row)
+    // become -inf, so p = 0.
     const bool masked = k0 + kTk - 1 > pos_first;
-    float mu[RS];
 #pragma unroll
     for (int r = 0; r < RS; ++r) {
       if (masked) {
@@ -465,19 +469,24 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) cm = fmaxf(cm, sc[r][tb][i]);
-      cm = group_max4(cm);
-      // wave-uniform branch (lanes that need no rescale scale by exactly
-      // 1), so the accumulators are updated in place
-      const bool up = cm > m[r] + slack;  // false while both are -inf
+      cm = group_max4(cm);  // relative to m (raw while m is -inf)
+      const bool first = m[r] == neg_inf();
+      // the tile's maximum passes m + slack (any finite score while m is
+      // -inf); wave-uniform branch (lanes that need no rescale scale by
+      // exactly 1 and shift by 0), so the accumulators are updated in place
+      const bool up = first ? cm > neg_inf() : cm > slack;
       if (__builtin_amdgcn_ballot_w64(up)) {
-        const float alpha =
-            up ? __builtin_amdgcn_exp2f((m[r] - cm) * sl2) : 1.f;  // 0 when m was -inf
+        // 0 when m was -inf (nothing accumulated yet)
+        const float alpha = up ? (first ? 0.f : __builtin_amdgcn_exp2f(-cm * sl2)) : 1.f;
+        const float shift = up ? cm : 0.f;
         lsum[r] *= alpha;
 #pragma unroll
         for (int b = 0; b < kDb; ++b) acc[r][b] *= alpha;
-        m[r] = up ? cm : m[r];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) sc[r][tb] -= shift;
+        m[r] = up ? (first ? cm : m[r] + cm) : m[r];
+        seed[r] = up ? f32x4{-m[r], -m[r], -m[r], -m[r]} : seed[r];
       }
-      mu[r] = (m[r] == neg_inf()) ? 0.f : m[r];
     }
 
     // The scores of tile it + 1 on the matrix cores while the vector unit
@@ -499,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
           for (int u = 0; u < 2; ++u) {
             const int jj = j + u;
             const int tb = 2 * kk + (jj >> 2);
-            pr[u] = __builtin_amdgcn_exp2f((sc[r][tb][jj & 3] - mu[r]) * sl2);
+            pr[u] = __builtin_amdgcn_exp2f(sc[r][tb][jj & 3] * sl2);
           }
           lsum[r] += pr[0] + pr[1];
           const uint32_t h = bf16x2_bits(pr[0], pr[1]);
