@@ -122,7 +122,8 @@ constexpr int kMqPrefixMembers = 16;
 // least two members (measured on the speculative-verification structure,
 // G = 4: 1 and 2 tokens per sequence gain 17% and 7%, 3 break even, 5 lose
 // 10%: each item walks the whole prefix, and L2 already serves most of the
-// members' repeated reads).
+// members' repeated reads).  Items of two column sets (32 rows, one pass per
+// two members at 5 tokens) lost too: 3, 4, 5 and 8 tokens 7-29% slower.
 constexpr int64_t kMqPrefixRows = 8;
 // Prefix items per group of such a call: each covers 16 (member, token,
 // head) rows.

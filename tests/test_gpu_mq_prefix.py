@@ -115,7 +115,8 @@ def compare(c, groups, shared, name, ps=0):
 
 @pytest.mark.parametrize("G,Hkv,maxq", [(4, 8, 2), (4, 2, 2), (8, 4, 1), (8, 1, 1),
                                          (2, 4, 4), (1, 8, 8), (4, 8, 1),
-                                         (4, 8, 5), (1, 8, 16)])  # the last two: plain
+                                         (4, 8, 5), (1, 8, 16), (4, 8, 8), (8, 4, 4),
+                                         (2, 4, 13), (1, 8, 12), (4, 8, 9)])
 @pytest.mark.parametrize("ps", [0, -1, 64, 512])
 def test_prefix_workloads(G, Hkv, maxq, ps):
     """Prefix groups of 16 sequences (lengths below, at and past the 1024-token
