@@ -283,15 +283,17 @@ size_t paged_attention_noalloc_scratch_bytes(void);
  * k_cache and v_cache hold one E4M3 code per element in the layout above; an
  * element's value is e4m3(code) * k_scale (K) or * v_scale (V), so the
  * result is that of paged_attention_decode on the dequantised pool.  q is
- * bfloat16.  Both products run on the bfloat16 matrix cores with fp32
- * accumulation: K and V codes are widened exactly to bfloat16 (an E4M3 value
- * has at most 4 significant bits), and the probabilities enter p.V as a pair
- * of bfloat16 values hi + lo (about 16 significant bits); k_scale joins the
- * softmax scale and v_scale multiplies the output.  Every other argument, the workspace (same size as
- * paged_attention_decode's) and the partition policy are those of
- * paged_attention_decode.
- * Supported: head_dim 128, G in {1, 2, 4, 8}; k_scale and v_scale finite and
- * > 0.
+ * bfloat16.  K and V codes are widened exactly to bfloat16 (an E4M3 value
+ * has at most 4 significant bits).  At head_dim 128 both products run on the
+ * bfloat16 matrix cores with fp32 accumulation, and the probabilities enter
+ * p.V as a pair of bfloat16 values hi + lo (about 16 significant bits); at
+ * head_dim 64 the vector kernel forms q.k with paired bfloat16 dot products
+ * and p.V with fp32 fused multiply-adds.  k_scale joins the softmax scale
+ * and v_scale multiplies the output.  Every other argument, the workspace
+ * (same size as paged_attention_decode's) and the partition policy are those
+ * of paged_attention_decode.
+ * Supported: head_dim 64 or 128, G in {1, 2, 4, 8}; k_scale and v_scale
+ * finite and > 0.
  * Errors: as paged_attention_decode.
  */
 int32_t paged_attention_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
@@ -308,7 +310,8 @@ int32_t paged_attention_decode_fp8(const void *q, const void *k_cache, const voi
  * pool ([P3] architecture figure: FP8/INT8 quantisation): an element's value
  * is code * k_scale (K) or * v_scale (V), the code a signed byte.  Codes are
  * widened exactly to bfloat16 (at most 7 significant bits) for both products,
- * with the probabilities entering p.V as a bfloat16 pair, as for FP8.
+ * with the probabilities entering p.V as a bfloat16 pair at head_dim 128, as
+ * for FP8.
  * Arguments, support and errors are those of paged_attention_decode_fp8.
  */
 int32_t paged_attention_decode_int8(const void *q, const void *k_cache, const void *v_cache,

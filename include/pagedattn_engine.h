@@ -153,8 +153,8 @@ typedef struct pa_step_info {
 
 /* Creates an engine over the caller's pool (device pointers laid out as in
  * pagedattn.h; ignored when cfg->device is 0).  *out receives the engine.
- * dtype PA_FP8_E4M3 or PA_INT8 needs head_dim 128 (the 8-bit decode) and
- * valid scales; other dtypes ignore the scales.
+ * dtype PA_FP8_E4M3 or PA_INT8 needs head_dim 64 or 128 (the 8-bit decode)
+ * and valid scales; other dtypes ignore the scales.
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_DTYPE, PA_ERR_UNSUPPORTED, PA_ERR_OOM
  * (host or device allocation failed), PA_ERR_LAUNCH. */
 int32_t pa_engine_create(const pa_engine_config *cfg, void *k_cache, void *v_cache,

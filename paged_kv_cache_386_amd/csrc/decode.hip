@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace pa {
@@ -70,6 +72,32 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                          __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Sixteen 8-bit codes (one 16-byte vector, code i in byte i) to sixteen
+// bfloat16 values, exactly (an E4M3 value has at most 4 significant bits, an
+// INT8 code at most 7): pair word j holds elements 2 j (low half) and 2 j + 1.
+// FP8 (Q8 = 1) through gfx950's scaled conversion at scale 1, two codes per
+// instruction; INT8 (Q8 = 2) widened to fp32, whose high halves are the
+// bfloat16 values, paired with one byte permute.
+template <int Q8>
+__device__ __forceinline__ void codes16_to_bf16(u32x4 w, uint32_t (&b)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (Q8 == 1) {
+      b[2 * i] = __builtin_bit_cast(uint32_t,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, false));
+      b[2 * i + 1] = __builtin_bit_cast(uint32_t,
+                                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.f, true));
+    } else {
+      float f[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[j] = (float)((int32_t)(w[i] << (24 - 8 * j)) >> 24);
+      b[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+      b[2 * i + 1] =
+          __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
+    }
+  }
 }
 
 // DPP lane moves inside a row of 16 lanes.
@@ -111,11 +139,16 @@ struct Shape {
   static_assert(TPL >= 1 && kChunk % ROWS == 0, "chunk must cover whole rows");
 };
 
-template <typename T, int D, int G, bool SMALLB>
+// Q8: the pool's element kind -- 0 the type T itself (fp32 or bfloat16), 1
+// FP8 (E4M3) or 2 INT8 codes (T = uint8_t, 16 per vector), each vector
+// widened to bfloat16 pairs when it is computed; q is then bfloat16, held as
+// QW = 2 vectors per code vector.
+template <typename T, int D, int G, bool SMALLB, int Q8 = 0>
 struct Decode {
   using S = Shape<T, D, G>;
   static constexpr int TPL = S::TPL, VPL = S::VPL, LPR = S::LPR, ROWS = S::ROWS,
                        EPV = S::EPV, DPL = S::DPL;
+  static constexpr int QW = Q8 ? 2 : 1;
 
   struct Regs {
     u32x4 k[TPL][VPL];
@@ -209,10 +242,18 @@ struct Decode {
 
   // Fold one chunk into this row's running (max, sum, accumulator).
   template <bool MASK>
-  static __device__ __forceinline__ void compute(const Regs &R, const u32x4 (&qv)[G][VPL],
+  static __device__ __forceinline__ void compute(const Regs &R, const u32x4 (&qv)[G][VPL * QW],
                                                  float (&acc)[G][DPL], float (&m)[G],
                                                  float (&l)[G], int cs, int t1, int r,
                                                  float sl2) {
+    // 8-bit codes: each K vector as 8 bfloat16 pairs, shared by the G heads
+    uint32_t kb[TPL][VPL][Q8 ? 8 : 1];
+    if constexpr (Q8 != 0) {
+#pragma unroll
+      for (int k = 0; k < TPL; ++k)
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) codes16_to_bf16<Q8>(R.k[k][v], kb[k][v]);
+    }
     float x[TPL][G];
 #pragma unroll
     for (int k = 0; k < TPL; ++k) {
@@ -221,12 +262,17 @@ struct Decode {
         float d = 0.f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
+          if constexpr (Q8 != 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (sizeof(T) == 2)
-              d = dot2_bf16(qv[h][v][i], R.k[k][v][i], d);
-            else
-              d = fmaf(__uint_as_float(qv[h][v][i]), __uint_as_float(R.k[k][v][i]), d);
+            for (int j = 0; j < 8; ++j) d = dot2_bf16(qv[h][2 * v + j / 4][j % 4], kb[k][v][j], d);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (sizeof(T) == 2)
+                d = dot2_bf16(qv[h][v][i], R.k[k][v][i], d);
+              else
+                d = fmaf(__uint_as_float(qv[h][v][i]), __uint_as_float(R.k[k][v][i]), d);
+            }
           }
         }
         d = row_sum<LPR>(d);
@@ -257,6 +303,20 @@ struct Decode {
     for (int k = 0; k < TPL; ++k) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
+        if constexpr (Q8 != 0) {
+          uint32_t vb[8];
+          codes16_to_bf16<Q8>(R.v[k][v], vb);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float lo = bf16_lo(vb[j]), hi = bf16_hi(vb[j]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              acc[h][v * EPV + 2 * j] = fmaf(p[k][h], lo, acc[h][v * EPV + 2 * j]);
+              acc[h][v * EPV + 2 * j + 1] = fmaf(p[k][h], hi, acc[h][v * EPV + 2 * j + 1]);
+            }
+          }
+          continue;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t w = R.v[k][v][i];
@@ -278,15 +338,19 @@ struct Decode {
   }
 };
 
-template <typename T, int D, int G, bool SMALLB>
+// (8-bit pools: q is bfloat16, the K scale is part of sl2 and the V scale
+// multiplies the normalised output)
+template <typename T, int D, int G, bool SMALLB, int Q8 = 0>
 __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
-    const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
+    const typename std::conditional<Q8 != 0, uint16_t, T>::type *__restrict__ q,
+    const T *__restrict__ kc, const T *__restrict__ vc,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
     float *__restrict__ out, float *__restrict__ ws_o, float *__restrict__ ws_ml, float sl2,
-    int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P,
+    float v_scale, int num_seqs, int hkv, int lgB, int nb, int mb, int ps, int P,
     const int32_t *__restrict__ order) {
-  using K = Decode<T, D, G, SMALLB>;
+  using K = Decode<T, D, G, SMALLB, Q8>;
   constexpr int TPL = K::TPL, VPL = K::VPL, LPR = K::LPR, EPV = K::EPV, DPL = K::DPL;
+  constexpr int QW = K::QW;
   (void)TPL;
 
   // Work item: KV head fastest, then item = (sequence, partition), from
@@ -318,13 +382,17 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
   const int32_t *tbl = block_tables + (int64_t)s * mb;
   const bool has_prev = s > 0, has_next = s + 1 < num_seqs;
 
-  u32x4 qv[G][VPL];
+  // this lane's elements of q: the EPV elements of each of its VPL vectors
+  // (QW 16-byte vectors of q per vector of the pool)
+  u32x4 qv[G][VPL * QW];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const u32x4 *qp =
-        reinterpret_cast<const u32x4 *>(q + ((int64_t)s * hq + kvh * G + h) * D) + c;
+        reinterpret_cast<const u32x4 *>(q + ((int64_t)s * hq + kvh * G + h) * D) + QW * c;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) qv[h][v] = qp[LPR * v];
+    for (int v = 0; v < VPL; ++v)
+#pragma unroll
+      for (int w = 0; w < QW; ++w) qv[h][QW * v + w] = qp[QW * LPR * v + w];
   }
 
   float acc[G][DPL];
@@ -438,9 +506,9 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(
     }
     const int64_t row = (int64_t)s * hq + kvh * G + h;
     if (final_out) {
-      out[row * D + d] = lsum > 0.f ? o / lsum : 0.f;
+      out[row * D + d] = lsum > 0.f ? (Q8 ? v_scale * (o / lsum) : o / lsum) : 0.f;
     } else {
-      ws_o[(row * P + p) * D + d] = o / lsum;
+      ws_o[(row * P + p) * D + d] = Q8 ? v_scale * (o / lsum) : o / lsum;
       if (d == 0) {
         ws_ml[(row * P + p) * 2 + 0] = M;
         ws_ml[(row * P + p) * 2 + 1] = lsum;
@@ -532,15 +600,18 @@ __global__ __launch_bounds__(64 * kMergeRows) void paged_decode_merge_kernel(
     out[(int64_t)row * D + lane * EPL + e] = den > 0.f ? num[e] / den : 0.f;
 }
 
-template <typename T, int D, int G, bool SMALLB>
+template <typename T, int D, int G, bool SMALLB, int Q8>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+  using QT = typename std::conditional<Q8 != 0, uint16_t, T>::type;
   const int64_t grid = (int64_t)a.num_seqs * a.num_kv_heads * a.num_partitions;
   if (grid <= 0) return hipSuccess;
-  const float sl2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, G, SMALLB>), dim3((uint32_t)grid), dim3(kThreads),
-                     0, stream, static_cast<const T *>(a.q), static_cast<const T *>(a.k_cache),
-                     static_cast<const T *>(a.v_cache), a.block_tables, a.context_lens, a.out,
-                     a.ws_o, a.ws_ml, sl2, a.num_seqs, a.num_kv_heads, a.log2_block_size,
+  // 8-bit pools: the K scale joins the softmax scale
+  const float sl2 = a.scale * (Q8 ? a.k_scale : 1.f) * kLog2e;
+  hipLaunchKernelGGL((paged_decode_kernel<T, D, G, SMALLB, Q8>), dim3((uint32_t)grid),
+                     dim3(kThreads), 0, stream, static_cast<const QT *>(a.q),
+                     static_cast<const T *>(a.k_cache), static_cast<const T *>(a.v_cache),
+                     a.block_tables, a.context_lens, a.out, a.ws_o, a.ws_ml, sl2,
+                     Q8 ? a.v_scale : 1.f, a.num_seqs, a.num_kv_heads, a.log2_block_size,
                      a.num_blocks, a.max_blocks_per_seq, a.partition_size, a.num_partitions,
                      a.order);
   hipError_t e = hipGetLastError();
@@ -548,19 +619,19 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
   return launch_partition_merge(a, stream);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int Q8>
 hipError_t launch_b(const DecodeArgs &a, hipStream_t stream) {
-  if (a.log2_block_size >= 4) return launch_typed<T, D, G, false>(a, stream);
-  return launch_typed<T, D, G, true>(a, stream);
+  if (a.log2_block_size >= 4) return launch_typed<T, D, G, false, Q8>(a, stream);
+  return launch_typed<T, D, G, true, Q8>(a, stream);
 }
 
-template <typename T, int D>
+template <typename T, int D, int Q8 = 0>
 hipError_t launch_g(const DecodeArgs &a, hipStream_t stream) {
   switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_b<T, D, 1>(a, stream);
-    case 2: return launch_b<T, D, 2>(a, stream);
-    case 4: return launch_b<T, D, 4>(a, stream);
-    case 8: return launch_b<T, D, 8>(a, stream);
+    case 1: return launch_b<T, D, 1, Q8>(a, stream);
+    case 2: return launch_b<T, D, 2, Q8>(a, stream);
+    case 4: return launch_b<T, D, 4, Q8>(a, stream);
+    case 8: return launch_b<T, D, 8, Q8>(a, stream);
     default: return hipErrorNotSupported;
   }
 }
@@ -618,8 +689,15 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
         pfx && short_members(a.kv_dtype));
     if (e != hipSuccess) return e;
   }
-  if (a.kv_dtype == 2 || a.kv_dtype == 3 ||  // 8-bit pools: matrix-core kernel only
-      pfx ||                                  // so are shared-prefix items
+  const bool q8 = a.kv_dtype == 2 || a.kv_dtype == 3;
+  // 8-bit pools at head_dim 64 (no shared-prefix items there): the vector
+  // kernel, widening each vector of codes as it computes it
+  if (q8 && a.head_dim == 64 && !pfx) {
+    if (a.kv_dtype == 2) return launch_g<uint8_t, 64, 1>(a, stream);
+    return launch_g<uint8_t, 64, 2>(a, stream);
+  }
+  if (q8 ||  // other 8-bit pools: the matrix-core kernel
+      pfx ||  // so are shared-prefix items
       decode_mfma_supported(a.dtype, a.head_dim, G))
     return launch_decode_mfma(a, stream);
   if (a.dtype == 0) return launch_d<float>(a, stream);

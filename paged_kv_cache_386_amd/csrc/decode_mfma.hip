@@ -1036,7 +1036,9 @@ bool decode_prefix_supported(int32_t head_dim, int32_t group) {
 }
 
 bool decode_q8_supported(int32_t head_dim, int32_t group) {
-  return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);
+  // head_dim 64 runs on the vector kernel (decode.hip)
+  return (head_dim == kD || head_dim == 64) &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
 template <int G>

@@ -226,7 +226,8 @@ def test_engine_create_rejects_bad_configs():
     assert create(dtype=pa.PA_INT8, k_scale=0.02, v_scale=0.03) == 0
     assert create(dtype=pa.PA_FP8_E4M3, k_scale=0.0) == -2
     assert create(dtype=pa.PA_INT8, v_scale=float("inf")) == -2
-    assert create(dtype=pa.PA_FP8_E4M3, head_dim=64, k_scale=0.25, v_scale=0.5) == -4
+    assert create(dtype=pa.PA_FP8_E4M3, head_dim=64, k_scale=0.25, v_scale=0.5) == 0
+    assert create(dtype=pa.PA_FP8_E4M3, head_dim=96, k_scale=0.25, v_scale=0.5) == -4
     assert lib.pa_engine_create(None, None, None, None) == -1
 
 

@@ -2,7 +2,8 @@
 quantising write bit for bit (ties, clamping, NaN, negative slots), every
 code read back exactly through decode, INT8 decode against the oracle on
 private, prefix-shared and forked pools at several block and partition
-sizes, and the full-size GQA prefix workload (every output element)."""
+sizes and at head_dim 64 and 128, and the full-size GQA prefix workload (every
+output element)."""
 import numpy as np
 import pytest
 import torch
@@ -116,6 +117,45 @@ def test_every_code_reads_back_exactly():
     for s in range(S):
         want = row[s].astype(np.float64) * 0.25
         assert np.array_equal(got[s], np.repeat(want, 4, axis=0).astype(np.float32))
+
+
+def test_every_code_reads_back_exactly_head_dim_64():
+    """The same at head_dim 64 (the vector kernel, 16 codes per lane vector)."""
+    codes = np.arange(-127, 128, dtype=np.int8)
+    S = 2
+    base = make_private_case("i8-codes-64", [1] * S, 8, 2, 64, 16, "bf16", 9)
+    c8 = make_int8_case(base, 9, v_scale=0.25)
+    row = np.resize(codes, S * 2 * 64).reshape(S, 2, 64)
+    for s in range(S):
+        c8.v8[base.block_tables[s, 0], :, 0] = row[s]
+    got = run_decode_int8(c8)
+    for s in range(S):
+        want = row[s].astype(np.float64) * 0.25
+        assert np.array_equal(got[s], np.repeat(want, 4, axis=0).astype(np.float32))
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("B", [1, 4, 16, 512])
+def test_decode_head_dim_64(G, Hkv, B):
+    """head_dim 64: the vector kernel, each 16-byte vector of codes widened to
+    bfloat16 as it is computed; NaN-poisoned slots past every context."""
+    lens = [1, 15, 16, 17, 63, 64, 65, 200, 513, 1030]
+    base = make_private_case(f"i8-d64-{G}-{B}", lens, G * Hkv, Hkv, 64, B, "bf16", 70 + G + B)
+    c8 = make_int8_case(base, 70 + G + B)
+    ref = oracle_decode(c8)
+    for ps in (0, -1, 64):
+        say(f"int8 decode D=64 G={G} B={B} ps={ps}")
+        err = max_err(run_decode_int8(c8, ps), ref)
+        assert err <= TOL["bf16"] and err <= REGRESS["bf16"], f"G={G} B={B} ps={ps}: {err}"
+
+
+@pytest.mark.parametrize("ps", [-1, 0])
+def test_decode_head_dim_64_long_contexts(ps):
+    base = make_private_case("i8-d64-long", [9000, 20001, 3], 16, 4, 64, 16, "bf16", 77)
+    c8 = make_int8_case(base, 77)
+    say(f"int8 decode D=64 long contexts ps={ps}")
+    err = max_err(run_decode_int8(c8, ps), oracle_decode(c8))
+    assert err <= TOL["bf16"] and err <= REGRESS["bf16"], f"ps={ps}: {err}"
 
 
 @pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2), (8, 1)])
