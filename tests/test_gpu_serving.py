@@ -112,16 +112,17 @@ def test_engine_steps_match_oracle(dtype, Hq, Hkv, D, B, NB, ps, host_plan):
 
 
 @pytest.mark.parametrize("kv8", ["fp8", "int8"])
-@pytest.mark.parametrize("Hq,Hkv,NB,ps", [(32, 8, 800, 0), (8, 8, 800, 64), (32, 8, 90, 0)])
-def test_engine_8bit_pools(kv8, Hq, Hkv, NB, ps):
+@pytest.mark.parametrize("Hq,Hkv,NB,ps,D", [(32, 8, 800, 0, 128), (8, 8, 800, 64, 128),
+                                            (32, 8, 90, 0, 128), (16, 4, 90, 0, 64)])
+def test_engine_8bit_pools(kv8, Hq, Hkv, NB, ps, D):
     """The engine over an FP8 / INT8 pool: bfloat16 token rows quantised by
     its writes; after every step the pool holds the oracle's codes of each
     row's tokens and decode matches dense attention over their dequantised
     values (forks sharing prompt blocks, copy-on-write, preemption in the
-    small pool)."""
+    small pools; head_dim 64 on the vector decode kernel)."""
     from serving_loop import EngineHarness, drive_engine
-    say(f"engine {kv8} Hq={Hq} Hkv={Hkv} NB={NB} ps={ps}")
-    h = EngineHarness("device", "bf16", Hq, Hkv, 128, 16, NB, max_batch=48, max_ctx=400,
+    say(f"engine {kv8} Hq={Hq} Hkv={Hkv} NB={NB} ps={ps} D={D}")
+    h = EngineHarness("device", "bf16", Hq, Hkv, D, 16, NB, max_batch=48, max_ctx=400,
                       seed=NB + Hq, partition_size=ps, kv8=kv8)
     drive_engine(h, num_requests=36, seed=NB + Hq, max_prompt=300, max_new=40)
     assert h.copies > 0
