@@ -579,15 +579,28 @@ def multi_query_bench(args) -> int:
             b.num_seqs, c.num_tokens, b.num_q_heads, b.num_kv_heads, b.head_dim,
             c.max_query_len, max_ctx, args.partition_size)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    # the dispatch list planned on the host, once (the lengths and groups are
+    # the host's); --device-sort sorts on the device in every call instead
+    plan_d = None
+    if not args.device_sort:
+        plan = pa.multi_query_plan(
+            b.context_lens, groups_np if use_prefix else None, shared_np if use_prefix else None,
+            num_q_heads=b.num_q_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
+            block_size=b.block_size, max_blocks_per_seq=b.block_tables.shape[1],
+            max_query_len=c.max_query_len, max_context_len=max_ctx, kv_dtype=kv_code,
+            partition_size=args.partition_size)
+        plan_d = torch.from_numpy(plan).to(dev)
 
     def call():
-        if use_prefix:
+        if use_prefix or plan_d is not None:
             pa.paged_attention_multi_query_prefix(
-                q, kc, vc, tables, lens, qs, groups_d, shared_d, float(b.scale), out,
+                q, kc, vc, tables, lens, qs, groups_d if use_prefix else None,
+                shared_d if use_prefix else None, float(b.scale), out,
                 max_query_len=c.max_query_len, max_context_len=max_ctx,
                 k_scale=1.0 if c8 is None else float(c8.k_scale),
                 v_scale=1.0 if c8 is None else float(c8.v_scale),
-                partition_size=args.partition_size, workspace=ws, stream=stream)
+                partition_size=args.partition_size, workspace=ws, dispatch=plan_d,
+                stream=stream)
         elif c8 is not None:
             mq8 = (pa.paged_attention_multi_query_fp8 if args.kv_fp8 else
                    pa.paged_attention_multi_query_int8)
@@ -667,9 +680,13 @@ def multi_query_bench(args) -> int:
                             "ignored: prefix items take bf16 pools with at most 8 rows per "
                             "sequence and KV head)"
                             if use_prefix else
+                            "paged_attention_multi_query_prefix with no groups (the plain "
+                            "call)" if plan_d is not None else
                             "paged_attention_multi_query" + ("" if c8 is None else
                                                              "_fp8" if args.kv_fp8 else
-                                                             "_int8"))},
+                                                             "_int8"))
+                           + ("; dispatch list planned on the host" if plan_d is not None else
+                              "; dispatch list sorted on the device")},
         "attended_pairs_per_s": round(attended * Hq / (us * 1e-6), 1),
         "query_tokens_per_s": round(c.num_tokens / (us * 1e-6), 1),
         "kernel_us": round(us, 2),
@@ -731,7 +748,8 @@ def main() -> int:
                          "kv_cache_write_fp8 / _int8) instead of one kv_cache_append launch")
     ap.add_argument("--device-sort", action="store_true",
                     help="sort the work on the device in every call instead of passing the "
-                         "dispatch list planned on the host (paged_attention_decode_plan)")
+                         "dispatch list planned on the host (paged_attention_decode_plan, "
+                         "paged_attention_multi_query_plan for --multi-query)")
     ap.add_argument("--verify-tokens", type=int, default=5,
                     help="--multi-query spec-verify: tokens to verify per sequence")
     ap.add_argument("--no-prefix", action="store_true",

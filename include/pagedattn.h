@@ -480,6 +480,14 @@ int32_t paged_attention_multi_query_int8(const void *q, const void *k_cache, con
  *   num_groups,
  *   shared_lens    as in paged_attention_decode_prefix, with at most 16
  *                  members per group (pa_prefix_groups with max_members 16)
+ *   dispatch       device int32 list of the launch's work items in the order
+ *                  to run them, as paged_attention_multi_query_plan writes
+ *                  it for the same arguments (planned on the host instead of
+ *                  sorted on the device each call), or NULL to sort on the
+ *                  device when the launch is large enough.  The order changes
+ *                  timing only; the list must hold every item of the launch
+ *                  exactly once (entries that are not an item of it are
+ *                  skipped and their outputs go unwritten)
  *   kv_dtype       PA_BF16, PA_FP8_E4M3 or PA_INT8 (q bfloat16; k_scale and
  *                  v_scale as in paged_attention_multi_query_fp8, ignored for
  *                  PA_BF16); prefix items over bf16 pools only (over 8-bit
@@ -497,7 +505,7 @@ int32_t paged_attention_multi_query_int8(const void *q, const void *k_cache, con
  * ascending position order.  With more rows per member an item covers too
  * few members for the shared walk to pay (each item walks the whole prefix):
  * there, as with num_groups 0, the call is the plain one and the groups are
- * ignored.
+ * ignored (a dispatch list still applies).
  * Supported and errors: as paged_attention_multi_query (and its FP8 / INT8
  * forms); PA_ERR_SHAPE for num_groups outside [0, num_seqs], PA_ERR_NULL for
  * missing groups or shared lengths.  Groups and shared lengths that break the
@@ -507,11 +515,40 @@ int32_t paged_attention_multi_query_int8(const void *q, const void *k_cache, con
 int32_t paged_attention_multi_query_prefix(
     const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
     const int32_t *context_lens, const int32_t *query_start, const int32_t *prefix_groups,
-    int32_t num_groups, const int32_t *shared_lens, float scale, float k_scale, float v_scale,
-    float *out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-    int32_t max_query_len, int32_t max_context_len, int32_t kv_dtype, int32_t partition_size,
-    void *workspace, size_t workspace_bytes, void *stream);
+    int32_t num_groups, const int32_t *shared_lens, const int32_t *dispatch, float scale,
+    float k_scale, float v_scale, float *out, int32_t num_seqs, int32_t num_tokens,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+    int32_t max_context_len, int32_t kv_dtype, int32_t partition_size, void *workspace,
+    size_t workspace_bytes, void *stream);
+
+/*
+ * paged_attention_multi_query_plan -- the dispatch list of
+ * paged_attention_multi_query_prefix for these arguments, computed on the
+ * host: every work item of the launch (the (sequence, partition) items, then
+ * the groups' prefix items when the prefix path runs), longest first by
+ * tokens to attend (a sequence item its private positions in its partition,
+ * a prefix item its group's longest shared length), equal sizes in item
+ * order, items with no work last -- the order the device sort gives, with
+ * exact token counts instead of size classes.
+ *
+ *   context_lens, prefix_groups, shared_lens   host copies of the device
+ *                  arrays the call will get (groups and shared lengths may
+ *                  be NULL when num_groups is 0)
+ *   dispatch       host int32 out, capacity entries
+ * Every other argument is paged_attention_multi_query_prefix's.  Returns the
+ * number of entries written, or PA_ERR_NULL, PA_ERR_SHAPE (including
+ * capacity too small), PA_ERR_DTYPE.
+ */
+int32_t paged_attention_multi_query_plan(const int32_t *context_lens,
+                                         const int32_t *prefix_groups, int32_t num_groups,
+                                         const int32_t *shared_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int32_t max_query_len,
+                                         int32_t max_context_len, int32_t kv_dtype,
+                                         int32_t partition_size, int32_t *dispatch,
+                                         int32_t capacity);
 
 /* Workspace bytes paged_attention_multi_query_prefix needs: with the prefix
  * path, 4 * num_tokens * num_q_heads * (P + 1) * (head_dim + 2) for the

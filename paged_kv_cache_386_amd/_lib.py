@@ -60,9 +60,11 @@ SIGNATURES = {
     "paged_attention_multi_query_partitions": (_I32, [_I32] * 6),
     "paged_attention_multi_query_workspace_size": (ctypes.c_size_t, [_I32] * 8),
     "paged_attention_multi_query_prefix": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP,
-                                                  ctypes.c_float, ctypes.c_float, ctypes.c_float,
-                                                  _VP] + [_I32] * 12 + [_VP, ctypes.c_size_t,
-                                                                       _VP]),
+                                                  _VP, ctypes.c_float, ctypes.c_float,
+                                                  ctypes.c_float, _VP] + [_I32] * 12 +
+                                           [_VP, ctypes.c_size_t, _VP]),
+    "paged_attention_multi_query_plan": (_I32, [_VP, _VP, _I32, _VP] + [_I32] * 10 +
+                                         [_VP, _I32]),
     "paged_attention_multi_query_prefix_workspace_size": (ctypes.c_size_t, [_I32] * 10),
     "paged_attention_decode_fp8": (_I32, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float,
                                           ctypes.c_float, ctypes.c_float, _VP, _I32, _I32, _I32,
@@ -434,12 +436,14 @@ def paged_attention_multi_query_prefix(q, k_cache, v_cache, block_tables, contex
                                        query_start, groups, shared_lens, scale: float, out, *,
                                        max_query_len: int, max_context_len: int,
                                        k_scale: float = 1.0, v_scale: float = 1.0,
-                                       partition_size: int = 0, workspace=None,
+                                       partition_size: int = 0, workspace=None, dispatch=None,
                                        stream=None) -> None:
     """paged_attention_multi_query for a batch whose sequences share prefix
     blocks (include/pagedattn.h): ``groups`` int32 [n, 2] (first sequence,
     members) and ``shared_lens`` int32 [S] on the device, as pa_prefix_groups
-    gives them.  The pool's dtype picks bf16, FP8 or INT8; q is bfloat16."""
+    gives them (None and 0 groups: the plain call).  The pool's dtype picks
+    bf16, FP8 or INT8; q is bfloat16.  ``dispatch``: a device int32 list from
+    multi_query_plan, or None to sort on the device."""
     import torch
     T, Hq, D = q.shape
     NB, Hkv, B, D2 = k_cache.shape
@@ -451,7 +455,7 @@ def paged_attention_multi_query_prefix(q, k_cache, v_cache, block_tables, contex
     MB = block_tables.shape[1] if block_tables.dim() == 2 else 0
     ng = int(groups.shape[0]) if groups is not None and groups.dim() == 2 else 0
     for t in (q, k_cache, v_cache, block_tables, context_lens, query_start, out, groups,
-              shared_lens):
+              shared_lens, dispatch):
         if t is not None and not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
     kv = _dtype_code(k_cache)
@@ -463,10 +467,42 @@ def paged_attention_multi_query_prefix(q, k_cache, v_cache, block_tables, contex
     st = lib().paged_attention_multi_query_prefix(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(query_start), _ptr(groups) if ng else None, ng,
-        _ptr(shared_lens) if ng else None, float(scale), float(k_scale), float(v_scale),
+        _ptr(shared_lens) if ng else None, _ptr(dispatch) if dispatch is not None else None,
+        float(scale), float(k_scale), float(v_scale),
         _ptr(out), S, T, Hq, Hkv, D, B, NB, MB, int(max_query_len), int(max_context_len), kv,
         int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
     _check("paged_attention_multi_query_prefix", st)
+
+
+def multi_query_plan(context_lens, groups, shared_lens, *, num_q_heads: int, num_kv_heads: int,
+                     head_dim: int, block_size: int, max_blocks_per_seq: int,
+                     max_query_len: int, max_context_len: int, kv_dtype: int,
+                     partition_size: int = 0):
+    """The dispatch list of paged_attention_multi_query_prefix planned on the
+    host (paged_attention_multi_query_plan): numpy int32.  ``context_lens``,
+    ``groups`` ([n, 2] or None) and ``shared_lens`` are host arrays."""
+    import numpy as np
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = int(lens.shape[0])
+    ng = 0 if groups is None else int(len(groups))
+    g = np.ascontiguousarray(groups if ng else np.zeros((1, 2)), dtype=np.int32)
+    sh = np.ascontiguousarray(shared_lens if ng else np.zeros(max(S, 1)), dtype=np.int32)
+    P = multi_query_partitions(S, num_q_heads, num_kv_heads, max_query_len, max_context_len,
+                               partition_size)
+    if P < 0:
+        raise PagedAttnError("paged_attention_multi_query_partitions", P)
+    G = num_q_heads // num_kv_heads
+    per = max_query_len * G
+    cap = max(S * P + ng * per, 1)  # at least the prefix items a group can have
+    out = np.zeros(cap, np.int32)
+    n = lib().paged_attention_multi_query_plan(
+        lens.ctypes.data, g.ctypes.data if ng else 0, ng, sh.ctypes.data if ng else 0, S,
+        num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        int(max_query_len), int(max_context_len), int(kv_dtype), int(partition_size),
+        out.ctypes.data, cap)
+    if n < 0:
+        raise PagedAttnError("paged_attention_multi_query_plan", n)
+    return out[:n].copy()
 
 
 def _multi_query_q8(fn, pool_dtype, q, k_cache, v_cache, block_tables, context_lens,

@@ -459,6 +459,29 @@ int32_t paged_attention_decode_prefix(const void *q, const void *k_cache, const 
                      pfx ? shared_lens : nullptr, dispatch);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The dispatch list of n items, longest first by tokens_of(c) (the tokens an
+// item attends, -1 when it does no work): sort keys hold (tokens + 1) in the
+// high word, complemented so that larger counts come first, and the item
+// number in the low word, so equal counts keep item order and items with no
+// work sort last.
+template <typename F>
+void plan_longest_first(int64_t n, F tokens_of, int32_t *dispatch) {
+  std::vector<uint64_t> keys((size_t)n);
+  for (int64_t c = 0; c < n; ++c)
+    keys[(size_t)c] =
+        ((uint64_t)(0xFFFFFFFFu - (uint32_t)(tokens_of(c) + 1)) << 32) | (uint32_t)c;
+  std::sort(keys.begin(), keys.end());
+  for (int64_t i = 0; i < n; ++i) dispatch[i] = (int32_t)(keys[(size_t)i] & 0xFFFFFFFFu);
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *prefix_groups,
                                     int32_t num_groups, const int32_t *shared_lens,
                                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -495,11 +518,9 @@ int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *
   auto shared_of = [&](int32_t s, int32_t L) {
     return ng > 0 ? (std::min(std::max(shared_lens[s], 0), L) & ~15) : 0;
   };
-  // sort keys: (tokens + 1) in the high word, complemented so that larger
-  // counts come first, the item number in the low word (equal counts keep
-  // item order; no work, tokens = -1, sorts last)
-  std::vector<uint64_t> keys((size_t)n);
-  for (int64_t c = 0; c < n; ++c) {
+  // longest first; equal sizes keep item order (members of a prefix group and
+  // the column sets of one group stay side by side); items with no work last
+  plan_longest_first(n, [&](int64_t c) -> int64_t {
     int64_t tokens;
     if (c < (int64_t)num_seqs * P) {
       const int32_t s = (int32_t)(c % num_seqs);
@@ -531,12 +552,72 @@ int32_t paged_attention_decode_plan(const int32_t *context_lens, const int32_t *
       }
       if (tokens > 0 && extra) tokens += 16;
     }
-    keys[(size_t)c] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)(tokens + 1)) << 32) | (uint32_t)c;
-  }
-  // longest first; equal sizes keep item order (members of a prefix group and
-  // the column sets of one group stay side by side); items with no work last
-  std::sort(keys.begin(), keys.end());
-  for (int64_t i = 0; i < n; ++i) dispatch[i] = (int32_t)(keys[(size_t)i] & 0xFFFFFFFFu);
+    return tokens;
+  }, dispatch);
+  return (int32_t)n;
+}
+
+int32_t paged_attention_multi_query_plan(const int32_t *context_lens,
+                                         const int32_t *prefix_groups, int32_t num_groups,
+                                         const int32_t *shared_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size,
+                                         int32_t max_blocks_per_seq, int32_t max_query_len,
+                                         int32_t max_context_len, int32_t kv_dtype,
+                                         int32_t partition_size, int32_t *dispatch,
+                                         int32_t capacity) {
+  if (!known_pool_dtype(kv_dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0 || num_groups < 0 ||
+      num_groups > num_seqs || num_q_heads % num_kv_heads != 0)
+    return PA_ERR_SHAPE;
+  if (!is_pow2(block_size) || block_size > 1024) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks_per_seq * block_size > kMaxTokensPerSeq) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return 0;
+  const bool pfx = mq_prefix_path(kv_dtype, head_dim, num_q_heads, num_kv_heads, max_query_len,
+                                  num_groups);
+  const int32_t ng = pfx ? num_groups : 0;
+  if (!context_lens || !dispatch || (ng > 0 && (!prefix_groups || !shared_lens)))
+    return PA_ERR_NULL;
+  int32_t ps = 0;
+  const int32_t P = resolve_mq_partitions(num_seqs, num_q_heads, num_kv_heads, max_query_len,
+                                          max_context_len, partition_size, &ps);
+  if (P < 0) return P;
+  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+  if (P <= 1) ps = (int32_t)cap;  // one partition spans any clamped context
+  const int64_t ipg =
+      ng > 0 ? pa::mq_prefix_items_per_group(max_query_len, num_q_heads / num_kv_heads) : 0;
+  const int64_t n = (int64_t)num_seqs * P + ipg * ng;
+  if (n >= (int64_t(1) << 31) || capacity < n) return PA_ERR_SHAPE;
+  // the multi-query kernels' clamps and item bounds, as the device sort takes
+  // them: a sequence item by its private positions in its partition, a
+  // prefix item by its group's longest shared length
+  auto L_of = [&](int32_t s) {
+    return (int32_t)std::min<int64_t>(std::max(context_lens[s], 0), cap);
+  };
+  auto shared_of = [&](int32_t s, int32_t L) {
+    return ng > 0 ? (std::min(std::max(shared_lens[s], 0), L) & ~15) : 0;
+  };
+  plan_longest_first(n, [&](int64_t c) -> int64_t {
+    if (c < (int64_t)num_seqs * P) {
+      const int32_t s = (int32_t)(c % num_seqs);
+      const int32_t p = (P - 1) - (int32_t)(c / num_seqs);
+      const int32_t L = L_of(s);
+      const int32_t nparts = std::min((int32_t)(((int64_t)L + ps - 1) / ps), P);
+      const int32_t sh = shared_of(s, L);
+      if (p >= std::max(nparts, 1) || (sh > 0 && p < sh / ps)) return -1;
+      return std::max<int64_t>(
+          0, std::min<int64_t>(L, (int64_t)p * ps + ps) - std::max<int64_t>((int64_t)p * ps, sh));
+    }
+    const int64_t gi = (c - (int64_t)num_seqs * P) / ipg;
+    const int32_t first = std::min(std::max(prefix_groups[2 * gi], 0), num_seqs - 1);
+    const int32_t count = std::min(std::max(prefix_groups[2 * gi + 1], 0),
+                                   std::min(num_seqs - first, pa::kMqPrefixMembers));
+    int64_t longest = 0;
+    for (int32_t m = 0; m < count; ++m)
+      longest = std::max<int64_t>(longest, shared_of(first + m, L_of(first + m)));
+    return longest > 0 ? longest : -1;
+  }, dispatch);
   return (int32_t)n;
 }
 
@@ -608,7 +689,8 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
                          int32_t max_context_len, int32_t dtype, int32_t kv_dtype, float k_scale,
                          float v_scale, int32_t partition_size, void *workspace,
                          size_t workspace_bytes, void *stream, const int32_t *groups = nullptr,
-                         int32_t num_groups = 0, const int32_t *shared_lens = nullptr) {
+                         int32_t num_groups = 0, const int32_t *shared_lens = nullptr,
+                         const int32_t *dispatch = nullptr) {
   if (!known_dtype(dtype)) return PA_ERR_DTYPE;
   if (num_groups < 0 || num_groups > std::max(num_seqs, 0)) return PA_ERR_SHAPE;
   if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
@@ -690,9 +772,14 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
   a.groups = groups;
   a.shared_lens = shared_lens;
   a.num_groups = num_groups;
-  // with room for it, the longest-first list; else the fixed order
-  if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order)
+  // a list the caller planned; else, with room for it, the longest-first
+  // list sorted on the device; else the fixed order
+  if (dispatch) {
+    a.order = const_cast<int32_t *>(dispatch);
+    a.order_ready = true;
+  } else if (w.order > 0 && workspace && workspace_bytes >= w.partials + w.order) {
     a.order = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) + w.partials);
+  }
   if (pa::index_check_on()) {
     const hipStream_t st_stream = static_cast<hipStream_t>(stream);
     int32_t st = pa::check_tables(context_lens, block_tables, num_seqs, max_blocks_per_seq,
@@ -704,6 +791,13 @@ int32_t multi_query_impl(const void *q, const void *k_cache, const void *v_cache
       st = pa::check_prefix_groups(context_lens, block_tables, groups, num_groups, shared_lens,
                                    num_seqs, max_blocks_per_seq, a.log2_block_size,
                                    max_context_len, pa::kMqPrefixMembers, st_stream);
+    if (st == PA_OK && dispatch)
+      st = pa::check_dispatch(
+          dispatch,
+          (int32_t)((int64_t)num_seqs * P +
+                    (num_groups > 0 ? pa::mq_prefix_items_per_group(max_query_len, G) : 0) *
+                        num_groups),
+          st_stream);
     if (st != PA_OK) return st;
   }
   const hipError_t e = pa::launch_multi_query(a, static_cast<hipStream_t>(stream));
@@ -800,11 +894,12 @@ int32_t paged_attention_multi_query_int8(const void *q, const void *k_cache, con
 int32_t paged_attention_multi_query_prefix(
     const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
     const int32_t *context_lens, const int32_t *query_start, const int32_t *prefix_groups,
-    int32_t num_groups, const int32_t *shared_lens, float scale, float k_scale, float v_scale,
-    float *out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
-    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-    int32_t max_query_len, int32_t max_context_len, int32_t kv_dtype, int32_t partition_size,
-    void *workspace, size_t workspace_bytes, void *stream) {
+    int32_t num_groups, const int32_t *shared_lens, const int32_t *dispatch, float scale,
+    float k_scale, float v_scale, float *out, int32_t num_seqs, int32_t num_tokens,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+    int32_t max_context_len, int32_t kv_dtype, int32_t partition_size, void *workspace,
+    size_t workspace_bytes, void *stream) {
   if (!known_pool_dtype(kv_dtype)) return PA_ERR_DTYPE;
   if (num_groups < 0) return PA_ERR_SHAPE;
   const bool pfx = mq_prefix_path(kv_dtype, head_dim, num_q_heads, num_kv_heads, max_query_len,
@@ -816,7 +911,7 @@ int32_t paged_attention_multi_query_prefix(
                           max_context_len, q8 ? PA_BF16 : kv_dtype, kv_dtype,
                           q8 ? k_scale : 1.f, q8 ? v_scale : 1.f, partition_size, workspace,
                           workspace_bytes, stream, pfx ? prefix_groups : nullptr,
-                          pfx ? num_groups : 0, pfx ? shared_lens : nullptr);
+                          pfx ? num_groups : 0, pfx ? shared_lens : nullptr, dispatch);
 }
 
 size_t paged_attention_multi_query_prefix_workspace_size(

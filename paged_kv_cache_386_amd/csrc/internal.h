@@ -104,6 +104,7 @@ struct MultiQueryArgs {
   float *ws_o;             // [num_tokens][Hq][P][D] (P > 1 only)
   float *ws_ml;            // [num_tokens][Hq][P][2]
   int32_t *order = nullptr;  // [S * P] longest-first (sequence, partition) list, or nullptr
+  bool order_ready = false;  // order was planned by the caller: no sort kernel
   int32_t kv_dtype = -1;     // 2 = FP8 E4M3, 3 = INT8 pool (decode walk only); -1 = dtype
   float k_scale = 1.f;       // 8-bit pools: stored code c means value(c) * scale
   float v_scale = 1.f;

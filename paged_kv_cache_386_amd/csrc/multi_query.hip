@@ -157,7 +157,9 @@ __global__ __launch_bounds__(kThreads, 2) void paged_multi_query_kernel(
   const int kvh = r % hkv;
   const int num_seqs = units / (hkv * P);
   const int item = order ? order[r / hkv] : r / hkv;
-  if (item < 0) return;  // listed as empty (past the sequence's end)
+  // listed as empty (past the sequence's end), or not an item of this launch
+  // (a list the caller planned is trusted only this far)
+  if (item < 0 || item >= units / hkv) return;
   const int s = item % num_seqs;
   const int part = (P - 1) - item / num_seqs;
   const int hq = hkv * G;
@@ -756,7 +758,7 @@ int64_t multi_query_workgroups(int64_t num_seqs, int64_t num_q_heads, int64_t nu
 }
 
 hipError_t launch_multi_query(const MultiQueryArgs &a, hipStream_t stream) {
-  if (a.order) {
+  if (a.order && !a.order_ready) {
     const int cap = (int)std::min<int64_t>((int64_t)a.max_blocks_per_seq << a.log2_block_size,
                                            INT32_MAX);
     const bool pfx = a.num_groups > 0;

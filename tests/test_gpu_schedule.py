@@ -256,6 +256,21 @@ def test_multi_query_prefix_list(ps):
         if nbytes == full:
             listed = ws[partial:].cpu().numpy().view(np.int32).copy()
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    # the list planned on the host: the same outputs, bit for bit
+    plan = pa.multi_query_plan(base.context_lens, g, sh, num_q_heads=Hq, num_kv_heads=Hkv,
+                               head_dim=D, block_size=base.block_size,
+                               max_blocks_per_seq=base.block_tables.shape[1],
+                               max_query_len=max_q, max_context_len=max_ctx,
+                               kv_dtype=pa.PA_BF16, partition_size=ps)
+    assert len(plan) == n_items
+    out.fill_(float("nan"))
+    pa.paged_attention_multi_query_prefix(*args, out, max_query_len=max_q, max_context_len=max_ctx,
+                                          partition_size=ps,
+                                          workspace=torch.empty(partial, dtype=torch.uint8,
+                                                                device="cuda"),
+                                          dispatch=torch.from_numpy(plan).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), outs[0].view(np.uint32))
     ref = O.paged_attention_multi_query(c.q, base.k_cache, base.v_cache, base.block_tables,
                                         base.context_lens, c.query_start, base.scale,
                                         base.block_size, base.dtype)
@@ -291,3 +306,66 @@ def test_multi_query_prefix_list(ps):
     key = np.array(key)
     assert (np.diff(key) <= 0).all(), "not longest first"
     assert np.array_equal(listed < 0, key < 0), "empty items are the negative entries"
+
+
+@pytest.mark.parametrize("S,G,Hkv,max_q,ps", [
+    (160, 4, 8, 5, 256),    # decode walk, split
+    (80, 4, 8, 40, 0),      # row tiles
+    (40, 2, 8, 64, 128),    # row tiles, split
+])
+def test_multi_query_planned_list(S, G, Hkv, max_q, ps):
+    """A list planned on the host (paged_attention_multi_query_plan, passed
+    through the prefix entry with no groups) gives the device-sorted call's
+    outputs bit for bit; a list holding an entry outside the launch skips it
+    (that item's rows keep what they held)."""
+    import paged_kv_cache_386_amd as pa
+    from workloads import make_multi_query_case
+    lens = np.maximum(_mixed_lengths(S, 51 + max_q, 1100), max_q)
+    rng = np.random.default_rng(max_q + 7)
+    q_lens = rng.integers(0, max_q + 1, size=S)
+    q_lens[:2] = [max_q, 1]
+    base = make_private_case("schedule-mq-plan", lens, G * Hkv, Hkv, 128, 16, "bf16", 12)
+    c = make_multi_query_case(base, q_lens, 12)
+    T, Hq, D = c.num_tokens, base.num_q_heads, base.head_dim
+    max_ctx = int(base.context_lens.max())
+    say(f"schedule mq plan: S={S} G={G} Hkv={Hkv} max_q={max_q} ps={ps}")
+    args = [to_torch(c.q, "bf16"), to_torch(base.k_cache, "bf16"), to_torch(base.v_cache, "bf16"),
+            torch.from_numpy(base.block_tables).cuda(), torch.from_numpy(base.context_lens).cuda(),
+            torch.from_numpy(c.query_start).cuda()]
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device="cuda")
+    out.fill_(float("nan"))
+    pa.paged_attention_multi_query(*args, float(base.scale), out, max_query_len=max_q,
+                                   max_context_len=max_ctx, partition_size=ps)
+    torch.cuda.synchronize()
+    sorted_out = out.cpu().numpy()
+    plan = pa.multi_query_plan(base.context_lens, None, None, num_q_heads=Hq, num_kv_heads=Hkv,
+                               head_dim=D, block_size=16,
+                               max_blocks_per_seq=base.block_tables.shape[1],
+                               max_query_len=max_q, max_context_len=max_ctx,
+                               kv_dtype=pa.PA_BF16, partition_size=ps)
+    P = pa.multi_query_partitions(S, Hq, Hkv, max_q, max_ctx, ps)
+    assert np.array_equal(np.sort(plan), np.arange(S * P))
+    out.fill_(float("nan"))
+    pa.paged_attention_multi_query_prefix(*args, None, None, float(base.scale), out,
+                                          max_query_len=max_q, max_context_len=max_ctx,
+                                          partition_size=ps,
+                                          dispatch=torch.from_numpy(plan).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), sorted_out.view(np.uint32))
+    # sequence 0's items replaced by an entry past the launch: its rows are
+    # left as they were, every other row is the same
+    P0 = [i for i, e in enumerate(plan.tolist()) if e % S == 0]
+    bad = plan.copy()
+    bad[P0] = S * P + 5
+    out.fill_(7.0)
+    pa.paged_attention_multi_query_prefix(*args, None, None, float(base.scale), out,
+                                          max_query_len=max_q, max_context_len=max_ctx,
+                                          partition_size=ps,
+                                          dispatch=torch.from_numpy(bad).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    r0 = slice(int(c.query_start[0]), int(c.query_start[1]))
+    rest = slice(int(c.query_start[1]), T)
+    if P == 1:
+        assert (got[r0] == 7.0).all()
+    assert np.array_equal(got[rest].view(np.uint32), sorted_out[rest].view(np.uint32))
